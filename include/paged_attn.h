@@ -1,0 +1,204 @@
+/*
+ * paged_attn.h -- C ABI of the MI355X (gfx950) paged-attention library.
+ *
+ * The library computes attention of a few new query rows against a long,
+ * growing KV cache that is stored in fixed-size pages and addressed through
+ * a block table:
+ *
+ *     out[t, h, :] = sum_j softmax_j(scale * q[t, h, :] . k~[g, j, :]) v~[g, j, :]
+ *     lse[t, h]    = ln sum_j exp(scale * q[t, h, :] . k~[g, j, :])
+ *
+ * over the keys j that row t may see, with query head h reading KV head
+ * g = h / (Hq / Hkv) (grouped-query attention: several query heads share each
+ * KV head, "Dual MI50, part 2", section "Decode: a new kernel for the shape
+ * MTP actually runs").  k~, v~ are the cached values after dequantisation.
+ *
+ * Positions.  A sequence's seq_len counts every cached token including its
+ * q_len new ones; the new tokens' keys and values are already in the cache
+ * as its last q_len entries, and new row i sits at position
+ * p_i = seq_len - q_len + i.  Row i sees key j iff j <= p_i (causal inside
+ * the new rows: speculative verification scores k+1 tokens in one pass,
+ * "Dual MI50, part 2", section "Kernels: why the generic code is slow here")
+ * and, when window W >= 1, j >= p_i - W + 1 (the W most recent keys, the
+ * drafter's sliding window of "Dual MI50, part 2", section "Bug 2: the
+ * drafter read freed memory").  Pages whose tokens all lie before the first
+ * row's window, slots past seq_len and unused block-table entries are never
+ * read, so their contents (freed and reused pages, NaN) cannot reach the
+ * output.
+ *
+ * The cache is read in place, with no copies ("Dual MI50, part 2", section
+ * "Prefill: teach the fork's fast kernel to read the int8 cache"), and
+ * forward allocates nothing and never waits on the host, so it can be
+ * captured in a HIP graph ("Dual MI50, part 2", section "Decode: a new
+ * kernel for the shape MTP actually runs").
+ *
+ * Conventions shared by every entry point:
+ *   - return value: PA_OK (0) or a PA_ERR_* code; paged_attn_last_error()
+ *     gives a message.  Nothing is launched when an argument is rejected.
+ *   - pointers named "device" must be device memory of the handle's GPU;
+ *     "host" pointers are read before the call returns.
+ *   - the caller owns every tensor and the stream; the handle owns only its
+ *     device workspace.
+ *   - all work is enqueued on `stream` (a hipStream_t, NULL = default
+ *     stream); results are visible once the stream reaches that point.
+ *   - a handle may be used by one stream at a time (its workspace is shared
+ *     between calls); use one handle per concurrent stream.
+ */
+#ifndef PAGED_ATTN_H
+#define PAGED_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define PA_OK                    0
+#define PA_ERR_INVALID_ARGUMENT  1
+#define PA_ERR_UNSUPPORTED       2
+#define PA_ERR_OUT_OF_MEMORY     3
+#define PA_ERR_HIP               4
+
+/* element types */
+#define PA_DTYPE_F16       1   /* IEEE binary16 */
+#define PA_DTYPE_BF16      2   /* bfloat16 */
+#define PA_DTYPE_FP8_E4M3  3   /* OCP E4M3FN: bias 7, max 448, no inf, S.1111.111 = NaN */
+
+/* execution paths (pa_tuning_t.path) */
+#define PA_PATH_AUTO   0   /* VALU split-KV kernel for rows-per-KV-head <= 8, MFMA tile kernel above */
+#define PA_PATH_VALU   1   /* every sequence through the VALU split-KV kernel */
+#define PA_PATH_MFMA   2   /* every sequence through the MFMA tile kernel */
+
+typedef struct pa_config {
+    int32_t num_q_heads;     /* Hq >= 1 */
+    int32_t num_kv_heads;    /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 16 */
+    int32_t head_dim;        /* D: 64 or 128 */
+    int32_t page_size;       /* P: tokens per page; 16 */
+    int32_t q_dtype;         /* PA_DTYPE_F16 or PA_DTYPE_BF16 */
+    int32_t kv_dtype;        /* PA_DTYPE_F16, PA_DTYPE_BF16 (== q_dtype) or PA_DTYPE_FP8_E4M3 */
+    int32_t max_num_seqs;    /* largest num_seqs passed to forward, 1..1024 */
+    int32_t max_q_len;       /* largest q_len of any sequence, >= 1 */
+    int64_t max_num_tokens;  /* largest T = sum of q_lens, >= 1 */
+    int32_t device;          /* HIP device ordinal the handle runs on */
+    int32_t flags;           /* reserved, must be 0 */
+} pa_config_t;
+
+/* Physical layout of the K and V page pools (identical for both).  Strides
+ * are in elements.  Within a token the D elements are contiguous; a token
+ * row must start on a 16-byte boundary.  The default (HND) layout
+ * [num_pages][Hkv][P][D] has page_stride = Hkv*P*D, head_stride = P*D,
+ * token_stride = D, so each (page, head) block is one contiguous run. */
+typedef struct pa_cache_layout {
+    int64_t num_pages;
+    int64_t page_stride;
+    int64_t head_stride;
+    int64_t token_stride;
+} pa_cache_layout_t;
+
+/* Optional knobs, mainly for tests and measurement.  Zero means automatic. */
+typedef struct pa_tuning {
+    int32_t path;             /* PA_PATH_* */
+    int32_t pages_per_split;  /* VALU kernel: KV pages per split (0: sized from the live context) */
+    int32_t kv_tiles_per_split; /* MFMA kernel: 64-key tiles per split (0: automatic) */
+    int32_t grid;             /* workgroups per launch (0: from the CU count) */
+} pa_tuning_t;
+
+typedef struct pa_handle pa_handle_t;
+
+/*
+ * paged_attn_create: validate `cfg`, allocate the device workspace on
+ * cfg->device (split partials and merge counters, sized from the maxima in
+ * cfg) and return a handle in *out.  Returns PA_ERR_INVALID_ARGUMENT or
+ * PA_ERR_UNSUPPORTED (with *out left NULL) for a bad or unsupported config,
+ * PA_ERR_OUT_OF_MEMORY if the workspace cannot be allocated, PA_ERR_HIP for
+ * other runtime failures.  May synchronise the device once (workspace
+ * clearing); forward never does.
+ */
+int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out);
+
+/*
+ * paged_attn_forward: enqueue attention of every sequence's new rows.
+ *
+ *  q            device, [T][Hq][D] of cfg.q_dtype, rows packed by sequence
+ *               (sequence b's q_len rows follow sequence b-1's); 16-B aligned.
+ *  num_tokens   host int: T = sum of q_lens (1..cfg.max_num_tokens).
+ *  k_cache,     device page pools of cfg.kv_dtype laid out per `layout`;
+ *  v_cache      16-B aligned.
+ *  layout       host, see pa_cache_layout_t.
+ *  block_table  device int32 [num_seqs][block_table_stride]: entry
+ *               [b][i] is the physical page holding tokens i*P .. i*P+P-1
+ *               of sequence b; entries past the sequence's last page are
+ *               never read.
+ *  num_seqs     host int, 1..cfg.max_num_seqs.
+ *  seq_lens     device int32 [num_seqs]: cached tokens incl. the new ones.
+ *  q_lens       device int32 [num_seqs]: new rows, 0 <= q_len <= min(seq_len,
+ *               cfg.max_q_len); sum must equal num_tokens.
+ *  window       host int: <= 0 no window; W >= 1 the W most recent keys.
+ *  scale        host float: multiplies q.k (after dequantisation).
+ *  kv_scale     device float [2][Hkv] (K scales, then V scales) for an fp8
+ *               cache: k~ = code * kv_scale[0][g], v~ = code * kv_scale[1][g].
+ *               Must be NULL for fp16/bf16 caches.
+ *  out          device float [T][Hq][D].
+ *  lse          device float [T][Hq] (natural log), or NULL.
+ *  stream       hipStream_t or NULL.
+ *
+ * Device-array contents (block table, lengths) are trusted: they are not
+ * read on the host.  Violating the documented ranges is undefined.
+ * Returns PA_ERR_INVALID_ARGUMENT for a rejected host argument (null or
+ * misaligned pointer, size out of range, scale not finite, kv_scale given
+ * or missing), PA_ERR_HIP if the launch fails.
+ */
+int paged_attn_forward(pa_handle_t* h,
+                       const void* q, int64_t num_tokens,
+                       const void* k_cache, const void* v_cache,
+                       const pa_cache_layout_t* layout,
+                       const int32_t* block_table, int32_t num_seqs, int32_t block_table_stride,
+                       const int32_t* seq_lens, const int32_t* q_lens,
+                       int32_t window, float scale, const float* kv_scale,
+                       float* out, float* lse, void* stream);
+
+/* paged_attn_destroy: free the workspace and the handle (NULL is a no-op).
+ * Does not synchronise: the caller must make sure no enqueued forward on the
+ * handle is still running. */
+void paged_attn_destroy(pa_handle_t* h);
+
+/* paged_attn_last_error: message of the last failed call on `h` (or of the
+ * last failed create / handle-less call on this thread when h is NULL);
+ * "" if none.  Valid until the next call on the same handle / thread. */
+const char* paged_attn_last_error(const pa_handle_t* h);
+
+/* paged_attn_set_tuning: replace the handle's knobs (NULL restores the
+ * defaults).  Results stay within the stated tolerances for every setting;
+ * only speed and the summation order change. */
+int paged_attn_set_tuning(pa_handle_t* h, const pa_tuning_t* t);
+
+/*
+ * paged_attn_debug_gather: de-page K through the same address computation
+ * the attention kernels use.  For every sequence b and every token j of its
+ * visible range [lo_b, seq_len_b) (lo_b = max(0, seq_len_b - q_len_b - W + 1)
+ * when window W >= 1, else 0), in order of b then j, it writes the token's
+ * physical slot index (page * P + slot) to slots_out and the raw bytes of
+ * its Hkv x D elements (KV head major) to rows_out.  Sequences with
+ * q_len == 0 contribute nothing.
+ *
+ *  slots_out   device int64 [n_visible]
+ *  rows_out    device bytes [n_visible][Hkv][D * element size]
+ *  capacity    host int: entries slots_out / rows_out can hold; tokens past
+ *              it are not written.
+ *  Other arguments as in paged_attn_forward.
+ */
+int paged_attn_debug_gather(pa_handle_t* h,
+                            const void* k_cache, const pa_cache_layout_t* layout,
+                            const int32_t* block_table, int32_t num_seqs, int32_t block_table_stride,
+                            const int32_t* seq_lens, const int32_t* q_lens, int32_t window,
+                            int64_t* slots_out, void* rows_out, int64_t capacity, void* stream);
+
+/* paged_attn_version: library version, e.g. "0.1.0". */
+const char* paged_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTN_H */

@@ -1,0 +1,273 @@
+// Device-side building blocks shared by the paged-attention kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "paged_attn.h"
+
+#define PA_DEVINLINE __device__ __forceinline__
+
+namespace pa {
+
+constexpr int kMaxSeqs = 1024;          // largest num_seqs a handle accepts
+constexpr int kWave = 64;               // CDNA wavefront width
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// ----------------------------------------------------------------- loads
+
+// 16-byte global load (global_load_dwordx4); p must be 16-B aligned.
+PA_DEVINLINE u32x4_t load_b128(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+PA_DEVINLINE u32x4_t load_b128_cached(const void* p) {
+    return *reinterpret_cast<const u32x4_t*>(p);
+}
+PA_DEVINLINE u32x2_t load_b64(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(p));
+}
+
+// ----------------------------------------------------------------- conversions
+
+PA_DEVINLINE float bf16lo_to_f32(uint32_t u) { return __uint_as_float(u << 16); }
+PA_DEVINLINE float bf16hi_to_f32(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+PA_DEVINLINE f32x2_t f16x2_to_f32(uint32_t u) {
+    f16x2_t h = __builtin_bit_cast(f16x2_t, u);
+    return f32x2_t{(float)h.x, (float)h.y};
+}
+
+// Two OCP E4M3FN bytes (low or high half of u) -> two floats, exact.
+PA_DEVINLINE f32x2_t fp8x2_to_f32(uint32_t u, bool hi) {
+    return hi ? __builtin_amdgcn_cvt_pk_f32_fp8(u, true) : __builtin_amdgcn_cvt_pk_f32_fp8(u, false);
+}
+
+// Exact narrowing of two floats that are representable in bf16 / f16.
+PA_DEVINLINE uint32_t f32x2_to_bf16x2(f32x2_t f) {
+    bf16x2_t b = {(__bf16)f.x, (__bf16)f.y};
+    return __builtin_bit_cast(uint32_t, b);
+}
+PA_DEVINLINE uint32_t f32x2_to_f16x2(f32x2_t f) {
+    f16x2_t h = {(_Float16)f.x, (_Float16)f.y};
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+// Dot product of two packed pairs, accumulated in fp32 (v_dot2_f32_{bf16,f16}).
+template <int QT>
+PA_DEVINLINE float dot2(uint32_t a, uint32_t b, float c);
+template <>
+PA_DEVINLINE float dot2<PA_DTYPE_BF16>(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
+template <>
+PA_DEVINLINE float dot2<PA_DTYPE_F16>(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+// ----------------------------------------------------------------- cross-lane
+
+// DPP controls (GFX9 encoding).
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // reverse within each 8-lane half row
+constexpr int kDppRowMirror = 0x140;    // reverse within each 16-lane row
+
+template <int CTRL>
+PA_DEVINLINE float dpp(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// All-reduce over aligned groups of N lanes (N = 8 or 16) inside a row.
+template <int N>
+PA_DEVINLINE float group_sum(float x) {
+    static_assert(N == 8 || N == 16, "group size");
+    x += dpp<kDppQuadXor1>(x);
+    x += dpp<kDppQuadXor2>(x);
+    x += dpp<kDppHalfMirror>(x);
+    if constexpr (N == 16) x += dpp<kDppRowMirror>(x);
+    return x;
+}
+
+PA_DEVINLINE float shfl_xor(float x, int m) { return __shfl_xor(x, m, kWave); }
+
+PA_DEVINLINE bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
+PA_DEVINLINE int wave_inclusive_scan(int x) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        int y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+PA_DEVINLINE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+PA_DEVINLINE float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// ----------------------------------------------------------------- positions
+
+// Visible key range of the new rows of one sequence: [lo, seq_len).
+PA_DEVINLINE int seq_visible_lo(int seq_len, int q_len, int window) {
+    return window > 0 ? max(0, seq_len - q_len - window + 1) : 0;
+}
+
+// Element offset of token slot `slot` of KV head g in physical page `page`.
+PA_DEVINLINE int64_t kv_offset(int64_t page, int g, int slot, int64_t page_stride, int64_t head_stride,
+                               int64_t token_stride) {
+    return page * page_stride + (int64_t)g * head_stride + (int64_t)slot * token_stride;
+}
+
+// ----------------------------------------------------------------- split plan
+
+// Work items of one launch, computed identically by every workgroup from the
+// device-resident lengths (no host round trip).  A sequence belongs to the
+// launch if its rows-per-KV-head count q_len*G lies in [rows_lo, rows_hi].
+// Its visible pages are cut into splits of `pps` pages; an item is one
+// (sequence, KV head, split).
+struct Plan {
+    int pps;        // pages per split
+    int n_items;
+    int item_base[kMaxSeqs + 1];  // items before sequence b (exclusive scan), [num_seqs] = n_items
+    int q_off[kMaxSeqs + 1];      // first query row of sequence b
+    int red[16];
+};
+
+struct SeqInfo {
+    int seq_len, q_len, q_off, lo, first_page, n_pages, splits;
+};
+
+PA_DEVINLINE SeqInfo seq_info(const Plan& pl, const int32_t* seq_lens, const int32_t* q_lens, int b, int window,
+                              int page_size) {
+    SeqInfo s;
+    s.seq_len = seq_lens[b];
+    s.q_len = q_lens[b];
+    s.q_off = pl.q_off[b];
+    s.lo = seq_visible_lo(s.seq_len, s.q_len, window);
+    s.first_page = s.lo / page_size;
+    s.n_pages = s.q_len > 0 ? (s.seq_len - 1) / page_size - s.first_page + 1 : 0;
+    s.splits = (s.n_pages + pl.pps - 1) / pl.pps;
+    return s;
+}
+
+// Build the plan in LDS.  Must be called by all threads of the block
+// (blockDim.x a multiple of 64, <= 1024).
+PA_DEVINLINE void build_plan(Plan& pl, const int32_t* seq_lens, const int32_t* q_lens, int num_seqs, int window,
+                             int page_size, int group, int num_kv_heads, int rows_lo, int rows_hi,
+                             int target_items, int min_pps, int forced_pps, int max_items) {
+    const int tid = threadIdx.x;
+    const int nthr = blockDim.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const int nwaves = nthr / kWave;
+    // pass 1: q_len prefix (all sequences) and in-class page-head total
+    long long pages_total = 0;
+    int carry_q = 0;
+    for (int b0 = 0; b0 < num_seqs; b0 += nthr) {
+        int b = b0 + tid;
+        int ql = 0, np = 0;
+        if (b < num_seqs) {
+            int sl = seq_lens[b];
+            ql = q_lens[b];
+            int rows = ql * group;
+            if (ql > 0 && rows >= rows_lo && rows <= rows_hi) {
+                int lo = seq_visible_lo(sl, ql, window);
+                np = (sl - 1) / page_size - lo / page_size + 1;
+            }
+        }
+        // block exclusive scan of ql
+        int inc = wave_inclusive_scan(ql);
+        if (lane == kWave - 1) pl.red[wid] = inc;
+        __syncthreads();
+        int wave_off = 0, chunk_tot = 0;
+        for (int w = 0; w < nwaves; ++w) {
+            int v = pl.red[w];
+            if (w < wid) wave_off += v;
+            chunk_tot += v;
+        }
+        if (b < num_seqs) pl.q_off[b] = carry_q + wave_off + inc - ql;
+        carry_q += chunk_tot;
+        __syncthreads();
+        // page-heads of this chunk
+        int npw = np;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) npw += __shfl_xor(npw, o, kWave);
+        if (lane == 0) pl.red[wid] = npw;
+        __syncthreads();
+        for (int w = 0; w < nwaves; ++w) pages_total += pl.red[w];
+        __syncthreads();
+    }
+    pages_total *= num_kv_heads;
+    int pps;
+    if (forced_pps > 0) {
+        pps = forced_pps;
+    } else {
+        long long t = target_items > 0 ? target_items : 1;
+        pps = (int)((pages_total + t - 1) / t);
+        pps = max(pps, min_pps);
+    }
+    // keep the item count within the workspace: items <= pages_total/pps + seqs*Hkv
+    {
+        long long cap = (long long)max_items - (long long)num_seqs * num_kv_heads;
+        if (cap < 1) cap = 1;
+        long long need = (pages_total + cap - 1) / cap;
+        if (pps < need) pps = (int)need;
+        if (pps < 1) pps = 1;
+    }
+    // pass 2: items per sequence, exclusive scan
+    int carry_i = 0;
+    for (int b0 = 0; b0 < num_seqs; b0 += nthr) {
+        int b = b0 + tid;
+        int it = 0;
+        if (b < num_seqs) {
+            int sl = seq_lens[b];
+            int ql = q_lens[b];
+            int rows = ql * group;
+            if (ql > 0 && rows >= rows_lo && rows <= rows_hi) {
+                int lo = seq_visible_lo(sl, ql, window);
+                int np = (sl - 1) / page_size - lo / page_size + 1;
+                it = ((np + pps - 1) / pps) * num_kv_heads;
+            }
+        }
+        int inc = wave_inclusive_scan(it);
+        if (lane == kWave - 1) pl.red[wid] = inc;
+        __syncthreads();
+        int wave_off = 0, chunk_tot = 0;
+        for (int w = 0; w < nwaves; ++w) {
+            int v = pl.red[w];
+            if (w < wid) wave_off += v;
+            chunk_tot += v;
+        }
+        if (b < num_seqs) pl.item_base[b] = carry_i + wave_off + inc - it;
+        carry_i += chunk_tot;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        pl.item_base[num_seqs] = carry_i;
+        pl.q_off[num_seqs] = carry_q;
+        pl.n_items = carry_i;
+        pl.pps = pps;
+    }
+    __syncthreads();
+}
+
+// Sequence owning item `it` (largest b with item_base[b] <= it).
+PA_DEVINLINE int item_seq(const Plan& pl, int num_seqs, int it) {
+    int lo = 0, hi = num_seqs - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (pl.item_base[mid] <= it) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace pa

@@ -1,0 +1,360 @@
+// Split-KV decode / verify kernel on the vector ALUs (gfx950).
+//
+// Shape: a few query rows per KV head (decode: the G query heads of one
+// token; verify: q_len tokens x G heads) against a long paged context.  The
+// work is bound by reading K and V once from HBM, so the kernel is built
+// around the loads:
+//   * one lane owns 8 consecutive head-dim elements of one token (16 B of an
+//     fp16/bf16 row, 8 B of fp8), so D/8 lanes cover a token row and a
+//     wavefront reads 64/(D/8) whole token rows per round; a 16-token page of
+//     one KV head is one contiguous run in the HND layout, read with
+//     128-bit loads;
+//   * every key is converted once and scored against every row the wave
+//     holds (the pages' decode kernel did the same: "Dual MI50, part 2",
+//     section "Decode: a new kernel for the shape MTP actually runs");
+//     scores use the packed dot instruction (v_dot2_f32_{bf16,f16}) with an
+//     fp32 accumulator and a DPP all-reduce over the D/8 lanes of a token;
+//   * each lane keeps its own online-softmax state (running max m, sum l,
+//     fp32 accumulator) for the tokens it sees, so no cross-lane reduction
+//     runs per page; the max is raised lazily, only when a score exceeds it
+//     by more than 2^8 (exact in real arithmetic, fp32 has the range);
+//   * masked keys are excluded by select, never multiplied by zero, and the
+//     V of a token outside [lo, seq_len) is zeroed before use, so NaN in
+//     freed pages, tail slots or padding cannot leak ("Dual MI50, part 2",
+//     section "Bug 2: the drafter read freed memory");
+//   * the context of each (sequence, KV head) is split across workgroups
+//     sized from the live lengths, and the last workgroup to finish merges
+//     the partials with a log-sum-exp merge (pa_merge.h).
+#include "pa_common.h"
+#include "pa_merge.h"
+#include "pa_kernels.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kPage = 16;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr float kTau = 8.0f;   // lazy max: rescale only when a score exceeds m by 2^8
+
+template <int KVT>
+struct KvChunk;
+template <>
+struct KvChunk<PA_DTYPE_F16> { using T = u32x4_t; static constexpr int bytes = 2; };
+template <>
+struct KvChunk<PA_DTYPE_BF16> { using T = u32x4_t; static constexpr int bytes = 2; };
+template <>
+struct KvChunk<PA_DTYPE_FP8_E4M3> { using T = u32x2_t; static constexpr int bytes = 1; };
+
+template <int KVT>
+PA_DEVINLINE typename KvChunk<KVT>::T load_chunk(const uint8_t* p) {
+    if constexpr (KVT == PA_DTYPE_FP8_E4M3) return load_b64(p);
+    else return load_b128(p);
+}
+
+// Eight K elements -> four packed pairs in the dot-product type QT.
+template <int KVT, int QT>
+PA_DEVINLINE void k_pairs(const typename KvChunk<KVT>::T& c, uint32_t kp[4]) {
+    if constexpr (KVT == PA_DTYPE_FP8_E4M3) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const uint32_t w = c[i];
+            f32x2_t lo = fp8x2_to_f32(w, false);
+            f32x2_t hi = fp8x2_to_f32(w, true);
+            if constexpr (QT == PA_DTYPE_BF16) {
+                kp[2 * i] = f32x2_to_bf16x2(lo);
+                kp[2 * i + 1] = f32x2_to_bf16x2(hi);
+            } else {
+                kp[2 * i] = f32x2_to_f16x2(lo);
+                kp[2 * i + 1] = f32x2_to_f16x2(hi);
+            }
+        }
+    } else {
+        kp[0] = c[0]; kp[1] = c[1]; kp[2] = c[2]; kp[3] = c[3];
+    }
+}
+
+// Eight V elements -> fp32.
+template <int KVT>
+PA_DEVINLINE void v_floats(const typename KvChunk<KVT>::T& c, float v[8]) {
+    if constexpr (KVT == PA_DTYPE_FP8_E4M3) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            f32x2_t lo = fp8x2_to_f32(c[i], false);
+            f32x2_t hi = fp8x2_to_f32(c[i], true);
+            v[4 * i] = lo.x; v[4 * i + 1] = lo.y; v[4 * i + 2] = hi.x; v[4 * i + 3] = hi.y;
+        }
+    } else if constexpr (KVT == PA_DTYPE_BF16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { v[2 * i] = bf16lo_to_f32(c[i]); v[2 * i + 1] = bf16hi_to_f32(c[i]); }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { f32x2_t f = f16x2_to_f32(c[i]); v[2 * i] = f.x; v[2 * i + 1] = f.y; }
+    }
+}
+
+struct WaveShared {
+    float acc[kWaves][8][128];   // [wave][row][d] (D <= 128, RW <= 8)
+    float m[kWaves][8];
+    float l[kWaves][8];
+};
+
+struct Smem {
+    Plan plan;
+    WaveShared ws;
+    int flag;
+};
+
+template <int D, int KVT, int QT, int RW>
+__global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
+    constexpr int LPT = D / 8;            // lanes per token row
+    constexpr int TPR = kWave / LPT;      // tokens per round
+    constexpr int RPP = kPage / TPR;      // rounds per page
+    constexpr int EB = KvChunk<KVT>::bytes;
+    using Chunk = typename KvChunk<KVT>::T;
+
+    __shared__ Smem sm;
+    Plan& pl = sm.plan;
+    build_plan(pl, a.seq_lens, a.q_lens, a.num_seqs, a.window, kPage, a.group, a.num_kv_heads, a.rows_lo,
+               a.rows_hi, a.target_items, a.min_pps, a.forced_pps, a.max_items);
+    const int n_items = pl.n_items;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const int tl = lane / LPT;            // token within a round
+    const int ch = lane % LPT;            // 8-element chunk of the row
+
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k_cache);
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
+    const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q);
+    MergeTarget tgt{a.out, a.lse, a.num_q_heads, a.group, 1.0f};
+
+    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+        const int b = item_seq(pl, a.num_seqs, it);
+        const SeqInfo si = seq_info(pl, a.seq_lens, a.q_lens, b, a.window, kPage);
+        const int local = it - pl.item_base[b];
+        const int g = local / si.splits;
+        const int split = local - g * si.splits;
+        const int p_begin = si.first_page + split * pl.pps;
+        const int p_end = min(si.first_page + si.n_pages, p_begin + pl.pps);
+        const int rows = si.q_len * a.group;
+        const int n_rg = (rows + RW - 1) / RW;
+        const float kscale = (KVT == PA_DTYPE_FP8_E4M3) ? a.kv_scale[g] : 1.0f;
+        const float vscale = (KVT == PA_DTYPE_FP8_E4M3) ? a.kv_scale[a.num_kv_heads + g] : 1.0f;
+        const float s2 = a.scale * kLog2e * kscale;
+        tgt.out_scale = vscale;
+        const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
+        const bool direct = (si.splits == 1);
+
+        // passes over row groups: up to kWaves row groups at a time
+        for (int rg0 = 0; rg0 < n_rg; rg0 += kWaves) {
+            const int n_here = min(kWaves, n_rg - rg0);
+            const int wprg = kWaves / n_here;           // waves per row group
+            const int rg = rg0 + wid / wprg;
+            const int sub = wid % wprg;
+            const bool active = (wid < n_here * wprg);
+
+            float m[RW], l[RW], acc[RW][8];
+            int pos[RW], lo_r[RW];
+            uint32_t qv[RW][4];
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                m[r] = kNegInf; l[r] = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+                const int row = rg * RW + r;
+                const bool valid = active && row < rows;
+                const int i = valid ? row / a.group : 0;
+                const int h = g * a.group + (valid ? row - i * a.group : 0);
+                pos[r] = valid ? si.seq_len - si.q_len + i : -1;   // -1: sees nothing
+                lo_r[r] = (a.window > 0) ? pos[r] - a.window + 1 : 0;
+                if (valid) {
+                    const u32x4_t qq = load_b128_cached(qbase + ((int64_t)(si.q_off + i) * a.num_q_heads + h) * D + ch * 8);
+                    qv[r][0] = qq[0]; qv[r][1] = qq[1]; qv[r][2] = qq[2]; qv[r][3] = qq[3];
+                } else {
+                    qv[r][0] = qv[r][1] = qv[r][2] = qv[r][3] = 0u;
+                }
+            }
+
+            if (active) {
+                const int64_t round_off = (int64_t)TPR * a.token_stride * EB;
+                Chunk kc[RPP], vc[RPP];
+                int pg = p_begin + sub;
+                if (pg < p_end) {
+                    const int64_t off =
+                        kv_offset(bt[pg], g, tl, a.page_stride, a.head_stride, a.token_stride) * EB + ch * 8 * EB;
+#pragma unroll
+                    for (int rr = 0; rr < RPP; ++rr) {
+                        kc[rr] = load_chunk<KVT>(kbase + off + rr * round_off);
+                        vc[rr] = load_chunk<KVT>(vbase + off + rr * round_off);
+                    }
+                }
+                for (; pg < p_end; pg += wprg) {
+                    Chunk kn[RPP], vn[RPP];
+                    const int nx = pg + wprg;
+                    if (nx < p_end) {
+                        const int64_t off =
+                            kv_offset(bt[nx], g, tl, a.page_stride, a.head_stride, a.token_stride) * EB + ch * 8 * EB;
+#pragma unroll
+                        for (int rr = 0; rr < RPP; ++rr) {
+                            kn[rr] = load_chunk<KVT>(kbase + off + rr * round_off);
+                            vn[rr] = load_chunk<KVT>(vbase + off + rr * round_off);
+                        }
+                    }
+#pragma unroll
+                    for (int rr = 0; rr < RPP; ++rr) {
+                        const int j = pg * kPage + rr * TPR + tl;
+                        const bool live = (j >= si.lo) && (j < si.seq_len);
+                        uint32_t kp[4];
+                        k_pairs<KVT, QT>(kc[rr], kp);
+                        float s[RW];
+#pragma unroll
+                        for (int r = 0; r < RW; ++r) {
+                            float x = dot2<QT>(qv[r][0], kp[0], 0.f);
+                            x = dot2<QT>(qv[r][1], kp[1], x);
+                            x = dot2<QT>(qv[r][2], kp[2], x);
+                            x = dot2<QT>(qv[r][3], kp[3], x);
+                            s[r] = group_sum<LPT>(x);
+                        }
+                        bool need = false;
+#pragma unroll
+                        for (int r = 0; r < RW; ++r) {
+                            const bool vis = (j <= pos[r]) && (j >= lo_r[r]) && live;
+                            s[r] = vis ? s[r] * s2 : kNegInf;
+                            need |= s[r] > m[r] + kTau;
+                        }
+                        if (wave_any(need)) {
+#pragma unroll
+                            for (int r = 0; r < RW; ++r) {
+                                const bool nd = s[r] > m[r] + kTau;
+                                const float al = nd ? fast_exp2(m[r] - s[r]) : 1.0f;
+                                m[r] = nd ? s[r] : m[r];
+                                l[r] *= al;
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) acc[r][e] *= al;
+                            }
+                        }
+                        float v[8];
+                        v_floats<KVT>(vc[rr], v);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) v[e] = live ? v[e] : 0.f;
+#pragma unroll
+                        for (int r = 0; r < RW; ++r) {
+                            const float p = (s[r] == kNegInf) ? 0.f : fast_exp2(s[r] - m[r]);
+                            l[r] += p;
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, v[e], acc[r][e]);
+                        }
+                    }
+#pragma unroll
+                    for (int rr = 0; rr < RPP; ++rr) { kc[rr] = kn[rr]; vc[rr] = vn[rr]; }
+                }
+            }
+
+            // merge the TPR token lanes of this wave (lanes ch, ch+LPT, ...)
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                float M = m[r];
+#pragma unroll
+                for (int o = LPT; o < kWave; o <<= 1) M = fmaxf(M, shfl_xor(M, o));
+                const float al = (m[r] == kNegInf) ? 0.f : fast_exp2(m[r] - M);
+                float lr = l[r] * al;
+#pragma unroll
+                for (int o = LPT; o < kWave; o <<= 1) lr += shfl_xor(lr, o);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float x = acc[r][e] * al;
+#pragma unroll
+                    for (int o = LPT; o < kWave; o <<= 1) x += shfl_xor(x, o);
+                    acc[r][e] = x;
+                }
+                m[r] = M;
+                l[r] = lr;
+            }
+            if (active && tl == 0) {
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) sm.ws.acc[wid][r][ch * 8 + e] = acc[r][e];
+                    if (ch == 0) { sm.ws.m[wid][r] = m[r]; sm.ws.l[wid][r] = l[r]; }
+                }
+            }
+            __syncthreads();
+            // combine the waves of each row group; write final rows or split partials
+            const int rows_here = min(rows - rg0 * RW, n_here * RW);
+            for (int e = tid; e < rows_here * D; e += kThreads) {
+                const int rl = e / D;              // row within this pass
+                const int d = e - rl * D;
+                const int rgl = rl / RW;           // row group within this pass
+                const int r = rl - rgl * RW;
+                const int w0 = rgl * wprg;
+                float M = kNegInf;
+                for (int w = 0; w < wprg; ++w) M = fmaxf(M, sm.ws.m[w0 + w][r]);
+                float L = 0.f, A = 0.f;
+                if (M != kNegInf) {
+                    for (int w = 0; w < wprg; ++w) {
+                        const float mw = sm.ws.m[w0 + w][r];
+                        const float al = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+                        L = fmaf(sm.ws.l[w0 + w][r], al, L);
+                        A = fmaf(sm.ws.acc[w0 + w][r][d], al, A);
+                    }
+                }
+                const int row = rg0 * RW + rl;
+                if (direct) {
+                    const int64_t orow = out_row(tgt, si.q_off, g, row);
+                    a.out[orow * D + d] = (L > 0.f) ? A * vscale / L : 0.f;
+                    if (a.lse != nullptr && d == 0) a.lse[orow] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
+                } else {
+                    const int64_t slot = (int64_t)it * a.r_max + row;
+                    a.ws_o[slot * D + d] = (L > 0.f) ? A / L : 0.f;
+                    if (d == 0) a.ws_lse[slot] = (L > 0.f) ? M + fast_log2(L) : kNegInf;
+                }
+            }
+            __syncthreads();
+        }
+
+        if (!direct) {
+            const int64_t first_item = pl.item_base[b] + (int64_t)g * si.splits;
+            if (arrive_last(a.counters + ((int64_t)b * a.num_kv_heads + g) * a.counter_stride, si.splits, &sm.flag)) {
+                merge_splits<D>(a.ws_o, a.ws_lse, first_item, si.splits, rows, a.r_max, tgt, si.q_off, g);
+            }
+            __syncthreads();
+        }
+    }
+}
+
+}  // namespace
+
+template <int D, int KVT, int QT, int RW>
+static hipError_t launch_t(const DecodeArgs& a, int grid, hipStream_t st) {
+    hipLaunchKernelGGL((decode_valu_kernel<D, KVT, QT, RW>), dim3(grid), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int D, int KVT, int QT>
+static hipError_t launch_rw(const DecodeArgs& a, int rw, int grid, hipStream_t st) {
+    switch (rw) {
+        case 1: return launch_t<D, KVT, QT, 1>(a, grid, st);
+        case 2: return launch_t<D, KVT, QT, 2>(a, grid, st);
+        case 4: return launch_t<D, KVT, QT, 4>(a, grid, st);
+        default: return launch_t<D, KVT, QT, 8>(a, grid, st);
+    }
+}
+
+template <int D>
+static hipError_t launch_d(const DecodeArgs& a, int kvt, int qt, int rw, int grid, hipStream_t st) {
+    if (kvt == PA_DTYPE_F16) return launch_rw<D, PA_DTYPE_F16, PA_DTYPE_F16>(a, rw, grid, st);
+    if (kvt == PA_DTYPE_BF16) return launch_rw<D, PA_DTYPE_BF16, PA_DTYPE_BF16>(a, rw, grid, st);
+    if (qt == PA_DTYPE_BF16) return launch_rw<D, PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16>(a, rw, grid, st);
+    return launch_rw<D, PA_DTYPE_FP8_E4M3, PA_DTYPE_F16>(a, rw, grid, st);
+}
+
+hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int rw, int grid,
+                              hipStream_t stream) {
+    if (head_dim == 64) return launch_d<64>(a, kv_dtype, q_dtype, rw, grid, stream);
+    return launch_d<128>(a, kv_dtype, q_dtype, rw, grid, stream);
+}
+
+}  // namespace pa

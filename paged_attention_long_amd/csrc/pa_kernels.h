@@ -1,0 +1,53 @@
+// Kernel argument blocks and launchers (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+// Arguments of the split-KV kernels (VALU decode/verify and MFMA tile).
+struct DecodeArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const int32_t* q_lens;
+    const float* kv_scale;     // [2][Hkv] or null
+    float* out;
+    float* lse;                // may be null
+    float* ws_o;               // split partials [max_items][r_max][D]
+    float* ws_lse;             // [max_items][r_max] (log2 domain)
+    int* counters;             // [max_num_seqs * Hkv * counter_stride]
+    int64_t page_stride, head_stride, token_stride;   // elements
+    int num_seqs, bt_stride;
+    int num_q_heads, num_kv_heads, group;
+    int window;
+    float scale;
+    int rows_lo, rows_hi;      // rows-per-KV-head class handled by this launch
+    int target_items, min_pps, forced_pps, max_items, r_max;
+    int counter_stride;        // counters per (sequence, KV head)
+};
+
+hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int rw, int grid,
+                              hipStream_t stream);
+
+hipError_t launch_mfma_attn(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int grid,
+                            hipStream_t stream);
+
+struct GatherArgs {
+    const uint8_t* k_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const int32_t* q_lens;
+    int64_t* slots_out;
+    uint8_t* rows_out;
+    int64_t capacity;
+    int64_t page_stride, head_stride, token_stride;   // elements
+    int num_seqs, bt_stride, num_kv_heads, head_dim, elem_bytes, page_size, window;
+};
+
+hipError_t launch_debug_gather(const GatherArgs& a, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,306 @@
+// Host side of the paged-attention C ABI: argument validation, workspace
+// ownership and kernel dispatch.  Every entry point validates its host
+// arguments before touching the GPU, so rejected calls launch nothing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "paged_attn.h"
+#include "pa_kernels.h"
+
+struct pa_handle {
+    pa_config_t cfg;
+    pa_tuning_t tune;
+    int cu_count = 0;
+    int grid_default = 0;
+    int max_items = 0;     // split-partial slots
+    int r_max = 0;         // rows per slot
+    int counter_stride = 0;
+    float* ws_o = nullptr;
+    float* ws_lse = nullptr;
+    int* counters = nullptr;
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    std::string err;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(pa_handle* h, int code, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
+int fail(pa_handle* h, int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    if (h) h->err = buf; else g_err = buf;
+    return code;
+}
+
+int elem_bytes(int dt) { return dt == PA_DTYPE_FP8_E4M3 ? 1 : 2; }
+
+int pow2ceil(int x) {
+    int p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMinPagesPerSplit = 4;
+constexpr int kValuRowsMax = 8;   // rows per KV head handled by the VALU kernel under PA_PATH_AUTO
+
+int validate_config(const pa_config_t* c, std::string* why) {
+    char buf[256];
+    auto bad = [&](int code, const char* msg) { *why = msg; return code; };
+    if (!c) return bad(PA_ERR_INVALID_ARGUMENT, "config is NULL");
+    if (c->num_q_heads < 1 || c->num_kv_heads < 1) return bad(PA_ERR_INVALID_ARGUMENT, "head counts must be >= 1");
+    if (c->num_q_heads % c->num_kv_heads) return bad(PA_ERR_INVALID_ARGUMENT, "num_q_heads % num_kv_heads != 0");
+    if (c->num_q_heads / c->num_kv_heads > 16) return bad(PA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
+    if (c->head_dim != 64 && c->head_dim != 128) return bad(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (c->page_size != 16) return bad(PA_ERR_UNSUPPORTED, "page_size must be 16");
+    if (c->q_dtype != PA_DTYPE_F16 && c->q_dtype != PA_DTYPE_BF16)
+        return bad(PA_ERR_UNSUPPORTED, "q_dtype must be F16 or BF16");
+    if (c->kv_dtype != PA_DTYPE_F16 && c->kv_dtype != PA_DTYPE_BF16 && c->kv_dtype != PA_DTYPE_FP8_E4M3)
+        return bad(PA_ERR_UNSUPPORTED, "kv_dtype must be F16, BF16 or FP8_E4M3");
+    if (c->kv_dtype != PA_DTYPE_FP8_E4M3 && c->kv_dtype != c->q_dtype)
+        return bad(PA_ERR_UNSUPPORTED, "a 16-bit cache must have the query's dtype");
+    if (c->max_num_seqs < 1 || c->max_num_seqs > 1024) return bad(PA_ERR_INVALID_ARGUMENT, "max_num_seqs must be 1..1024");
+    if (c->max_q_len < 1) return bad(PA_ERR_INVALID_ARGUMENT, "max_q_len must be >= 1");
+    if (c->max_num_tokens < 1 || c->max_num_tokens > (int64_t)1 << 24)
+        return bad(PA_ERR_INVALID_ARGUMENT, "max_num_tokens must be 1..2^24");
+    if ((int64_t)c->max_q_len * (c->num_q_heads / c->num_kv_heads) > (1 << 20))
+        return bad(PA_ERR_UNSUPPORTED, "max_q_len * group too large");
+    if (c->flags != 0) return bad(PA_ERR_INVALID_ARGUMENT, "flags must be 0");
+    if (c->device < 0) return bad(PA_ERR_INVALID_ARGUMENT, "device must be >= 0");
+    (void)buf;
+    return PA_OK;
+}
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = false;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) return;
+        ok = hipSetDevice(dev) == hipSuccess;
+    }
+    ~DeviceGuard() {
+        if (prev >= 0) (void)hipSetDevice(prev);
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* paged_attn_version(void) { return "0.1.0"; }
+
+const char* paged_attn_last_error(const pa_handle_t* h) { return h ? h->err.c_str() : g_err.c_str(); }
+
+int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
+    if (!out) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "out is NULL");
+    *out = nullptr;
+    std::string why;
+    int rc = validate_config(cfg, &why);
+    if (rc != PA_OK) return fail(nullptr, rc, "%s", why.c_str());
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= cfg->device)
+        return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "device %d not present (%d devices)", cfg->device, ndev);
+    DeviceGuard guard(cfg->device);
+    if (!guard.ok) return fail(nullptr, PA_ERR_HIP, "hipSetDevice(%d) failed", cfg->device);
+
+    pa_handle* h = new (std::nothrow) pa_handle();
+    if (!h) return fail(nullptr, PA_ERR_OUT_OF_MEMORY, "host allocation failed");
+    h->cfg = *cfg;
+    std::memset(&h->tune, 0, sizeof h->tune);
+    if (hipDeviceGetAttribute(&h->cu_count, hipDeviceAttributeMultiprocessorCount, cfg->device) != hipSuccess ||
+        h->cu_count <= 0)
+        h->cu_count = 256;
+    h->grid_default = 2 * h->cu_count;
+
+    const int G = cfg->num_q_heads / cfg->num_kv_heads;
+    const int D = cfg->head_dim;
+    // Split-partial slots: at most grid + one per (sequence, KV head) for the
+    // VALU kernel (pages per split is raised until the items fit).
+    const int grid_cap = 8 * h->cu_count;
+    h->max_items = grid_cap + cfg->max_num_seqs * cfg->num_kv_heads;
+    h->r_max = cfg->max_q_len * G;
+    h->counter_stride = 1;
+    const size_t o_bytes = (size_t)h->max_items * h->r_max * D * sizeof(float);
+    const size_t l_bytes = (size_t)h->max_items * h->r_max * sizeof(float);
+    const size_t c_bytes = (size_t)cfg->max_num_seqs * cfg->num_kv_heads * h->counter_stride * sizeof(int);
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    h->ws_bytes = up(o_bytes) + up(l_bytes) + up(c_bytes);
+    if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
+        const size_t want = h->ws_bytes;
+        delete h;
+        (void)hipGetLastError();
+        return fail(nullptr, PA_ERR_OUT_OF_MEMORY, "workspace of %zu bytes could not be allocated", want);
+    }
+    char* p = static_cast<char*>(h->ws);
+    h->ws_o = reinterpret_cast<float*>(p);
+    h->ws_lse = reinterpret_cast<float*>(p + up(o_bytes));
+    h->counters = reinterpret_cast<int*>(p + up(o_bytes) + up(l_bytes));
+    if (hipMemset(h->counters, 0, c_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(h->ws);
+        delete h;
+        return fail(nullptr, PA_ERR_HIP, "workspace clear failed");
+    }
+    *out = h;
+    return PA_OK;
+}
+
+void paged_attn_destroy(pa_handle_t* h) {
+    if (!h) return;
+    if (h->ws) {
+        DeviceGuard guard(h->cfg.device);
+        (void)hipFree(h->ws);
+    }
+    delete h;
+}
+
+int paged_attn_set_tuning(pa_handle_t* h, const pa_tuning_t* t) {
+    if (!h) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "handle is NULL");
+    if (!t) {
+        std::memset(&h->tune, 0, sizeof h->tune);
+        return PA_OK;
+    }
+    if (t->path < PA_PATH_AUTO || t->path > PA_PATH_MFMA) return fail(h, PA_ERR_INVALID_ARGUMENT, "bad path %d", t->path);
+    if (t->path == PA_PATH_MFMA) return fail(h, PA_ERR_UNSUPPORTED, "the MFMA path is not built");
+    if (t->pages_per_split < 0 || t->kv_tiles_per_split < 0 || t->grid < 0 || t->grid > 8 * h->cu_count)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "tuning values out of range (grid <= %d)", 8 * h->cu_count);
+    h->tune = *t;
+    return PA_OK;
+}
+
+static int validate_cache(pa_handle* h, const pa_cache_layout_t* L, const void* k, const void* v) {
+    const pa_config_t& c = h->cfg;
+    const int eb = elem_bytes(c.kv_dtype);
+    if (!L) return fail(h, PA_ERR_INVALID_ARGUMENT, "layout is NULL");
+    if (!k || !v) return fail(h, PA_ERR_INVALID_ARGUMENT, "k_cache / v_cache is NULL");
+    if (!aligned16(k) || !aligned16(v)) return fail(h, PA_ERR_INVALID_ARGUMENT, "caches must be 16-byte aligned");
+    if (L->num_pages < 1) return fail(h, PA_ERR_INVALID_ARGUMENT, "num_pages must be >= 1");
+    if (L->page_stride < 1 || L->head_stride < 1 || L->token_stride < c.head_dim)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "strides must be positive and token_stride >= head_dim");
+    if ((L->page_stride * eb) % 16 || (L->head_stride * eb) % 16 || (L->token_stride * eb) % 16)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "every stride must be a multiple of 16 bytes");
+    if (L->num_pages > ((int64_t)1 << 31)) return fail(h, PA_ERR_INVALID_ARGUMENT, "num_pages must fit in int32");
+    return PA_OK;
+}
+
+int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const void* k_cache, const void* v_cache,
+                       const pa_cache_layout_t* layout, const int32_t* block_table, int32_t num_seqs,
+                       int32_t block_table_stride, const int32_t* seq_lens, const int32_t* q_lens, int32_t window,
+                       float scale, const float* kv_scale, float* out, float* lse, void* stream) {
+    if (!h) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "handle is NULL");
+    const pa_config_t& c = h->cfg;
+    if (!q || !out || !block_table || !seq_lens || !q_lens)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "q, out, block_table, seq_lens and q_lens must be non-NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(h, PA_ERR_INVALID_ARGUMENT, "q and out must be 16-byte aligned");
+    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(h, PA_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+    if (num_tokens < 1 || num_tokens > c.max_num_tokens)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "num_tokens %lld outside 1..%lld", (long long)num_tokens,
+                    (long long)c.max_num_tokens);
+    if (num_seqs < 1 || num_seqs > c.max_num_seqs)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "num_seqs %d outside 1..%d", num_seqs, c.max_num_seqs);
+    if (block_table_stride < 1) return fail(h, PA_ERR_INVALID_ARGUMENT, "block_table_stride must be >= 1");
+    if (!std::isfinite(scale)) return fail(h, PA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if ((c.kv_dtype == PA_DTYPE_FP8_E4M3) != (kv_scale != nullptr))
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "kv_scale is required for an fp8 cache and must be NULL otherwise");
+    int rc = validate_cache(h, layout, k_cache, v_cache);
+    if (rc != PA_OK) return rc;
+
+    DeviceGuard guard(c.device);
+    if (!guard.ok) return fail(h, PA_ERR_HIP, "hipSetDevice(%d) failed", c.device);
+
+    const int G = c.num_q_heads / c.num_kv_heads;
+    pa::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.q_lens = q_lens;
+    a.kv_scale = kv_scale;
+    a.out = out;
+    a.lse = lse;
+    a.ws_o = h->ws_o;
+    a.ws_lse = h->ws_lse;
+    a.counters = h->counters;
+    a.page_stride = layout->page_stride;
+    a.head_stride = layout->head_stride;
+    a.token_stride = layout->token_stride;
+    a.num_seqs = num_seqs;
+    a.bt_stride = block_table_stride;
+    a.num_q_heads = c.num_q_heads;
+    a.num_kv_heads = c.num_kv_heads;
+    a.group = G;
+    a.window = window;
+    a.scale = scale;
+    a.min_pps = kMinPagesPerSplit;
+    a.forced_pps = h->tune.pages_per_split;
+    a.max_items = h->max_items;
+    a.r_max = h->r_max;
+    a.counter_stride = h->counter_stride;
+    const int grid = h->tune.grid > 0 ? h->tune.grid : h->grid_default;
+    a.target_items = grid;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    // Row classes: everything through the VALU kernel until the tile kernel exists.
+    a.rows_lo = 1;
+    a.rows_hi = 1 << 30;
+    const int rw = std::min(kValuRowsMax, pow2ceil(G));
+    hipError_t e = pa::launch_decode_valu(a, c.head_dim, c.kv_dtype, c.q_dtype, rw, grid, st);
+    if (e != hipSuccess) return fail(h, PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
+int paged_attn_debug_gather(pa_handle_t* h, const void* k_cache, const pa_cache_layout_t* layout,
+                            const int32_t* block_table, int32_t num_seqs, int32_t block_table_stride,
+                            const int32_t* seq_lens, const int32_t* q_lens, int32_t window, int64_t* slots_out,
+                            void* rows_out, int64_t capacity, void* stream) {
+    if (!h) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "handle is NULL");
+    const pa_config_t& c = h->cfg;
+    int rc = validate_cache(h, layout, k_cache, k_cache);
+    if (rc != PA_OK) return rc;
+    if (!block_table || !seq_lens || !q_lens || !slots_out || !rows_out)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "NULL pointer argument");
+    if (!aligned16(rows_out)) return fail(h, PA_ERR_INVALID_ARGUMENT, "rows_out must be 16-byte aligned");
+    if (num_seqs < 1 || num_seqs > c.max_num_seqs || block_table_stride < 1 || capacity < 0)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "size argument out of range");
+    DeviceGuard guard(c.device);
+    if (!guard.ok) return fail(h, PA_ERR_HIP, "hipSetDevice(%d) failed", c.device);
+    pa::GatherArgs a{};
+    a.k_cache = static_cast<const uint8_t*>(k_cache);
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.q_lens = q_lens;
+    a.slots_out = slots_out;
+    a.rows_out = static_cast<uint8_t*>(rows_out);
+    a.capacity = capacity;
+    a.page_stride = layout->page_stride;
+    a.head_stride = layout->head_stride;
+    a.token_stride = layout->token_stride;
+    a.num_seqs = num_seqs;
+    a.bt_stride = block_table_stride;
+    a.num_kv_heads = c.num_kv_heads;
+    a.head_dim = c.head_dim;
+    a.elem_bytes = elem_bytes(c.kv_dtype);
+    a.page_size = c.page_size;
+    a.window = window;
+    hipError_t e = pa::launch_debug_gather(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(h, PA_ERR_HIP, "gather launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
+}  // extern "C"

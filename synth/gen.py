@@ -328,3 +328,24 @@ def named(name: str, batches: int = 1, **overrides) -> List[PagedInputs]:
     if overrides:
         spec = spec.replace(**overrides)
     return generate(spec, batches=batches)
+
+
+def replicate(inp: PagedInputs, copies: int, seed: int = 0, pool_pages: int = 0) -> List[PagedInputs]:
+    """``copies`` batches with inp's logical content at disjoint physical pages.
+
+    Used to rotate a benchmark over more memory than the GPU caches hold,
+    without drawing new values.  Copy 0 is inp itself.
+    """
+    n_live = len(inp.live_pages)
+    pool = max(pool_pages, inp.num_pages, copies * n_live + 1)
+    rng = np.random.default_rng(seed)
+    used = set(inp.live_pages.tolist()) | {inp.nan_page}
+    free = np.array([p for p in rng.permutation(pool) if p not in used], dtype=np.int64)
+    out = [dataclasses.replace(inp, num_pages=int(pool))]
+    for c in range(1, copies):
+        new_live = free[(c - 1) * n_live:c * n_live]
+        remap = dict(zip(inp.live_pages.tolist(), new_live.tolist()))
+        bt = np.vectorize(lambda x: remap.get(int(x), inp.nan_page), otypes=[np.int64])(inp.block_table)
+        out.append(dataclasses.replace(inp, num_pages=int(pool), live_pages=new_live,
+                                       block_table=bt.astype(np.int32), batch=c))
+    return out

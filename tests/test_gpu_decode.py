@@ -1,0 +1,268 @@
+"""GPU parity of the decode / verify path against the fp64 oracle, through
+the C ABI (libpaged_attn.so).  Every input is seeded and synthetic."""
+import numpy as np
+import pytest
+
+import oracle
+import paged_attention_long_amd as pal
+from synth import Spec, generate, named
+from synth.gen import permute_pool
+from tests.gpu_helpers import GpuCase, compare, progress
+
+pytestmark = pytest.mark.gpu
+
+
+def _spec(**kw):
+    base = dict(name="case", num_q_heads=32, num_kv_heads=8, head_dim=128, seq_lens=(1000,), q_lens=(1,),
+                q_dtype="bf16", kv_dtype="bf16", seed=5)
+    base.update(kw)
+    return Spec(**base)
+
+
+SMALL = {
+    "bf16_g4_ragged": dict(seq_lens=(1000,), q_lens=(1,)),
+    "f16_verify8_causal": dict(seq_lens=(777,), q_lens=(8,), q_dtype="f16", kv_dtype="f16"),
+    "f16_verify8_window_poison": dict(seq_lens=(3000,), q_lens=(8,), q_dtype="f16", kv_dtype="f16", window=100,
+                                      poison_out_of_window=True, k_outlier_frac=0.01),
+    "f16_d64_multi": dict(num_q_heads=8, num_kv_heads=2, head_dim=64, seq_lens=(257, 31, 600), q_lens=(1, 2, 1),
+                          q_dtype="f16", kv_dtype="f16"),
+    "fp8_mixed": dict(seq_lens=(2001, 1313, 333, 41), q_lens=(1, 4, 8, 1), kv_dtype="fp8_e4m3"),
+    "fp8_f16q": dict(seq_lens=(999,), q_lens=(2,), q_dtype="f16", kv_dtype="fp8_e4m3"),
+    "bf16_g6": dict(num_q_heads=24, num_kv_heads=4, seq_lens=(1234,), q_lens=(3,)),
+    "f16_mha": dict(num_q_heads=4, num_kv_heads=4, seq_lens=(517,), q_lens=(1,), q_dtype="f16", kv_dtype="f16"),
+    "bf16_g8": dict(num_q_heads=32, num_kv_heads=4, seq_lens=(2500,), q_lens=(1,)),
+    "qlen0_in_batch": dict(seq_lens=(300, 50, 129), q_lens=(2, 0, 1)),
+    "all_new_rows": dict(seq_lens=(8, 5), q_lens=(8, 5), q_dtype="f16", kv_dtype="f16"),
+    "single_token": dict(seq_lens=(1,), q_lens=(1,)),
+    "window_1": dict(seq_lens=(400,), q_lens=(4,), window=1, poison_out_of_window=True),
+    "window_wide": dict(seq_lens=(400,), q_lens=(4,), window=5000),
+    "bf16_long_ragged_split": dict(seq_lens=(20007,), q_lens=(1,), num_kv_heads=2, num_q_heads=8),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_small_parity(name):
+    inp = generate(_spec(name=name, **SMALL[name]))[0]
+    progress(f"small parity {name}: seqs={inp.seq_lens.tolist()} q_lens={inp.q_lens.tolist()} "
+             f"kv={inp.kv_dtype} D={inp.head_dim} G={inp.group} W={inp.window}")
+    ref_o, ref_l = oracle.attention(inp)
+    c = GpuCase([inp])
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare(name, inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("name", ["tiny_decode", "decode", "verify", "verify_window"])
+def test_named_full(name):
+    inp = named(name)[0]
+    progress(f"named {name} full oracle")
+    ref_o, ref_l = oracle.attention(inp)
+    c = GpuCase([inp])
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare(name, inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+def test_mixed_fp8_sampled_rows():
+    inp = named("mixed_fp8")[0]
+    progress("mixed_fp8 sampled rows")
+    rng = np.random.default_rng(0)
+    cu = np.concatenate([[0], np.cumsum(inp.q_lens)])
+    rows = []
+    for b in range(inp.num_seqs):
+        for t in range(int(cu[b]), int(cu[b + 1])):
+            for h in rng.choice(inp.num_q_heads, size=6, replace=False):
+                rows.append((t, int(h)))
+    ref = oracle.attention_rows(inp, rows)
+    c = GpuCase([inp])
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    compare("mixed_fp8", inp.kv_dtype, out, lse, None, None, rows=ref)
+
+
+def test_window_nan_poison_bit_identical():
+    """Every out-of-window page NaN: output finite and bit-identical to the
+    same windowed run over clean pages ("Dual MI50, part 2", section "Bug 2")."""
+    clean = named("verify_window", poison_out_of_window=False)[0]
+    dirty = named("verify_window")[0]
+    assert dirty.extra["poisoned_pages"] == [(0, 3712)]
+    progress("window poison bit-identity")
+    c1, c2 = GpuCase([clean]), GpuCase([dirty])
+    try:
+        o1, l1 = c1.run()
+        o2, l2 = c2.run()
+    finally:
+        c1.close()
+        c2.close()
+    assert np.all(np.isfinite(o2)) and np.all(np.isfinite(l2))
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3"])
+def test_page_permutation_bit_identical(kv):
+    inp = generate(_spec(seq_lens=(3001, 77), q_lens=(1, 4), kv_dtype=kv, pool_pages=1000))[0]
+    perm = permute_pool(inp, 9)
+    progress(f"permutation bit-identity {kv}")
+    c1, c2 = GpuCase([inp]), GpuCase([perm])
+    try:
+        o1, l1 = c1.run()
+        o2, l2 = c2.run()
+    finally:
+        c1.close()
+        c2.close()
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+def test_deterministic_and_reusable():
+    inp = generate(_spec(seq_lens=(5000, 123), q_lens=(2, 1)))[0]
+    c = GpuCase([inp])
+    try:
+        o1, l1 = c.run()
+        o2, l2 = c.run()
+    finally:
+        c.close()
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+@pytest.mark.parametrize("pps", [1, 4, 7, 100000])
+def test_split_count_invariance(pps):
+    """Forcing the split size changes only the summation order."""
+    inp = generate(_spec(seq_lens=(4097, 900), q_lens=(1, 3), q_dtype="f16", kv_dtype="f16"))[0]
+    progress(f"split invariance pps={pps}")
+    ref_o, ref_l = oracle.attention(inp)
+    c = GpuCase([inp], path=pal.PA_PATH_VALU, pages_per_split=pps)
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare(f"pps={pps}", inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+def test_rotating_batches_share_a_pool():
+    """Consecutive calls on different batches (split counters must reset)."""
+    bs = generate(_spec(seq_lens=(2049,), q_lens=(1,)), batches=3)
+    c = GpuCase(bs)
+    try:
+        for i, b in enumerate(bs):
+            ref_o, ref_l = oracle.attention(b)
+            out, lse = c.run(i)
+            compare(f"batch{i}", b.kv_dtype, out, lse, ref_o, ref_l)
+    finally:
+        c.close()
+
+
+def test_nhd_layout_through_strides():
+    inp = generate(_spec(seq_lens=(1500,), q_lens=(2,)))[0]
+    c1 = GpuCase([inp])
+    c2 = GpuCase([inp], layout="nhd")
+    try:
+        assert c2.pools["k"].stride(2) == inp.num_kv_heads * inp.head_dim
+        o1, l1 = c1.run()
+        o2, l2 = c2.run()
+    finally:
+        c1.close()
+        c2.close()
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
+def test_graph_replay_matches_eager():
+    import torch
+
+    inp = generate(_spec(seq_lens=(4097,), q_lens=(1,)))[0]
+    c = GpuCase([inp])
+    try:
+        eager_o, eager_l = c.run()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            c.forward(0, stream=s)          # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            c.forward(0, stream=torch.cuda.current_stream())
+        for rep in range(4):
+            c.out[0].fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            o = c.out[0].cpu().numpy()
+            l = c.lse[0].cpu().numpy()
+            assert np.array_equal(o.view(np.uint32), eager_o.view(np.uint32)), f"replay {rep}"
+            assert np.array_equal(l.view(np.uint32), eager_l.view(np.uint32)), f"replay {rep}"
+    finally:
+        c.close()
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3"])
+def test_debug_gather_bit_exact(kv):
+    import torch
+
+    inp = generate(_spec(seq_lens=(333, 20, 1000), q_lens=(2, 1, 8), kv_dtype=kv, window=300,
+                         pool_pages=200))[0]
+    c = GpuCase([inp])
+    try:
+        d = c.dev[0]
+        P = inp.page_size
+        n = sum(hi - lo for lo, hi in (inp.visible_range(b) for b in range(inp.num_seqs)))
+        eb = 1 if kv == "fp8_e4m3" else 2
+        slots = torch.full((n,), -1, dtype=torch.int64, device="cuda")
+        rows = torch.zeros((n, inp.num_kv_heads, inp.head_dim * eb), dtype=torch.uint8, device="cuda")
+        pal.paged_attn_debug_gather(c.h, c.pools["k"], d["block_table"], d["seq_lens"], d["q_lens"], inp.window,
+                                    slots, rows)
+        torch.cuda.synchronize()
+        slots = slots.cpu().numpy()
+        rows = rows.cpu().numpy()
+    finally:
+        c.close()
+    # expected: generator's logical order (never through the block table)
+    k = 0
+    for b in range(inp.num_seqs):
+        lo, hi = inp.visible_range(b)
+        o0 = int(inp.page_offsets[b])
+        for j in range(lo, hi):
+            pg = o0 + j // P
+            assert slots[k] == int(inp.live_pages[pg]) * P + j % P
+            want = np.ascontiguousarray(inp.k_live[pg, :, j % P, :]).view(np.uint8).reshape(inp.num_kv_heads, -1)
+            assert np.array_equal(rows[k], want), (b, j)
+            k += 1
+    assert k == n
+    # the oracle's de-paging of sequence 0 decodes exactly these bytes
+    lo, hi = inp.visible_range(0)
+    for g in range(inp.num_kv_heads):
+        raw = np.ascontiguousarray(rows[:hi - lo, g]).view(np.uint16 if eb == 2 else np.uint8)
+        dec = oracle.decode_bits(raw, kv)
+        if kv == "fp8_e4m3":
+            dec = dec * float(inp.kv_scale[0][g])
+        assert np.array_equal(dec, oracle.depage(inp, "k", 0, g, lo, hi))
+
+
+def test_host_argument_errors():
+    import torch
+
+    inp = generate(_spec(seq_lens=(64,), q_lens=(1,)))[0]
+    c = GpuCase([inp])
+    try:
+        d = c.dev[0]
+        with pytest.raises(pal.PagedAttnError) as e:
+            pal.paged_attn_forward(c.h, d["q"], c.pools["k"], c.pools["v"], d["block_table"], d["seq_lens"],
+                                   d["q_lens"], 0, float("nan"), None, c.out[0], c.lse[0])
+        assert e.value.code == 1
+        with pytest.raises(pal.PagedAttnError):
+            scale = torch.ones(2, 8, device="cuda")
+            pal.paged_attn_forward(c.h, d["q"], c.pools["k"], c.pools["v"], d["block_table"], d["seq_lens"],
+                                   d["q_lens"], 0, 0.1, scale, c.out[0], c.lse[0])
+        with pytest.raises(pal.PagedAttnError):
+            pal.paged_attn_set_tuning(c.h, grid=10 ** 7)
+    finally:
+        c.close()
