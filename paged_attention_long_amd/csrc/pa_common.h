@@ -99,6 +99,17 @@ PA_DEVINLINE float group_sum(float x) {
 
 PA_DEVINLINE float shfl_xor(float x, int m) { return __shfl_xor(x, m, kWave); }
 
+PA_DEVINLINE float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+    return x;
+}
+PA_DEVINLINE float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+    return x;
+}
+
 PA_DEVINLINE bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
 PA_DEVINLINE int wave_inclusive_scan(int x) {
@@ -134,23 +145,26 @@ PA_DEVINLINE int64_t kv_offset(int64_t page, int g, int slot, int64_t page_strid
 // launch if its rows-per-KV-head count q_len*G lies in [rows_lo, rows_hi].
 // Its visible pages are cut into splits of `pps` pages; an item is one
 // (sequence, KV head, split).
+constexpr int kMaxSplits = 64;   // splits per (sequence, KV head): one merge value per lane
+
 struct Plan {
     int pps;        // pages per split
     int n_items;
     int item_base[kMaxSeqs + 1];  // items before sequence b (exclusive scan), [num_seqs] = n_items
     int q_off[kMaxSeqs + 1];      // first query row of sequence b
-    int red[16];
+    int seq_len[kMaxSeqs];
+    int q_len[kMaxSeqs];
+    int red[32];
 };
 
 struct SeqInfo {
     int seq_len, q_len, q_off, lo, first_page, n_pages, splits;
 };
 
-PA_DEVINLINE SeqInfo seq_info(const Plan& pl, const int32_t* seq_lens, const int32_t* q_lens, int b, int window,
-                              int page_size) {
+PA_DEVINLINE SeqInfo seq_info(const Plan& pl, int b, int window, int page_size) {
     SeqInfo s;
-    s.seq_len = seq_lens[b];
-    s.q_len = q_lens[b];
+    s.seq_len = pl.seq_len[b];
+    s.q_len = pl.q_len[b];
     s.q_off = pl.q_off[b];
     s.lo = seq_visible_lo(s.seq_len, s.q_len, window);
     s.first_page = s.lo / page_size;
@@ -171,6 +185,7 @@ PA_DEVINLINE void build_plan(Plan& pl, const int32_t* seq_lens, const int32_t* q
     const int nwaves = nthr / kWave;
     // pass 1: q_len prefix (all sequences) and in-class page-head total
     long long pages_total = 0;
+    int max_np = 0;
     int carry_q = 0;
     for (int b0 = 0; b0 < num_seqs; b0 += nthr) {
         int b = b0 + tid;
@@ -178,6 +193,8 @@ PA_DEVINLINE void build_plan(Plan& pl, const int32_t* seq_lens, const int32_t* q
         if (b < num_seqs) {
             int sl = seq_lens[b];
             ql = q_lens[b];
+            pl.seq_len[b] = sl;
+            pl.q_len[b] = ql;
             int rows = ql * group;
             if (ql > 0 && rows >= rows_lo && rows <= rows_hi) {
                 int lo = seq_visible_lo(sl, ql, window);
@@ -197,13 +214,16 @@ PA_DEVINLINE void build_plan(Plan& pl, const int32_t* seq_lens, const int32_t* q
         if (b < num_seqs) pl.q_off[b] = carry_q + wave_off + inc - ql;
         carry_q += chunk_tot;
         __syncthreads();
-        // page-heads of this chunk
-        int npw = np;
+        // page-heads of this chunk, and its longest sequence
+        int npw = np, npm = np;
 #pragma unroll
-        for (int o = 32; o > 0; o >>= 1) npw += __shfl_xor(npw, o, kWave);
-        if (lane == 0) pl.red[wid] = npw;
+        for (int o = 32; o > 0; o >>= 1) {
+            npw += __shfl_xor(npw, o, kWave);
+            npm = max(npm, __shfl_xor(npm, o, kWave));
+        }
+        if (lane == 0) { pl.red[wid] = npw; pl.red[16 + wid] = npm; }
         __syncthreads();
-        for (int w = 0; w < nwaves; ++w) pages_total += pl.red[w];
+        for (int w = 0; w < nwaves; ++w) { pages_total += pl.red[w]; max_np = max(max_np, pl.red[16 + w]); }
         __syncthreads();
     }
     pages_total *= num_kv_heads;
@@ -215,6 +235,8 @@ PA_DEVINLINE void build_plan(Plan& pl, const int32_t* seq_lens, const int32_t* q
         pps = (int)((pages_total + t - 1) / t);
         pps = max(pps, min_pps);
     }
+    // at most kMaxSplits splits per (sequence, KV head)
+    pps = max(pps, (max_np + kMaxSplits - 1) / kMaxSplits);
     // keep the item count within the workspace: items <= pages_total/pps + seqs*Hkv
     {
         long long cap = (long long)max_items - (long long)num_seqs * num_kv_heads;
@@ -223,14 +245,16 @@ PA_DEVINLINE void build_plan(Plan& pl, const int32_t* seq_lens, const int32_t* q
         if (pps < need) pps = (int)need;
         if (pps < 1) pps = 1;
     }
+    // whole pages per wave: round automatic split sizes up to a multiple of min_pps
+    if (forced_pps <= 0 && min_pps > 1) pps = (pps + min_pps - 1) / min_pps * min_pps;
     // pass 2: items per sequence, exclusive scan
     int carry_i = 0;
     for (int b0 = 0; b0 < num_seqs; b0 += nthr) {
         int b = b0 + tid;
         int it = 0;
         if (b < num_seqs) {
-            int sl = seq_lens[b];
-            int ql = q_lens[b];
+            int sl = pl.seq_len[b];
+            int ql = pl.q_len[b];
             int rows = ql * group;
             if (ql > 0 && rows >= rows_lo && rows <= rows_hi) {
                 int lo = seq_visible_lo(sl, ql, window);

@@ -100,9 +100,15 @@ struct WaveShared {
     float l[kWaves][8];
 };
 
+constexpr int kPidChunk = 1024;   // page ids staged in LDS at a time
+
 struct Smem {
     Plan plan;
-    WaveShared ws;
+    int pid[kPidChunk];
+    union {
+        WaveShared ws;
+        MergeShared merge;
+    } u;
     int flag;
 };
 
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wid = tid / kWave;
+    const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // wave-uniform
     const int tl = lane / LPT;            // token within a round
     const int ch = lane % LPT;            // 8-element chunk of the row
 
@@ -130,10 +136,11 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
     const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q);
     MergeTarget tgt{a.out, a.lse, a.num_q_heads, a.group, 1.0f};
+    const int64_t page_bytes = a.page_stride * EB;
 
     for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
         const int b = item_seq(pl, a.num_seqs, it);
-        const SeqInfo si = seq_info(pl, a.seq_lens, a.q_lens, b, a.window, kPage);
+        const SeqInfo si = seq_info(pl, b, a.window, kPage);
         const int local = it - pl.item_base[b];
         const int g = local / si.splits;
         const int split = local - g * si.splits;
@@ -147,6 +154,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         tgt.out_scale = vscale;
         const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
         const bool direct = (si.splits == 1);
+        // byte offset of this lane's chunk inside a page, per round (< 2^31: checked on the host)
+        uint32_t lane_off[RPP];
+#pragma unroll
+        for (int rr = 0; rr < RPP; ++rr)
+            lane_off[rr] = (uint32_t)(kv_offset(0, g, rr * TPR + tl, a.page_stride, a.head_stride, a.token_stride) * EB +
+                                      ch * 8 * EB);
 
         // passes over row groups: up to kWaves row groups at a time
         for (int rg0 = 0; rg0 < n_rg; rg0 += kWaves) {
@@ -178,79 +191,92 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
                 }
             }
 
-            if (active) {
-                const int64_t round_off = (int64_t)TPR * a.token_stride * EB;
-                Chunk kc[RPP], vc[RPP];
-                int pg = p_begin + sub;
-                if (pg < p_end) {
-                    const int64_t off =
-                        kv_offset(bt[pg], g, tl, a.page_stride, a.head_stride, a.token_stride) * EB + ch * 8 * EB;
-#pragma unroll
-                    for (int rr = 0; rr < RPP; ++rr) {
-                        kc[rr] = load_chunk<KVT>(kbase + off + rr * round_off);
-                        vc[rr] = load_chunk<KVT>(vbase + off + rr * round_off);
-                    }
-                }
-                for (; pg < p_end; pg += wprg) {
-                    Chunk kn[RPP], vn[RPP];
-                    const int nx = pg + wprg;
-                    if (nx < p_end) {
-                        const int64_t off =
-                            kv_offset(bt[nx], g, tl, a.page_stride, a.head_stride, a.token_stride) * EB + ch * 8 * EB;
+            for (int c0 = p_begin; c0 < p_end; c0 += kPidChunk) {
+                const int c1 = min(p_end, c0 + kPidChunk);
+                for (int k = tid; k < c1 - c0; k += kThreads) sm.pid[k] = bt[c0 + k];
+                __syncthreads();
+                if (active) {
+                    // Two page buffers in ping-pong: the next page's loads are in flight
+                    // while the current one is scored (no register copies of pending loads).
+                    Chunk ka[RPP], va[RPP], kb[RPP], vb[RPP];
+                    auto issue = [&](Chunk (&kd)[RPP], Chunk (&vd)[RPP], int pg) {
+                        // wave-uniform page base (scalar registers) + per-lane 32-bit offsets
+                        const int pid = __builtin_amdgcn_readfirstlane(sm.pid[pg - c0]);
+                        const int64_t pbase = (int64_t)pid * page_bytes;
+                        const uint8_t* kp = kbase + pbase;
+                        const uint8_t* vp = vbase + pbase;
 #pragma unroll
                         for (int rr = 0; rr < RPP; ++rr) {
-                            kn[rr] = load_chunk<KVT>(kbase + off + rr * round_off);
-                            vn[rr] = load_chunk<KVT>(vbase + off + rr * round_off);
+                            kd[rr] = load_chunk<KVT>(kp + lane_off[rr]);
+                            vd[rr] = load_chunk<KVT>(vp + lane_off[rr]);
                         }
-                    }
+                    };
+                    auto consume = [&](const Chunk (&kd)[RPP], const Chunk (&vd)[RPP], int pg) {
 #pragma unroll
-                    for (int rr = 0; rr < RPP; ++rr) {
-                        const int j = pg * kPage + rr * TPR + tl;
-                        const bool live = (j >= si.lo) && (j < si.seq_len);
-                        uint32_t kp[4];
-                        k_pairs<KVT, QT>(kc[rr], kp);
-                        float s[RW];
-#pragma unroll
-                        for (int r = 0; r < RW; ++r) {
-                            float x = dot2<QT>(qv[r][0], kp[0], 0.f);
-                            x = dot2<QT>(qv[r][1], kp[1], x);
-                            x = dot2<QT>(qv[r][2], kp[2], x);
-                            x = dot2<QT>(qv[r][3], kp[3], x);
-                            s[r] = group_sum<LPT>(x);
-                        }
-                        bool need = false;
-#pragma unroll
-                        for (int r = 0; r < RW; ++r) {
-                            const bool vis = (j <= pos[r]) && (j >= lo_r[r]) && live;
-                            s[r] = vis ? s[r] * s2 : kNegInf;
-                            need |= s[r] > m[r] + kTau;
-                        }
-                        if (wave_any(need)) {
+                        for (int rr = 0; rr < RPP; ++rr) {
+                            const int j = pg * kPage + rr * TPR + tl;
+                            const bool live = (j >= si.lo) && (j < si.seq_len);
+                            uint32_t kp[4];
+                            k_pairs<KVT, QT>(kd[rr], kp);
+                            float s[RW];
 #pragma unroll
                             for (int r = 0; r < RW; ++r) {
-                                const bool nd = s[r] > m[r] + kTau;
-                                const float al = nd ? fast_exp2(m[r] - s[r]) : 1.0f;
-                                m[r] = nd ? s[r] : m[r];
-                                l[r] *= al;
+                                float x = dot2<QT>(qv[r][0], kp[0], 0.f);
+                                x = dot2<QT>(qv[r][1], kp[1], x);
+                                x = dot2<QT>(qv[r][2], kp[2], x);
+                                x = dot2<QT>(qv[r][3], kp[3], x);
+                                s[r] = group_sum<LPT>(x);
+                            }
+                            bool need = false;
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) acc[r][e] *= al;
+                            for (int r = 0; r < RW; ++r) {
+                                const bool vis = (j <= pos[r]) && (j >= lo_r[r]) && live;
+                                s[r] = vis ? s[r] * s2 : kNegInf;
+                                need |= s[r] > m[r] + kTau;
+                            }
+                            if (wave_any(need)) {
+#pragma unroll
+                                for (int r = 0; r < RW; ++r) {
+                                    const bool nd = s[r] > m[r] + kTau;
+                                    const float al = nd ? fast_exp2(m[r] - s[r]) : 1.0f;
+                                    m[r] = nd ? s[r] : m[r];
+                                    l[r] *= al;
+#pragma unroll
+                                    for (int e = 0; e < 8; ++e) acc[r][e] *= al;
+                                }
+                            }
+                            float v[8];
+                            v_floats<KVT>(vd[rr], v);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] = live ? v[e] : 0.f;
+#pragma unroll
+                            for (int r = 0; r < RW; ++r) {
+                                const float p = (s[r] == kNegInf) ? 0.f : fast_exp2(s[r] - m[r]);
+                                l[r] += p;
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, v[e], acc[r][e]);
                             }
                         }
-                        float v[8];
-                        v_floats<KVT>(vc[rr], v);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) v[e] = live ? v[e] : 0.f;
-#pragma unroll
-                        for (int r = 0; r < RW; ++r) {
-                            const float p = (s[r] == kNegInf) ? 0.f : fast_exp2(s[r] - m[r]);
-                            l[r] += p;
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, v[e], acc[r][e]);
+                    };
+                    // The prefetch is unconditional (past the end it re-reads a page this
+                    // wave already holds) so the wait counts are the same on every path.
+                    int pg = c0 + sub;
+                    if (pg < c1) {
+                        issue(ka, va, pg);
+                        while (true) {
+                            const int p1 = pg + wprg;
+                            issue(kb, vb, p1 < c1 ? p1 : pg);
+                            consume(ka, va, pg);
+                            if (p1 >= c1) break;
+                            const int p2 = p1 + wprg;
+                            issue(ka, va, p2 < c1 ? p2 : p1);
+                            consume(kb, vb, p1);
+                            if (p2 >= c1) break;
+                            pg = p2;
                         }
                     }
-#pragma unroll
-                    for (int rr = 0; rr < RPP; ++rr) { kc[rr] = kn[rr]; vc[rr] = vn[rr]; }
                 }
+                __syncthreads();
             }
 
             // merge the TPR token lanes of this wave (lanes ch, ch+LPT, ...)
@@ -277,8 +303,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int r = 0; r < RW; ++r) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) sm.ws.acc[wid][r][ch * 8 + e] = acc[r][e];
-                    if (ch == 0) { sm.ws.m[wid][r] = m[r]; sm.ws.l[wid][r] = l[r]; }
+                    for (int e = 0; e < 8; ++e) sm.u.ws.acc[wid][r][ch * 8 + e] = acc[r][e];
+                    if (ch == 0) { sm.u.ws.m[wid][r] = m[r]; sm.u.ws.l[wid][r] = l[r]; }
                 }
             }
             __syncthreads();
@@ -291,14 +317,14 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
                 const int r = rl - rgl * RW;
                 const int w0 = rgl * wprg;
                 float M = kNegInf;
-                for (int w = 0; w < wprg; ++w) M = fmaxf(M, sm.ws.m[w0 + w][r]);
+                for (int w = 0; w < wprg; ++w) M = fmaxf(M, sm.u.ws.m[w0 + w][r]);
                 float L = 0.f, A = 0.f;
                 if (M != kNegInf) {
                     for (int w = 0; w < wprg; ++w) {
-                        const float mw = sm.ws.m[w0 + w][r];
+                        const float mw = sm.u.ws.m[w0 + w][r];
                         const float al = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
-                        L = fmaf(sm.ws.l[w0 + w][r], al, L);
-                        A = fmaf(sm.ws.acc[w0 + w][r][d], al, A);
+                        L = fmaf(sm.u.ws.l[w0 + w][r], al, L);
+                        A = fmaf(sm.u.ws.acc[w0 + w][r][d], al, A);
                     }
                 }
                 const int row = rg0 * RW + rl;
@@ -318,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         if (!direct) {
             const int64_t first_item = pl.item_base[b] + (int64_t)g * si.splits;
             if (arrive_last(a.counters + ((int64_t)b * a.num_kv_heads + g) * a.counter_stride, si.splits, &sm.flag)) {
-                merge_splits<D>(a.ws_o, a.ws_lse, first_item, si.splits, rows, a.r_max, tgt, si.q_off, g);
+                merge_splits<D>(a.ws_o, a.ws_lse, first_item, si.splits, rows, a.r_max, tgt, si.q_off, g, sm.u.merge);
             }
             __syncthreads();
         }

@@ -8,7 +8,9 @@
 // Splitting along the context and merging the partial results at the end is
 // how the pages' decode kernel keeps every compute unit busy ("Dual MI50,
 // part 2", section "Decode: a new kernel for the shape MTP actually runs").
-// The merge visits splits in index order, so results are deterministic.
+// A (sequence, KV head) has at most kMaxSplits splits, so one lane per split
+// reads every lse_s in a single round trip; the merge visits splits in index
+// order, so results are deterministic.
 #pragma once
 
 #include "pa_common.h"
@@ -21,6 +23,14 @@ struct MergeTarget {
     int hq;              // query heads
     int group;           // query heads per KV head
     float out_scale;     // multiplies the final output (fp8 V scale, else 1)
+};
+
+constexpr int kMergeRows = 64;   // rows merged per pass
+
+// LDS scratch of one merge pass.
+struct MergeShared {
+    float w[kMergeRows][kMaxSplits];   // normalised split weights
+    float lse[kMergeRows];             // final lse (log2 domain)
 };
 
 // Row r (token-major: r = i*G + h_in_group) of KV head g -> output row index.
@@ -51,37 +61,58 @@ PA_DEVINLINE bool arrive_last(int* counter, int n_splits, int* lds_flag) {
     return last;
 }
 
-// Merge n_splits partials of `rows` rows: ws_o[(base + s) * rstride + r][D],
-// ws_lse[(base + s) * rstride + r]; write final rows.  All threads call.
+// Merge n_splits (<= kMaxSplits) partials of `rows` rows:
+// ws_o[(base + s) * rstride + r][D], ws_lse[(base + s) * rstride + r];
+// write the final rows.  All threads of the block call.
 template <int D>
 PA_DEVINLINE void merge_splits(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int64_t base,
-                               int n_splits, int rows, int rstride, const MergeTarget& t, int q_off, int g) {
+                               int n_splits, int rows, int rstride, const MergeTarget& t, int q_off, int g,
+                               MergeShared& sh) {
     const int nthr = blockDim.x;
-    const int total = rows * (D / 4);
-    for (int e = threadIdx.x; e < total; e += nthr) {
-        const int r = e / (D / 4);
-        const int d4 = (e - r * (D / 4)) * 4;
-        float M = kNegInf;
-        for (int s = 0; s < n_splits; ++s) M = fmaxf(M, ws_lse[(base + s) * rstride + r]);
-        float L = 0.f;
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-        if (M != kNegInf) {
-            for (int s = 0; s < n_splits; ++s) {
-                const int64_t slot = (base + s) * rstride + r;
-                const float ls = ws_lse[slot];
-                const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
-                const float4 o = *reinterpret_cast<const float4*>(ws_o + slot * D + d4);
-                L += w;
-                a0 = fmaf(w, o.x, a0);
-                a1 = fmaf(w, o.y, a1);
-                a2 = fmaf(w, o.z, a2);
-                a3 = fmaf(w, o.w, a3);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    const int nwaves = nthr / kWave;
+    for (int r0 = 0; r0 < rows; r0 += kMergeRows) {
+        const int nr = min(kMergeRows, rows - r0);
+        for (int rl = wid; rl < nr; rl += nwaves) {
+            const float ls = (lane < n_splits) ? ws_lse[(base + lane) * rstride + r0 + rl] : kNegInf;
+            const float M = wave_max(ls);
+            const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
+            const float L = wave_sum(w);
+            sh.w[rl][lane] = (L > 0.f) ? w / L : 0.f;
+            if (lane == 0) sh.lse[rl] = (L > 0.f) ? M + fast_log2(L) : kNegInf;
+        }
+        __syncthreads();
+        for (int e = threadIdx.x; e < nr * (D / 4); e += nthr) {
+            const int rl = e / (D / 4);
+            const int d4 = (e - rl * (D / 4)) * 4;
+            const float* src = ws_o + ((base * rstride) + r0 + rl) * (int64_t)D + d4;
+            const int64_t sstride = (int64_t)rstride * D;
+            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+            for (int s0 = 0; s0 < n_splits; s0 += 8) {
+                float4 o[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    o[k] = (s0 + k < n_splits) ? *reinterpret_cast<const float4*>(src + (s0 + k) * sstride)
+                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float w = (s0 + k < n_splits) ? sh.w[rl][s0 + k] : 0.f;
+                    a0 = fmaf(w, o[k].x, a0);
+                    a1 = fmaf(w, o[k].y, a1);
+                    a2 = fmaf(w, o[k].z, a2);
+                    a3 = fmaf(w, o[k].w, a3);
+                }
+            }
+            const float sc = t.out_scale;
+            const int64_t orow = out_row(t, q_off, g, r0 + rl);
+            *reinterpret_cast<float4*>(t.out + orow * D + d4) = make_float4(a0 * sc, a1 * sc, a2 * sc, a3 * sc);
+            if (t.lse != nullptr && d4 == 0) {
+                const float l2 = sh.lse[rl];
+                t.lse[orow] = (l2 == kNegInf) ? kNegInf : l2 * kLn2;
             }
         }
-        const float inv = (L > 0.f) ? t.out_scale / L : 0.f;
-        const int64_t orow = out_row(t, q_off, g, r);
-        *reinterpret_cast<float4*>(t.out + orow * D + d4) = make_float4(a0 * inv, a1 * inv, a2 * inv, a3 * inv);
-        if (t.lse != nullptr && d4 == 0) t.lse[orow] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
+        __syncthreads();
     }
 }
 

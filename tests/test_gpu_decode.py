@@ -209,7 +209,7 @@ def test_debug_gather_bit_exact(kv):
     import torch
 
     inp = generate(_spec(seq_lens=(333, 20, 1000), q_lens=(2, 1, 8), kv_dtype=kv, window=300,
-                         pool_pages=200))[0]
+                         q_dtype="f16", pool_pages=200))[0]
     c = GpuCase([inp])
     try:
         d = c.dev[0]
