@@ -79,6 +79,8 @@ typedef struct pa_config {
     int32_t kv_dtype;        /* PA_DTYPE_F16, PA_DTYPE_BF16 (== q_dtype) or PA_DTYPE_FP8_E4M3 */
     int32_t max_num_seqs;    /* largest num_seqs passed to forward, 1..1024 */
     int32_t max_q_len;       /* largest q_len of any sequence, >= 1 */
+    int32_t min_q_len;       /* smallest q_len of any sequence with q_len > 0 (1..max_q_len); a
+                                hint: kernels for narrower rows are not launched */
     int64_t max_num_tokens;  /* largest T = sum of q_lens, >= 1 */
     int32_t device;          /* HIP device ordinal the handle runs on */
     int32_t flags;           /* reserved, must be 0 */

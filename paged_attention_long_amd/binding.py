@@ -50,6 +50,7 @@ class pa_config_t(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("max_num_seqs", ctypes.c_int32),
         ("max_q_len", ctypes.c_int32),
+        ("min_q_len", ctypes.c_int32),
         ("max_num_tokens", ctypes.c_int64),
         ("device", ctypes.c_int32),
         ("flags", ctypes.c_int32),
@@ -152,9 +153,9 @@ def _stream_ptr(stream) -> Optional[int]:
 
 def make_config(num_q_heads: int, num_kv_heads: int, head_dim: int, q_dtype: str, kv_dtype: str,
                 max_num_seqs: int, max_q_len: int, max_num_tokens: int, page_size: int = 16,
-                device: int = 0) -> pa_config_t:
+                device: int = 0, min_q_len: int = 1) -> pa_config_t:
     return pa_config_t(num_q_heads, num_kv_heads, head_dim, page_size, DTYPE_CODES[q_dtype],
-                       DTYPE_CODES[kv_dtype], max_num_seqs, max_q_len, max_num_tokens, device, 0)
+                       DTYPE_CODES[kv_dtype], max_num_seqs, max_q_len, min_q_len, max_num_tokens, device, 0)
 
 
 def paged_attn_create(cfg: pa_config_t) -> Handle:

@@ -147,15 +147,28 @@ PA_DEVINLINE int64_t kv_offset(int64_t page, int g, int slot, int64_t page_strid
 // (sequence, KV head, split).
 constexpr int kMaxSplits = 64;   // splits per (sequence, KV head): one merge value per lane
 
+// Per-sequence plan arrays live in dynamic LDS, sized from num_seqs by the
+// host (plan_lds_bytes).
 struct Plan {
-    int pps;        // pages per split
+    int pps;        // pages (or tiles) per split
     int n_items;
-    int item_base[kMaxSeqs + 1];  // items before sequence b (exclusive scan), [num_seqs] = n_items
-    int q_off[kMaxSeqs + 1];      // first query row of sequence b
-    int seq_len[kMaxSeqs];
-    int q_len[kMaxSeqs];
     int red[32];
+    int* item_base;  // [num_seqs + 1] items before sequence b; [num_seqs] = n_items
+    int* q_off;      // [num_seqs + 1] first query row of sequence b
+    int* seq_len;    // [num_seqs]
+    int* q_len;      // [num_seqs]
+    int* aux;        // [num_seqs] kernel-specific per-sequence value
 };
+
+inline __host__ __device__ size_t plan_lds_bytes(int num_seqs) { return (size_t)(5 * num_seqs + 2) * sizeof(int); }
+
+PA_DEVINLINE void plan_bind(Plan& pl, int* dyn, int num_seqs) {
+    pl.item_base = dyn;
+    pl.q_off = dyn + (num_seqs + 1);
+    pl.seq_len = dyn + 2 * (num_seqs + 1);
+    pl.q_len = pl.seq_len + num_seqs;
+    pl.aux = pl.q_len + num_seqs;
+}
 
 struct SeqInfo {
     int seq_len, q_len, q_off, lo, first_page, n_pages, splits;
@@ -173,48 +186,62 @@ PA_DEVINLINE SeqInfo seq_info(const Plan& pl, int b, int window, int page_size) 
     return s;
 }
 
-// Build the plan in LDS.  Must be called by all threads of the block
-// (blockDim.x a multiple of 64, <= 1024).
-PA_DEVINLINE void build_plan(Plan& pl, const int32_t* seq_lens, const int32_t* q_lens, int num_seqs, int window,
-                             int page_size, int group, int num_kv_heads, int rows_lo, int rows_hi,
+// Block-wide exclusive scan of one int per thread, chunked over sequences.
+// Returns this thread's exclusive prefix plus `carry`; *total gets the chunk sum.
+PA_DEVINLINE int block_exclusive_scan(int v, int* red, int* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wid = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    const int inc = wave_inclusive_scan(v);
+    if (lane == kWave - 1) red[wid] = inc;
+    __syncthreads();
+    int off = 0, tot = 0;
+    for (int w = 0; w < nwaves; ++w) {
+        const int x = red[w];
+        if (w < wid) off += x;
+        tot += x;
+    }
+    __syncthreads();
+    *total = tot;
+    return off + inc - v;
+}
+
+// Split plan of the paged split-KV kernel: a sequence belongs to the launch if
+// its rows-per-KV-head count q_len*G lies in [rows_lo, rows_hi]; its visible
+// pages are cut into splits of `pps` pages; an item is one (sequence, KV head,
+// split).  Computed identically by every workgroup from the device-resident
+// lengths (no host round trip).  All threads of the block call.
+PA_DEVINLINE void build_plan(Plan& pl, int* dyn, const int32_t* seq_lens, const int32_t* q_lens, int num_seqs,
+                             int window, int page_size, int group, int num_kv_heads, int rows_lo, int rows_hi,
                              int target_items, int min_pps, int forced_pps, int max_items) {
+    plan_bind(pl, dyn, num_seqs);
     const int tid = threadIdx.x;
     const int nthr = blockDim.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid / kWave;
     const int nwaves = nthr / kWave;
-    // pass 1: q_len prefix (all sequences) and in-class page-head total
     long long pages_total = 0;
     int max_np = 0;
     int carry_q = 0;
     for (int b0 = 0; b0 < num_seqs; b0 += nthr) {
-        int b = b0 + tid;
+        const int b = b0 + tid;
         int ql = 0, np = 0;
         if (b < num_seqs) {
-            int sl = seq_lens[b];
+            const int sl = seq_lens[b];
             ql = q_lens[b];
             pl.seq_len[b] = sl;
             pl.q_len[b] = ql;
-            int rows = ql * group;
+            const int rows = ql * group;
             if (ql > 0 && rows >= rows_lo && rows <= rows_hi) {
-                int lo = seq_visible_lo(sl, ql, window);
+                const int lo = seq_visible_lo(sl, ql, window);
                 np = (sl - 1) / page_size - lo / page_size + 1;
             }
+            pl.aux[b] = np;
         }
-        // block exclusive scan of ql
-        int inc = wave_inclusive_scan(ql);
-        if (lane == kWave - 1) pl.red[wid] = inc;
-        __syncthreads();
-        int wave_off = 0, chunk_tot = 0;
-        for (int w = 0; w < nwaves; ++w) {
-            int v = pl.red[w];
-            if (w < wid) wave_off += v;
-            chunk_tot += v;
-        }
-        if (b < num_seqs) pl.q_off[b] = carry_q + wave_off + inc - ql;
-        carry_q += chunk_tot;
-        __syncthreads();
-        // page-heads of this chunk, and its longest sequence
+        int tot;
+        const int ex = block_exclusive_scan(ql, pl.red, &tot);
+        if (b < num_seqs) pl.q_off[b] = carry_q + ex;
+        carry_q += tot;
         int npw = np, npm = np;
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
@@ -231,7 +258,7 @@ PA_DEVINLINE void build_plan(Plan& pl, const int32_t* seq_lens, const int32_t* q
     if (forced_pps > 0) {
         pps = forced_pps;
     } else {
-        long long t = target_items > 0 ? target_items : 1;
+        const long long t = target_items > 0 ? target_items : 1;
         pps = (int)((pages_total + t - 1) / t);
         pps = max(pps, min_pps);
     }
@@ -241,39 +268,20 @@ PA_DEVINLINE void build_plan(Plan& pl, const int32_t* seq_lens, const int32_t* q
     {
         long long cap = (long long)max_items - (long long)num_seqs * num_kv_heads;
         if (cap < 1) cap = 1;
-        long long need = (pages_total + cap - 1) / cap;
+        const long long need = (pages_total + cap - 1) / cap;
         if (pps < need) pps = (int)need;
         if (pps < 1) pps = 1;
     }
     // whole pages per wave: round automatic split sizes up to a multiple of min_pps
     if (forced_pps <= 0 && min_pps > 1) pps = (pps + min_pps - 1) / min_pps * min_pps;
-    // pass 2: items per sequence, exclusive scan
     int carry_i = 0;
     for (int b0 = 0; b0 < num_seqs; b0 += nthr) {
-        int b = b0 + tid;
-        int it = 0;
-        if (b < num_seqs) {
-            int sl = pl.seq_len[b];
-            int ql = pl.q_len[b];
-            int rows = ql * group;
-            if (ql > 0 && rows >= rows_lo && rows <= rows_hi) {
-                int lo = seq_visible_lo(sl, ql, window);
-                int np = (sl - 1) / page_size - lo / page_size + 1;
-                it = ((np + pps - 1) / pps) * num_kv_heads;
-            }
-        }
-        int inc = wave_inclusive_scan(it);
-        if (lane == kWave - 1) pl.red[wid] = inc;
-        __syncthreads();
-        int wave_off = 0, chunk_tot = 0;
-        for (int w = 0; w < nwaves; ++w) {
-            int v = pl.red[w];
-            if (w < wid) wave_off += v;
-            chunk_tot += v;
-        }
-        if (b < num_seqs) pl.item_base[b] = carry_i + wave_off + inc - it;
-        carry_i += chunk_tot;
-        __syncthreads();
+        const int b = b0 + tid;
+        const int it = (b < num_seqs) ? ((pl.aux[b] + pps - 1) / pps) * num_kv_heads : 0;
+        int tot;
+        const int ex = block_exclusive_scan(it, pl.red, &tot);
+        if (b < num_seqs) pl.item_base[b] = carry_i + ex;
+        carry_i += tot;
     }
     if (tid == 0) {
         pl.item_base[num_seqs] = carry_i;
@@ -288,7 +296,7 @@ PA_DEVINLINE void build_plan(Plan& pl, const int32_t* seq_lens, const int32_t* q
 PA_DEVINLINE int item_seq(const Plan& pl, int num_seqs, int it) {
     int lo = 0, hi = num_seqs - 1;
     while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
+        const int mid = (lo + hi + 1) >> 1;
         if (pl.item_base[mid] <= it) lo = mid; else hi = mid - 1;
     }
     return lo;

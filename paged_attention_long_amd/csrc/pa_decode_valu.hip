@@ -121,8 +121,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     using Chunk = typename KvChunk<KVT>::T;
 
     __shared__ Smem sm;
+    extern __shared__ int dyn_lds[];
     Plan& pl = sm.plan;
-    build_plan(pl, a.seq_lens, a.q_lens, a.num_seqs, a.window, kPage, a.group, a.num_kv_heads, a.rows_lo,
+    build_plan(pl, dyn_lds, a.seq_lens, a.q_lens, a.num_seqs, a.window, kPage, a.group, a.num_kv_heads, a.rows_lo,
                a.rows_hi, a.target_items, a.min_pps, a.forced_pps, a.max_items);
     const int n_items = pl.n_items;
 
@@ -355,7 +356,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 
 template <int D, int KVT, int QT, int RW>
 static hipError_t launch_t(const DecodeArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((decode_valu_kernel<D, KVT, QT, RW>), dim3(grid), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decode_valu_kernel<D, KVT, QT, RW>), dim3(grid), dim3(kThreads), plan_lds_bytes(a.num_seqs), st,
+                       a);
     return hipGetLastError();
 }
 

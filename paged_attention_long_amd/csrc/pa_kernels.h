@@ -26,15 +26,18 @@ struct DecodeArgs {
     int window;
     float scale;
     int rows_lo, rows_hi;      // rows-per-KV-head class handled by this launch
-    int target_items, min_pps, forced_pps, max_items, r_max;
+    int target_items, min_pps, forced_pps, max_items, r_max;   // forced_pps: pages (VALU) or tiles (MFMA) per split
     int counter_stride;        // counters per (sequence, KV head)
 };
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int rw, int grid,
                               hipStream_t stream);
 
-hipError_t launch_mfma_attn(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int grid,
+// wr: waves along query rows (4: 128-row blocks for prefill; 1: 32-row blocks,
+// four waves splitting the keys, for verification widths).
+hipError_t launch_mfma_attn(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int wr, int grid,
                             hipStream_t stream);
+int mfma_rows_per_item(int wr);
 
 struct GatherArgs {
     const uint8_t* k_cache;

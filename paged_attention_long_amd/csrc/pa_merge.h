@@ -63,11 +63,12 @@ PA_DEVINLINE bool arrive_last(int* counter, int n_splits, int* lds_flag) {
 
 // Merge n_splits (<= kMaxSplits) partials of `rows` rows:
 // ws_o[(base + s) * rstride + r][D], ws_lse[(base + s) * rstride + r];
-// write the final rows.  All threads of the block call.
+// write them as rows row0 .. row0 + rows - 1 of KV head g.  All threads of
+// the block call.
 template <int D>
 PA_DEVINLINE void merge_splits(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int64_t base,
                                int n_splits, int rows, int rstride, const MergeTarget& t, int q_off, int g,
-                               MergeShared& sh) {
+                               MergeShared& sh, int row0 = 0) {
     const int nthr = blockDim.x;
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
@@ -105,7 +106,7 @@ PA_DEVINLINE void merge_splits(const float* __restrict__ ws_o, const float* __re
                 }
             }
             const float sc = t.out_scale;
-            const int64_t orow = out_row(t, q_off, g, r0 + rl);
+            const int64_t orow = out_row(t, q_off, g, row0 + r0 + rl);
             *reinterpret_cast<float4*>(t.out + orow * D + d4) = make_float4(a0 * sc, a1 * sc, a2 * sc, a3 * sc);
             if (t.lse != nullptr && d4 == 0) {
                 const float l2 = sh.lse[rl];

@@ -20,8 +20,11 @@ struct pa_handle {
     pa_tuning_t tune;
     int cu_count = 0;
     int grid_default = 0;
-    int max_items = 0;     // split-partial slots
-    int r_max = 0;         // rows per slot
+    int max_items_valu = 0;  // split-partial slots of the VALU kernel
+    int r_max_valu = 0;      // rows per VALU slot (largest rows-per-KV-head it may handle)
+    bool valu_all_ok = false;  // the VALU kernel's slots hold every sequence's rows
+    int mfma_wr = 1;         // MFMA kernel: waves along rows (rows per item = 32 * mfma_wr)
+    int max_items_mfma = 0;
     int counter_stride = 0;
     float* ws_o = nullptr;
     float* ws_lse = nullptr;
@@ -76,6 +79,10 @@ int validate_config(const pa_config_t* c, std::string* why) {
         return bad(PA_ERR_UNSUPPORTED, "a 16-bit cache must have the query's dtype");
     if (c->max_num_seqs < 1 || c->max_num_seqs > 1024) return bad(PA_ERR_INVALID_ARGUMENT, "max_num_seqs must be 1..1024");
     if (c->max_q_len < 1) return bad(PA_ERR_INVALID_ARGUMENT, "max_q_len must be >= 1");
+    if (c->min_q_len < 1 || c->min_q_len > c->max_q_len)
+        return bad(PA_ERR_INVALID_ARGUMENT, "min_q_len must be 1..max_q_len");
+    if (c->head_dim == 64 && (int64_t)c->max_q_len * (c->num_q_heads / c->num_kv_heads) > 64)
+        return bad(PA_ERR_UNSUPPORTED, "head_dim 64 supports at most 64 rows per KV head");
     if (c->max_num_tokens < 1 || c->max_num_tokens > (int64_t)1 << 24)
         return bad(PA_ERR_INVALID_ARGUMENT, "max_num_tokens must be 1..2^24");
     if ((int64_t)c->max_q_len * (c->num_q_heads / c->num_kv_heads) > (1 << 20))
@@ -130,14 +137,23 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
 
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
     const int D = cfg->head_dim;
-    // Split-partial slots: at most grid + one per (sequence, KV head) for the
-    // VALU kernel (pages per split is raised until the items fit).
+    const int64_t rows_max = (int64_t)cfg->max_q_len * G;
+    // Split-partial slots.  Each kernel raises its split size until its items
+    // fit: the VALU kernel has at most grid + one item per (sequence, KV head),
+    // the MFMA kernel grid + one per (sequence, KV head, row block).
     const int grid_cap = 8 * h->cu_count;
-    h->max_items = grid_cap + cfg->max_num_seqs * cfg->num_kv_heads;
-    h->r_max = cfg->max_q_len * G;
-    h->counter_stride = 1;
-    const size_t o_bytes = (size_t)h->max_items * h->r_max * D * sizeof(float);
-    const size_t l_bytes = (size_t)h->max_items * h->r_max * sizeof(float);
+    h->valu_all_ok = rows_max <= 64;
+    h->r_max_valu = (int)(h->valu_all_ok ? rows_max : kValuRowsMax);
+    h->max_items_valu = grid_cap + cfg->max_num_seqs * cfg->num_kv_heads;
+    h->mfma_wr = rows_max > 64 ? 4 : 1;
+    const int bm = 32 * h->mfma_wr;
+    const int64_t qblocks = ((int64_t)cfg->max_num_tokens * G + bm - 1) / bm + cfg->max_num_seqs;
+    h->max_items_mfma = (int)std::min<int64_t>((int64_t)1 << 30, grid_cap + qblocks * cfg->num_kv_heads);
+    h->counter_stride = (int)((rows_max + 31) / 32);
+    const size_t slots = std::max((size_t)h->max_items_valu * h->r_max_valu,
+                                  D == 128 ? (size_t)h->max_items_mfma * bm : (size_t)0);
+    const size_t o_bytes = slots * D * sizeof(float);
+    const size_t l_bytes = slots * sizeof(float);
     const size_t c_bytes = (size_t)cfg->max_num_seqs * cfg->num_kv_heads * h->counter_stride * sizeof(int);
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     h->ws_bytes = up(o_bytes) + up(l_bytes) + up(c_bytes);
@@ -176,7 +192,10 @@ int paged_attn_set_tuning(pa_handle_t* h, const pa_tuning_t* t) {
         return PA_OK;
     }
     if (t->path < PA_PATH_AUTO || t->path > PA_PATH_MFMA) return fail(h, PA_ERR_INVALID_ARGUMENT, "bad path %d", t->path);
-    if (t->path == PA_PATH_MFMA) return fail(h, PA_ERR_UNSUPPORTED, "the MFMA path is not built");
+    if (t->path == PA_PATH_MFMA && h->cfg.head_dim != 128)
+        return fail(h, PA_ERR_UNSUPPORTED, "the MFMA path needs head_dim 128");
+    if (t->path == PA_PATH_VALU && !h->valu_all_ok)
+        return fail(h, PA_ERR_UNSUPPORTED, "the VALU path holds at most 64 rows per KV head");
     if (t->pages_per_split < 0 || t->kv_tiles_per_split < 0 || t->grid < 0 || t->grid > 8 * h->cu_count)
         return fail(h, PA_ERR_INVALID_ARGUMENT, "tuning values out of range (grid <= %d)", 8 * h->cu_count);
     h->tune = *t;
@@ -247,21 +266,47 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     a.group = G;
     a.window = window;
     a.scale = scale;
-    a.min_pps = kMinPagesPerSplit;
-    a.forced_pps = h->tune.pages_per_split;
-    a.max_items = h->max_items;
-    a.r_max = h->r_max;
     a.counter_stride = h->counter_stride;
     const int grid = h->tune.grid > 0 ? h->tune.grid : h->grid_default;
     a.target_items = grid;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    // Row classes: everything through the VALU kernel until the tile kernel exists.
-    a.rows_lo = 1;
-    a.rows_hi = 1 << 30;
-    const int rw = std::min(kValuRowsMax, pow2ceil(G));
-    hipError_t e = pa::launch_decode_valu(a, c.head_dim, c.kv_dtype, c.q_dtype, rw, grid, st);
-    if (e != hipSuccess) return fail(h, PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    // Rows per KV head decide the kernel: a few rows (decode) stream K/V
+    // through the vector ALUs; verification widths and prefill chunks are
+    // dense enough for the matrix cores.
+    const int rows_min = c.min_q_len * G, rows_max = c.max_q_len * G;
+    bool run_valu, run_mfma;
+    int valu_hi;
+    if (c.head_dim != 128 || h->tune.path == PA_PATH_VALU) {
+        run_valu = true; run_mfma = false; valu_hi = 1 << 30;
+    } else if (h->tune.path == PA_PATH_MFMA) {
+        run_valu = false; run_mfma = true; valu_hi = 0;
+    } else {
+        valu_hi = kValuRowsMax;
+        run_valu = rows_min <= valu_hi;
+        run_mfma = rows_max > valu_hi;
+    }
+    if (run_valu) {
+        a.rows_lo = 1;
+        a.rows_hi = valu_hi;
+        a.min_pps = kMinPagesPerSplit;
+        a.forced_pps = h->tune.pages_per_split;
+        a.max_items = h->max_items_valu;
+        a.r_max = h->r_max_valu;
+        const int rw = std::min(kValuRowsMax, pow2ceil(G));
+        hipError_t e = pa::launch_decode_valu(a, c.head_dim, c.kv_dtype, c.q_dtype, rw, grid, st);
+        if (e != hipSuccess) return fail(h, PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    }
+    if (run_mfma) {
+        a.rows_lo = valu_hi + 1;
+        a.rows_hi = 1 << 30;
+        a.min_pps = 1;
+        a.forced_pps = h->tune.kv_tiles_per_split;
+        a.max_items = h->max_items_mfma;
+        a.r_max = pa::mfma_rows_per_item(h->mfma_wr);
+        hipError_t e = pa::launch_mfma_attn(a, c.head_dim, c.kv_dtype, c.q_dtype, h->mfma_wr, grid, st);
+        if (e != hipSuccess) return fail(h, PA_ERR_HIP, "tile launch failed: %s", hipGetErrorString(e));
+    }
     return PA_OK;
 }
 

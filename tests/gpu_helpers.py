@@ -31,10 +31,13 @@ def progress(msg: str) -> None:
 
 
 def make_handle(inp, max_q_len: Optional[int] = None, max_num_tokens: Optional[int] = None,
-                max_num_seqs: Optional[int] = None, **tuning):
+                max_num_seqs: Optional[int] = None, min_q_len: Optional[int] = None, **tuning):
+    qmax = max_q_len or int(max(inp.q_lens.max(), 1))
+    pos = inp.q_lens[inp.q_lens > 0]
+    qmin = min_q_len or int(pos.min() if pos.size else 1)
     cfg = pal.make_config(inp.num_q_heads, inp.num_kv_heads, inp.head_dim, inp.q_dtype, inp.kv_dtype,
-                          max_num_seqs or inp.num_seqs, max_q_len or int(max(inp.q_lens.max(), 1)),
-                          max_num_tokens or inp.num_tokens, page_size=inp.page_size)
+                          max_num_seqs or inp.num_seqs, qmax, max_num_tokens or inp.num_tokens,
+                          page_size=inp.page_size, min_q_len=min(qmin, qmax))
     h = pal.paged_attn_create(cfg)
     if tuning:
         pal.paged_attn_set_tuning(h, **tuning)
@@ -51,10 +54,11 @@ class GpuCase:
         self.pools = upload_pool(batches, layout=layout)
         self.dev = [upload_batch(b) for b in batches]
         first = batches[0]
+        pos = [int(b.q_lens[b.q_lens > 0].min()) for b in batches if (b.q_lens > 0).any()]
         self.h = handle or make_handle(
             first, max_q_len=max(int(b.q_lens.max()) for b in batches),
             max_num_tokens=max(b.num_tokens for b in batches),
-            max_num_seqs=max(b.num_seqs for b in batches), **tuning)
+            max_num_seqs=max(b.num_seqs for b in batches), min_q_len=min(pos) if pos else 1, **tuning)
         self.own = handle is None
         self.out = [torch.empty((b.num_tokens, b.num_q_heads, b.head_dim), dtype=torch.float32, device="cuda")
                     for b in batches]
