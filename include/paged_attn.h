@@ -104,6 +104,9 @@ typedef struct pa_tuning {
     int32_t pages_per_split;  /* VALU kernel: KV pages per split (0: sized from the live context) */
     int32_t kv_tiles_per_split; /* MFMA kernel: 64-key tiles per split (0: automatic) */
     int32_t grid;             /* workgroups per launch (0: from the CU count) */
+    int32_t split_mode;       /* VALU kernel: 0 automatic, 1 static splits from the block-table
+                                 width (one round trip to start), 2 splits planned on the device
+                                 from the live lengths (balances mixed lengths) */
 } pa_tuning_t;
 
 typedef struct pa_handle pa_handle_t;

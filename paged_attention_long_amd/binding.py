@@ -72,6 +72,7 @@ class pa_tuning_t(ctypes.Structure):
         ("pages_per_split", ctypes.c_int32),
         ("kv_tiles_per_split", ctypes.c_int32),
         ("grid", ctypes.c_int32),
+        ("split_mode", ctypes.c_int32),
     ]
 
 
@@ -177,8 +178,8 @@ def paged_attn_last_error(h: Optional[Handle]) -> str:
 
 
 def paged_attn_set_tuning(h: Handle, path: int = 0, pages_per_split: int = 0, kv_tiles_per_split: int = 0,
-                          grid: int = 0) -> None:
-    t = pa_tuning_t(path, pages_per_split, kv_tiles_per_split, grid)
+                          grid: int = 0, split_mode: int = 0) -> None:
+    t = pa_tuning_t(path, pages_per_split, kv_tiles_per_split, grid, split_mode)
     _check(load_library().paged_attn_set_tuning(h.ptr, ctypes.byref(t)), h.ptr)
 
 

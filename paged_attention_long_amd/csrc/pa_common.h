@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "paged_attn.h"
+#include "pa_kernels.h"
 
 #define PA_DEVINLINE __device__ __forceinline__
 
@@ -145,7 +146,6 @@ PA_DEVINLINE int64_t kv_offset(int64_t page, int g, int slot, int64_t page_strid
 // launch if its rows-per-KV-head count q_len*G lies in [rows_lo, rows_hi].
 // Its visible pages are cut into splits of `pps` pages; an item is one
 // (sequence, KV head, split).
-constexpr int kMaxSplits = 64;   // splits per (sequence, KV head): one merge value per lane
 
 // Per-sequence plan arrays live in dynamic LDS, sized from num_seqs by the
 // host (plan_lds_bytes).

@@ -100,10 +100,11 @@ struct WaveShared {
     float l[kWaves][8];
 };
 
-constexpr int kPidChunk = 1024;   // page ids staged in LDS at a time
+constexpr int kPidChunk = kPidChunkPages;   // page ids staged in LDS at a time
 
 struct Smem {
     Plan plan;
+    int stat[4];
     int pid[kPidChunk];
     union {
         WaveShared ws;
@@ -123,9 +124,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     __shared__ Smem sm;
     extern __shared__ int dyn_lds[];
     Plan& pl = sm.plan;
-    build_plan(pl, dyn_lds, a.seq_lens, a.q_lens, a.num_seqs, a.window, kPage, a.group, a.num_kv_heads, a.rows_lo,
-               a.rows_hi, a.target_items, a.min_pps, a.forced_pps, a.max_items);
-    const int n_items = pl.n_items;
+    if (a.static_pps <= 0)
+        build_plan(pl, dyn_lds, a.seq_lens, a.q_lens, a.num_seqs, a.window, kPage, a.group, a.num_kv_heads,
+                   a.rows_lo, a.rows_hi, a.target_items, a.min_pps, a.forced_pps, a.max_items);
+    const int n_items = (a.static_pps <= 0) ? pl.n_items : 0;
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -139,14 +141,12 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     MergeTarget tgt{a.out, a.lse, a.num_q_heads, a.group, 1.0f};
     const int64_t page_bytes = a.page_stride * EB;
 
-    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-        const int b = item_seq(pl, a.num_seqs, it);
-        const SeqInfo si = seq_info(pl, b, a.window, kPage);
-        const int local = it - pl.item_base[b];
-        const int g = local / si.splits;
-        const int split = local - g * si.splits;
-        const int p_begin = si.first_page + split * pl.pps;
-        const int p_end = min(si.first_page + si.n_pages, p_begin + pl.pps);
+    // One work item: pages [p_begin, p_end) of sequence b, KV head g, whose
+    // partial goes to slot `it`; the (b, g) pair has n_splits items starting
+    // at first_item.  With pid_ready the page ids of the first chunk are
+    // already in sm.pid.
+    auto run_item = [&](const SeqInfo& si, int b, int g, int it, int p_begin, int p_end, int64_t first_item,
+                        int n_splits, bool pid_ready) {
         const int rows = si.q_len * a.group;
         const int n_rg = (rows + RW - 1) / RW;
         const float kscale = (KVT == PA_DTYPE_FP8_E4M3) ? a.kv_scale[g] : 1.0f;
@@ -154,7 +154,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         const float s2 = a.scale * kLog2e * kscale;
         tgt.out_scale = vscale;
         const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
-        const bool direct = (si.splits == 1);
+        const bool direct = (n_splits == 1);
         // byte offset of this lane's chunk inside a page, per round (< 2^31: checked on the host)
         uint32_t lane_off[RPP];
 #pragma unroll
@@ -194,7 +194,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 
             for (int c0 = p_begin; c0 < p_end; c0 += kPidChunk) {
                 const int c1 = min(p_end, c0 + kPidChunk);
-                for (int k = tid; k < c1 - c0; k += kThreads) sm.pid[k] = bt[c0 + k];
+                if (!(pid_ready && c0 == p_begin && rg0 == 0)) {
+                    __syncthreads();
+                    for (int k = tid; k < c1 - c0; k += kThreads) sm.pid[k] = bt[c0 + k];
+                }
                 __syncthreads();
                 if (active) {
                     // Two page buffers in ping-pong: the next page's loads are in flight
@@ -343,12 +346,76 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         }
 
         if (!direct) {
-            const int64_t first_item = pl.item_base[b] + (int64_t)g * si.splits;
-            if (arrive_last(a.counters + ((int64_t)b * a.num_kv_heads + g) * a.counter_stride, si.splits, &sm.flag)) {
-                merge_splits<D>(a.ws_o, a.ws_lse, first_item, si.splits, rows, a.r_max, tgt, si.q_off, g, sm.u.merge);
+            if (arrive_last(a.counters + ((int64_t)b * a.num_kv_heads + g) * a.counter_stride, n_splits, &sm.flag)) {
+                merge_splits<D>(a.ws_o, a.ws_lse, first_item, n_splits, rows, a.r_max, tgt, si.q_off, g, sm.u.merge);
             }
             __syncthreads();
         }
+    };
+
+    if (a.static_pps > 0) {
+        // Static split mode (small batches): workgroup -> (sequence, KV head,
+        // split of static_pps pages counted from page 0).  The sequence's
+        // lengths, its query offset and the split's page ids are fetched in
+        // one round trip; splits outside the visible pages leave at once.
+        const int S = a.static_splits;
+        const int it = blockIdx.x;
+        const int b = it / (a.num_kv_heads * S);
+        const int rem = it - b * a.num_kv_heads * S;
+        const int g = rem / S;
+        const int split = rem - g * S;
+        if (b >= a.num_seqs) return;
+        const int pps = a.static_pps;
+        const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
+        for (int k = tid; k < pps; k += kThreads)
+            sm.pid[k] = (split * pps + k < a.bt_stride) ? bt[split * pps + k] : 0;
+        if (wid == 0) {
+            int qs = 0;
+            for (int b0 = 0; b0 < b; b0 += kWave) qs += (b0 + lane < b) ? a.q_lens[b0 + lane] : 0;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) qs += __shfl_xor(qs, o, kWave);
+            if (lane == 0) {
+                sm.stat[0] = a.seq_lens[b];
+                sm.stat[1] = a.q_lens[b];
+                sm.stat[2] = qs;
+            }
+        }
+        __syncthreads();
+        SeqInfo si;
+        si.seq_len = sm.stat[0];
+        si.q_len = sm.stat[1];
+        si.q_off = sm.stat[2];
+        si.lo = seq_visible_lo(si.seq_len, si.q_len, a.window);
+        si.first_page = si.lo / kPage;
+        const int rows = si.q_len * a.group;
+        if (si.q_len <= 0 || rows < a.rows_lo || rows > a.rows_hi) return;
+        const int last_page = (si.seq_len - 1) / kPage;
+        si.n_pages = last_page - si.first_page + 1;
+        const int s_first = si.first_page / pps, s_last = last_page / pps;
+        if (split < s_first || split > s_last) return;
+        si.splits = s_last - s_first + 1;
+        const int p_begin = max(split * pps, si.first_page);
+        const int p_end = min((split + 1) * pps, last_page + 1);
+        if (p_begin > split * pps) {   // window start inside this split: realign the staged ids
+            __syncthreads();
+            for (int k = tid; k < p_end - p_begin; k += kThreads) sm.pid[k] = bt[p_begin + k];
+            __syncthreads();
+        }
+        const int64_t first_item = (int64_t)(b * a.num_kv_heads + g) * S + s_first;
+        run_item(si, b, g, it, p_begin, p_end, first_item, si.splits, true);
+        return;
+    }
+
+    for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
+        const int b = item_seq(pl, a.num_seqs, it);
+        const SeqInfo si = seq_info(pl, b, a.window, kPage);
+        const int local = it - pl.item_base[b];
+        const int g = local / si.splits;
+        const int split = local - g * si.splits;
+        const int p_begin = si.first_page + split * pl.pps;
+        const int p_end = min(si.first_page + si.n_pages, p_begin + pl.pps);
+        const int64_t first_item = pl.item_base[b] + (int64_t)g * si.splits;
+        run_item(si, b, g, it, p_begin, p_end, first_item, si.splits, false);
     }
 }
 

@@ -6,6 +6,9 @@
 
 namespace pa {
 
+constexpr int kMaxSplits = 64;        // splits per (sequence, KV head) the merge reads in one pass
+constexpr int kPidChunkPages = 1024;  // page ids a workgroup stages in LDS at a time
+
 // Arguments of the split-KV kernels (VALU decode/verify and MFMA tile).
 struct DecodeArgs {
     const void* q;
@@ -28,6 +31,8 @@ struct DecodeArgs {
     int rows_lo, rows_hi;      // rows-per-KV-head class handled by this launch
     int target_items, min_pps, forced_pps, max_items, r_max;   // forced_pps: pages (VALU) or tiles (MFMA) per split
     int counter_stride;        // counters per (sequence, KV head)
+    int static_pps;            // VALU kernel: > 0 selects static splits of this many pages
+    int static_splits;         // splits per (sequence, KV head) in static mode
 };
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int rw, int grid,

@@ -61,10 +61,13 @@ PA_DEVINLINE bool arrive_last(int* counter, int n_splits, int* lds_flag) {
     return last;
 }
 
+constexpr int kMergeBatch = 16;   // partials in flight per thread
+
 // Merge n_splits (<= kMaxSplits) partials of `rows` rows:
 // ws_o[(base + s) * rstride + r][D], ws_lse[(base + s) * rstride + r];
 // write them as rows row0 .. row0 + rows - 1 of KV head g.  All threads of
-// the block call.
+// the block call.  Each thread's first batch of partial rows is requested
+// before the weights are known, so the two reads overlap.
 template <int D>
 PA_DEVINLINE void merge_splits(const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int64_t base,
                                int n_splits, int rows, int rstride, const MergeTarget& t, int q_off, int g,
@@ -73,8 +76,21 @@ PA_DEVINLINE void merge_splits(const float* __restrict__ ws_o, const float* __re
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = threadIdx.x / kWave;
     const int nwaves = nthr / kWave;
+    const int64_t sstride = (int64_t)rstride * D;
     for (int r0 = 0; r0 < rows; r0 += kMergeRows) {
         const int nr = min(kMergeRows, rows - r0);
+        const int n_el = nr * (D / 4);
+        // prefetch the first element's first batch
+        const int e0 = threadIdx.x;
+        float4 pre[kMergeBatch];
+        if (e0 < n_el) {
+            const int rl = e0 / (D / 4);
+            const float* src = ws_o + ((base * rstride) + r0 + rl) * (int64_t)D + (e0 - rl * (D / 4)) * 4;
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k)
+                pre[k] = (k < n_splits) ? *reinterpret_cast<const float4*>(src + k * sstride)
+                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
         for (int rl = wid; rl < nr; rl += nwaves) {
             const float ls = (lane < n_splits) ? ws_lse[(base + lane) * rstride + r0 + rl] : kNegInf;
             const float M = wave_max(ls);
@@ -84,30 +100,35 @@ PA_DEVINLINE void merge_splits(const float* __restrict__ ws_o, const float* __re
             if (lane == 0) sh.lse[rl] = (L > 0.f) ? M + fast_log2(L) : kNegInf;
         }
         __syncthreads();
-        for (int e = threadIdx.x; e < nr * (D / 4); e += nthr) {
+        for (int e = e0; e < n_el; e += nthr) {
             const int rl = e / (D / 4);
             const int d4 = (e - rl * (D / 4)) * 4;
             const float* src = ws_o + ((base * rstride) + r0 + rl) * (int64_t)D + d4;
-            const int64_t sstride = (int64_t)rstride * D;
-            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-            for (int s0 = 0; s0 < n_splits; s0 += 8) {
-                float4 o[8];
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
+                float4 o[kMergeBatch];
+                if (e == e0 && s0 == 0) {
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    o[k] = (s0 + k < n_splits) ? *reinterpret_cast<const float4*>(src + (s0 + k) * sstride)
-                                               : make_float4(0.f, 0.f, 0.f, 0.f);
+                    for (int k = 0; k < kMergeBatch; ++k) o[k] = pre[k];
+                } else {
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
+                    for (int k = 0; k < kMergeBatch; ++k)
+                        o[k] = (s0 + k < n_splits) ? *reinterpret_cast<const float4*>(src + (s0 + k) * sstride)
+                                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+#pragma unroll
+                for (int k = 0; k < kMergeBatch; ++k) {
                     const float w = (s0 + k < n_splits) ? sh.w[rl][s0 + k] : 0.f;
-                    a0 = fmaf(w, o[k].x, a0);
-                    a1 = fmaf(w, o[k].y, a1);
-                    a2 = fmaf(w, o[k].z, a2);
-                    a3 = fmaf(w, o[k].w, a3);
+                    acc.x = fmaf(w, o[k].x, acc.x);
+                    acc.y = fmaf(w, o[k].y, acc.y);
+                    acc.z = fmaf(w, o[k].z, acc.z);
+                    acc.w = fmaf(w, o[k].w, acc.w);
                 }
             }
             const float sc = t.out_scale;
             const int64_t orow = out_row(t, q_off, g, row0 + r0 + rl);
-            *reinterpret_cast<float4*>(t.out + orow * D + d4) = make_float4(a0 * sc, a1 * sc, a2 * sc, a3 * sc);
+            *reinterpret_cast<float4*>(t.out + orow * D + d4) =
+                make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
             if (t.lse != nullptr && d4 == 0) {
                 const float l2 = sh.lse[rl];
                 t.lse[orow] = (l2 == kNegInf) ? kNegInf : l2 * kLn2;

@@ -196,7 +196,8 @@ int paged_attn_set_tuning(pa_handle_t* h, const pa_tuning_t* t) {
         return fail(h, PA_ERR_UNSUPPORTED, "the MFMA path needs head_dim 128");
     if (t->path == PA_PATH_VALU && !h->valu_all_ok)
         return fail(h, PA_ERR_UNSUPPORTED, "the VALU path holds at most 64 rows per KV head");
-    if (t->pages_per_split < 0 || t->kv_tiles_per_split < 0 || t->grid < 0 || t->grid > 8 * h->cu_count)
+    if (t->pages_per_split < 0 || t->kv_tiles_per_split < 0 || t->grid < 0 || t->grid > 8 * h->cu_count ||
+        t->split_mode < 0 || t->split_mode > 2)
         return fail(h, PA_ERR_INVALID_ARGUMENT, "tuning values out of range (grid <= %d)", 8 * h->cu_count);
     h->tune = *t;
     return PA_OK;
@@ -294,10 +295,37 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         a.max_items = h->max_items_valu;
         a.r_max = h->r_max_valu;
         const int rw = std::min(kValuRowsMax, pow2ceil(G));
-        hipError_t e = pa::launch_decode_valu(a, c.head_dim, c.kv_dtype, c.q_dtype, rw, grid, st);
+        // Static splits: a workgroup's (sequence, KV head, split) follows from
+        // its index, so its first loads need no plan.  Used for one sequence
+        // or a batch whose whole block-table capacity is small; the device
+        // plan balances mixed lengths otherwise.
+        int vgrid = grid;
+        a.static_pps = 0;
+        a.static_splits = 0;
+        {
+            const int64_t cap_pages = (int64_t)block_table_stride;
+            const int64_t units = (int64_t)num_seqs * c.num_kv_heads * cap_pages;
+            int64_t pps = h->tune.pages_per_split > 0
+                              ? h->tune.pages_per_split
+                              : std::max<int64_t>(kMinPagesPerSplit, (units + grid - 1) / grid);
+            pps = std::max<int64_t>(pps, (cap_pages + pa::kMaxSplits - 1) / pa::kMaxSplits);
+            if (h->tune.pages_per_split <= 0) pps = (pps + kMinPagesPerSplit - 1) / kMinPagesPerSplit * kMinPagesPerSplit;
+            const int64_t S = (cap_pages + pps - 1) / pps;
+            const int64_t items = (int64_t)num_seqs * c.num_kv_heads * S;
+            const bool small = num_seqs == 1 || units <= (int64_t)4 * kMinPagesPerSplit * grid;
+            const bool want = h->tune.split_mode == 1 || (h->tune.split_mode == 0 && small);
+            if (want && pps <= pa::kPidChunkPages && items <= h->max_items_valu && items <= 8 * h->cu_count) {
+                a.static_pps = (int)pps;
+                a.static_splits = (int)S;
+                vgrid = (int)items;
+            }
+        }
+        hipError_t e = pa::launch_decode_valu(a, c.head_dim, c.kv_dtype, c.q_dtype, rw, vgrid, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
     }
     if (run_mfma) {
+        a.static_pps = 0;
+        a.static_splits = 0;
         a.rows_lo = valu_hi + 1;
         a.rows_hi = 1 << 30;
         a.min_pps = 1;

@@ -40,13 +40,15 @@ SMALL = {
 }
 
 
+@pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("name", list(SMALL))
-def test_small_parity(name):
+def test_small_parity(name, mode):
+    """mode: VALU-kernel split mode (0 automatic, 1 static, 2 device plan)."""
     inp = generate(_spec(name=name, **SMALL[name]))[0]
-    progress(f"small parity {name}: seqs={inp.seq_lens.tolist()} q_lens={inp.q_lens.tolist()} "
+    progress(f"small parity {name} mode {mode}: seqs={inp.seq_lens.tolist()} q_lens={inp.q_lens.tolist()} "
              f"kv={inp.kv_dtype} D={inp.head_dim} G={inp.group} W={inp.window}")
     ref_o, ref_l = oracle.attention(inp)
-    c = GpuCase([inp])
+    c = GpuCase([inp], split_mode=mode)
     try:
         out, lse = c.run()
     finally:
@@ -134,13 +136,14 @@ def test_deterministic_and_reusable():
     assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
 
 
+@pytest.mark.parametrize("mode", [1, 2])
 @pytest.mark.parametrize("pps", [1, 4, 7, 100000])
-def test_split_count_invariance(pps):
+def test_split_count_invariance(pps, mode):
     """Forcing the split size changes only the summation order."""
     inp = generate(_spec(seq_lens=(4097, 900), q_lens=(1, 3), q_dtype="f16", kv_dtype="f16"))[0]
-    progress(f"split invariance pps={pps}")
+    progress(f"split invariance pps={pps} mode={mode}")
     ref_o, ref_l = oracle.attention(inp)
-    c = GpuCase([inp], path=pal.PA_PATH_VALU, pages_per_split=pps)
+    c = GpuCase([inp], path=pal.PA_PATH_VALU, pages_per_split=pps, split_mode=mode)
     try:
         out, lse = c.run()
     finally:
@@ -148,10 +151,11 @@ def test_split_count_invariance(pps):
     compare(f"pps={pps}", inp.kv_dtype, out, lse, ref_o, ref_l)
 
 
-def test_rotating_batches_share_a_pool():
+@pytest.mark.parametrize("mode", [1, 2])
+def test_rotating_batches_share_a_pool(mode):
     """Consecutive calls on different batches (split counters must reset)."""
     bs = generate(_spec(seq_lens=(2049,), q_lens=(1,)), batches=3)
-    c = GpuCase(bs)
+    c = GpuCase(bs, split_mode=mode)
     try:
         for i, b in enumerate(bs):
             ref_o, ref_l = oracle.attention(b)
