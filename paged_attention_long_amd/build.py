@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpaged_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["paged_attn.cpp", "pa_decode_valu.hip", "pa_mfma_attn.hip", "pa_gather.hip"]
+SOURCES = ["paged_attn.cpp", "pa_decode_valu.hip", "pa_tile_attn.hip", "pa_gather.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",
@@ -50,6 +50,10 @@ def build(verbose: bool = True, extra=()) -> str:
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
         raise RuntimeError(f"hipcc failed ({res.returncode})")
+    # a library with an unresolved symbol must fail the build, not the first caller
+    import ctypes
+
+    ctypes.CDLL(os.path.abspath(tmp))
     os.replace(tmp, LIB)
     if verbose:
         warn = [l for l in res.stderr.splitlines() if "warning" in l and "packed-fp32-ops" not in l]

@@ -2,34 +2,41 @@
 // verification-width query blocks.
 //
 // A work item is (sequence, KV head, block of BM query rows, split of the
-// KV tiles).  Query rows of one KV head are token-major (row = i*G + h), so
-// a row block holds the G query heads of consecutive new tokens and every
-// K/V tile it loads is reused by all of them (grouped-query sharing, as in
-// "Dual MI50, part 2", section "Decode: a new kernel for the shape MTP
-// actually runs"), and large query tiles amortise each tile load ("Dual MI50,
-// part 2", section "Prefill: teach the fork's fast kernel to read the int8
-// cache": going from 16 to 64 query rows per tile was 1.8x).
+// KV tiles).  Query rows of one KV head are token-major (row = i*G + h), so a
+// row block holds the G query heads of consecutive new tokens and every K/V
+// tile it loads is reused by all of them (grouped-query sharing, "Dual MI50,
+// part 2", section "Decode: a new kernel for the shape MTP actually runs"),
+// and big query tiles amortise each tile load ("Dual MI50, part 2", section
+// "Prefill: teach the fork's fast kernel to read the int8 cache": 16 to 64
+// query rows per tile was 1.8x there).
+//
+// Two shapes share the code:
+//   * WR = 4 (prefill): four waves own 32 rows each (BM = 128) and share
+//     64-key tiles in LDS;
+//   * WR = 1 (verification widths, <= 64 rows per KV head): each wave owns the
+//     same 32 rows and streams its own 32-key tiles through its own LDS
+//     buffers, so the tile loop has no workgroup barrier; the four waves'
+//     softmax states are merged at the end.
 //
 // Per tile of BN keys (BN/16 pages gathered through the block table):
-//   * K is staged row-major in LDS, V transposed (V^T[d][key]) so that the
-//     key dimension, which P.V contracts, is contiguous for the MFMA operand;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q^T
-//     held in registers for the whole item): each lane then holds 16 keys of
-//     one query row, so the row max / sum need one cross-half exchange;
-//   * online softmax in fp32 with an exact running max (a row's largest
-//     weight is exactly 1); masked keys are set to -inf by select and dead
-//     keys' K and V are zeroed when staged, so NaN in freed pages never
-//     reaches a product;
-//   * P^T is rounded to the MFMA input type in registers and O^T = V^T P^T is
-//     accumulated in fp32; the output is normalised by the sum of the rounded
-//     weights (a weighted mean with exactly normalised weights), the lse by
-//     the sum of the fp32 weights; at verification widths, which are bound
-//     by memory, a second MFMA adds the rounding error of P;
-//   * the next tile's global loads are issued before the current tile is
-//     computed (register prefetch) and written to LDS after it.
-// fp8 (E4M3FN) K is widened to the query's type and fp8 V to fp16 while
-// staging; both conversions are exact.  Splits are merged by the last
-// workgroup to finish (pa_merge.h).
+//   * 16-bit K and V arrive by asynchronous global->LDS loads (no staging
+//     registers), double-buffered, row-major with the 16-byte chunks of a row
+//     XOR-swizzled by the row index so that both operand reads are free of
+//     bank conflicts; fp8 (E4M3FN) K/V are loaded to registers, widened
+//     exactly (K to the query type, V to fp16) and written in the same layout;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q^T held
+//     in registers): each lane then holds 16 keys of one query row;
+//   * V^T operands come straight from the row-major V tile through the
+//     gfx950 transposing LDS read (ds_read_b64_tr_b16): four lanes' 8-byte
+//     reads of four key rows come back as four keys of one head-dim column;
+//   * online softmax in fp32 with an exact running max; masked keys are set
+//     to -inf by select and dead keys' V rows are zeroed in LDS, so NaN in
+//     freed pages never reaches a product;
+//   * P^T is rounded to the MFMA input type; the output is normalised by the
+//     sum of the rounded weights, the lse by the sum of the fp32 weights; at
+//     verification widths (memory-bound) and while a row has few effective
+//     keys, a second MFMA adds P's rounding error.
+// Splits are merged by the last workgroup to finish (pa_merge.h).
 #include "pa_common.h"
 #include "pa_merge.h"
 #include "pa_kernels.h"
@@ -40,10 +47,14 @@ namespace {
 
 constexpr int kPage = 16;
 constexpr float kSplitBelow = 32.0f;   // weight sum below which P.V also runs on P's rounding error
+constexpr int kRowBytes = 256;         // one K or V row in LDS: 128 16-bit elements
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 template <int T>
 PA_DEVINLINE f32x16_t mma32(const u32x4_t& a, const u32x4_t& b, const f32x16_t& c) {
@@ -55,13 +66,11 @@ PA_DEVINLINE f32x16_t mma32(const u32x4_t& a, const u32x4_t& b, const f32x16_t& 
                                                       0, 0, 0);
 }
 
-// Round two floats to the 16-bit type T (RNE) and pack.
 template <int T>
 PA_DEVINLINE uint32_t pack2(float x, float y) {
     if constexpr (T == PA_DTYPE_BF16) return f32x2_to_bf16x2(f32x2_t{x, y});
     else return f32x2_to_f16x2(f32x2_t{x, y});
 }
-// The two packed values back as floats (exact).
 template <int T>
 PA_DEVINLINE float unpack_lo(uint32_t u) {
     if constexpr (T == PA_DTYPE_BF16) return bf16lo_to_f32(u);
@@ -72,13 +81,30 @@ PA_DEVINLINE float unpack_hi(uint32_t u) {
     if constexpr (T == PA_DTYPE_BF16) return bf16hi_to_f32(u);
     else return f16x2_to_f32(u).y;
 }
-template <int T>
-PA_DEVINLINE float unpack_sum(uint32_t u) {
-    return unpack_lo<T>(u) + unpack_hi<T>(u);
+
+// s_waitcnt immediates (gfx9 layout: vmcnt[3:0] in bits 3:0, expcnt in 6:4,
+// lgkmcnt in 11:8, vmcnt[5:4] in 15:14); a field at its maximum is not waited on.
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int kWaitLgkm0 = 15 | (7 << 4) | (0 << 8) | (3 << 14);
+
+// Asynchronous 16-byte load per lane into LDS: lane l's bytes land at
+// lds + 16*l (gfx950 global_load_lds_dwordx4).  The body exists only in the
+// device compilation pass (the host pass never runs kernel code).
+PA_DEVINLINE void async_load16(const void* src, lds_void_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, lds, 16, 0, 0);
+#else
+    (void)src;
+    (void)lds;
+#endif
 }
+
+// Byte offset of 16-byte chunk c of row r inside a tile (swizzled).
+PA_DEVINLINE int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 15)) << 4); }
 
 template <int D, int KVT, int QT, int WR>
 struct Cfg {
+    static_assert(D == 128, "the tile kernel is built for head_dim 128");
     static constexpr int WK = 4 / WR;                      // wave groups along keys
     static constexpr int BN = (WR == 4) ? 64 : 32;         // keys per tile
     static constexpr int PPT = BN / kPage;                 // pages per tile
@@ -88,17 +114,16 @@ struct Cfg {
     static constexpr int DB = D / 32;                      // 32-wide head-dim blocks of O^T
     static constexpr int NB = BN / 32;                     // 32-key blocks of S^T
     static constexpr int TS = BN / 16;                     // 16-key k-steps of P.V
-    static constexpr int KROW = D + 8;                     // K tile row stride in LDS (elements)
-    static constexpr int VROW = BN + 8;                    // V^T tile row stride in LDS (elements)
-    static constexpr int EB = (KVT == PA_DTYPE_FP8_E4M3) ? 1 : 2;
-    static constexpr int KCH = BN * (D / 8) / NT;          // 8-element K chunks per thread
-    static constexpr int VUN = (BN / 4) * (D / 8) / NT;    // (4 keys x 8 elements) V units per thread
-    static constexpr int PVT = (KVT == PA_DTYPE_FP8_E4M3) ? PA_DTYPE_F16 : KVT;  // P.V operand type
-    // Verification widths are bound by memory, so P.V runs twice there: on the
-    // rounded weights and on their rounding error (near-exact P).
-    static constexpr bool PSPLIT = (WR == 1);
-    static_assert(KCH >= 1 && VUN >= 1, "tile too small for the thread count");
-    static constexpr int GROUP_LDS = (BN * KROW + D * VROW) * 2;   // bytes per wave group
+    static constexpr bool FP8 = (KVT == PA_DTYPE_FP8_E4M3);
+    static constexpr int EB = FP8 ? 1 : 2;
+    static constexpr int PVT = FP8 ? PA_DTYPE_F16 : KVT;   // P.V operand type
+    static constexpr bool PSPLIT = (WR == 1);              // memory-bound: P.V always on the split P
+    static constexpr int TILE = BN * kRowBytes;            // bytes of one K (or V) tile in LDS
+    static constexpr int NBUF = FP8 ? 1 : 2;               // LDS buffers per wave group
+    static constexpr int GROUP_LDS = NBUF * 2 * TILE;
+    static constexpr int DMA_PER_WAVE = BN * kRowBytes / 1024 / WR;   // 1 KB async loads per wave per tile
+    // fp8 register staging: 8-element chunks per thread per tile
+    static constexpr int FCH = BN * (D / 8) / NT;
 };
 
 template <int KVT>
@@ -110,94 +135,83 @@ struct Raw<PA_DTYPE_BF16> { using T = u32x4_t; };
 template <>
 struct Raw<PA_DTYPE_FP8_E4M3> { using T = u32x2_t; };
 
-// Eight raw cache elements -> four packed pairs of type T (exact).
-template <int KVT, int T>
-PA_DEVINLINE u32x4_t widen8(const typename Raw<KVT>::T& c) {
-    if constexpr (KVT == PA_DTYPE_FP8_E4M3) {
-        u32x4_t r;
+template <int T>
+PA_DEVINLINE u32x4_t widen_fp8x8(const u32x2_t& c) {
+    u32x4_t r;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const f32x2_t lo = fp8x2_to_f32(c[i], false);
-            const f32x2_t hi = fp8x2_to_f32(c[i], true);
-            if constexpr (T == PA_DTYPE_BF16) {
-                r[2 * i] = f32x2_to_bf16x2(lo);
-                r[2 * i + 1] = f32x2_to_bf16x2(hi);
-            } else {
-                r[2 * i] = f32x2_to_f16x2(lo);
-                r[2 * i + 1] = f32x2_to_f16x2(hi);
-            }
+    for (int i = 0; i < 2; ++i) {
+        const f32x2_t lo = fp8x2_to_f32(c[i], false);
+        const f32x2_t hi = fp8x2_to_f32(c[i], true);
+        if constexpr (T == PA_DTYPE_BF16) {
+            r[2 * i] = f32x2_to_bf16x2(lo);
+            r[2 * i + 1] = f32x2_to_bf16x2(hi);
+        } else {
+            r[2 * i] = f32x2_to_f16x2(lo);
+            r[2 * i + 1] = f32x2_to_f16x2(hi);
         }
-        return r;
-    } else {
-        return c;
     }
+    return r;
 }
 
-template <int KVT>
-PA_DEVINLINE typename Raw<KVT>::T load_raw(const uint8_t* p) {
-    if constexpr (KVT == PA_DTYPE_FP8_E4M3) return load_b64(p);
-    else return load_b128(p);
-}
-
-template <int KVT>
-PA_DEVINLINE typename Raw<KVT>::T zero_raw() {
-    typename Raw<KVT>::T z;
-    if constexpr (KVT == PA_DTYPE_FP8_E4M3) { z[0] = 0; z[1] = 0; }
-    else { z[0] = 0; z[1] = 0; z[2] = 0; z[3] = 0; }
-    return z;
-}
-
-// Per-item geometry shared by all waves.
 struct ItemGeom {
-    int b, g, qt, split;
+    int b, g, qt, split, splits;
     SeqInfo si;
-    int row0;            // first row (of the KV head's rows) of this item
-    int rows;            // valid rows in this item (<= BM)
-    int pg_first;        // first logical page of tile 0
-    int pg_end;          // one past the last page with visible keys
-    int n_tiles;         // tiles of this row block
-    int t_begin, t_end;  // tiles of this split
-    int splits;
+    int row0, rows;
+    int pg_first, pg_end;
+    int n_tiles, t_begin, t_end;
 };
 
 template <int D, int KVT, int QT, int WR>
-__global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void tile_attn_kernel(DecodeArgs a) {
     using C = Cfg<D, KVT, QT, WR>;
-    using RawT = typename Raw<KVT>::T;
     constexpr int BM = C::BM, BN = C::BN, PPT = C::PPT;
 
     __shared__ Plan pl;
     __shared__ int flag;
-    __shared__ __attribute__((aligned(16))) uint8_t tiles[C::WK * C::GROUP_LDS];
-    __shared__ float red_m[4][32];   // per wave: row max / sum exchange for the WK merge
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[C::WK * C::GROUP_LDS];
+    __shared__ float red_m[4][32];
     __shared__ float red_l[4][32];
     __shared__ float red_e[4][32];
+    __shared__ long long redw[8], redq[8];
     extern __shared__ int dyn_lds[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wid = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int gi = wid / WR;            // wave group (own KV tile stream)
-    const int rb = wid % WR;            // row block of this wave
-    const int gtid = tid - gi * C::NT;  // thread index inside the group
-    const int h32 = lane >> 5;          // lane half
+    const int gi = wid / WR;             // wave group (own K/V tile stream)
+    const int rb = wid % WR;             // row block of this wave
+    const int wig = wid % WR;            // wave index inside its group
+    const int gtid = tid - gi * C::NT;   // thread index inside the group
+    const int h32 = lane >> 5;
     const int l32 = lane & 31;
 
-    uint16_t* Ks = reinterpret_cast<uint16_t*>(tiles + gi * C::GROUP_LDS);
-    uint16_t* Vt = Ks + BN * C::KROW;
+    uint8_t* gbase = tiles + gi * C::GROUP_LDS;
+    auto kbuf = [&](int buf) { return gbase + buf * 2 * C::TILE; };
+    auto vbuf = [&](int buf) { return gbase + buf * 2 * C::TILE + C::TILE; };
 
     // ---------------------------------------------------------------- plan
-    // A sequence is in this launch if q_len*G lies in [rows_lo, rows_hi].
-    // Its rows form ceil(rows/BM) row blocks; each row block's visible keys
-    // are cut into tiles of BN keys; tiles are grouped into `splits` splits
-    // of `tps` tiles (the same for every row block of the sequence).
+    // A sequence is in this launch if q_len*G lies in [rows_lo, rows_hi].  Its
+    // rows form ceil(rows/BM) row blocks; each row block's visible keys are cut
+    // into tiles of BN keys; tiles are grouped into `splits` splits (the same
+    // number for every row block of the sequence).
     plan_bind(pl, dyn_lds, a.num_seqs);
+    auto widest_tiles = [&](int sl, int ql) {
+        const int rows = ql * a.group;
+        const int nqt = (rows + BM - 1) / BM;
+        int tub = 0;
+        for (int q = max(0, nqt - 2); q < nqt; ++q) {
+            const int r0 = q * BM, r1 = min(rows, r0 + BM) - 1;
+            const int p0 = sl - ql + r0 / a.group, p1 = sl - ql + r1 / a.group;
+            const int klo = a.window > 0 ? max(0, p0 - a.window + 1) : 0;
+            const int pages = p1 / kPage - klo / kPage + 1;
+            tub = max(tub, (pages + PPT - 1) / PPT);
+        }
+        return tub;
+    };
     {
         const int nthr = blockDim.x;
-        long long work = 0;
-        long long qtiles = 0;
-        int max_tiles = 0;
-        int carry_q = 0;
+        long long work = 0, qtiles = 0;
+        int max_tiles = 0, carry_q = 0;
         for (int b0 = 0; b0 < a.num_seqs; b0 += nthr) {
             const int b = b0 + tid;
             int ql = 0, nqt = 0, tub = 0;
@@ -209,14 +223,7 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
                 const int rows = ql * a.group;
                 if (ql > 0 && rows >= a.rows_lo && rows <= a.rows_hi) {
                     nqt = (rows + BM - 1) / BM;
-                    // widest key range over the row blocks: the last full or the last block
-                    for (int q = max(0, nqt - 2); q < nqt; ++q) {
-                        const int r0 = q * BM, r1 = min(rows, r0 + BM) - 1;
-                        const int p0 = sl - ql + r0 / a.group, p1 = sl - ql + r1 / a.group;
-                        const int klo = a.window > 0 ? max(0, p0 - a.window + 1) : 0;
-                        const int pages = p1 / kPage - klo / kPage + 1;
-                        tub = max(tub, (pages + PPT - 1) / PPT);
-                    }
+                    tub = widest_tiles(sl, ql);
                 }
                 pl.aux[b] = tub;
                 pl.item_base[b] = nqt;   // temporary
@@ -225,16 +232,14 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
             const int ex = block_exclusive_scan(ql, pl.red, &tot);
             if (b < a.num_seqs) pl.q_off[b] = carry_q + ex;
             carry_q += tot;
-            long long w = (long long)nqt * tub;
+            long long w = (long long)nqt * tub, nq = nqt;
             int mt = tub;
-            long long nq = nqt;
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) {
                 w += __shfl_xor(w, o, 64);
                 nq += __shfl_xor(nq, o, 64);
                 mt = max(mt, __shfl_xor(mt, o, 64));
             }
-            __shared__ long long redw[8], redq[8];
             if (lane == 0) { redw[wid] = w; redq[wid] = nq; pl.red[16 + wid] = mt; }
             __syncthreads();
             for (int ww = 0; ww < (int)(blockDim.x / 64); ++ww) {
@@ -269,7 +274,7 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
                 const int nqt = pl.item_base[b];
                 const int S = (pl.aux[b] + tps - 1) / tps;
                 it = nqt * a.num_kv_heads * S;
-                pl.aux[b] = S;   // splits per (sequence, KV head, row block)
+                pl.aux[b] = S;
             }
             int tot;
             const int ex = block_exclusive_scan(it, pl.red, &tot);
@@ -290,34 +295,25 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
     const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.v_cache);
     const uint16_t* qbase = reinterpret_cast<const uint16_t*>(a.q);
     const int64_t page_bytes = a.page_stride * C::EB;
+    const int64_t tok_bytes = a.token_stride * C::EB;
 
     for (int it = blockIdx.x; it < n_items; it += gridDim.x) {
-        // ------------------------------------------------------------ item geometry
+        // ------------------------------------------------------------ item geometry (uniform)
         ItemGeom ig;
-        ig.b = item_seq(pl, a.num_seqs, it);
-        ig.si.seq_len = pl.seq_len[ig.b];
-        ig.si.q_len = pl.q_len[ig.b];
-        ig.si.q_off = pl.q_off[ig.b];
+        ig.b = __builtin_amdgcn_readfirstlane(item_seq(pl, a.num_seqs, it));
+        ig.si.seq_len = __builtin_amdgcn_readfirstlane(pl.seq_len[ig.b]);
+        ig.si.q_len = __builtin_amdgcn_readfirstlane(pl.q_len[ig.b]);
+        ig.si.q_off = __builtin_amdgcn_readfirstlane(pl.q_off[ig.b]);
         ig.si.lo = seq_visible_lo(ig.si.seq_len, ig.si.q_len, a.window);
-        ig.splits = pl.aux[ig.b];
+        ig.splits = __builtin_amdgcn_readfirstlane(pl.aux[ig.b]);
         {
-            const int local = it - pl.item_base[ig.b];
+            const int local = it - __builtin_amdgcn_readfirstlane(pl.item_base[ig.b]);
             const int per_qt = a.num_kv_heads * ig.splits;
             ig.qt = local / per_qt;
             const int rem = local - ig.qt * per_qt;
             ig.g = rem / ig.splits;
             ig.split = rem - ig.g * ig.splits;
         }
-        // every field is the same in all lanes; keep it in scalar registers
-        ig.b = __builtin_amdgcn_readfirstlane(ig.b);
-        ig.g = __builtin_amdgcn_readfirstlane(ig.g);
-        ig.qt = __builtin_amdgcn_readfirstlane(ig.qt);
-        ig.split = __builtin_amdgcn_readfirstlane(ig.split);
-        ig.splits = __builtin_amdgcn_readfirstlane(ig.splits);
-        ig.si.seq_len = __builtin_amdgcn_readfirstlane(ig.si.seq_len);
-        ig.si.q_len = __builtin_amdgcn_readfirstlane(ig.si.q_len);
-        ig.si.q_off = __builtin_amdgcn_readfirstlane(ig.si.q_off);
-        ig.si.lo = __builtin_amdgcn_readfirstlane(ig.si.lo);
         const int rows_all = ig.si.q_len * a.group;
         ig.row0 = ig.qt * BM;
         ig.rows = min(BM, rows_all - ig.row0);
@@ -328,36 +324,25 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
         ig.pg_end = pos_last / kPage + 1;
         ig.n_tiles = (ig.pg_end - ig.pg_first + PPT - 1) / PPT;
         {
-            // tiles per split of this sequence (same for every row block)
-            const int rows_b = rows_all;
-            const int nqt = (rows_b + BM - 1) / BM;
-            int tub = 0;
-            for (int q = max(0, nqt - 2); q < nqt; ++q) {
-                const int r0 = q * BM, r1 = min(rows_b, r0 + BM) - 1;
-                const int p0 = ig.si.seq_len - ig.si.q_len + r0 / a.group;
-                const int p1 = ig.si.seq_len - ig.si.q_len + r1 / a.group;
-                const int kl = a.window > 0 ? max(0, p0 - a.window + 1) : 0;
-                const int pages = p1 / kPage - kl / kPage + 1;
-                tub = max(tub, (pages + PPT - 1) / PPT);
-            }
+            const int tub = widest_tiles(ig.si.seq_len, ig.si.q_len);
             const int tpsb = (tub + ig.splits - 1) / ig.splits;
             ig.t_begin = min(ig.n_tiles, ig.split * tpsb);
             ig.t_end = min(ig.n_tiles, ig.t_begin + tpsb);
         }
-        const float kscale = (KVT == PA_DTYPE_FP8_E4M3) ? a.kv_scale[ig.g] : 1.0f;
-        const float vscale = (KVT == PA_DTYPE_FP8_E4M3) ? a.kv_scale[a.num_kv_heads + ig.g] : 1.0f;
+        const float kscale = C::FP8 ? a.kv_scale[ig.g] : 1.0f;
+        const float vscale = C::FP8 ? a.kv_scale[a.num_kv_heads + ig.g] : 1.0f;
         const float s2 = a.scale * kLog2e * kscale;
         const int32_t* bt = a.block_table + (int64_t)ig.b * a.bt_stride;
         const bool direct = (ig.splits == 1);
+        const int64_t head_off = kv_offset(0, ig.g, 0, a.page_stride, a.head_stride, a.token_stride) * C::EB;
 
         // ------------------------------------------------------------ this lane's query row
-        const int row_l = rb * 32 + l32;               // row within the item
-        const int row_g = ig.row0 + row_l;             // row within the KV head
+        const int row_l = rb * 32 + l32;
+        const int row_g = ig.row0 + row_l;
         const bool row_ok = row_l < ig.rows;
         const int tok_i = row_ok ? row_g / a.group : 0;
         const int pos_r = row_ok ? ig.si.seq_len - ig.si.q_len + tok_i : -1;
         const int lo_r = (a.window > 0) ? pos_r - a.window + 1 : 0;
-        // rows of this wave: position range, for the "tile needs no mask" test
         const int w_row0 = ig.row0 + rb * 32;
         const int w_rows = max(0, min(32, ig.rows - rb * 32));
         const int w_pmin = ig.si.seq_len - ig.si.q_len + w_row0 / a.group;
@@ -380,111 +365,90 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o_acc[db][i] = 0.f;
-        float m_run = kNegInf;
-        float l_run = 0.f;      // sum of the rounded weights that multiplied V (output normalisation)
-        float l_exact = 0.f;    // sum of the fp32 weights (lse)
+        float m_run = kNegInf, l_run = 0.f, l_exact = 0.f;
 
-        // ------------------------------------------------------------ staging
-        // The PPT page ids of a tile are the same for the whole workgroup:
-        // they are read with scalar loads one tile ahead of the K/V loads.
-        RawT kraw[C::KCH];
-        RawT vraw[C::VUN][4];
-        // K chunk c: key ch / (D/8), element (ch % (D/8)) * 8 (a wave reads whole rows).
-        // V unit u: keys 4*(un % (BN/4)) .. +3, element (un / (BN/4)) * 8 (keys fastest, so
-        // the transposed LDS writes of a wave fall in distinct banks).
-        // Loads are unconditional so the wait counts stay exact: a page past
-        // the visible range reads the last visible page's id, and dead keys
-        // (outside [lo, seq_len) or past that page) are zeroed when stored.
-        auto load_pids = [&](int t, int (&pid)[PPT]) {
+        // ------------------------------------------------------------ tile staging
+        // Tile t covers logical pages pg_first + t*PPT ...; a page past the
+        // visible range reads the last visible page (in bounds) and its keys
+        // are dead.  Key k of a tile is live iff it lies in [lo, seq_len).
+        // The block table is read-only while the kernel runs: read it through
+        // the constant address space so the wave-uniform page ids come from
+        // scalar loads, which do not wait behind the asynchronous tile loads.
+        const __attribute__((address_space(4))) int32_t* bt_c =
+            (const __attribute__((address_space(4))) int32_t*)bt;
+        auto tile_pid = [&](int t, int p) {
+            const int pg = __builtin_amdgcn_readfirstlane(min(ig.pg_first + t * PPT + p, ig.pg_end - 1));
+            return bt_c[pg];
+        };
+        auto key_pos = [&](int t, int key) { return (ig.pg_first + t * PPT) * kPage + key; };
+        auto row_src = [&](const uint8_t* base, const int (&pid)[PPT], int key) -> const uint8_t* {
+            return base + (int64_t)pid[key / kPage] * page_bytes + head_off + (int64_t)(key % kPage) * tok_bytes;
+        };
+        // 16-bit caches: asynchronous loads straight into LDS.  Async load i of a
+        // group covers tile rows 4i .. 4i+3; lane l fills row 4i + l/16, physical
+        // chunk l%16, which holds logical chunk (l%16) ^ (row & 15).
+        auto dma_tile = [&](int t, int buf) {
+            int pid[PPT];
 #pragma unroll
-            for (int p = 0; p < PPT; ++p) {
-                const int pg = min(ig.pg_first + t * PPT + p, ig.pg_end - 1);
-                pid[p] = bt[pg];
+            for (int p = 0; p < PPT; ++p) pid[p] = tile_pid(t, p);
+#pragma unroll
+            for (int ii = 0; ii < C::DMA_PER_WAVE; ++ii) {
+                const int i = ii * WR + wig;
+                const int row = 4 * i + (lane >> 4);
+                const int c = (lane & 15) ^ (row & 15);
+                const int off = i * 1024;
+                async_load16(row_src(kbase, pid, row) + c * 16, (lds_void_t*)(kbuf(buf) + off));
+                async_load16(row_src(vbase, pid, row) + c * 16, (lds_void_t*)(vbuf(buf) + off));
             }
         };
-        auto key_live = [&](int t, int key) -> bool {
-            const int pg = ig.pg_first + t * PPT + key / kPage;
-            const int j = pg * kPage + key % kPage;
-            return pg < ig.pg_end && j >= ig.si.lo && j < ig.si.seq_len;
-        };
-        const int64_t head_off = kv_offset(0, ig.g, 0, a.page_stride, a.head_stride, a.token_stride) * C::EB;
-        auto key_off = [&](const int (&pid)[PPT], int key) -> int64_t {
-            return (int64_t)pid[key / kPage] * page_bytes + head_off + (int64_t)(key % kPage) * a.token_stride * C::EB;
-        };
-        uint32_t live_k = 0, live_v = 0;      // live masks of the staged chunks
-        auto load_tile = [&](int t, const int (&pid)[PPT]) {
-            live_k = 0;
-            live_v = 0;
+        // fp8 caches: registers, widened, then written in the same layout.
+        typename Raw<KVT>::T fk[C::FCH], fv[C::FCH];
+        auto fp8_load = [&](int t) {
+            int pid[PPT];
 #pragma unroll
-            for (int c = 0; c < C::KCH; ++c) {
+            for (int p = 0; p < PPT; ++p) pid[p] = tile_pid(t, p);
+#pragma unroll
+            for (int c = 0; c < C::FCH; ++c) {
                 const int ch = gtid + c * C::NT;
-                const int key = ch / (D / 8), e = (ch % (D / 8)) * 8;
-                kraw[c] = load_raw<KVT>(kbase + key_off(pid, key) + e * C::EB);
-                live_k |= key_live(t, key) ? (1u << c) : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < C::VUN; ++u) {
-                const int un = gtid + u * C::NT;
-                const int k4 = (un % (BN / 4)) * 4, e = (un / (BN / 4)) * 8;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    vraw[u][q] = load_raw<KVT>(vbase + key_off(pid, k4 + q) + e * C::EB);
-                    live_v |= key_live(t, k4 + q) ? (1u << (4 * u + q)) : 0u;
+                const int key = ch / (D / 8), e = ch % (D / 8);
+                if constexpr (C::FP8) {
+                    fk[c] = load_b64(row_src(kbase, pid, key) + e * 8);
+                    fv[c] = load_b64(row_src(vbase, pid, key) + e * 8);
                 }
             }
         };
-        auto store_tile = [&]() {
+        auto fp8_store = [&](int buf) {
 #pragma unroll
-            for (int c = 0; c < C::KCH; ++c) {
+            for (int c = 0; c < C::FCH; ++c) {
                 const int ch = gtid + c * C::NT;
-                const int key = ch / (D / 8), e = (ch % (D / 8)) * 8;
-                const RawT r = (live_k >> c) & 1u ? kraw[c] : zero_raw<KVT>();
-                *reinterpret_cast<u32x4_t*>(Ks + key * C::KROW + e) = widen8<KVT, QT>(r);
-            }
-#pragma unroll
-            for (int u = 0; u < C::VUN; ++u) {
-                const int un = gtid + u * C::NT;
-                const int k4 = (un % (BN / 4)) * 4, e = (un / (BN / 4)) * 8;
-                u32x4_t w[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    w[q] = widen8<KVT, C::PVT>((live_v >> (4 * u + q)) & 1u ? vraw[u][q] : zero_raw<KVT>());
-                // transpose 4 keys x 8 elements into V^T[e + x][k4 .. k4 + 3]
-#pragma unroll
-                for (int x = 0; x < 4; ++x) {
-                    // element pair (2x, 2x+1) of each key
-                    const uint32_t lo01 = __builtin_amdgcn_perm(w[1][x], w[0][x], 0x05040100u);
-                    const uint32_t lo23 = __builtin_amdgcn_perm(w[3][x], w[2][x], 0x05040100u);
-                    const uint32_t hi01 = __builtin_amdgcn_perm(w[1][x], w[0][x], 0x07060302u);
-                    const uint32_t hi23 = __builtin_amdgcn_perm(w[3][x], w[2][x], 0x07060302u);
-                    *reinterpret_cast<u32x2_t*>(Vt + (e + 2 * x) * C::VROW + k4) = u32x2_t{lo01, lo23};
-                    *reinterpret_cast<u32x2_t*>(Vt + (e + 2 * x + 1) * C::VROW + k4) = u32x2_t{hi01, hi23};
+                const int key = ch / (D / 8), e = ch % (D / 8);
+                if constexpr (C::FP8) {
+                    *reinterpret_cast<u32x4_t*>(kbuf(buf) + swz(key, e)) = widen_fp8x8<QT>(fk[c]);
+                    *reinterpret_cast<u32x4_t*>(vbuf(buf) + swz(key, e)) = widen_fp8x8<C::PVT>(fv[c]);
                 }
             }
         };
+        // Zero the V rows of dead keys (only tiles that touch a range edge).
+        auto zero_dead_v = [&](int t, int buf) {
+            const int k0 = key_pos(t, 0);
+            const bool edge = (k0 < ig.si.lo) || (k0 + BN > ig.si.seq_len) || (ig.pg_first + (t + 1) * PPT > ig.pg_end);
+            if (!edge) return false;
+            for (int e = gtid; e < BN * 16; e += C::NT) {
+                const int key = e >> 4, c = e & 15;
+                const int j = k0 + key;
+                const bool live = (j >= ig.si.lo) && (j < ig.si.seq_len) && (ig.pg_first + t * PPT + key / kPage < ig.pg_end);
+                if (!live) *reinterpret_cast<u32x4_t*>(vbuf(buf) + swz(key, c)) = u32x4_t{0u, 0u, 0u, 0u};
+            }
+            return true;
+        };
+        // Synchronise the wave group after LDS writes (WR == 1: one wave).
+        auto group_sync = [&]() {
+            if constexpr (WR == 1) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wave's LDS writes are done
+            else __syncthreads();
+        };
 
-        // ------------------------------------------------------------ tile loop
-        const int my_first = ig.t_begin + gi;
-        const int n_iter = (ig.t_end - ig.t_begin + C::WK - 1) / C::WK;
-        int pid_next[PPT];                     // page ids of the tile after the one in flight
-        if (n_iter > 0) {
-            int pid0[PPT];
-            load_pids(my_first, pid0);
-            load_tile(my_first, pid0);
-            load_pids(my_first + C::WK, pid_next);
-        }
-        for (int iter = 0; iter < n_iter; ++iter) {
-            const int t = my_first + iter * C::WK;
-            const bool have = t < ig.t_end;
-            __syncthreads();                  // previous tile's LDS reads are done
-            if (have) store_tile();
-            __syncthreads();
-            const int tn = t + C::WK;
-            if (iter + 1 < n_iter) load_tile(tn, pid_next);   // in flight while this tile is computed
-            load_pids(tn + C::WK, pid_next);
-            if (!have) continue;
-
-            // S^T = K Q^T: NB blocks of 32 keys x 32 rows
+        // ------------------------------------------------------------ compute one tile
+        auto compute_tile = [&](int t, const uint8_t* kb, const uint8_t* vb) {
             f32x16_t sacc[C::NB];
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
@@ -492,13 +456,12 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
                 for (int i = 0; i < 16; ++i) sacc[nb][i] = 0.f;
 #pragma unroll
                 for (int s = 0; s < C::KS; ++s) {
-                    const u32x4_t kf =
-                        *reinterpret_cast<const u32x4_t*>(Ks + (nb * 32 + l32) * C::KROW + 16 * s + 8 * h32);
+                    const int r = nb * 32 + l32;
+                    const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kb + swz(r, 2 * s + h32));
                     sacc[nb] = mma32<QT>(kf, qreg[s], sacc[nb]);
                 }
             }
-            // scale, mask, tile max
-            const int key0 = (ig.pg_first + t * PPT) * kPage;   // position of the tile's first key
+            const int key0 = key_pos(t, 0);
             const bool full = (key0 >= w_lomax) && (key0 + BN - 1 <= w_pmin) && (key0 >= ig.si.lo) &&
                               (key0 + BN <= ig.si.seq_len) && (ig.pg_first + (t + 1) * PPT <= ig.pg_end);
             float tmax = kNegInf;
@@ -517,12 +480,9 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
                 }
             }
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-            // exact running max: the largest weight of a row is exactly 1, so a
-            // row dominated by one key loses nothing to the rounding of P
             if (wave_any(tmax > m_run)) {
                 const float mn = fmaxf(m_run, tmax);
                 const float al = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - mn);
-                // rows whose max did not move keep al == 1 (mn == m_run)
                 m_run = mn;
                 l_run *= al;
                 l_exact *= al;
@@ -531,7 +491,6 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) o_acc[db][i] *= al;
             }
-            // P^T (rounded to the P.V type) and O^T += V^T P^T
             u32x4_t pb[C::TS];
 #pragma unroll
             for (int ts = 0; ts < C::TS; ++ts) {
@@ -545,13 +504,15 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
                     sacc[nb][i0 + 2 * j + 1] = p1;
                     l_exact += p0 + p1;
                     pb[ts][j] = pack2<C::PVT>(p0, p1);
-                    l_run += unpack_sum<C::PVT>(pb[ts][j]);
+                    l_run += unpack_lo<C::PVT>(pb[ts][j]) + unpack_hi<C::PVT>(pb[ts][j]);
                 }
             }
-            // While a row has few effective keys (small weight sum), rounding P
-            // to 8 or 11 bits is visible in the output: add a second P.V on the
-            // rounding error.  Always on at verification widths (memory-bound).
             const bool split = C::PSPLIT || wave_any(l_exact < kSplitBelow);
+            // V^T operand (d = db*32 + l32, keys 16ts + 4h .. +3 and 16ts + 8 + 4h .. +3)
+            // by transposing reads: within each 16-lane group, source lane s reads
+            // row kb + s/4 at columns cb + 4(s%4) .. +3; lane j gets 4 keys of column cb + j.
+            const int s16 = lane & 15;
+            const int cq = (lane >> 4) & 1;     // which 16-column half of the 32-wide d block
 #pragma unroll
             for (int ts = 0; ts < C::TS; ++ts) {
                 const int nb = ts / 2, i0 = 8 * (ts % 2);
@@ -561,28 +522,74 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
                     for (int j = 0; j < 4; ++j) {
                         pl2[j] = pack2<C::PVT>(sacc[nb][i0 + 2 * j] - unpack_lo<C::PVT>(pb[ts][j]),
                                                sacc[nb][i0 + 2 * j + 1] - unpack_hi<C::PVT>(pb[ts][j]));
-                        l_run += unpack_sum<C::PVT>(pl2[j]);
+                        l_run += unpack_lo<C::PVT>(pl2[j]) + unpack_hi<C::PVT>(pl2[j]);
                     }
                 }
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db) {
-                    const uint16_t* vr = Vt + (db * 32 + l32) * C::VROW + 16 * ts + 4 * h32;
-                    const u32x2_t va = *reinterpret_cast<const u32x2_t*>(vr);
-                    const u32x2_t vb = *reinterpret_cast<const u32x2_t*>(vr + 8);
-                    const u32x4_t vf = {va[0], va[1], vb[0], vb[1]};
+                    const int col = db * 32 + cq * 16 + 4 * (s16 & 3);     // this source lane's 4 columns
+                    const int ra = 16 * ts + 4 * h32 + (s16 >> 2);          // first key group row
+                    const int rbv = ra + 8;                                 // second key group row
+                    const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4_t*)(vb + swz(ra, col >> 3) + (col & 7) * 2));
+                    const i16x4_t vbb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4_t*)(vb + swz(rbv, col >> 3) + (col & 7) * 2));
+                    const u32x2_t a2 = __builtin_bit_cast(u32x2_t, va);
+                    const u32x2_t b2 = __builtin_bit_cast(u32x2_t, vbb);
+                    const u32x4_t vf = {a2[0], a2[1], b2[0], b2[1]};
                     o_acc[db] = mma32<C::PVT>(vf, pb[ts], o_acc[db]);
                     if (split) o_acc[db] = mma32<C::PVT>(vf, pl2, o_acc[db]);
                 }
             }
+        };
+
+        // ------------------------------------------------------------ tile loop
+        const int my_first = ig.t_begin + gi;
+        const int n_iter = (ig.t_end - ig.t_begin + C::WK - 1) / C::WK;
+        if constexpr (!C::FP8) {
+            // double-buffered asynchronous loads; buffers alternate by iteration parity
+            if (n_iter > 0) dma_tile(min(my_first, ig.t_end - 1), 0);
+            if (n_iter > 1) dma_tile(min(my_first + C::WK, ig.t_end - 1), 1);
+            for (int iter = 0; iter < n_iter; iter += 2) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int itn = iter + half;
+                    if (itn < n_iter) {
+                        const int t = my_first + itn * C::WK;
+                        const bool have = t < ig.t_end;
+                        // this buffer's loads are the older ones in flight
+                        if (itn + 1 < n_iter) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * C::DMA_PER_WAVE));
+                        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+                        if constexpr (WR > 1) __syncthreads();
+                        if (have) {
+                            if (zero_dead_v(t, half)) group_sync();
+                            compute_tile(t, kbuf(half), vbuf(half));
+                        }
+                        if constexpr (WR > 1) __syncthreads();    // everyone is done with this buffer
+                        if (itn + 2 < n_iter) dma_tile(min(t + 2 * C::WK, ig.t_end - 1), half);
+                    }
+                }
+            }
+        } else {
+            if (n_iter > 0) fp8_load(min(my_first, ig.t_end - 1));
+            for (int iter = 0; iter < n_iter; ++iter) {
+                const int t = my_first + iter * C::WK;
+                const bool have = t < ig.t_end;
+                if constexpr (WR > 1) __syncthreads();
+                fp8_store(0);
+                if (have) zero_dead_v(t, 0);
+                group_sync();
+                if (iter + 1 < n_iter) fp8_load(min(t + C::WK, ig.t_end - 1));
+                if (have) compute_tile(t, kbuf(0), vbuf(0));
+                if constexpr (WR == 1) __builtin_amdgcn_wave_barrier();
+            }
         }
 
-        // ------------------------------------------------------------ finish the row
-        // each row lives in lanes l32 and l32 + 32 (same m_run); sum their l
+        // ------------------------------------------------------------ finish the rows
         float L = l_run + __shfl_xor(l_run, 32, 64);
         float LE = l_exact + __shfl_xor(l_exact, 32, 64);
         float M = m_run;
         if (C::WK > 1) {
-            // combine the WK wave groups (same rows, disjoint tiles) through LDS
             __syncthreads();
             if (h32 == 0) { red_m[wid][l32] = M; red_l[wid][l32] = L; red_e[wid][l32] = LE; }
             __syncthreads();
@@ -598,7 +605,6 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
                 Lx += red_l[w * WR + rb][l32] * f;
                 LEx += red_e[w * WR + rb][l32] * f;
             }
-            // reuse the tile LDS as a [WK][32][D] fp32 reduction buffer per row block
             __syncthreads();
             float* accbuf = reinterpret_cast<float*>(tiles);
 #pragma unroll
@@ -606,9 +612,9 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int d = db * 32 + 8 * jj + 4 * h32;
-                    float4 v = make_float4(o_acc[db][4 * jj] * al, o_acc[db][4 * jj + 1] * al, o_acc[db][4 * jj + 2] * al,
-                                           o_acc[db][4 * jj + 3] * al);
-                    *reinterpret_cast<float4*>(accbuf + ((gi * WR + rb) * 32 + l32) * D + d) = v;
+                    *reinterpret_cast<float4*>(accbuf + ((gi * WR + rb) * 32 + l32) * D + d) =
+                        make_float4(o_acc[db][4 * jj] * al, o_acc[db][4 * jj + 1] * al, o_acc[db][4 * jj + 2] * al,
+                                    o_acc[db][4 * jj + 3] * al);
                 }
             __syncthreads();
             if (gi == 0) {
@@ -636,12 +642,12 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
             if (direct) {
                 const int64_t orow = out_row(tgt, ig.si.q_off, ig.g, row_g);
                 float* op = a.out + orow * D;
+                const float sc = inv * vscale;
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int d = db * 32 + 8 * jj + 4 * h32;
-                        const float sc = inv * vscale;
                         *reinterpret_cast<float4*>(op + d) =
                             make_float4(o_acc[db][4 * jj] * sc, o_acc[db][4 * jj + 1] * sc, o_acc[db][4 * jj + 2] * sc,
                                         o_acc[db][4 * jj + 3] * sc);
@@ -656,8 +662,8 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
                     for (int jj = 0; jj < 4; ++jj) {
                         const int d = db * 32 + 8 * jj + 4 * h32;
                         *reinterpret_cast<float4*>(op + d) =
-                            make_float4(o_acc[db][4 * jj] * inv, o_acc[db][4 * jj + 1] * inv, o_acc[db][4 * jj + 2] * inv,
-                                        o_acc[db][4 * jj + 3] * inv);
+                            make_float4(o_acc[db][4 * jj] * inv, o_acc[db][4 * jj + 1] * inv,
+                                        o_acc[db][4 * jj + 2] * inv, o_acc[db][4 * jj + 3] * inv);
                     }
                 if (h32 == 0) a.ws_lse[slot] = (LE > 0.f) ? M + fast_log2(LE) : kNegInf;
             }
@@ -680,7 +686,7 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(DecodeArgs a) {
 
 template <int D, int KVT, int QT, int WR>
 static hipError_t launch_t(const DecodeArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((mfma_attn_kernel<D, KVT, QT, WR>), dim3(grid), dim3(256), plan_lds_bytes(a.num_seqs), st, a);
+    hipLaunchKernelGGL((tile_attn_kernel<D, KVT, QT, WR>), dim3(grid), dim3(256), plan_lds_bytes(a.num_seqs), st, a);
     return hipGetLastError();
 }
 
