@@ -140,9 +140,10 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out);
  *  q_lens       device int32 [num_seqs]: new rows, 0 <= q_len <= min(seq_len,
  *               cfg.max_q_len); sum must equal num_tokens.
  *  window       host int: <= 0 no window; W >= 1 the W most recent keys.
- *  scale        host float: multiplies q.k (after dequantisation).
+ *  scale        host float > 0: multiplies q.k (after dequantisation).
  *  kv_scale     device float [2][Hkv] (K scales, then V scales) for an fp8
- *               cache: k~ = code * kv_scale[0][g], v~ = code * kv_scale[1][g].
+ *               cache: k~ = code * kv_scale[0][g], v~ = code * kv_scale[1][g];
+ *               every scale > 0.
  *               Must be NULL for fp16/bf16 caches.
  *  out          device float [T][Hq][D].
  *  lse          device float [T][Hq] (natural log), or NULL.
@@ -151,7 +152,7 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out);
  * Device-array contents (block table, lengths) are trusted: they are not
  * read on the host.  Violating the documented ranges is undefined.
  * Returns PA_ERR_INVALID_ARGUMENT for a rejected host argument (null or
- * misaligned pointer, size out of range, scale not finite, kv_scale given
+ * misaligned pointer, size out of range, scale not finite and positive, kv_scale given
  * or missing), PA_ERR_HIP if the launch fails.
  */
 int paged_attn_forward(pa_handle_t* h,

@@ -32,14 +32,17 @@
 //   * online softmax in fp32 with an exact running max; masked keys are set
 //     to -inf by select and dead keys' V rows are zeroed in LDS, so NaN in
 //     freed pages never reaches a product;
-//   * P^T is rounded to the MFMA input type; the output is normalised by the
-//     sum of the rounded weights, the lse by the sum of the fp32 weights; at
-//     verification widths (memory-bound) and while a row has few effective
-//     keys, a second MFMA adds P's rounding error.
+//   * P^T is rounded to the MFMA input type and output and lse are
+//     normalised by the fp32 weight sum; at verification widths
+//     (memory-bound) and while a row has few effective keys, a second MFMA
+//     adds P's rounding error, so rows dominated by a few keys keep full
+//     precision.
 // Splits are merged by the last workgroup to finish (pa_merge.h).
 #include "pa_common.h"
 #include "pa_merge.h"
 #include "pa_kernels.h"
+
+#include <utility>
 
 namespace pa {
 
@@ -99,8 +102,45 @@ PA_DEVINLINE void async_load16(const void* src, lds_void_t* lds) {
 #endif
 }
 
-// Byte offset of 16-byte chunk c of row r inside a tile (swizzled).
-PA_DEVINLINE int swz(int r, int c) { return r * kRowBytes + ((c ^ (r & 15)) << 4); }
+// Byte offset of 16-byte chunk c of row r inside a tile.  Rows are 256 B (one
+// full pass over the banks), so the chunk index is XOR-ed with a row key that
+// puts the row's low two bits into the chunk's high two bits: the K operand
+// read (16 rows, one chunk each) and the transposing V read (4 consecutive
+// rows x 4 consecutive chunks per 32 lanes) both land in distinct banks.
+PA_DEVINLINE int swz_key(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+PA_DEVINLINE int swz(int r, int c) { return r * kRowBytes + ((c ^ swz_key(r)) << 4); }
+
+// Eight transposing 64-bit LDS reads (ds_read_b64_tr_b16) at addr[k] + OFF,
+// completed inside the block.  Inline asm because the compiler cannot tell
+// which LDS object the transposing-read builtin touches and would make it
+// wait for every asynchronous tile load in flight, including the prefetch
+// into the other buffer.  Outputs are early-clobber: each read lands while
+// later addresses are still being consumed.
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <typename F, int... I>
+PA_DEVINLINE void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+PA_DEVINLINE void static_for(F&& f) { static_for_impl(f, std::make_integer_sequence<int, N>{}); }
+
+template <int OFF>
+PA_DEVINLINE void lds_read_tr16_x8(const uint32_t (&addr)[8], u32x2_t (&r)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %1, %9 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %2, %10 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %3, %11 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %4, %12 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %5, %13 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %6, %14 offset:%16\n\t"
+        "ds_read_b64_tr_b16 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+          "v"(addr[7]), "i"(OFF)
+        : "memory");
+}
 
 template <int D, int KVT, int QT, int WR>
 struct Cfg {
@@ -162,15 +202,18 @@ struct ItemGeom {
 };
 
 template <int D, int KVT, int QT, int WR>
-__global__ __launch_bounds__(256) void tile_attn_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tile_attn_kernel(DecodeArgs a) {
     using C = Cfg<D, KVT, QT, WR>;
     constexpr int BM = C::BM, BN = C::BN, PPT = C::PPT;
 
     __shared__ Plan pl;
     __shared__ int flag;
-    __shared__ __attribute__((aligned(1024))) uint8_t tiles[C::WK * C::GROUP_LDS];
+    // Two distinct LDS objects for the two buffers: the compiler tracks
+    // asynchronous LDS loads per object, so reading one buffer does not wait
+    // for the loads still in flight into the other.
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[C::WK * C::GROUP_LDS / C::NBUF];
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles2[C::NBUF > 1 ? C::WK * C::GROUP_LDS / C::NBUF : 16];
     __shared__ float red_m[4][32];
-    __shared__ float red_l[4][32];
     __shared__ float red_e[4][32];
     __shared__ long long redw[8], redq[8];
     extern __shared__ int dyn_lds[];
@@ -184,10 +227,27 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(DecodeArgs a) {
     const int gtid = tid - gi * C::NT;   // thread index inside the group
     const int h32 = lane >> 5;
     const int l32 = lane & 31;
+    // Transposing V reads (PV operand, d = db*32 + l32, keys 16ts + 4h32 .. +3
+    // and 16ts + 8 + 4h32 .. +3): within each 16-lane group source lane s
+    // reads tile row 4h32 + s/4 (+8) at columns cq*16 + 4(s%4) .. +3 of d block
+    // db; lane j of the group receives 4 keys of column j.  Byte offsets for
+    // ts = 0 (read 2db, then 2db+1 for the +8 rows).
+    uint32_t v_lane_off[8];
+    {
+        const int s16 = lane & 15, cq = (lane >> 4) & 1;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int col = db * 32 + cq * 16 + 4 * (s16 & 3);
+                const int row = 4 * h32 + (s16 >> 2) + 8 * hh;
+                v_lane_off[2 * db + hh] = (uint32_t)(swz(row, col >> 3) + (col & 7) * 2);
+            }
+    }
 
-    uint8_t* gbase = tiles + gi * C::GROUP_LDS;
-    auto kbuf = [&](int buf) { return gbase + buf * 2 * C::TILE; };
-    auto vbuf = [&](int buf) { return gbase + buf * 2 * C::TILE + C::TILE; };
+    // buffer b of wave group gi: K tile then V tile
+    auto kbuf = [&](int buf) { return (buf == 0 ? tiles : tiles2) + gi * 2 * C::TILE; };
+    auto vbuf = [&](int buf) { return (buf == 0 ? tiles : tiles2) + gi * 2 * C::TILE + C::TILE; };
 
     // ---------------------------------------------------------------- plan
     // A sequence is in this launch if q_len*G lies in [rows_lo, rows_hi].  Its
@@ -365,7 +425,7 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(DecodeArgs a) {
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o_acc[db][i] = 0.f;
-        float m_run = kNegInf, l_run = 0.f, l_exact = 0.f;
+        float m_run = kNegInf, l_exact = 0.f;
 
         // ------------------------------------------------------------ tile staging
         // Tile t covers logical pages pg_first + t*PPT ...; a page past the
@@ -387,6 +447,14 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(DecodeArgs a) {
         // 16-bit caches: asynchronous loads straight into LDS.  Async load i of a
         // group covers tile rows 4i .. 4i+3; lane l fills row 4i + l/16, physical
         // chunk l%16, which holds logical chunk (l%16) ^ (row & 15).
+        // Per-lane byte offset inside its page for async load ii (constant per item).
+        uint32_t dma_off[C::DMA_PER_WAVE];
+#pragma unroll
+        for (int ii = 0; ii < C::DMA_PER_WAVE; ++ii) {
+            const int row = 4 * (ii * WR + wig) + (lane >> 4);
+            const int c = (lane & 15) ^ swz_key(row);
+            dma_off[ii] = (uint32_t)(head_off + (int64_t)(row % kPage) * tok_bytes + c * 16);
+        }
         auto dma_tile = [&](int t, int buf) {
             int pid[PPT];
 #pragma unroll
@@ -394,11 +462,9 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(DecodeArgs a) {
 #pragma unroll
             for (int ii = 0; ii < C::DMA_PER_WAVE; ++ii) {
                 const int i = ii * WR + wig;
-                const int row = 4 * i + (lane >> 4);
-                const int c = (lane & 15) ^ (row & 15);
-                const int off = i * 1024;
-                async_load16(row_src(kbase, pid, row) + c * 16, (lds_void_t*)(kbuf(buf) + off));
-                async_load16(row_src(vbase, pid, row) + c * 16, (lds_void_t*)(vbuf(buf) + off));
+                const int64_t pb = (int64_t)pid[(4 * i) / kPage] * page_bytes;   // page of rows 4i .. 4i+3
+                async_load16(kbase + pb + dma_off[ii], (lds_void_t*)(kbuf(buf) + i * 1024));
+                async_load16(vbase + pb + dma_off[ii], (lds_void_t*)(vbuf(buf) + i * 1024));
             }
         };
         // fp8 caches: registers, widened, then written in the same layout.
@@ -449,97 +515,111 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(DecodeArgs a) {
 
         // ------------------------------------------------------------ compute one tile
         auto compute_tile = [&](int t, const uint8_t* kb, const uint8_t* vb) {
+            // S^T = K Q^T: all K fragments of the tile are read first, then the
+            // MFMAs run back to back (the scheduling barriers keep the reads
+            // grouped instead of one read / wait / MFMA at a time).
+            u32x4_t kf[C::NB][C::KS];
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                for (int s = 0; s < C::KS; ++s)
+                    kf[nb][s] = *reinterpret_cast<const u32x4_t*>(kb + swz(nb * 32 + l32, 2 * s + h32));
             f32x16_t sacc[C::NB];
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) sacc[nb][i] = 0.f;
 #pragma unroll
-                for (int s = 0; s < C::KS; ++s) {
-                    const int r = nb * 32 + l32;
-                    const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(kb + swz(r, 2 * s + h32));
-                    sacc[nb] = mma32<QT>(kf, qreg[s], sacc[nb]);
-                }
+                for (int s = 0; s < C::KS; ++s) sacc[nb] = mma32<QT>(kf[nb][s], qreg[s], sacc[nb]);
             }
+            __builtin_amdgcn_sched_group_barrier(0x100, C::NB * C::KS, 0);   // LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, C::NB * C::KS, 0);   // MFMAs
+            // Scores stay unscaled (s2 > 0 preserves the order): the running max
+            // m_run is kept in scaled units and p = 2^(s*s2 - m_run) is one fma
+            // and one exp.  Masked keys become -inf by select.
             const int key0 = key_pos(t, 0);
             const bool full = (key0 >= w_lomax) && (key0 + BN - 1 <= w_pmin) && (key0 >= ig.si.lo) &&
                               (key0 + BN <= ig.si.seq_len) && (ig.pg_first + (t + 1) * PPT <= ig.pg_end);
-            float tmax = kNegInf;
+            if (!full) {
 #pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb) {
+                for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float x = sacc[nb][i] * s2;
-                    if (!full) {
+                    for (int i = 0; i < 16; ++i) {
                         const int j = key0 + nb * 32 + 8 * (i / 4) + 4 * h32 + (i % 4);
                         const bool vis = (j <= pos_r) && (j >= lo_r) && (j >= ig.si.lo) && (j < ig.si.seq_len);
-                        x = vis ? x : kNegInf;
+                        sacc[nb][i] = vis ? sacc[nb][i] : kNegInf;
                     }
-                    sacc[nb][i] = x;
-                    tmax = fmaxf(tmax, x);
-                }
             }
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            float tmax = kNegInf;
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(sacc[nb][i], sacc[nb][i + 1]));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * s2;
             if (wave_any(tmax > m_run)) {
                 const float mn = fmaxf(m_run, tmax);
                 const float al = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - mn);
                 m_run = mn;
-                l_run *= al;
                 l_exact *= al;
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) o_acc[db][i] *= al;
             }
+            // a row that has seen no visible key yet keeps m_run = -inf; its p are 0
+            const float nm = (m_run == kNegInf) ? 0.f : -m_run;
             u32x4_t pb[C::TS];
 #pragma unroll
             for (int ts = 0; ts < C::TS; ++ts) {
                 const int nb = ts / 2, i0 = 8 * (ts % 2);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float x0 = sacc[nb][i0 + 2 * j], x1 = sacc[nb][i0 + 2 * j + 1];
-                    const float p0 = (x0 == kNegInf) ? 0.f : fast_exp2(x0 - m_run);
-                    const float p1 = (x1 == kNegInf) ? 0.f : fast_exp2(x1 - m_run);
+                    const float p0 = fast_exp2(fmaf(sacc[nb][i0 + 2 * j], s2, nm));
+                    const float p1 = fast_exp2(fmaf(sacc[nb][i0 + 2 * j + 1], s2, nm));
                     sacc[nb][i0 + 2 * j] = p0;
                     sacc[nb][i0 + 2 * j + 1] = p1;
                     l_exact += p0 + p1;
                     pb[ts][j] = pack2<C::PVT>(p0, p1);
-                    l_run += unpack_lo<C::PVT>(pb[ts][j]) + unpack_hi<C::PVT>(pb[ts][j]);
                 }
             }
             const bool split = C::PSPLIT || wave_any(l_exact < kSplitBelow);
-            // V^T operand (d = db*32 + l32, keys 16ts + 4h .. +3 and 16ts + 8 + 4h .. +3)
-            // by transposing reads: within each 16-lane group, source lane s reads
-            // row kb + s/4 at columns cb + 4(s%4) .. +3; lane j gets 4 keys of column cb + j.
-            const int s16 = lane & 15;
-            const int cq = (lane >> 4) & 1;     // which 16-column half of the 32-wide d block
+            // V^T operands by transposing reads.  Row 16ts + r0 has the same swizzle key for every ts, so one set of
+            // eight lane addresses serves the whole tile with ts in the offset.
+            uint32_t va[8];
+            const uint32_t vb32 = (uint32_t)(uintptr_t)(lds_void_t*)vb;
 #pragma unroll
-            for (int ts = 0; ts < C::TS; ++ts) {
-                const int nb = ts / 2, i0 = 8 * (ts % 2);
-                u32x4_t pl2;
-                if (split) {
+            for (int k = 0; k < 8; ++k) va[k] = vb32 + v_lane_off[k];
+            auto v_frags = [&](auto ts_c, u32x4_t (&vf)[C::DB]) {
+                constexpr int ts = decltype(ts_c)::value;
+                u32x2_t r[8];
+                lds_read_tr16_x8<ts * 16 * kRowBytes>(va, r);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                for (int db = 0; db < C::DB; ++db) vf[db] = u32x4_t{r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]};
+            };
+            if (split) {
+                static_for<C::TS>([&](auto ts_c) {
+                    constexpr int ts = decltype(ts_c)::value;
+                    const int nb = ts / 2, i0 = 8 * (ts % 2);
+                    u32x4_t vf[C::DB], pl2;
+                    v_frags(ts_c, vf);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
                         pl2[j] = pack2<C::PVT>(sacc[nb][i0 + 2 * j] - unpack_lo<C::PVT>(pb[ts][j]),
                                                sacc[nb][i0 + 2 * j + 1] - unpack_hi<C::PVT>(pb[ts][j]));
-                        l_run += unpack_lo<C::PVT>(pl2[j]) + unpack_hi<C::PVT>(pl2[j]);
-                    }
-                }
 #pragma unroll
-                for (int db = 0; db < C::DB; ++db) {
-                    const int col = db * 32 + cq * 16 + 4 * (s16 & 3);     // this source lane's 4 columns
-                    const int ra = 16 * ts + 4 * h32 + (s16 >> 2);          // first key group row
-                    const int rbv = ra + 8;                                 // second key group row
-                    const i16x4_t va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4_t*)(vb + swz(ra, col >> 3) + (col & 7) * 2));
-                    const i16x4_t vbb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_i16x4_t*)(vb + swz(rbv, col >> 3) + (col & 7) * 2));
-                    const u32x2_t a2 = __builtin_bit_cast(u32x2_t, va);
-                    const u32x2_t b2 = __builtin_bit_cast(u32x2_t, vbb);
-                    const u32x4_t vf = {a2[0], a2[1], b2[0], b2[1]};
-                    o_acc[db] = mma32<C::PVT>(vf, pb[ts], o_acc[db]);
-                    if (split) o_acc[db] = mma32<C::PVT>(vf, pl2, o_acc[db]);
-                }
+                    for (int db = 0; db < C::DB; ++db) {
+                        o_acc[db] = mma32<C::PVT>(vf[db], pb[ts], o_acc[db]);
+                        o_acc[db] = mma32<C::PVT>(vf[db], pl2, o_acc[db]);
+                    }
+                });
+            } else {
+                static_for<C::TS>([&](auto ts_c) {
+                    constexpr int ts = decltype(ts_c)::value;
+                    u32x4_t vf[C::DB];
+                    v_frags(ts_c, vf);
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) o_acc[db] = mma32<C::PVT>(vf[db], pb[ts], o_acc[db]);
+                });
             }
         };
 
@@ -586,23 +666,22 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(DecodeArgs a) {
         }
 
         // ------------------------------------------------------------ finish the rows
-        float L = l_run + __shfl_xor(l_run, 32, 64);
         float LE = l_exact + __shfl_xor(l_exact, 32, 64);
+        float L = LE;
         float M = m_run;
         if (C::WK > 1) {
             __syncthreads();
-            if (h32 == 0) { red_m[wid][l32] = M; red_l[wid][l32] = L; red_e[wid][l32] = LE; }
+            if (h32 == 0) { red_m[wid][l32] = M; red_e[wid][l32] = LE; }
             __syncthreads();
             float Mx = kNegInf;
 #pragma unroll
             for (int w = 0; w < C::WK; ++w) Mx = fmaxf(Mx, red_m[w * WR + rb][l32]);
             const float al = (M == kNegInf) ? 0.f : fast_exp2(M - Mx);
-            float Lx = 0.f, LEx = 0.f;
+            float LEx = 0.f;
 #pragma unroll
             for (int w = 0; w < C::WK; ++w) {
                 const float mw = red_m[w * WR + rb][l32];
                 const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - Mx);
-                Lx += red_l[w * WR + rb][l32] * f;
                 LEx += red_e[w * WR + rb][l32] * f;
             }
             __syncthreads();
@@ -633,7 +712,7 @@ __global__ __launch_bounds__(256) void tile_attn_kernel(DecodeArgs a) {
                     }
             }
             M = Mx;
-            L = Lx;
+            L = LEx;
             LE = LEx;
         }
         if (gi == 0 && row_ok) {

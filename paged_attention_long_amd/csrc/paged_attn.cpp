@@ -234,7 +234,7 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     if (num_seqs < 1 || num_seqs > c.max_num_seqs)
         return fail(h, PA_ERR_INVALID_ARGUMENT, "num_seqs %d outside 1..%d", num_seqs, c.max_num_seqs);
     if (block_table_stride < 1) return fail(h, PA_ERR_INVALID_ARGUMENT, "block_table_stride must be >= 1");
-    if (!std::isfinite(scale)) return fail(h, PA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(h, PA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
     if ((c.kv_dtype == PA_DTYPE_FP8_E4M3) != (kv_scale != nullptr))
         return fail(h, PA_ERR_INVALID_ARGUMENT, "kv_scale is required for an fp8 cache and must be NULL otherwise");
     int rc = validate_cache(h, layout, k_cache, v_cache);
