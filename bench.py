@@ -42,7 +42,9 @@ WORKLOADS = {
     "prefill": "chunked prefill: 2,048-token chunk on 65,536 cached, 24/4 heads, D 128, bf16 KV",
     "mixed_fp8": "mixed batch: 4 seqs, 200,001/131,076/32,776/4,097 tokens, q_len 1/4/8/1, 32/8 heads, fp8 e4m3 KV",
 }
-DTYPE_NAME = {"f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3 (kv) / fp32 accumulate"}
+# inputs as stored; every product is accumulated, and every softmax step computed, in fp32
+DTYPE_NAME = {"f16": "f16 in / f32 accumulate", "bf16": "bf16 in / f32 accumulate",
+              "fp8_e4m3": "fp8_e4m3 kv, bf16 q / f32 accumulate"}
 
 
 def log(msg: str) -> None:
@@ -73,7 +75,7 @@ def load_traffic(workload: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def measure(workload: str, steps: int, warmup: int):
+def measure(workload: str, steps: int, warmup: int, use_graph: bool = True):
     import numpy as np
     import torch
 
@@ -93,8 +95,9 @@ def measure(workload: str, steps: int, warmup: int):
     log(f"[bench] {workload}: inputs ready in {time.time() - t0:.1f}s ({copies} rotating copies, "
         f"{kv_bytes / 1e6:.2f} MB KV per step)")
 
+    pos = base.q_lens[base.q_lens > 0]
     cfg = pal.make_config(base.num_q_heads, base.num_kv_heads, base.head_dim, base.q_dtype, base.kv_dtype,
-                          base.num_seqs, int(base.q_lens.max()), base.num_tokens)
+                          base.num_seqs, int(base.q_lens.max()), base.num_tokens, min_q_len=int(pos.min()))
     h = pal.paged_attn_create(cfg)
     out = torch.empty((base.num_tokens, base.num_q_heads, base.head_dim), dtype=torch.float32, device="cuda")
     lse = torch.empty((base.num_tokens, base.num_q_heads), dtype=torch.float32, device="cuda")
@@ -103,26 +106,42 @@ def measure(workload: str, steps: int, warmup: int):
     def step(i):
         d = devs[i % copies]
         pal.paged_attn_forward(h, d["q"], pools["k"], pools["v"], d["block_table"], d["seq_lens"], d["q_lens"],
-                               base.window, base.scale, d["kv_scale"], out, lse, stream=stream)
+                               base.window, base.scale, d["kv_scale"], out, lse,
+                               stream=torch.cuda.current_stream())
+
+    def timed(fn):
+        """Wall clock and HIP-event time of fn(), synchronised on both sides."""
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return time.perf_counter() - w0, e0.elapsed_time(e1) * 1e-3
 
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    for i in range(steps):
-        ev0[i].record(stream)
-        step(warmup + i)
-        ev1[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    kt = np.array([a.elapsed_time(b) for a, b in zip(ev0, ev1)]) * 1e-3     # seconds per forward
+    # Eager: one launch per step from Python.
+    eager_wall, eager_ev = timed(lambda: [step(warmup + i) for i in range(steps)])
+    graph_wall = graph_ev = None
+    if use_graph:
+        # The same K steps captured once into a HIP graph and replayed: no
+        # host launch cost between the forwards.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(steps):
+                step(i)
+        g.replay()
+        torch.cuda.synchronize()
+        graph_wall, graph_ev = timed(g.replay)
     pal.paged_attn_destroy(h)
     assert torch.isfinite(out).all().item(), "non-finite output"
 
-    k_mean = float(kt.mean())
+    wall = graph_wall if use_graph else eager_wall
+    k_mean = (graph_ev if use_graph else eager_ev) / steps
     if workload == "prefill":
         unit = "TFLOP/s"
         value = flops * steps / wall / 1e12
@@ -136,15 +155,20 @@ def measure(workload: str, steps: int, warmup: int):
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
     roof["traffic"] = load_traffic(workload)
+    work = flops if workload == "prefill" else kv_bytes
     res = {
         "value": value, "unit": unit, "ms_per_step": wall / steps * 1e3, "roofline": roof,
-        "kernel_us": {"mean": k_mean * 1e6, "median": float(np.median(kt)) * 1e6, "min": float(kt.min()) * 1e6,
-                      "max": float(kt.max()) * 1e6},
+        "forward_us": {"graph_events": graph_ev / steps * 1e6 if use_graph else None,
+                       "eager_events": eager_ev / steps * 1e6, "eager_wall": eager_wall / steps * 1e6},
+        "eager_value": work * steps / eager_wall / (1e12 if workload == "prefill" else 1e9),
+        "timing": "graph replay of the timed steps" if use_graph else "eager launches",
+        "forwards_run": warmup + steps + (2 * steps if use_graph else 0),
         "kv_bytes_per_step": kv_bytes, "flops_per_step": flops, "rotating_copies": copies,
         "dtype": DTYPE_NAME[base.kv_dtype],
     }
-    log(f"[bench] {workload}: {value:.1f} {unit} (wall), kernel mean {k_mean * 1e6:.2f} us -> "
-        f"{achieved:.1f} {roof['unit']} = {roof['frac'] * 100:.1f}% of peak")
+    log(f"[bench] {workload}: {value:.1f} {unit} ({res['timing']}, wall), {k_mean * 1e6:.2f} us per forward "
+        f"(events) -> {achieved:.1f} {roof['unit']} = {roof['frac'] * 100:.1f}% of peak; eager "
+        f"{res['eager_value']:.1f} {unit}")
     return res, base
 
 
@@ -200,6 +224,153 @@ def cpu_baseline(workload: str, base, budget_s: float = 12.0):
             "sample": sample, "seconds": el}
 
 
+COPY_KERNEL_TAG = "neg_kernel"     # torch.neg: reads N bytes, writes N bytes
+OUR_KERNEL_TAGS = ("decode_valu_kernel", "tile_attn_kernel")
+
+
+def calibrate_copy(mib: int) -> None:
+    """Runs a plain elementwise kernel of known traffic (torch.neg over mib
+    MiB of fp32, three times) so a counter pass over the same process can
+    scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: {COPY_KERNEL_TAG} over {mib} MiB read + {mib} MiB written, x3")
+    del src, dst
+
+
+def _csv_rows(path_glob: str):
+    import csv
+    import glob
+
+    rows = []
+    for f in sorted(glob.glob(path_glob, recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _short(name: str) -> str:
+    if COPY_KERNEL_TAG in name:
+        return COPY_KERNEL_TAG
+    for tag in OUR_KERNEL_TAGS:
+        if tag in name:
+            i = name.find(tag)
+            j = name.find("(", i)
+            return name[i:j if j > 0 else None]
+    return name[:60]
+
+
+def reduce_profiles(prof_dir: str, workload: str, calib_mib: int, commands: list) -> dict:
+    """Turns one workload's rocprofv3 runs (kernel trace + stats, a FETCH_SIZE
+    pass, a WRITE_SIZE pass) into profiles/<kernel>_<workload>.md and its
+    entry in profiles/traffic.json."""
+    import collections
+
+    stats = [r for r in _csv_rows(os.path.join(prof_dir, "kt", "**", "*kernel_stats.csv"))]
+    per = {}
+    for cname, sub in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        vals = collections.defaultdict(list)
+        for r in _csv_rows(os.path.join(prof_dir, sub, "**", "*counter_collection.csv")):
+            if r["Counter_Name"] == cname:
+                vals[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+        per[cname] = vals
+    calib_bytes = calib_mib << 20
+    fetch_copy = per["FETCH_SIZE"][COPY_KERNEL_TAG]
+    write_copy = per["WRITE_SIZE"][COPY_KERNEL_TAG]
+    if not fetch_copy or not write_copy:
+        raise RuntimeError("no calibration kernel in the counter passes")
+    # KiB per dispatch -> bytes: scale so the copy reads / writes exactly its size
+    f_scale = calib_bytes / (sum(fetch_copy) / len(fetch_copy) * 1024)
+    w_scale = calib_bytes / (sum(write_copy) / len(write_copy) * 1024)
+    ours = sorted(k for k in per["FETCH_SIZE"] if any(t in k for t in OUR_KERNEL_TAGS))
+    kern = {}
+    for k in ours:
+        fv, wv = per["FETCH_SIZE"][k], per["WRITE_SIZE"].get(k, [])
+        kern[k] = {"dispatches": len(fv), "fetch_kib": sum(fv) / len(fv),
+                   "write_kib": (sum(wv) / len(wv)) if wv else float("nan")}
+    # dispatches per forward: dispatches in the counter pass / forwards that (eager) run made
+    with open(os.path.join(prof_dir, "fetch", "bench.json")) as f:
+        fetch_run = json.loads(f.read().strip().splitlines()[-1])
+    with open(os.path.join(prof_dir, "kt", "bench.json")) as f:
+        n_fwd = json.loads(f.read().strip().splitlines()[-1])
+    from synth import named
+
+    base = named(workload)[0]
+    alg = base.flops() if workload == "prefill" else base.kv_bytes()
+    hbm = 0.0
+    for k, v in kern.items():
+        v["per_forward"] = v["dispatches"] / max(1, fetch_run["forwards_run"])
+        v["hbm_bytes"] = v["fetch_kib"] * 1024 * f_scale + v["write_kib"] * 1024 * w_scale
+        hbm += v["hbm_bytes"] * v["per_forward"]
+    lines = [f"# {', '.join(kern) or 'kernels'}: {workload}", "",
+             f"Workload: {WORKLOADS[workload]}.", "", "Commands (run from the repository root):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+              "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in stats:
+        if any(t in r["Name"] for t in OUR_KERNEL_TAGS):
+            lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    lines += ["", f"The traced bench.py run: {n_fwd['timing']}, forward time from HIP events "
+              f"{json.dumps(n_fwd['forward_us'])} us, roofline {json.dumps(n_fwd['roofline'])}.", "",
+              "## HBM traffic (FETCH_SIZE, WRITE_SIZE passes)", "",
+              f"Calibration: {COPY_KERNEL_TAG} over {calib_mib} MiB reads and writes {calib_bytes} B each; "
+              f"counters read {sum(fetch_copy) / len(fetch_copy):.0f} KiB fetched and "
+              f"{sum(write_copy) / len(write_copy):.0f} KiB written per dispatch, so bytes = "
+              f"FETCH_SIZE x 1024 x {f_scale:.4f} and WRITE_SIZE x 1024 x {w_scale:.4f}.", "",
+              "| kernel | dispatches | per forward | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per dispatch |",
+              "|---|---|---|---|---|---|"]
+    for k, v in kern.items():
+        lines.append(f"| {k} | {v['dispatches']} | {v['per_forward']:.2f} | {v['fetch_kib']:.0f} | "
+                     f"{v['write_kib']:.0f} | {v['hbm_bytes']:.4g} |")
+    unit = "flop" if workload == "prefill" else "B of KV"
+    lines += ["", f"HBM bytes per forward: {hbm:.4g}; algorithmic {alg:.4g} {unit} per forward"
+              + ("" if workload == "prefill" else f" (ratio {hbm / alg:.3f})") + ".", ""]
+    name = "_".join(sorted({k.split("<")[0] for k in kern})) or "kernels"
+    out_md = os.path.join(ROOT, "profiles", f"{name}_{workload}.md")
+    os.makedirs(os.path.dirname(out_md), exist_ok=True)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    tj = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(tj) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        data = {}
+    data[workload] = {"kernel_hash": kernel_source_hash(), "hbm_bytes_per_launch": hbm,
+                      "fetch_scale": f_scale, "write_scale": w_scale, "summary": os.path.basename(out_md)}
+    with open(tj, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    log(f"[bench] wrote {out_md} and the {workload} entry of {tj}")
+    return data[workload]
+
+
+def profile_commands(workload: str, calib_mib: int = 512) -> list:
+    """The rocprofv3 runs behind profiles/<kernel>_<workload>.md, from the
+    repository root $REPO (counters in passes of their own, as the profiler
+    collects them)."""
+    out = f"$REPO/gpurun_out/prof/{workload}"
+    run = f"python3 $REPO/bench.py --workload {workload} --no-cpu-baseline"
+    return [
+        "cd /tmp && export TMPDIR=/tmp",
+        f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/kt -o run -- "
+        f"{run} --steps 50 --warmup 5 --json-out {out}/kt/bench.json",
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/fetch -o run -- "
+        f"{run} --steps 5 --warmup 1 --eager --calibrate-copy {calib_mib} --json-out {out}/fetch/bench.json",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/write -o run -- "
+        f"{run} --steps 5 --warmup 1 --eager --calibrate-copy {calib_mib} --json-out {out}/write/bench.json",
+        f"python3 bench.py --workload {workload} --reduce-profiles gpurun_out/prof/{workload}   # on any host",
+    ]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -207,17 +378,31 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
     ap.add_argument("--all", action="store_true", help="also measure every other workload (per_config)")
+    ap.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run a copy kernel of known size (for counter scaling)")
+    ap.add_argument("--profile-commands", action="store_true", help="print the rocprofv3 commands and exit")
+    ap.add_argument("--reduce-profiles", default=None, metavar="DIR",
+                    help="summarise the rocprofv3 runs in DIR into profiles/ (no GPU needed)")
     ap.add_argument("--json-out", default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU mode (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.profile_commands:
+        print("\n".join(profile_commands(args.workload)))
+        return
+    if args.reduce_profiles:
+        reduce_profiles(args.reduce_profiles, args.workload, 512, profile_commands(args.workload))
+        return
 
     import torch
 
     torch.cuda.set_device(0)
-    res, base = measure(args.workload, args.steps, args.warmup)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+    res, base = measure(args.workload, args.steps, args.warmup, use_graph=not args.eager)
     line = {
         "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -225,7 +410,8 @@ def main():
         "config": {"workload": WORKLOADS[args.workload], "name": args.workload,
                    "kv_bytes_per_step": res["kv_bytes_per_step"], "flops_per_step": res["flops_per_step"],
                    "rotating_copies": res["rotating_copies"], "parallelism": "single GPU"},
-        "roofline": res["roofline"], "kernel_us": res["kernel_us"],
+        "roofline": res["roofline"], "timing": res["timing"], "forward_us": res["forward_us"],
+        "eager_value": res["eager_value"], "forwards_run": res["forwards_run"],
     }
     if args.all:
         per = {}
@@ -233,9 +419,9 @@ def main():
             if w == args.workload:
                 continue
             try:
-                r, _ = measure(w, max(20, args.steps // 4), max(5, args.warmup // 2))
+                r, _ = measure(w, max(20, args.steps // 4), max(5, args.warmup // 2), use_graph=not args.eager)
                 per[w] = {"value": r["value"], "unit": r["unit"], "roofline": r["roofline"],
-                          "kernel_us": r["kernel_us"]}
+                          "forward_us": r["forward_us"], "eager_value": r["eager_value"]}
             except Exception as e:  # report, do not hide
                 per[w] = {"error": repr(e)}
         line["per_config"] = per
@@ -244,6 +430,7 @@ def main():
     text = json.dumps(line)
     print(text, flush=True)
     if args.json_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
         with open(args.json_out, "w") as f:
             f.write(text + "\n")
 
