@@ -43,6 +43,8 @@ hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, int kv_dtype, i
 hipError_t launch_mfma_attn(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int wr, int grid,
                             hipStream_t stream);
 int mfma_rows_per_item(int wr);
+// Workgroups of the tile kernel resident per CU (registers and LDS bound it).
+int mfma_blocks_per_cu(int kv_dtype, int q_dtype, int wr, int max_num_seqs);
 
 struct GatherArgs {
     const uint8_t* k_cache;

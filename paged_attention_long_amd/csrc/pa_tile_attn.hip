@@ -311,20 +311,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         work *= a.num_kv_heads;
         qtiles *= a.num_kv_heads;
-        int tps;
-        if (a.forced_pps > 0) {
-            tps = a.forced_pps;
-        } else {
-            const long long t = a.target_items > 0 ? a.target_items : 1;
-            tps = (int)((work + t - 1) / t);
-        }
-        tps = max(tps, (max_tiles + kMaxSplits - 1) / kMaxSplits);
+        // Lower bounds on tiles per split: at most kMaxSplits splits, items
+        // within the partial workspace.
+        int tmin = max(1, (max_tiles + kMaxSplits - 1) / kMaxSplits);
         {
             long long cap = (long long)a.max_items - qtiles;
             if (cap < 1) cap = 1;
-            const long long need = (work + cap - 1) / cap;
-            if (tps < need) tps = (int)need;
-            if (tps < 1) tps = 1;
+            tmin = max(tmin, (int)((work + cap - 1) / cap));
+        }
+        int tps;
+        if (a.forced_pps > 0) {
+            tps = max(a.forced_pps, tmin);
+        } else {
+            // The grid is one round of resident workgroups (t of them) and each
+            // takes items it, it + t, ...  Try splits sized for 1..4 rounds and
+            // keep the one whose rounds x largest item is smallest (split sizes
+            // are equalised within a sequence).
+            const long long t = a.target_items > 0 ? a.target_items : 1;
+            long long best = -1;
+            tps = tmin;
+            for (int k = 1; k <= 4; ++k) {
+                const int c = max(tmin, (int)((work + t * k - 1) / (t * k)));
+                long long items = 0;
+                int big = 0;
+                for (int b = tid; b < a.num_seqs; b += nthr) {
+                    const int tub = pl.aux[b];
+                    if (tub > 0) {
+                        const int S = (tub + c - 1) / c;
+                        items += (long long)pl.item_base[b] * S;
+                        big = max(big, (tub + S - 1) / S);
+                    }
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    items += __shfl_xor(items, o, 64);
+                    big = max(big, __shfl_xor(big, o, 64));
+                }
+                if (lane == 0) { redw[wid] = items; redq[wid] = big; }
+                __syncthreads();
+                items = 0;
+                big = 0;
+                for (int ww = 0; ww < (int)(blockDim.x / 64); ++ww) {
+                    items += redw[ww];
+                    big = max(big, (int)redq[ww]);
+                }
+                __syncthreads();
+                const long long cost = (items * a.num_kv_heads + t - 1) / t * big;
+                if (best < 0 || cost < best) { best = cost; tps = c; }
+            }
         }
         int carry_i = 0;
         for (int b0 = 0; b0 < a.num_seqs; b0 += nthr) {
@@ -778,6 +812,26 @@ static hipError_t launch_wr(const DecodeArgs& a, int kvt, int qt, int grid, hipS
 }
 
 int mfma_rows_per_item(int wr) { return 32 * wr; }
+
+template <int WR>
+static int blocks_per_cu_wr(int kvt, int qt, size_t dyn_lds) {
+    int n = 0;
+    hipError_t e;
+    if (kvt == PA_DTYPE_F16)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_F16, PA_DTYPE_F16, WR>, 256, dyn_lds);
+    else if (kvt == PA_DTYPE_BF16)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_BF16, PA_DTYPE_BF16, WR>, 256, dyn_lds);
+    else if (qt == PA_DTYPE_BF16)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, WR>, 256, dyn_lds);
+    else
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, WR>, 256, dyn_lds);
+    return (e == hipSuccess && n > 0) ? n : 1;
+}
+
+int mfma_blocks_per_cu(int kv_dtype, int q_dtype, int wr, int max_num_seqs) {
+    const size_t dyn = plan_lds_bytes(max_num_seqs);
+    return wr == 4 ? blocks_per_cu_wr<4>(kv_dtype, q_dtype, dyn) : blocks_per_cu_wr<1>(kv_dtype, q_dtype, dyn);
+}
 
 hipError_t launch_mfma_attn(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int wr, int grid,
                             hipStream_t stream) {

@@ -25,6 +25,7 @@ struct pa_handle {
     bool valu_all_ok = false;  // the VALU kernel's slots hold every sequence's rows
     int mfma_wr = 1;         // MFMA kernel: waves along rows (rows per item = 32 * mfma_wr)
     int max_items_mfma = 0;
+    int mfma_grid = 0;       // tile-kernel workgroups: one per resident slot
     int counter_stride = 0;
     float* ws_o = nullptr;
     float* ws_lse = nullptr;
@@ -146,6 +147,11 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
     h->r_max_valu = (int)(h->valu_all_ok ? rows_max : kValuRowsMax);
     h->max_items_valu = grid_cap + cfg->max_num_seqs * cfg->num_kv_heads;
     h->mfma_wr = rows_max > 64 ? 4 : 1;
+    // The tile kernel launches exactly one round of resident workgroups; its
+    // in-kernel plan sizes the splits for that many items.
+    h->mfma_grid = D == 128 ? h->cu_count * pa::mfma_blocks_per_cu(cfg->kv_dtype, cfg->q_dtype, h->mfma_wr,
+                                                                    cfg->max_num_seqs)
+                            : h->cu_count;
     const int bm = 32 * h->mfma_wr;
     const int64_t qblocks = ((int64_t)cfg->max_num_tokens * G + bm - 1) / bm + cfg->max_num_seqs;
     h->max_items_mfma = (int)std::min<int64_t>((int64_t)1 << 30, grid_cap + qblocks * cfg->num_kv_heads);
@@ -305,9 +311,12 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         {
             const int64_t cap_pages = (int64_t)block_table_stride;
             const int64_t units = (int64_t)num_seqs * c.num_kv_heads * cap_pages;
+            // one workgroup per CU: a second resident workgroup on some CUs
+            // would double their share of the bytes
+            const int sgrid = h->tune.grid > 0 ? h->tune.grid : h->cu_count;
             int64_t pps = h->tune.pages_per_split > 0
                               ? h->tune.pages_per_split
-                              : std::max<int64_t>(kMinPagesPerSplit, (units + grid - 1) / grid);
+                              : std::max<int64_t>(kMinPagesPerSplit, (units + sgrid - 1) / sgrid);
             pps = std::max<int64_t>(pps, (cap_pages + pa::kMaxSplits - 1) / pa::kMaxSplits);
             if (h->tune.pages_per_split <= 0) pps = (pps + kMinPagesPerSplit - 1) / kMinPagesPerSplit * kMinPagesPerSplit;
             const int64_t S = (cap_pages + pps - 1) / pps;
@@ -332,7 +341,9 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         a.forced_pps = h->tune.kv_tiles_per_split;
         a.max_items = h->max_items_mfma;
         a.r_max = pa::mfma_rows_per_item(h->mfma_wr);
-        hipError_t e = pa::launch_mfma_attn(a, c.head_dim, c.kv_dtype, c.q_dtype, h->mfma_wr, grid, st);
+        const int tgrid = h->tune.grid > 0 ? h->tune.grid : h->mfma_grid;
+        a.target_items = tgrid;
+        hipError_t e = pa::launch_mfma_attn(a, c.head_dim, c.kv_dtype, c.q_dtype, h->mfma_wr, tgrid, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "tile launch failed: %s", hipGetErrorString(e));
     }
     return PA_OK;
