@@ -31,6 +31,9 @@ FLAGS = [
     # Packed FP32 VALU instructions are kept out of the generated code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics",
+    # MFMA accumulators in ordinary VGPRs: no copies between the AGPR and VGPR
+    # files around the softmax rescale.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -29,8 +29,9 @@
 //   * V^T operands come straight from the row-major V tile through the
 //     gfx950 transposing LDS read (ds_read_b64_tr_b16): four lanes' 8-byte
 //     reads of four key rows come back as four keys of one head-dim column;
-//   * online softmax in fp32 with an exact running max; masked keys are set
-//     to -inf by select and dead keys' V rows are zeroed in LDS, so NaN in
+//   * online softmax in fp32 against a lazily raised reference max (moved
+//     only when a score passes it by 2^8, so weights stay <= 256 and the
+//     accumulators are rarely rescaled); masked keys are set to -inf by select and dead keys' V rows are zeroed in LDS, so NaN in
 //     freed pages never reaches a product;
 //   * P^T is rounded to the MFMA input type and output and lse are
 //     normalised by the fp32 weight sum; at verification widths
@@ -49,7 +50,8 @@ namespace pa {
 namespace {
 
 constexpr int kPage = 16;
-constexpr float kSplitBelow = 32.0f;   // weight sum below which P.V also runs on P's rounding error
+constexpr float kSplitBelow = 32.0f;   // weight sum (in units of the largest weight) below which P.V also runs on P's rounding error
+constexpr float kTau = 8.0f;           // lazy max: rescale when a score passes the reference by 2^8
 constexpr int kRowBytes = 256;         // one K or V row in LDS: 128 16-bit elements
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -459,7 +461,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
             for (int i = 0; i < 16; ++i) o_acc[db][i] = 0.f;
-        float m_run = kNegInf, l_exact = 0.f;
+        float m_run = kNegInf, m_true = kNegInf, l_exact = 0.f;
 
         // ------------------------------------------------------------ tile staging
         // Tile t covers logical pages pg_first + t*PPT ...; a page past the
@@ -590,8 +592,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int i = 0; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(sacc[nb][i], sacc[nb][i + 1]));
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * s2;
-            if (wave_any(tmax > m_run)) {
-                const float mn = fmaxf(m_run, tmax);
+            m_true = fmaxf(m_true, tmax);
+            // Lazy rescale: the reference max m_run moves (to the exact max) only
+            // when a score passes it by 2^kTau, so p <= 2^kTau and the
+            // accumulators are rescaled a handful of times per row, not per tile.
+            if (wave_any(tmax > m_run + kTau)) {
+                const float mn = m_true;
                 const float al = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - mn);
                 m_run = mn;
                 l_exact *= al;
@@ -616,7 +622,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     pb[ts][j] = pack2<C::PVT>(p0, p1);
                 }
             }
-            const bool split = C::PSPLIT || wave_any(l_exact < kSplitBelow);
+            // few effective keys so far (weight sum small against the largest weight)
+            const float p_top = (m_run == kNegInf) ? 1.f : fast_exp2(m_true - m_run);
+            const bool split = C::PSPLIT || wave_any(l_exact < kSplitBelow * p_top);
             // V^T operands by transposing reads.  Row 16ts + r0 has the same swizzle key for every ts, so one set of
             // eight lane addresses serves the whole tile with ts in the offset.
             uint32_t va[8];
