@@ -23,8 +23,8 @@
 //     freed pages, tail slots or padding cannot leak ("Dual MI50, part 2",
 //     section "Bug 2: the drafter read freed memory");
 //   * the context of each (sequence, KV head) is split across workgroups
-//     sized from the live lengths, and the last workgroup to finish merges
-//     the partials with a log-sum-exp merge (pa_merge.h).
+//     sized from the live lengths; the partials are combined by the merge
+//     launch that follows (log-sum-exp merge, pa_merge.h).
 #include "pa_common.h"
 #include "pa_merge.h"
 #include "pa_kernels.h"
@@ -108,9 +108,7 @@ struct Smem {
     int pid[kPidChunk];
     union {
         WaveShared ws;
-        MergeShared merge;
     } u;
-    int flag;
 };
 
 template <int D, int KVT, int QT, int RW>
@@ -345,12 +343,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
             __syncthreads();
         }
 
-        if (!direct) {
-            if (arrive_last(a.counters + ((int64_t)b * a.num_kv_heads + g) * a.counter_stride, n_splits, &sm.flag)) {
-                merge_splits<D>(a.ws_o, a.ws_lse, first_item, n_splits, rows, a.r_max, tgt, si.q_off, g, sm.u.merge);
-            }
-            __syncthreads();
-        }
+        if (!direct && it == first_item && tid == 0)
+            publish_merge(a, MergeDesc{(int)first_item, n_splits, rows, a.r_max, si.q_off, g, 0, vscale});
     };
 
     if (a.static_pps > 0) {

@@ -9,6 +9,20 @@ namespace pa {
 constexpr int kMaxSplits = 64;        // splits per (sequence, KV head) the merge reads in one pass
 constexpr int kPidChunkPages = 1024;  // page ids a workgroup stages in LDS at a time
 
+// One group of split partials to merge: rows [0, rows) of items
+// first_item .. first_item + n_splits - 1 (row stride rstride in the partial
+// arrays) become output rows row0 .. row0 + rows - 1 of KV head g.
+struct MergeDesc {
+    int first_item;
+    int n_splits;
+    int rows;
+    int rstride;
+    int q_off;
+    int g;
+    int row0;
+    float out_scale;   // fp8 V scale, else 1
+};
+
 // Arguments of the split-KV kernels (VALU decode/verify and MFMA tile).
 struct DecodeArgs {
     const void* q;
@@ -22,7 +36,8 @@ struct DecodeArgs {
     float* lse;                // may be null
     float* ws_o;               // split partials [max_items][r_max][D]
     float* ws_lse;             // [max_items][r_max] (log2 domain)
-    int* counters;             // [max_num_seqs * Hkv * counter_stride]
+    MergeDesc* mdesc;          // merge groups published by this forward
+    int* mcount;               // [0]: groups published, [1]: merge workgroups done
     int64_t page_stride, head_stride, token_stride;   // elements
     int num_seqs, bt_stride;
     int num_q_heads, num_kv_heads, group;
@@ -30,10 +45,24 @@ struct DecodeArgs {
     float scale;
     int rows_lo, rows_hi;      // rows-per-KV-head class handled by this launch
     int target_items, min_pps, forced_pps, max_items, r_max;   // forced_pps: pages (VALU) or tiles (MFMA) per split
-    int counter_stride;        // counters per (sequence, KV head)
     int static_pps;            // VALU kernel: > 0 selects static splits of this many pages
     int static_splits;         // splits per (sequence, KV head) in static mode
+    int item_off;              // tile kernel: its partial items start at this item
 };
+
+// Merge every group the attention kernels of this forward published, then
+// reset the group count for the next forward.
+struct MergeArgs {
+    const float* ws_o;
+    const float* ws_lse;
+    const MergeDesc* mdesc;
+    int* mcount;
+    float* out;
+    float* lse;
+    int num_q_heads, group, max_rows;
+};
+hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, hipStream_t stream);
+int merge_rows_per_unit(int head_dim);
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int rw, int grid,
                               hipStream_t stream);

@@ -1,0 +1,115 @@
+// Merge of split-KV partial results: one launch per forward, ordered after
+// the attention kernels on the caller's stream (see pa_merge.h).
+//
+// A unit is RPU consecutive rows of one published group; a thread owns one
+// float4 column of one row and requests that column of every split's partial
+// before the weights are known, so the partial reads overlap the LSE reads.
+#include "pa_common.h"
+#include "pa_merge.h"
+#include "pa_kernels.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kMergeThreads = 256;
+constexpr int kMergeBatch = 32;   // partial rows in flight per thread
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
+    constexpr int EPR = D / 4;                    // float4 columns per row
+    constexpr int RPU = kMergeThreads / EPR;      // rows per unit
+    constexpr int NW = kMergeThreads / kWave;
+    __shared__ float w_sh[RPU][kMaxSplits];
+    __shared__ float lse_sh[RPU];
+    __shared__ int n_sh;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+
+    // The attention kernels' writes are visible across the kernel boundary.
+    if (tid == 0) n_sh = __hip_atomic_load(m.mcount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid == 0) {
+        // Every workgroup has read the count (it is in LDS) before it arrives
+        // here; the last to arrive clears the count and the arrival counter
+        // for the next forward.
+        const int done = __hip_atomic_fetch_add(m.mcount + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == (int)gridDim.x - 1) {
+            __hip_atomic_store(m.mcount + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(m.mcount, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    const int n_groups = n_sh;
+    const int upg = (m.max_rows + RPU - 1) / RPU;   // units per group
+    const int64_t n_units = (int64_t)n_groups * upg;
+    const int rl = tid / EPR;                       // row of this thread within the unit
+    const int col = (tid - rl * EPR) * 4;           // first of its four columns
+    MergeTarget tgt{m.out, m.lse, m.num_q_heads, m.group, 1.0f};
+
+    for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x) {
+        const int gidx = (int)(u / upg);
+        const int r0 = (int)(u - (int64_t)gidx * upg) * RPU;
+        const MergeDesc d = m.mdesc[gidx];
+        if (r0 >= d.rows) continue;                  // uniform
+        const int nr = min(RPU, d.rows - r0);
+        const int S = d.n_splits;
+        const bool act = rl < nr;
+        const int64_t sstride = (int64_t)d.rstride * D;
+        const float* src = m.ws_o + ((int64_t)d.first_item * d.rstride + r0 + rl) * D + col;
+        float4 o[kMergeBatch];
+        auto issue = [&](int s0) {
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k)
+                o[k] = (act && s0 + k < S) ? *reinterpret_cast<const float4*>(src + (int64_t)(s0 + k) * sstride)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        };
+        issue(0);
+        for (int r = wid; r < nr; r += NW) {
+            const float ls = (lane < S) ? m.ws_lse[((int64_t)d.first_item + lane) * d.rstride + r0 + r] : kNegInf;
+            const float M = wave_max(ls);
+            const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
+            const float L = wave_sum(w);
+            w_sh[r][lane] = (L > 0.f) ? w / L : 0.f;
+            if (lane == 0) lse_sh[r] = (L > 0.f) ? M + fast_log2(L) : kNegInf;
+        }
+        __syncthreads();
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
+            if (s0 > 0) issue(s0);
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k) {
+                const float w = (s0 + k < S) ? w_sh[rl][s0 + k] : 0.f;
+                acc.x = fmaf(w, o[k].x, acc.x);
+                acc.y = fmaf(w, o[k].y, acc.y);
+                acc.z = fmaf(w, o[k].z, acc.z);
+                acc.w = fmaf(w, o[k].w, acc.w);
+            }
+        }
+        if (act) {
+            const int64_t orow = out_row(tgt, d.q_off, d.g, d.row0 + r0 + rl);
+            const float sc = d.out_scale;
+            *reinterpret_cast<float4*>(m.out + orow * D + col) =
+                make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+            if (m.lse != nullptr && col == 0) {
+                const float l2 = lse_sh[rl];
+                m.lse[orow] = (l2 == kNegInf) ? kNegInf : l2 * kLn2;
+            }
+        }
+        __syncthreads();   // w_sh is rewritten by the next unit
+    }
+}
+
+}  // namespace
+
+int merge_rows_per_unit(int head_dim) { return kMergeThreads / (head_dim / 4); }
+
+hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, hipStream_t stream) {
+    if (head_dim == 64)
+        hipLaunchKernelGGL((merge_kernel<64>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+    else
+        hipLaunchKernelGGL((merge_kernel<128>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+    return hipGetLastError();
+}
+
+}  // namespace pa

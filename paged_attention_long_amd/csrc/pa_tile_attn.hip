@@ -38,7 +38,7 @@
 //     (memory-bound) and while a row has few effective keys, a second MFMA
 //     adds P's rounding error, so rows dominated by a few keys keep full
 //     precision.
-// Splits are merged by the last workgroup to finish (pa_merge.h).
+// Splits are combined by the merge launch that follows (pa_merge.h).
 #include "pa_common.h"
 #include "pa_merge.h"
 #include "pa_kernels.h"
@@ -209,7 +209,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int BM = C::BM, BN = C::BN, PPT = C::PPT;
 
     __shared__ Plan pl;
-    __shared__ int flag;
     // Two distinct LDS objects for the two buffers: the compiler tracks
     // asynchronous LDS loads per object, so reading one buffer does not wait
     // for the loads still in flight into the other.
@@ -711,55 +710,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         float LE = l_exact + __shfl_xor(l_exact, 32, 64);
         float L = LE;
         float M = m_run;
-        if (C::WK > 1) {
+        MergeTarget tgt{a.out, a.lse, a.num_q_heads, a.group, vscale};
+        if constexpr (C::WK > 1) {
+            // The waves of the group streamed different tiles of the same rows:
+            // bring their accumulators to a common max through LDS, then every
+            // thread finishes 16 columns of one row (row tid/8).
+            static_assert(WR == 1, "key-split waves are used with 32-row items only");
             __syncthreads();
             if (h32 == 0) { red_m[wid][l32] = M; red_e[wid][l32] = LE; }
             __syncthreads();
             float Mx = kNegInf;
 #pragma unroll
-            for (int w = 0; w < C::WK; ++w) Mx = fmaxf(Mx, red_m[w * WR + rb][l32]);
+            for (int w = 0; w < C::WK; ++w) Mx = fmaxf(Mx, red_m[w][l32]);
             const float al = (M == kNegInf) ? 0.f : fast_exp2(M - Mx);
-            float LEx = 0.f;
-#pragma unroll
-            for (int w = 0; w < C::WK; ++w) {
-                const float mw = red_m[w * WR + rb][l32];
-                const float f = (mw == kNegInf) ? 0.f : fast_exp2(mw - Mx);
-                LEx += red_e[w * WR + rb][l32] * f;
-            }
-            __syncthreads();
-            float* accbuf = reinterpret_cast<float*>(tiles);
+            float* accbuf = reinterpret_cast<float*>(tiles);   // [WK][32][D]
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int d = db * 32 + 8 * jj + 4 * h32;
-                    *reinterpret_cast<float4*>(accbuf + ((gi * WR + rb) * 32 + l32) * D + d) =
+                    *reinterpret_cast<float4*>(accbuf + (wid * 32 + l32) * D + d) =
                         make_float4(o_acc[db][4 * jj] * al, o_acc[db][4 * jj + 1] * al, o_acc[db][4 * jj + 2] * al,
                                     o_acc[db][4 * jj + 3] * al);
                 }
             __syncthreads();
-            if (gi == 0) {
+            const int r = tid >> 3;
+            const int c0 = (tid & 7) * 16;
+            float Mr = kNegInf;
 #pragma unroll
-                for (int db = 0; db < C::DB; ++db)
+            for (int w = 0; w < C::WK; ++w) Mr = fmaxf(Mr, red_m[w][r]);
+            float LEr = 0.f;
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int d = db * 32 + 8 * jj + 4 * h32;
-                        float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-                        for (int w = 0; w < C::WK; ++w) {
-                            const float4 v = *reinterpret_cast<const float4*>(accbuf + ((w * WR + rb) * 32 + l32) * D + d);
-                            s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
-                        }
-                        o_acc[db][4 * jj] = s.x; o_acc[db][4 * jj + 1] = s.y;
-                        o_acc[db][4 * jj + 2] = s.z; o_acc[db][4 * jj + 3] = s.w;
-                    }
+            for (int w = 0; w < C::WK; ++w) {
+                const float mw = red_m[w][r];
+                LEr += (mw == kNegInf) ? 0.f : red_e[w][r] * fast_exp2(mw - Mr);
             }
-            M = Mx;
-            L = LEx;
-            LE = LEx;
-        }
-        if (gi == 0 && row_ok) {
+            float4 sum[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sum[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int w = 0; w < C::WK; ++w)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *reinterpret_cast<const float4*>(accbuf + (w * 32 + r) * D + c0 + 4 * q);
+                    sum[q].x += v.x; sum[q].y += v.y; sum[q].z += v.z; sum[q].w += v.w;
+                }
+            if (r < ig.rows) {
+                const float inv = (LEr > 0.f) ? 1.0f / LEr : 0.f;
+                float* op;
+                float sc;
+                if (direct) {
+                    const int64_t orow = out_row(tgt, ig.si.q_off, ig.g, ig.row0 + r);
+                    op = a.out + orow * D + c0;
+                    sc = inv * vscale;
+                    if (a.lse != nullptr && c0 == 0) a.lse[orow] = (LEr > 0.f) ? (Mr + fast_log2(LEr)) * kLn2 : kNegInf;
+                } else {
+                    const int64_t slot = (int64_t)(it + a.item_off) * BM + r;
+                    op = a.ws_o + slot * D + c0;
+                    sc = inv;
+                    if (c0 == 0) a.ws_lse[slot] = (LEr > 0.f) ? Mr + fast_log2(LEr) : kNegInf;
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<float4*>(op + 4 * q) =
+                        make_float4(sum[q].x * sc, sum[q].y * sc, sum[q].z * sc, sum[q].w * sc);
+            }
+        } else if (row_ok) {
             const float inv = (L > 0.f) ? 1.0f / L : 0.f;
-            MergeTarget tgt{a.out, a.lse, a.num_q_heads, a.group, vscale};
             if (direct) {
                 const int64_t orow = out_row(tgt, ig.si.q_off, ig.g, row_g);
                 float* op = a.out + orow * D;
@@ -775,7 +792,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     }
                 if (a.lse != nullptr && h32 == 0) a.lse[orow] = (LE > 0.f) ? (M + fast_log2(LE)) * kLn2 : kNegInf;
             } else {
-                const int64_t slot = (int64_t)it * BM + row_l;
+                const int64_t slot = (int64_t)(it + a.item_off) * BM + row_l;
                 float* op = a.ws_o + slot * D;
 #pragma unroll
                 for (int db = 0; db < C::DB; ++db)
@@ -789,16 +806,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 if (h32 == 0) a.ws_lse[slot] = (LE > 0.f) ? M + fast_log2(LE) : kNegInf;
             }
         }
-        if (!direct) {
-            const int64_t first_item = it - ig.split;
-            int* ctr = a.counters + ((int64_t)ig.b * a.num_kv_heads + ig.g) * a.counter_stride + ig.qt;
-            if (arrive_last(ctr, ig.splits, &flag)) {
-                __syncthreads();
-                MergeTarget tgt{a.out, a.lse, a.num_q_heads, a.group, vscale};
-                merge_splits<D>(a.ws_o, a.ws_lse, first_item, ig.splits, ig.rows, BM, tgt, ig.si.q_off, ig.g,
-                                *reinterpret_cast<MergeShared*>(tiles), ig.row0);
-            }
-        }
+        if (!direct && ig.split == 0 && tid == 0)
+            publish_merge(a, MergeDesc{it + a.item_off, ig.splits, ig.rows, BM, ig.si.q_off, ig.g, ig.row0, vscale});
         __syncthreads();
     }
 }

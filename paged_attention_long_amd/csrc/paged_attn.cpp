@@ -26,10 +26,12 @@ struct pa_handle {
     int mfma_wr = 1;         // MFMA kernel: waves along rows (rows per item = 32 * mfma_wr)
     int max_items_mfma = 0;
     int mfma_grid = 0;       // tile-kernel workgroups: one per resident slot
-    int counter_stride = 0;
+    int merge_rows = 0;      // largest row count of one merge group
+    int mfma_item_off = 0;   // first partial item of the tile kernel
     float* ws_o = nullptr;
     float* ws_lse = nullptr;
-    int* counters = nullptr;
+    pa::MergeDesc* mdesc = nullptr;   // merge groups published by the attention kernels
+    int* mcount = nullptr;            // [0] groups published, [1] merge workgroups done
     void* ws = nullptr;
     size_t ws_bytes = 0;
     std::string err;
@@ -155,14 +157,20 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
     const int bm = 32 * h->mfma_wr;
     const int64_t qblocks = ((int64_t)cfg->max_num_tokens * G + bm - 1) / bm + cfg->max_num_seqs;
     h->max_items_mfma = (int)std::min<int64_t>((int64_t)1 << 30, grid_cap + qblocks * cfg->num_kv_heads);
-    h->counter_stride = (int)((rows_max + 31) / 32);
-    const size_t slots = std::max((size_t)h->max_items_valu * h->r_max_valu,
-                                  D == 128 ? (size_t)h->max_items_mfma * bm : (size_t)0);
+    h->merge_rows = (int)std::max<int64_t>(h->r_max_valu, D == 128 ? bm : 0);
+    // The two kernels' partials live side by side until the merge launch: VALU
+    // slots first, then the tile kernel's, starting at a whole tile item.
+    const size_t valu_slots = ((size_t)h->max_items_valu * h->r_max_valu + bm - 1) / bm * bm;
+    h->mfma_item_off = (int)(valu_slots / bm);
+    const size_t slots = valu_slots + (D == 128 ? (size_t)h->max_items_mfma * bm : (size_t)0);
     const size_t o_bytes = slots * D * sizeof(float);
     const size_t l_bytes = slots * sizeof(float);
-    const size_t c_bytes = (size_t)cfg->max_num_seqs * cfg->num_kv_heads * h->counter_stride * sizeof(int);
+    // a merge group has at least two items
+    const size_t d_bytes = ((size_t)h->max_items_valu + (D == 128 ? (size_t)h->max_items_mfma : 0)) / 2 *
+                           sizeof(pa::MergeDesc);
+    const size_t c_bytes = 2 * sizeof(int);
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    h->ws_bytes = up(o_bytes) + up(l_bytes) + up(c_bytes);
+    h->ws_bytes = up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes);
     if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
         const size_t want = h->ws_bytes;
         delete h;
@@ -172,8 +180,9 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
     char* p = static_cast<char*>(h->ws);
     h->ws_o = reinterpret_cast<float*>(p);
     h->ws_lse = reinterpret_cast<float*>(p + up(o_bytes));
-    h->counters = reinterpret_cast<int*>(p + up(o_bytes) + up(l_bytes));
-    if (hipMemset(h->counters, 0, c_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    h->mdesc = reinterpret_cast<pa::MergeDesc*>(p + up(o_bytes) + up(l_bytes));
+    h->mcount = reinterpret_cast<int*>(p + up(o_bytes) + up(l_bytes) + up(d_bytes));
+    if (hipMemset(h->mcount, 0, c_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(h->ws);
         delete h;
         return fail(nullptr, PA_ERR_HIP, "workspace clear failed");
@@ -262,7 +271,8 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     a.lse = lse;
     a.ws_o = h->ws_o;
     a.ws_lse = h->ws_lse;
-    a.counters = h->counters;
+    a.mdesc = h->mdesc;
+    a.mcount = h->mcount;
     a.page_stride = layout->page_stride;
     a.head_stride = layout->head_stride;
     a.token_stride = layout->token_stride;
@@ -273,7 +283,6 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     a.group = G;
     a.window = window;
     a.scale = scale;
-    a.counter_stride = h->counter_stride;
     const int grid = h->tune.grid > 0 ? h->tune.grid : h->grid_default;
     a.target_items = grid;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -293,6 +302,7 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         run_valu = rows_min <= valu_hi;
         run_mfma = rows_max > valu_hi;
     }
+    bool need_merge_valu = run_valu;
     if (run_valu) {
         a.rows_lo = 1;
         a.rows_hi = valu_hi;
@@ -331,6 +341,7 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         }
         hipError_t e = pa::launch_decode_valu(a, c.head_dim, c.kv_dtype, c.q_dtype, rw, vgrid, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+        if (a.static_pps > 0 && a.static_splits == 1) need_merge_valu = false;
     }
     if (run_mfma) {
         a.static_pps = 0;
@@ -341,10 +352,27 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         a.forced_pps = h->tune.kv_tiles_per_split;
         a.max_items = h->max_items_mfma;
         a.r_max = pa::mfma_rows_per_item(h->mfma_wr);
+        a.item_off = h->mfma_item_off;
         const int tgrid = h->tune.grid > 0 ? h->tune.grid : h->mfma_grid;
         a.target_items = tgrid;
         hipError_t e = pa::launch_mfma_attn(a, c.head_dim, c.kv_dtype, c.q_dtype, h->mfma_wr, tgrid, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "tile launch failed: %s", hipGetErrorString(e));
+    }
+    if (need_merge_valu || run_mfma) {
+        // Merges whatever split groups the launches above published.  Grid:
+        // enough workgroups for the most units those launches can publish
+        // (each group is merged in units of a few rows), at most two per CU.
+        const int64_t upg = (h->merge_rows + pa::merge_rows_per_unit(c.head_dim) - 1) / pa::merge_rows_per_unit(c.head_dim);
+        int64_t groups = 0;
+        if (need_merge_valu) groups += (int64_t)num_seqs * c.num_kv_heads;
+        if (run_mfma) {
+            const int bm = pa::mfma_rows_per_item(h->mfma_wr);
+            groups += (int64_t)c.num_kv_heads * ((num_tokens * G + bm - 1) / bm + num_seqs);
+        }
+        const int mgrid = (int)std::max<int64_t>(1, std::min<int64_t>(2 * h->cu_count, groups * upg));
+        pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, out, lse, c.num_q_heads, G, h->merge_rows};
+        hipError_t e = pa::launch_merge(m, c.head_dim, mgrid, st);
+        if (e != hipSuccess) return fail(h, PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
     }
     return PA_OK;
 }
