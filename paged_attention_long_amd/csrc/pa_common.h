@@ -143,8 +143,7 @@ PA_DEVINLINE int64_t kv_offset(int64_t page, int g, int slot, int64_t page_strid
 
 // Work items of one launch, computed identically by every workgroup from the
 // device-resident lengths (no host round trip).  A sequence belongs to the
-// launch if its rows-per-KV-head count q_len*G lies in [rows_lo, rows_hi].
-// Its visible pages are cut into splits of `pps` pages; an item is one
+// launch if in_launch() says so.  Its visible pages are cut into splits of `pps` pages; an item is one
 // (sequence, KV head, split).
 
 // Per-sequence plan arrays live in dynamic LDS, sized from num_seqs by the
@@ -206,13 +205,21 @@ PA_DEVINLINE int block_exclusive_scan(int v, int* red, int* total) {
     return off + inc - v;
 }
 
+// Which launch takes a sequence.  The VALU kernel takes sequences with at
+// most cls_rows rows per KV head and at most cls_len visible keys; the tile
+// kernel takes every other sequence.  cls_side selects the side (0: VALU).
+PA_DEVINLINE bool in_launch(const DecodeArgs& a, int rows, int vis_len) {
+    const bool valu = rows <= a.cls_rows && vis_len <= a.cls_len;
+    return a.cls_side == 0 ? valu : !valu;
+}
+
 // Split plan of the paged split-KV kernel: a sequence belongs to the launch if
-// its rows-per-KV-head count q_len*G lies in [rows_lo, rows_hi]; its visible
+// in_launch() says so; its visible
 // pages are cut into splits of `pps` pages; an item is one (sequence, KV head,
 // split).  Computed identically by every workgroup from the device-resident
 // lengths (no host round trip).  All threads of the block call.
-PA_DEVINLINE void build_plan(Plan& pl, int* dyn, const int32_t* seq_lens, const int32_t* q_lens, int num_seqs,
-                             int window, int page_size, int group, int num_kv_heads, int rows_lo, int rows_hi,
+PA_DEVINLINE void build_plan(Plan& pl, int* dyn, const DecodeArgs& a, const int32_t* seq_lens, const int32_t* q_lens,
+                             int num_seqs, int window, int page_size, int group, int num_kv_heads,
                              int target_items, int min_pps, int forced_pps, int max_items) {
     plan_bind(pl, dyn, num_seqs);
     const int tid = threadIdx.x;
@@ -232,10 +239,8 @@ PA_DEVINLINE void build_plan(Plan& pl, int* dyn, const int32_t* seq_lens, const 
             pl.seq_len[b] = sl;
             pl.q_len[b] = ql;
             const int rows = ql * group;
-            if (ql > 0 && rows >= rows_lo && rows <= rows_hi) {
-                const int lo = seq_visible_lo(sl, ql, window);
-                np = (sl - 1) / page_size - lo / page_size + 1;
-            }
+            const int lo = seq_visible_lo(sl, ql, window);
+            if (ql > 0 && in_launch(a, rows, sl - lo)) np = (sl - 1) / page_size - lo / page_size + 1;
             pl.aux[b] = np;
         }
         int tot;

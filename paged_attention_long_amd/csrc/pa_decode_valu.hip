@@ -123,8 +123,8 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     extern __shared__ int dyn_lds[];
     Plan& pl = sm.plan;
     if (a.static_pps <= 0)
-        build_plan(pl, dyn_lds, a.seq_lens, a.q_lens, a.num_seqs, a.window, kPage, a.group, a.num_kv_heads,
-                   a.rows_lo, a.rows_hi, a.target_items, a.min_pps, a.forced_pps, a.max_items);
+        build_plan(pl, dyn_lds, a, a.seq_lens, a.q_lens, a.num_seqs, a.window, kPage, a.group, a.num_kv_heads,
+                   a.target_items, a.min_pps, a.forced_pps, a.max_items);
     const int n_items = (a.static_pps <= 0) ? pl.n_items : 0;
 
     const int tid = threadIdx.x;
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         si.lo = seq_visible_lo(si.seq_len, si.q_len, a.window);
         si.first_page = si.lo / kPage;
         const int rows = si.q_len * a.group;
-        if (si.q_len <= 0 || rows < a.rows_lo || rows > a.rows_hi) return;
+        if (si.q_len <= 0 || !in_launch(a, rows, si.seq_len - si.lo)) return;
         const int last_page = (si.seq_len - 1) / kPage;
         si.n_pages = last_page - si.first_page + 1;
         const int s_first = si.first_page / pps, s_last = last_page / pps;

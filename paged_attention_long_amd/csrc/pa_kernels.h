@@ -43,7 +43,8 @@ struct DecodeArgs {
     int num_q_heads, num_kv_heads, group;
     int window;
     float scale;
-    int rows_lo, rows_hi;      // rows-per-KV-head class handled by this launch
+    int cls_side;              // 0: VALU launch (short, few-row sequences), 1: tile launch (the rest)
+    int cls_rows, cls_len;     // VALU class: rows per KV head <= cls_rows and visible keys <= cls_len
     int target_items, min_pps, forced_pps, max_items, r_max;   // forced_pps: pages (VALU) or tiles (MFMA) per split
     int static_pps;            // VALU kernel: > 0 selects static splits of this many pages
     int static_splits;         // splits per (sequence, KV head) in static mode

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     auto vbuf = [&](int buf) { return (buf == 0 ? tiles : tiles2) + gi * 2 * C::TILE + C::TILE; };
 
     // ---------------------------------------------------------------- plan
-    // A sequence is in this launch if q_len*G lies in [rows_lo, rows_hi].  Its
+    // A sequence is in this launch if in_launch() says so.  Its
     // rows form ceil(rows/BM) row blocks; each row block's visible keys are cut
     // into tiles of BN keys; tiles are grouped into `splits` splits (the same
     // number for every row block of the sequence).
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 pl.seq_len[b] = sl;
                 pl.q_len[b] = ql;
                 const int rows = ql * a.group;
-                if (ql > 0 && rows >= a.rows_lo && rows <= a.rows_hi) {
+                if (ql > 0 && in_launch(a, rows, sl - seq_visible_lo(sl, ql, a.window))) {
                     nqt = (rows + BM - 1) / BM;
                     tub = widest_tiles(sl, ql);
                 }

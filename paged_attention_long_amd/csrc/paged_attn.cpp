@@ -64,6 +64,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int kMinPagesPerSplit = 4;
 constexpr int kValuRowsMax = 8;   // rows per KV head handled by the VALU kernel under PA_PATH_AUTO
+constexpr int kValuMaxKeys = 16384;   // and visible keys (longer contexts go to the tile kernel)
 
 int validate_config(const pa_config_t* c, std::string* why) {
     char buf[256];
@@ -287,25 +288,29 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     a.target_items = grid;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    // Rows per KV head decide the kernel: a few rows (decode) stream K/V
-    // through the vector ALUs; verification widths and prefill chunks are
-    // dense enough for the matrix cores.
+    // Each sequence goes to one kernel, decided on the device from its
+    // lengths: a few rows per KV head over a short context stream K/V through
+    // the vector ALUs (lowest latency); verification widths, prefill chunks
+    // and long contexts go to the MFMA tile kernel, whose per-key VALU work is
+    // several times smaller.  The host launches a kernel only if some
+    // sequence can belong to it.
     const int rows_min = c.min_q_len * G, rows_max = c.max_q_len * G;
+    const int64_t cap_tokens = (int64_t)block_table_stride * c.page_size;
     bool run_valu, run_mfma;
-    int valu_hi;
     if (c.head_dim != 128 || h->tune.path == PA_PATH_VALU) {
-        run_valu = true; run_mfma = false; valu_hi = 1 << 30;
+        run_valu = true; run_mfma = false;
+        a.cls_rows = 1 << 30; a.cls_len = 1 << 30;
     } else if (h->tune.path == PA_PATH_MFMA) {
-        run_valu = false; run_mfma = true; valu_hi = 0;
+        run_valu = false; run_mfma = true;
+        a.cls_rows = 0; a.cls_len = 0;
     } else {
-        valu_hi = kValuRowsMax;
-        run_valu = rows_min <= valu_hi;
-        run_mfma = rows_max > valu_hi;
+        a.cls_rows = kValuRowsMax; a.cls_len = kValuMaxKeys;
+        run_valu = rows_min <= kValuRowsMax;
+        run_mfma = rows_max > kValuRowsMax || cap_tokens > kValuMaxKeys;
     }
     bool need_merge_valu = run_valu;
     if (run_valu) {
-        a.rows_lo = 1;
-        a.rows_hi = valu_hi;
+        a.cls_side = 0;
         a.min_pps = kMinPagesPerSplit;
         a.forced_pps = h->tune.pages_per_split;
         a.max_items = h->max_items_valu;
@@ -319,7 +324,11 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         a.static_pps = 0;
         a.static_splits = 0;
         {
-            const int64_t cap_pages = (int64_t)block_table_stride;
+            // Pages a VALU-class sequence can reach (static splits count from
+            // page 0): without a window its visible keys start at 0.
+            const int64_t cap_pages =
+                window > 0 ? (int64_t)block_table_stride
+                           : std::min<int64_t>(block_table_stride, (int64_t)a.cls_len / c.page_size + 1);
             const int64_t units = (int64_t)num_seqs * c.num_kv_heads * cap_pages;
             // one workgroup per CU: a second resident workgroup on some CUs
             // would double their share of the bytes
@@ -346,8 +355,7 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     if (run_mfma) {
         a.static_pps = 0;
         a.static_splits = 0;
-        a.rows_lo = valu_hi + 1;
-        a.rows_hi = 1 << 30;
+        a.cls_side = 1;
         a.min_pps = 1;
         a.forced_pps = h->tune.kv_tiles_per_split;
         a.max_items = h->max_items_mfma;
