@@ -61,6 +61,7 @@ struct MergeArgs {
     float* out;
     float* lse;
     int num_q_heads, group, max_rows;
+    int desc_cap;              // descriptors the workspace holds
 };
 hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, hipStream_t stream);
 int merge_rows_per_unit(int head_dim);

@@ -27,7 +27,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
     const int lane = tid & (kWave - 1);
     const int wid = tid / kWave;
 
+    const int upg = (m.max_rows + RPU - 1) / RPU;   // units per group
     // The attention kernels' writes are visible across the kernel boundary.
+    // This workgroup's first group descriptor is read together with the count
+    // (one round trip for both); it is only used if the group exists.
+    const MergeDesc d_first = m.mdesc[min((int)(blockIdx.x / upg), m.desc_cap - 1)];
     if (tid == 0) n_sh = __hip_atomic_load(m.mcount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (tid == 0) {
@@ -41,7 +45,6 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
         }
     }
     const int n_groups = n_sh;
-    const int upg = (m.max_rows + RPU - 1) / RPU;   // units per group
     const int64_t n_units = (int64_t)n_groups * upg;
     const int rl = tid / EPR;                       // row of this thread within the unit
     const int col = (tid - rl * EPR) * 4;           // first of its four columns
@@ -50,7 +53,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
     for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x) {
         const int gidx = (int)(u / upg);
         const int r0 = (int)(u - (int64_t)gidx * upg) * RPU;
-        const MergeDesc d = m.mdesc[gidx];
+        const MergeDesc d = (u == blockIdx.x) ? d_first : m.mdesc[gidx];
         if (r0 >= d.rows) continue;                  // uniform
         const int nr = min(RPU, d.rows - r0);
         const int S = d.n_splits;

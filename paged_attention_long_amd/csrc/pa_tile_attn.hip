@@ -118,6 +118,26 @@ PA_DEVINLINE int swz(int r, int c) { return r * kRowBytes + ((c ^ swz_key(r)) <<
 // wait for every asynchronous tile load in flight, including the prefetch
 // into the other buffer.  Outputs are early-clobber: each read lands while
 // later addresses are still being consumed.
+// Eight 128-bit LDS reads at addr[k] + OFF, completed inside the block (the
+// pipelined path manages its asynchronous-load waits itself).
+template <int OFF>
+PA_DEVINLINE void lds_read_b128_x8(const uint32_t (&addr)[8], u32x4_t (&r)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %8 offset:%16\n\t"
+        "ds_read_b128 %1, %9 offset:%16\n\t"
+        "ds_read_b128 %2, %10 offset:%16\n\t"
+        "ds_read_b128 %3, %11 offset:%16\n\t"
+        "ds_read_b128 %4, %12 offset:%16\n\t"
+        "ds_read_b128 %5, %13 offset:%16\n\t"
+        "ds_read_b128 %6, %14 offset:%16\n\t"
+        "ds_read_b128 %7, %15 offset:%16\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+          "v"(addr[7]), "i"(OFF)
+        : "memory");
+}
+
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1.
 template <typename F, int... I>
 PA_DEVINLINE void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -166,6 +186,14 @@ struct Cfg {
     static constexpr int DMA_PER_WAVE = BN * kRowBytes / 1024 / WR;   // 1 KB async loads per wave per tile
     // fp8 register staging: 8-element chunks per thread per tile
     static constexpr int FCH = BN * (D / 8) / NT;
+    // 128-row items on 16-bit caches run a software pipeline: K tiles in a
+    // ring of NKB buffers, V tiles in a ring of NVB, loads issued LEAD tiles
+    // ahead; the item's page ids are staged in LDS (PID_CAP of them).
+    static constexpr bool PIPE = (WR == 4) && !FP8;
+    static constexpr int NKB = 3, NVB = 4, LEAD = 3;
+    static constexpr int PID_CAP = PIPE ? 4096 : 1;
+    static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : WK * GROUP_LDS / NBUF;
+    static constexpr int TILES2_LDS = (PIPE || NBUF == 1) ? 16 : WK * GROUP_LDS / NBUF;
 };
 
 template <int KVT>
@@ -212,8 +240,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // Two distinct LDS objects for the two buffers: the compiler tracks
     // asynchronous LDS loads per object, so reading one buffer does not wait
     // for the loads still in flight into the other.
-    __shared__ __attribute__((aligned(1024))) uint8_t tiles[C::WK * C::GROUP_LDS / C::NBUF];
-    __shared__ __attribute__((aligned(1024))) uint8_t tiles2[C::NBUF > 1 ? C::WK * C::GROUP_LDS / C::NBUF : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles[C::TILES_LDS];
+    __shared__ __attribute__((aligned(1024))) uint8_t tiles2[C::TILES2_LDS];
+    __shared__ int ipid[C::PID_CAP];
     __shared__ float red_m[4][32];
     __shared__ float red_e[4][32];
     __shared__ long long redw[8], redq[8];
@@ -548,6 +577,117 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             else __syncthreads();
         };
 
+        // ------------------------------------------------------------ pieces of one tile
+        // Scores stay unscaled (s2 > 0 preserves the order): the reference max
+        // m_run is kept in scaled units and p = 2^(s*s2 - m_run) is one fma and
+        // one exp.  Masked keys become -inf by select (only tiles that touch a
+        // range edge or the causal diagonal).
+        auto mask_scores = [&](int t, f32x16_t (&S)[C::NB]) {
+            const int key0 = key_pos(t, 0);
+            const bool full = (key0 >= w_lomax) && (key0 + BN - 1 <= w_pmin) && (key0 >= ig.si.lo) &&
+                              (key0 + BN <= ig.si.seq_len) && (ig.pg_first + (t + 1) * PPT <= ig.pg_end);
+            if (!full) {
+#pragma unroll
+                for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int j = key0 + nb * 32 + 8 * (i / 4) + 4 * h32 + (i % 4);
+                        const bool vis = (j <= pos_r) && (j >= lo_r) && (j >= ig.si.lo) && (j < ig.si.seq_len);
+                        S[nb][i] = vis ? S[nb][i] : kNegInf;
+                    }
+            }
+        };
+        // Row max of the tile; lazy rescale: the reference max m_run moves (to
+        // the exact max) only when a score passes it by 2^kTau, so p <= 2^kTau
+        // and the accumulators are rescaled a handful of times per row.
+        auto raise_max = [&](const f32x16_t (&S)[C::NB]) {
+            float tmax = kNegInf;
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(S[nb][i], S[nb][i + 1]));
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * s2;
+            m_true = fmaxf(m_true, tmax);
+            if (wave_any(tmax > m_run + kTau)) {
+                const float mn = m_true;
+                const float al = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - mn);
+                m_run = mn;
+                l_exact *= al;
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) o_acc[db][i] *= al;
+            }
+        };
+        // P = 2^(s*s2 - m_run) rounded to the P.V operand type; while a row has
+        // few effective keys (weight sum small against its largest weight) the
+        // rounding error of P goes into pl as a second operand.
+        auto exp_pack = [&](f32x16_t (&S)[C::NB], u32x4_t (&pb)[C::TS], u32x4_t (&pl)[C::TS]) {
+            // a row that has seen no visible key yet keeps m_run = -inf; its p are 0
+            const float nm = (m_run == kNegInf) ? 0.f : -m_run;
+#pragma unroll
+            for (int ts = 0; ts < C::TS; ++ts) {
+                const int nb = ts / 2, i0 = 8 * (ts % 2);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float p0 = fast_exp2(fmaf(S[nb][i0 + 2 * j], s2, nm));
+                    const float p1 = fast_exp2(fmaf(S[nb][i0 + 2 * j + 1], s2, nm));
+                    S[nb][i0 + 2 * j] = p0;
+                    S[nb][i0 + 2 * j + 1] = p1;
+                    l_exact += p0 + p1;
+                    pb[ts][j] = pack2<C::PVT>(p0, p1);
+                }
+            }
+            const float p_top = (m_run == kNegInf) ? 1.f : fast_exp2(m_true - m_run);
+            const bool split = C::PSPLIT || wave_any(l_exact < kSplitBelow * p_top);
+            if (split) {
+#pragma unroll
+                for (int ts = 0; ts < C::TS; ++ts) {
+                    const int nb = ts / 2, i0 = 8 * (ts % 2);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        pl[ts][j] = pack2<C::PVT>(S[nb][i0 + 2 * j] - unpack_lo<C::PVT>(pb[ts][j]),
+                                                  S[nb][i0 + 2 * j + 1] - unpack_hi<C::PVT>(pb[ts][j]));
+                }
+            }
+            return split;
+        };
+        // O^T += V^T P^T; V^T operands by transposing reads.  Row 16ts + r0 has
+        // the same swizzle key for every ts, so one set of eight lane addresses
+        // serves the whole tile with ts in the offset.
+        auto pv = [&](uint32_t vb32, const u32x4_t (&pb)[C::TS], const u32x4_t (&pl)[C::TS], bool split) {
+            uint32_t va[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) va[k] = vb32 + v_lane_off[k];
+            auto v_frags = [&](auto ts_c, u32x4_t (&vf)[C::DB]) {
+                constexpr int ts = decltype(ts_c)::value;
+                u32x2_t r[8];
+                lds_read_tr16_x8<ts * 16 * kRowBytes>(va, r);
+#pragma unroll
+                for (int db = 0; db < C::DB; ++db) vf[db] = u32x4_t{r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]};
+            };
+            if (split) {
+                static_for<C::TS>([&](auto ts_c) {
+                    constexpr int ts = decltype(ts_c)::value;
+                    u32x4_t vf[C::DB];
+                    v_frags(ts_c, vf);
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) {
+                        o_acc[db] = mma32<C::PVT>(vf[db], pb[ts], o_acc[db]);
+                        o_acc[db] = mma32<C::PVT>(vf[db], pl[ts], o_acc[db]);
+                    }
+                });
+            } else {
+                static_for<C::TS>([&](auto ts_c) {
+                    constexpr int ts = decltype(ts_c)::value;
+                    u32x4_t vf[C::DB];
+                    v_frags(ts_c, vf);
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) o_acc[db] = mma32<C::PVT>(vf[db], pb[ts], o_acc[db]);
+                });
+            }
+        };
+
         // ------------------------------------------------------------ compute one tile
         auto compute_tile = [&](int t, const uint8_t* kb, const uint8_t* vb) {
             // S^T = K Q^T: all K fragments of the tile are read first, then the
@@ -569,105 +709,112 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             __builtin_amdgcn_sched_group_barrier(0x100, C::NB * C::KS, 0);   // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x008, C::NB * C::KS, 0);   // MFMAs
-            // Scores stay unscaled (s2 > 0 preserves the order): the running max
-            // m_run is kept in scaled units and p = 2^(s*s2 - m_run) is one fma
-            // and one exp.  Masked keys become -inf by select.
-            const int key0 = key_pos(t, 0);
-            const bool full = (key0 >= w_lomax) && (key0 + BN - 1 <= w_pmin) && (key0 >= ig.si.lo) &&
-                              (key0 + BN <= ig.si.seq_len) && (ig.pg_first + (t + 1) * PPT <= ig.pg_end);
-            if (!full) {
-#pragma unroll
-                for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int j = key0 + nb * 32 + 8 * (i / 4) + 4 * h32 + (i % 4);
-                        const bool vis = (j <= pos_r) && (j >= lo_r) && (j >= ig.si.lo) && (j < ig.si.seq_len);
-                        sacc[nb][i] = vis ? sacc[nb][i] : kNegInf;
-                    }
-            }
-            float tmax = kNegInf;
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-                for (int i = 0; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(sacc[nb][i], sacc[nb][i + 1]));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * s2;
-            m_true = fmaxf(m_true, tmax);
-            // Lazy rescale: the reference max m_run moves (to the exact max) only
-            // when a score passes it by 2^kTau, so p <= 2^kTau and the
-            // accumulators are rescaled a handful of times per row, not per tile.
-            if (wave_any(tmax > m_run + kTau)) {
-                const float mn = m_true;
-                const float al = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - mn);
-                m_run = mn;
-                l_exact *= al;
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) o_acc[db][i] *= al;
-            }
-            // a row that has seen no visible key yet keeps m_run = -inf; its p are 0
-            const float nm = (m_run == kNegInf) ? 0.f : -m_run;
-            u32x4_t pb[C::TS];
-#pragma unroll
-            for (int ts = 0; ts < C::TS; ++ts) {
-                const int nb = ts / 2, i0 = 8 * (ts % 2);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float p0 = fast_exp2(fmaf(sacc[nb][i0 + 2 * j], s2, nm));
-                    const float p1 = fast_exp2(fmaf(sacc[nb][i0 + 2 * j + 1], s2, nm));
-                    sacc[nb][i0 + 2 * j] = p0;
-                    sacc[nb][i0 + 2 * j + 1] = p1;
-                    l_exact += p0 + p1;
-                    pb[ts][j] = pack2<C::PVT>(p0, p1);
-                }
-            }
-            // few effective keys so far (weight sum small against the largest weight)
-            const float p_top = (m_run == kNegInf) ? 1.f : fast_exp2(m_true - m_run);
-            const bool split = C::PSPLIT || wave_any(l_exact < kSplitBelow * p_top);
-            // V^T operands by transposing reads.  Row 16ts + r0 has the same swizzle key for every ts, so one set of
-            // eight lane addresses serves the whole tile with ts in the offset.
-            uint32_t va[8];
-            const uint32_t vb32 = (uint32_t)(uintptr_t)(lds_void_t*)vb;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) va[k] = vb32 + v_lane_off[k];
-            auto v_frags = [&](auto ts_c, u32x4_t (&vf)[C::DB]) {
-                constexpr int ts = decltype(ts_c)::value;
-                u32x2_t r[8];
-                lds_read_tr16_x8<ts * 16 * kRowBytes>(va, r);
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db) vf[db] = u32x4_t{r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]};
-            };
-            if (split) {
-                static_for<C::TS>([&](auto ts_c) {
-                    constexpr int ts = decltype(ts_c)::value;
-                    const int nb = ts / 2, i0 = 8 * (ts % 2);
-                    u32x4_t vf[C::DB], pl2;
-                    v_frags(ts_c, vf);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        pl2[j] = pack2<C::PVT>(sacc[nb][i0 + 2 * j] - unpack_lo<C::PVT>(pb[ts][j]),
-                                               sacc[nb][i0 + 2 * j + 1] - unpack_hi<C::PVT>(pb[ts][j]));
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db) {
-                        o_acc[db] = mma32<C::PVT>(vf[db], pb[ts], o_acc[db]);
-                        o_acc[db] = mma32<C::PVT>(vf[db], pl2, o_acc[db]);
-                    }
-                });
-            } else {
-                static_for<C::TS>([&](auto ts_c) {
-                    constexpr int ts = decltype(ts_c)::value;
-                    u32x4_t vf[C::DB];
-                    v_frags(ts_c, vf);
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db) o_acc[db] = mma32<C::PVT>(vf[db], pb[ts], o_acc[db]);
-                });
-            }
+            mask_scores(t, sacc);
+            raise_max(sacc);
+            u32x4_t pb[C::TS], pl[C::TS];
+            const bool split = exp_pack(sacc, pb, pl);
+            pv((uint32_t)(uintptr_t)(lds_void_t*)vb, pb, pl, split);
         };
 
         // ------------------------------------------------------------ tile loop
         const int my_first = ig.t_begin + gi;
         const int n_iter = (ig.t_end - ig.t_begin + C::WK - 1) / C::WK;
-        if constexpr (!C::FP8) {
+        if constexpr (C::PIPE) {
+            // Iteration k: P.V of tile k-1, then (after tile k+1 has landed) the
+            // scores of tile k+1 on the matrix cores while the VALU turns tile
+            // k's scores into P.  Tile k's K sits in K buffer k % NKB from its
+            // load (issued at iteration k - LEAD) to its QK (iteration k - 1); its
+            // V in V buffer k % NVB until its P.V (iteration k + 1).
+            const int n_pid = max(0, min(C::PID_CAP, (ig.t_end - ig.t_begin) * PPT));
+            const int pid0 = ig.pg_first + ig.t_begin * PPT;
+            for (int k = tid; k < n_pid; k += blockDim.x) ipid[k] = bt[min(pid0 + k, ig.pg_end - 1)];
+            __syncthreads();
+            const uint32_t ring32 = (uint32_t)(uintptr_t)(lds_void_t*)tiles;
+            auto k_lds = [&](int k) { return ring32 + (uint32_t)((k % C::NKB) * C::TILE); };
+            auto v_lds = [&](int k) { return ring32 + (uint32_t)((C::NKB + k % C::NVB) * C::TILE); };
+            auto dma_pipe = [&](int k) {
+                const int t = min(ig.t_begin + k, ig.t_end - 1);
+                int pid[PPT];
+#pragma unroll
+                for (int p = 0; p < PPT; ++p) {
+                    const int q = (t - ig.t_begin) * PPT + p;
+                    pid[p] = (q < n_pid) ? __builtin_amdgcn_readfirstlane(ipid[q]) : tile_pid(t, p);
+                }
+                uint8_t* kb = tiles + (k % C::NKB) * C::TILE;
+                uint8_t* vb = tiles + (C::NKB + k % C::NVB) * C::TILE;
+#pragma unroll
+                for (int ii = 0; ii < C::DMA_PER_WAVE; ++ii) {
+                    const int i = ii * WR + wig;
+                    const int64_t pb = (int64_t)pid[(4 * i) / kPage] * page_bytes;
+                    async_load16(kbase + pb + dma_off[ii], (lds_void_t*)(kb + i * 1024));
+                    async_load16(vbase + pb + dma_off[ii], (lds_void_t*)(vb + i * 1024));
+                }
+            };
+            // K fragment offsets of this lane inside a tile (row l32 of each 32-key block)
+            uint32_t k_off[8];
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) k_off[s8] = (uint32_t)swz(l32, 2 * s8 + h32);
+            auto qk = [&](uint32_t kb32, f32x16_t (&S)[C::NB]) {
+                uint32_t ka[8];
+#pragma unroll
+                for (int s8 = 0; s8 < 8; ++s8) ka[s8] = kb32 + k_off[s8];
+                static_for<C::NB>([&](auto nb_c) {
+                    constexpr int nb = decltype(nb_c)::value;
+                    u32x4_t kf[C::KS];
+                    lds_read_b128_x8<nb * 32 * kRowBytes>(ka, kf);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) S[nb][i] = 0.f;
+#pragma unroll
+                    for (int s8 = 0; s8 < C::KS; ++s8) S[nb] = mma32<QT>(kf[s8], qreg[s8], S[nb]);
+                });
+            };
+            // dead V rows of tile k (range edges only) are zeroed in its buffer
+            auto zero_dead_v_pipe = [&](int k) {
+                const int t = ig.t_begin + k;
+                const int k0 = key_pos(t, 0);
+                const bool edge = (k0 < ig.si.lo) || (k0 + BN > ig.si.seq_len) || (ig.pg_first + (t + 1) * PPT > ig.pg_end);
+                if (!edge) return false;
+                uint8_t* vb = tiles + (C::NKB + k % C::NVB) * C::TILE;
+                for (int e = tid; e < BN * 16; e += blockDim.x) {
+                    const int key = e >> 4, c = e & 15;
+                    const int j = k0 + key;
+                    const bool live = (j >= ig.si.lo) && (j < ig.si.seq_len) && (ig.pg_first + t * PPT + key / kPage < ig.pg_end);
+                    if (!live) *reinterpret_cast<u32x4_t*>(vb + swz(key, c)) = u32x4_t{0u, 0u, 0u, 0u};
+                }
+                return true;
+            };
+            const int n_it = ig.t_end - ig.t_begin;
+            if (n_it > 0) {
+#pragma unroll
+                for (int k = 0; k < C::LEAD; ++k) dma_pipe(k);
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 1) * 2 * C::DMA_PER_WAVE));   // tile 0 landed
+                __syncthreads();
+                if (zero_dead_v_pipe(0)) __syncthreads();
+                f32x16_t S[C::NB];
+                qk(k_lds(0), S);
+                u32x4_t pb[C::TS], pl[C::TS];
+                bool split = false;
+                for (int k = 0; k < n_it; ++k) {
+                    mask_scores(ig.t_begin + k, S);
+                    if (k > 0) pv(v_lds(k - 1), pb, pl, split);
+                    raise_max(S);
+                    // tile k+1 landed for this wave (tile k+2 may still be in flight) ...
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 2) * 2 * C::DMA_PER_WAVE));
+                    // ... and for every wave; every wave is past P.V of tile k-1
+                    __syncthreads();
+                    if (zero_dead_v_pipe(k + 1)) __syncthreads();
+                    dma_pipe(k + C::LEAD);
+                    f32x16_t Sn[C::NB];
+                    qk(k_lds(k + 1), Sn);
+                    split = exp_pack(S, pb, pl);
+#pragma unroll
+                    for (int nb = 0; nb < C::NB; ++nb) S[nb] = Sn[nb];
+                }
+                pv(v_lds(n_it - 1), pb, pl, split);
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the clamped prefetches past the end
+                __syncthreads();
+            }
+        } else if constexpr (!C::FP8) {
             // double-buffered asynchronous loads; buffers alternate by iteration parity
             if (n_iter > 0) dma_tile(min(my_first, ig.t_end - 1), 0);
             if (n_iter > 1) dma_tile(min(my_first + C::WK, ig.t_end - 1), 1);

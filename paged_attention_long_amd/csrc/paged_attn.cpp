@@ -28,6 +28,7 @@ struct pa_handle {
     int mfma_grid = 0;       // tile-kernel workgroups: one per resident slot
     int merge_rows = 0;      // largest row count of one merge group
     int mfma_item_off = 0;   // first partial item of the tile kernel
+    int desc_cap = 0;        // merge descriptors the workspace holds
     float* ws_o = nullptr;
     float* ws_lse = nullptr;
     pa::MergeDesc* mdesc = nullptr;   // merge groups published by the attention kernels
@@ -167,8 +168,8 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
     const size_t o_bytes = slots * D * sizeof(float);
     const size_t l_bytes = slots * sizeof(float);
     // a merge group has at least two items
-    const size_t d_bytes = ((size_t)h->max_items_valu + (D == 128 ? (size_t)h->max_items_mfma : 0)) / 2 *
-                           sizeof(pa::MergeDesc);
+    h->desc_cap = (int)std::max<size_t>(1, ((size_t)h->max_items_valu + (D == 128 ? (size_t)h->max_items_mfma : 0)) / 2);
+    const size_t d_bytes = (size_t)h->desc_cap * sizeof(pa::MergeDesc);
     const size_t c_bytes = 2 * sizeof(int);
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
     h->ws_bytes = up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes);
@@ -378,7 +379,8 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
             groups += (int64_t)c.num_kv_heads * ((num_tokens * G + bm - 1) / bm + num_seqs);
         }
         const int mgrid = (int)std::max<int64_t>(1, std::min<int64_t>(2 * h->cu_count, groups * upg));
-        pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, out, lse, c.num_q_heads, G, h->merge_rows};
+        pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, out, lse, c.num_q_heads, G, h->merge_rows,
+                        h->desc_cap};
         hipError_t e = pa::launch_merge(m, c.head_dim, mgrid, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
     }
