@@ -138,6 +138,66 @@ PA_DEVINLINE void lds_read_b128_x8(const uint32_t (&addr)[8], u32x4_t (&r)[8]) {
         : "memory");
 }
 
+// Sixteen 128-bit LDS reads: addr[k] (into r0) and addr[k] + OFF (into r1),
+// completed inside the block.
+template <int OFF>
+PA_DEVINLINE void lds_read_b128_x16(const uint32_t (&addr)[8], u32x4_t (&r0)[8], u32x4_t (&r1)[8]) {
+    asm volatile(
+        "ds_read_b128 %0, %16\n\t"
+        "ds_read_b128 %1, %17\n\t"
+        "ds_read_b128 %2, %18\n\t"
+        "ds_read_b128 %3, %19\n\t"
+        "ds_read_b128 %4, %20\n\t"
+        "ds_read_b128 %5, %21\n\t"
+        "ds_read_b128 %6, %22\n\t"
+        "ds_read_b128 %7, %23\n\t"
+        "ds_read_b128 %8, %16 offset:%24\n\t"
+        "ds_read_b128 %9, %17 offset:%24\n\t"
+        "ds_read_b128 %10, %18 offset:%24\n\t"
+        "ds_read_b128 %11, %19 offset:%24\n\t"
+        "ds_read_b128 %12, %20 offset:%24\n\t"
+        "ds_read_b128 %13, %21 offset:%24\n\t"
+        "ds_read_b128 %14, %22 offset:%24\n\t"
+        "ds_read_b128 %15, %23 offset:%24\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0[0]), "=&v"(r0[1]), "=&v"(r0[2]), "=&v"(r0[3]), "=&v"(r0[4]), "=&v"(r0[5]), "=&v"(r0[6]),
+          "=&v"(r0[7]), "=&v"(r1[0]), "=&v"(r1[1]), "=&v"(r1[2]), "=&v"(r1[3]), "=&v"(r1[4]), "=&v"(r1[5]),
+          "=&v"(r1[6]), "=&v"(r1[7])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+          "v"(addr[7]), "i"(OFF)
+        : "memory");
+}
+
+// Sixteen transposing 64-bit LDS reads at addr[k] + OFF0 (into r0) and
+// addr[k] + OFF1 (into r1), completed inside the block.
+template <int OFF0, int OFF1>
+PA_DEVINLINE void lds_read_tr16_x16(const uint32_t (&addr)[8], u32x2_t (&r0)[8], u32x2_t (&r1)[8]) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %1, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %2, %18 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %3, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %4, %20 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %5, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %6, %22 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %7, %23 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %9, %17 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %11, %19 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %12, %20 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %13, %21 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %14, %22 offset:%25\n\t"
+        "ds_read_b64_tr_b16 %15, %23 offset:%25\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r0[0]), "=&v"(r0[1]), "=&v"(r0[2]), "=&v"(r0[3]), "=&v"(r0[4]), "=&v"(r0[5]), "=&v"(r0[6]),
+          "=&v"(r0[7]), "=&v"(r1[0]), "=&v"(r1[1]), "=&v"(r1[2]), "=&v"(r1[3]), "=&v"(r1[4]), "=&v"(r1[5]),
+          "=&v"(r1[6]), "=&v"(r1[7])
+        : "v"(addr[0]), "v"(addr[1]), "v"(addr[2]), "v"(addr[3]), "v"(addr[4]), "v"(addr[5]), "v"(addr[6]),
+          "v"(addr[7]), "i"(OFF0), "i"(OFF1)
+        : "memory");
+}
+
 // Calls f(std::integral_constant<int, i>) for i = 0 .. N-1.
 template <typename F, int... I>
 PA_DEVINLINE void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
@@ -242,7 +302,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // for the loads still in flight into the other.
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[C::TILES_LDS];
     __shared__ __attribute__((aligned(1024))) uint8_t tiles2[C::TILES2_LDS];
-    __shared__ int ipid[C::PID_CAP];
+    __shared__ __attribute__((aligned(16))) int ipid[C::PID_CAP];
     __shared__ float red_m[4][32];
     __shared__ float red_e[4][32];
     __shared__ long long redw[8], redq[8];
@@ -659,33 +719,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             uint32_t va[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) va[k] = vb32 + v_lane_off[k];
-            auto v_frags = [&](auto ts_c, u32x4_t (&vf)[C::DB]) {
-                constexpr int ts = decltype(ts_c)::value;
-                u32x2_t r[8];
-                lds_read_tr16_x8<ts * 16 * kRowBytes>(va, r);
+            // V fragments of key steps 2u and 2u+1 in one batch of reads; the
+            // next batch is read while the previous MFMAs run.
+            static_assert(C::TS % 2 == 0, "key steps come in pairs");
+            auto v_frags2 = [&](auto u_c, u32x4_t (&vf0)[C::DB], u32x4_t (&vf1)[C::DB]) {
+                constexpr int u = decltype(u_c)::value;
+                u32x2_t r0[8], r1[8];
+                lds_read_tr16_x16<(2 * u) * 16 * kRowBytes, (2 * u + 1) * 16 * kRowBytes>(va, r0, r1);
 #pragma unroll
-                for (int db = 0; db < C::DB; ++db) vf[db] = u32x4_t{r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]};
+                for (int db = 0; db < C::DB; ++db) {
+                    vf0[db] = u32x4_t{r0[2 * db][0], r0[2 * db][1], r0[2 * db + 1][0], r0[2 * db + 1][1]};
+                    vf1[db] = u32x4_t{r1[2 * db][0], r1[2 * db][1], r1[2 * db + 1][0], r1[2 * db + 1][1]};
+                }
             };
-            if (split) {
-                static_for<C::TS>([&](auto ts_c) {
-                    constexpr int ts = decltype(ts_c)::value;
-                    u32x4_t vf[C::DB];
-                    v_frags(ts_c, vf);
+            static_for<C::TS / 2>([&](auto u_c) {
+                constexpr int u = decltype(u_c)::value;
+                u32x4_t vf[2][C::DB];
+                v_frags2(u_c, vf[0], vf[1]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int db = 0; db < C::DB; ++db) {
-                        o_acc[db] = mma32<C::PVT>(vf[db], pb[ts], o_acc[db]);
-                        o_acc[db] = mma32<C::PVT>(vf[db], pl[ts], o_acc[db]);
+                        o_acc[db] = mma32<C::PVT>(vf[h][db], pb[2 * u + h], o_acc[db]);
+                        if (split) o_acc[db] = mma32<C::PVT>(vf[h][db], pl[2 * u + h], o_acc[db]);
                     }
-                });
-            } else {
-                static_for<C::TS>([&](auto ts_c) {
-                    constexpr int ts = decltype(ts_c)::value;
-                    u32x4_t vf[C::DB];
-                    v_frags(ts_c, vf);
-#pragma unroll
-                    for (int db = 0; db < C::DB; ++db) o_acc[db] = mma32<C::PVT>(vf[db], pb[ts], o_acc[db]);
-                });
-            }
+            });
         };
 
         // ------------------------------------------------------------ compute one tile
@@ -735,10 +793,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             auto dma_pipe = [&](int k) {
                 const int t = min(ig.t_begin + k, ig.t_end - 1);
                 int pid[PPT];
+                const int q0 = (t - ig.t_begin) * PPT;
+                if (q0 + PPT <= n_pid) {
+                    static_assert(PPT == 4, "one 128-bit read per tile's page ids");
+                    const int4 w = *reinterpret_cast<const int4*>(ipid + q0);
+                    pid[0] = __builtin_amdgcn_readfirstlane(w.x);
+                    pid[1] = __builtin_amdgcn_readfirstlane(w.y);
+                    pid[2] = __builtin_amdgcn_readfirstlane(w.z);
+                    pid[3] = __builtin_amdgcn_readfirstlane(w.w);
+                } else {
 #pragma unroll
-                for (int p = 0; p < PPT; ++p) {
-                    const int q = (t - ig.t_begin) * PPT + p;
-                    pid[p] = (q < n_pid) ? __builtin_amdgcn_readfirstlane(ipid[q]) : tile_pid(t, p);
+                    for (int p = 0; p < PPT; ++p) pid[p] = tile_pid(t, p);
                 }
                 uint8_t* kb = tiles + (k % C::NKB) * C::TILE;
                 uint8_t* vb = tiles + (C::NKB + k % C::NVB) * C::TILE;
@@ -755,18 +820,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int s8 = 0; s8 < 8; ++s8) k_off[s8] = (uint32_t)swz(l32, 2 * s8 + h32);
             auto qk = [&](uint32_t kb32, f32x16_t (&S)[C::NB]) {
+                static_assert(C::NB == 2, "two 32-key blocks per tile");
                 uint32_t ka[8];
 #pragma unroll
                 for (int s8 = 0; s8 < 8; ++s8) ka[s8] = kb32 + k_off[s8];
-                static_for<C::NB>([&](auto nb_c) {
-                    constexpr int nb = decltype(nb_c)::value;
-                    u32x4_t kf[C::KS];
-                    lds_read_b128_x8<nb * 32 * kRowBytes>(ka, kf);
+                u32x4_t kf[2][C::KS];
+                lds_read_b128_x16<32 * kRowBytes>(ka, kf[0], kf[1]);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) S[nb][i] = 0.f;
+                }
 #pragma unroll
-                    for (int s8 = 0; s8 < C::KS; ++s8) S[nb] = mma32<QT>(kf[s8], qreg[s8], S[nb]);
-                });
+                for (int s8 = 0; s8 < C::KS; ++s8) {
+                    S[0] = mma32<QT>(kf[0][s8], qreg[s8], S[0]);
+                    S[1] = mma32<QT>(kf[1][s8], qreg[s8], S[1]);
+                }
             };
             // dead V rows of tile k (range edges only) are zeroed in its buffer
             auto zero_dead_v_pipe = [&](int k) {
