@@ -155,6 +155,9 @@ def measure(workload: str, steps: int, warmup: int, use_graph: bool = True):
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
     roof["traffic"] = load_traffic(workload)
+    # A forward is the attention launch(es) plus the split-merge launch; the
+    # events bracket whole forwards, so achieved and traffic are per forward.
+    roof["scope"] = "one forward: attention kernel(s) + split-merge kernel, HIP events over the timed region / steps"
     work = flops if workload == "prefill" else kv_bytes
     res = {
         "value": value, "unit": unit, "ms_per_step": wall / steps * 1e3, "roofline": roof,
@@ -225,7 +228,7 @@ def cpu_baseline(workload: str, base, budget_s: float = 12.0):
 
 
 COPY_KERNEL_TAG = "neg_kernel"     # torch.neg: reads N bytes, writes N bytes
-OUR_KERNEL_TAGS = ("decode_valu_kernel", "tile_attn_kernel")
+OUR_KERNEL_TAGS = ("decode_valu_kernel", "tile_attn_kernel", "merge_kernel")
 
 
 def calibrate_copy(mib: int) -> None:
