@@ -37,7 +37,19 @@ SMALL = {
     "window_1": dict(seq_lens=(400,), q_lens=(4,), window=1, poison_out_of_window=True),
     "window_wide": dict(seq_lens=(400,), q_lens=(4,), window=5000),
     "bf16_long_ragged_split": dict(seq_lens=(20007,), q_lens=(1,), num_kv_heads=2, num_q_heads=8),
+    # a 4-row sequence past the VALU kernel's key limit (tile kernel) beside a short one (VALU kernel)
+    "bf16_long_4row_and_short": dict(seq_lens=(17011, 300), q_lens=(1, 1), num_kv_heads=2, num_q_heads=8),
+    # wide block table (both kernels launched) while every sequence is short (all on the VALU kernel)
+    "wide_table_short_seqs": dict(seq_lens=(90, 17, 260), q_lens=(1, 1, 2), block_table_width=1500),
 }
+
+# More sequences than a workgroup has threads (the device plans loop over
+# them), every row class, some with no new rows.
+_rng = np.random.default_rng(77)
+_MANY_Q = _rng.choice([0, 1, 1, 2, 4, 8], size=300)
+_MANY_S = np.maximum(_MANY_Q, _rng.integers(1, 180, size=300))
+SMALL["many_seqs_mixed_classes"] = dict(num_q_heads=8, num_kv_heads=2, seq_lens=tuple(int(x) for x in _MANY_S),
+                                        q_lens=tuple(int(x) for x in _MANY_Q), q_dtype="f16", kv_dtype="f16")
 
 
 @pytest.mark.parametrize("mode", [0, 1, 2])
