@@ -224,10 +224,16 @@ PA_DEVINLINE void lds_read_tr16_x8(const uint32_t (&addr)[8], u32x2_t (&r)[8]) {
         : "memory");
 }
 
+template <int WR>
+constexpr int tile_threads() { return WR == 8 ? 512 : 256; }
+
 template <int D, int KVT, int QT, int WR>
 struct Cfg {
     static_assert(D == 128, "the tile kernel is built for head_dim 128");
-    static constexpr int WK = 4 / WR;                      // wave groups along keys
+    static constexpr int NW = (WR == 8) ? 8 : 4;           // waves per workgroup
+    static constexpr int NTH = 64 * NW;                    // threads per workgroup
+    static_assert(NTH == tile_threads<WR>(), "launch bounds");
+    static constexpr int WK = NW / WR;                     // wave groups along keys
     static constexpr int BN = (WR == 4) ? 64 : 32;         // keys per tile
     static constexpr int PPT = BN / kPage;                 // pages per tile
     static constexpr int BM = 32 * WR;                     // query rows per item
@@ -249,7 +255,7 @@ struct Cfg {
     // 128-row items on 16-bit caches run a software pipeline: K tiles in a
     // ring of NKB buffers, V tiles in a ring of NVB, loads issued LEAD tiles
     // ahead; the item's page ids are staged in LDS (PID_CAP of them).
-    static constexpr bool PIPE = (WR == 4) && !FP8;
+    static constexpr bool PIPE = (WR >= 4) && !FP8;
     static constexpr int NKB = 3, NVB = 4, LEAD = 3;
     static constexpr int PID_CAP = PIPE ? 4096 : 1;
     static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : WK * GROUP_LDS / NBUF;
@@ -292,7 +298,7 @@ struct ItemGeom {
 };
 
 template <int D, int KVT, int QT, int WR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void tile_attn_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArgs a) {
     using C = Cfg<D, KVT, QT, WR>;
     constexpr int BM = C::BM, BN = C::BN, PPT = C::PPT;
 
@@ -795,12 +801,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 int pid[PPT];
                 const int q0 = (t - ig.t_begin) * PPT;
                 if (q0 + PPT <= n_pid) {
-                    static_assert(PPT == 4, "one 128-bit read per tile's page ids");
-                    const int4 w = *reinterpret_cast<const int4*>(ipid + q0);
-                    pid[0] = __builtin_amdgcn_readfirstlane(w.x);
-                    pid[1] = __builtin_amdgcn_readfirstlane(w.y);
-                    pid[2] = __builtin_amdgcn_readfirstlane(w.z);
-                    pid[3] = __builtin_amdgcn_readfirstlane(w.w);
+                    if constexpr (PPT == 4) {
+                        const int4 w = *reinterpret_cast<const int4*>(ipid + q0);
+                        pid[0] = __builtin_amdgcn_readfirstlane(w.x);
+                        pid[1] = __builtin_amdgcn_readfirstlane(w.y);
+                        pid[2] = __builtin_amdgcn_readfirstlane(w.z);
+                        pid[3] = __builtin_amdgcn_readfirstlane(w.w);
+                    } else {
+                        static_assert(PPT == 2, "tiles of 2 or 4 pages");
+                        const int2 w = *reinterpret_cast<const int2*>(ipid + q0);
+                        pid[0] = __builtin_amdgcn_readfirstlane(w.x);
+                        pid[1] = __builtin_amdgcn_readfirstlane(w.y);
+                    }
                 } else {
 #pragma unroll
                     for (int p = 0; p < PPT; ++p) pid[p] = tile_pid(t, p);
@@ -820,21 +832,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int s8 = 0; s8 < 8; ++s8) k_off[s8] = (uint32_t)swz(l32, 2 * s8 + h32);
             auto qk = [&](uint32_t kb32, f32x16_t (&S)[C::NB]) {
-                static_assert(C::NB == 2, "two 32-key blocks per tile");
                 uint32_t ka[8];
 #pragma unroll
                 for (int s8 = 0; s8 < 8; ++s8) ka[s8] = kb32 + k_off[s8];
-                u32x4_t kf[2][C::KS];
-                lds_read_b128_x16<32 * kRowBytes>(ka, kf[0], kf[1]);
+                if constexpr (C::NB == 2) {
+                    u32x4_t kf[2][C::KS];
+                    lds_read_b128_x16<32 * kRowBytes>(ka, kf[0], kf[1]);
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb) {
+                    for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) S[nb][i] = 0.f;
-                }
+                        for (int i = 0; i < 16; ++i) S[nb][i] = 0.f;
+                    }
 #pragma unroll
-                for (int s8 = 0; s8 < C::KS; ++s8) {
-                    S[0] = mma32<QT>(kf[0][s8], qreg[s8], S[0]);
-                    S[1] = mma32<QT>(kf[1][s8], qreg[s8], S[1]);
+                    for (int s8 = 0; s8 < C::KS; ++s8) {
+                        S[0] = mma32<QT>(kf[0][s8], qreg[s8], S[0]);
+                        S[1] = mma32<QT>(kf[1][s8], qreg[s8], S[1]);
+                    }
+                } else {
+                    u32x4_t kf[C::KS];
+                    lds_read_b128_x8<0>(ka, kf);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) S[0][i] = 0.f;
+#pragma unroll
+                    for (int s8 = 0; s8 < C::KS; ++s8) S[0] = mma32<QT>(kf[s8], qreg[s8], S[0]);
                 }
             };
             // dead V rows of tile k (range edges only) are zeroed in its buffer
@@ -1032,7 +1052,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 template <int D, int KVT, int QT, int WR>
 static hipError_t launch_t(const DecodeArgs& a, int grid, hipStream_t st) {
-    hipLaunchKernelGGL((tile_attn_kernel<D, KVT, QT, WR>), dim3(grid), dim3(256), plan_lds_bytes(a.num_seqs), st, a);
+    hipLaunchKernelGGL((tile_attn_kernel<D, KVT, QT, WR>), dim3(grid), dim3(Cfg<D, KVT, QT, WR>::NTH),
+                       plan_lds_bytes(a.num_seqs), st, a);
     return hipGetLastError();
 }
 
@@ -1051,24 +1072,44 @@ static int blocks_per_cu_wr(int kvt, int qt, size_t dyn_lds) {
     int n = 0;
     hipError_t e;
     if (kvt == PA_DTYPE_F16)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_F16, PA_DTYPE_F16, WR>, 256, dyn_lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_F16, PA_DTYPE_F16, WR>,
+                                                          Cfg<128, PA_DTYPE_F16, PA_DTYPE_F16, WR>::NTH, dyn_lds);
     else if (kvt == PA_DTYPE_BF16)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_BF16, PA_DTYPE_BF16, WR>, 256, dyn_lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_BF16, PA_DTYPE_BF16, WR>,
+                                                          Cfg<128, PA_DTYPE_BF16, PA_DTYPE_BF16, WR>::NTH, dyn_lds);
     else if (qt == PA_DTYPE_BF16)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, WR>, 256, dyn_lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, WR>,
+                                                          Cfg<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, WR>::NTH, dyn_lds);
     else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, WR>, 256, dyn_lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, WR>,
+                                                          Cfg<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, WR>::NTH, dyn_lds);
     return (e == hipSuccess && n > 0) ? n : 1;
 }
 
 int mfma_blocks_per_cu(int kv_dtype, int q_dtype, int wr, int max_num_seqs) {
     const size_t dyn = plan_lds_bytes(max_num_seqs);
+    if (wr == 8) {
+        if (kv_dtype == PA_DTYPE_FP8_E4M3) return 1;
+        int n = 0;
+        const hipError_t e =
+            kv_dtype == PA_DTYPE_F16
+                ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_F16, PA_DTYPE_F16, 8>,
+                                                               Cfg<128, PA_DTYPE_F16, PA_DTYPE_F16, 8>::NTH, dyn)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_BF16, PA_DTYPE_BF16, 8>,
+                                                               Cfg<128, PA_DTYPE_BF16, PA_DTYPE_BF16, 8>::NTH, dyn);
+        return (e == hipSuccess && n > 0) ? n : 1;
+    }
     return wr == 4 ? blocks_per_cu_wr<4>(kv_dtype, q_dtype, dyn) : blocks_per_cu_wr<1>(kv_dtype, q_dtype, dyn);
 }
 
 hipError_t launch_mfma_attn(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int wr, int grid,
                             hipStream_t stream) {
     if (head_dim != 128) return hipErrorInvalidValue;
+    if (wr == 8) {   // 256-row items: 16-bit caches only
+        if (kv_dtype == PA_DTYPE_F16) return launch_t<128, PA_DTYPE_F16, PA_DTYPE_F16, 8>(a, grid, stream);
+        if (kv_dtype == PA_DTYPE_BF16) return launch_t<128, PA_DTYPE_BF16, PA_DTYPE_BF16, 8>(a, grid, stream);
+        return hipErrorInvalidValue;
+    }
     if (wr == 4) return launch_wr<4>(a, kv_dtype, q_dtype, grid, stream);
     return launch_wr<1>(a, kv_dtype, q_dtype, grid, stream);
 }

@@ -150,7 +150,9 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
     h->valu_all_ok = rows_max <= 64;
     h->r_max_valu = (int)(h->valu_all_ok ? rows_max : kValuRowsMax);
     h->max_items_valu = grid_cap + cfg->max_num_seqs * cfg->num_kv_heads;
-    h->mfma_wr = rows_max > 64 ? 4 : 1;
+    // rows per tile-kernel item: 32 (verification widths), else 256 rows over
+    // eight waves for 16-bit caches and 128 over four for fp8
+    h->mfma_wr = rows_max > 64 ? (cfg->kv_dtype == PA_DTYPE_FP8_E4M3 ? 4 : 8) : 1;
     // The tile kernel launches exactly one round of resident workgroups; its
     // in-kernel plan sizes the splits for that many items.
     h->mfma_grid = D == 128 ? h->cu_count * pa::mfma_blocks_per_cu(cfg->kv_dtype, cfg->q_dtype, h->mfma_wr,
