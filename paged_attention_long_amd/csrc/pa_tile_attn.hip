@@ -43,6 +43,7 @@
 #include "pa_merge.h"
 #include "pa_kernels.h"
 
+#include <type_traits>
 #include <utility>
 
 namespace pa {
@@ -85,6 +86,17 @@ template <int T>
 PA_DEVINLINE float unpack_hi(uint32_t u) {
     if constexpr (T == PA_DTYPE_BF16) return bf16hi_to_f32(u);
     else return f16x2_to_f32(u).y;
+}
+
+// Maximum that propagates NaN (IEEE maximum): gfx950 issues it as one
+// three-operand instruction with no canonicalising of its inputs.
+PA_DEVINLINE float fmax_nan(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
+// max(x[l], x[l ^ 32]) for every lane l: the two halves of the wave swap
+// through one cross-half permute (gfx950), no LDS round trip.
+PA_DEVINLINE float half_swap_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // s_waitcnt immediates (gfx9 layout: vmcnt[3:0] in bits 3:0, expcnt in 6:4,
@@ -671,9 +683,9 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-                for (int i = 0; i < 16; i += 2) tmax = fmaxf(tmax, fmaxf(S[nb][i], S[nb][i + 1]));
-            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * s2;
-            m_true = fmaxf(m_true, tmax);
+                for (int i = 0; i < 16; ++i) tmax = fmax_nan(tmax, S[nb][i]);
+            tmax = half_swap_max(tmax) * s2;
+            m_true = fmax_nan(m_true, tmax);
             if (wave_any(tmax > m_run + kTau)) {
                 const float mn = m_true;
                 const float al = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - mn);
@@ -738,18 +750,22 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                     vf1[db] = u32x4_t{r1[2 * db][0], r1[2 * db][1], r1[2 * db + 1][0], r1[2 * db + 1][1]};
                 }
             };
-            static_for<C::TS / 2>([&](auto u_c) {
-                constexpr int u = decltype(u_c)::value;
-                u32x4_t vf[2][C::DB];
-                v_frags2(u_c, vf[0], vf[1]);
+            // P's rounding error, when it is used, takes a second pass over the
+            // V fragments (re-read from LDS): one branch per tile, and the
+            // plain pass holds no extra registers.
+            auto pass = [&](const u32x4_t (&p)[C::TS]) {
+                static_for<C::TS / 2>([&](auto u_c) {
+                    constexpr int u = decltype(u_c)::value;
+                    u32x4_t vf[2][C::DB];
+                    v_frags2(u_c, vf[0], vf[1]);
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int db = 0; db < C::DB; ++db) {
-                        o_acc[db] = mma32<C::PVT>(vf[h][db], pb[2 * u + h], o_acc[db]);
-                        if (split) o_acc[db] = mma32<C::PVT>(vf[h][db], pl[2 * u + h], o_acc[db]);
-                    }
-            });
+                        for (int db = 0; db < C::DB; ++db) o_acc[db] = mma32<C::PVT>(vf[h][db], p[2 * u + h], o_acc[db]);
+                });
+            };
+            pass(pb);
+            if (split) pass(pl);
         };
 
         // ------------------------------------------------------------ compute one tile
