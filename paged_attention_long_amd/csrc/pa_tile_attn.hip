@@ -264,11 +264,12 @@ struct Cfg {
     static constexpr int DMA_PER_WAVE = BN * kRowBytes / 1024 / WR;   // 1 KB async loads per wave per tile
     // fp8 register staging: 8-element chunks per thread per tile
     static constexpr int FCH = BN * (D / 8) / NT;
-    // 128-row items on 16-bit caches run a software pipeline: K tiles in a
+    // 256-row items on 16-bit caches run a software pipeline: K tiles in a
     // ring of NKB buffers, V tiles in a ring of NVB, loads issued LEAD tiles
-    // ahead; the item's page ids are staged in LDS (PID_CAP of them).
-    static constexpr bool PIPE = (WR >= 4) && !FP8;
-    static constexpr int NKB = 3, NVB = 4, LEAD = 3;
+    // ahead; the item's page ids are staged in LDS (PID_CAP of them).  The
+    // loop is unrolled over the ring, so buffer offsets are immediates.
+    static constexpr bool PIPE = (WR == 8) && !FP8;
+    static constexpr int NKB = 4, NVB = 4, LEAD = 3;
     static constexpr int PID_CAP = PIPE ? 4096 : 1;
     static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : WK * GROUP_LDS / NBUF;
     static constexpr int TILES2_LDS = (PIPE || NBUF == 1) ? 16 : WK * GROUP_LDS / NBUF;
@@ -733,39 +734,35 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
         // O^T += V^T P^T; V^T operands by transposing reads.  Row 16ts + r0 has
         // the same swizzle key for every ts, so one set of eight lane addresses
         // serves the whole tile with ts in the offset.
+        // One pass of O^T += V^T P^T over a tile (P as TS packed key steps);
+        // va holds this lane's read addresses, OFF the tile's offset from them.
+        auto pv_frags = [&](const uint32_t (&va)[8], auto off_c, const u32x4_t (&p)[C::TS]) {
+            constexpr int OFF = decltype(off_c)::value;
+            // V fragments of key steps 2u and 2u+1 in one batch of reads
+            static_assert(C::TS % 2 == 0, "key steps come in pairs");
+            static_for<C::TS / 2>([&](auto u_c) {
+                constexpr int u = decltype(u_c)::value;
+                u32x2_t r0[8], r1[8];
+                lds_read_tr16_x16<OFF + (2 * u) * 16 * kRowBytes, OFF + (2 * u + 1) * 16 * kRowBytes>(va, r0, r1);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) {
+                        const u32x2_t(&r)[8] = h ? r1 : r0;
+                        o_acc[db] = mma32<C::PVT>(u32x4_t{r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]},
+                                                  p[2 * u + h], o_acc[db]);
+                    }
+            });
+        };
+        // P's rounding error, when it is used, takes a second pass over the V
+        // fragments (re-read from LDS): one branch per tile, and the plain pass
+        // holds no extra registers.
         auto pv = [&](uint32_t vb32, const u32x4_t (&pb)[C::TS], const u32x4_t (&pl)[C::TS], bool split) {
             uint32_t va[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) va[k] = vb32 + v_lane_off[k];
-            // V fragments of key steps 2u and 2u+1 in one batch of reads; the
-            // next batch is read while the previous MFMAs run.
-            static_assert(C::TS % 2 == 0, "key steps come in pairs");
-            auto v_frags2 = [&](auto u_c, u32x4_t (&vf0)[C::DB], u32x4_t (&vf1)[C::DB]) {
-                constexpr int u = decltype(u_c)::value;
-                u32x2_t r0[8], r1[8];
-                lds_read_tr16_x16<(2 * u) * 16 * kRowBytes, (2 * u + 1) * 16 * kRowBytes>(va, r0, r1);
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db) {
-                    vf0[db] = u32x4_t{r0[2 * db][0], r0[2 * db][1], r0[2 * db + 1][0], r0[2 * db + 1][1]};
-                    vf1[db] = u32x4_t{r1[2 * db][0], r1[2 * db][1], r1[2 * db + 1][0], r1[2 * db + 1][1]};
-                }
-            };
-            // P's rounding error, when it is used, takes a second pass over the
-            // V fragments (re-read from LDS): one branch per tile, and the
-            // plain pass holds no extra registers.
-            auto pass = [&](const u32x4_t (&p)[C::TS]) {
-                static_for<C::TS / 2>([&](auto u_c) {
-                    constexpr int u = decltype(u_c)::value;
-                    u32x4_t vf[2][C::DB];
-                    v_frags2(u_c, vf[0], vf[1]);
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-#pragma unroll
-                        for (int db = 0; db < C::DB; ++db) o_acc[db] = mma32<C::PVT>(vf[h][db], p[2 * u + h], o_acc[db]);
-                });
-            };
-            pass(pb);
-            if (split) pass(pl);
+            pv_frags(va, std::integral_constant<int, 0>{}, pb);
+            if (split) pv_frags(va, std::integral_constant<int, 0>{}, pl);
         };
 
         // ------------------------------------------------------------ compute one tile
@@ -810,7 +807,6 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             for (int k = tid; k < n_pid; k += blockDim.x) ipid[k] = bt[min(pid0 + k, ig.pg_end - 1)];
             __syncthreads();
             const uint32_t ring32 = (uint32_t)(uintptr_t)(lds_void_t*)tiles;
-            auto k_lds = [&](int k) { return ring32 + (uint32_t)((k % C::NKB) * C::TILE); };
             auto v_lds = [&](int k) { return ring32 + (uint32_t)((C::NKB + k % C::NVB) * C::TILE); };
             auto dma_pipe = [&](int k) {
                 const int t = min(ig.t_begin + k, ig.t_end - 1);
@@ -843,35 +839,25 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                     async_load16(vbase + pb + dma_off[ii], (lds_void_t*)(vb + i * 1024));
                 }
             };
-            // K fragment offsets of this lane inside a tile (row l32 of each 32-key block)
-            uint32_t k_off[8];
+            // This lane's LDS read addresses at ring offset 0: K fragments (row
+            // l32, chunks 2*s8 + h32) and the transposing V reads.  A buffer's
+            // offset from them is an immediate of the read instructions.
+            static_assert(C::NB == 1 && C::NKB == C::NVB, "one 32-key block per tile, rings of equal length");
+            uint32_t ka[8], va[8];
 #pragma unroll
-            for (int s8 = 0; s8 < 8; ++s8) k_off[s8] = (uint32_t)swz(l32, 2 * s8 + h32);
-            auto qk = [&](uint32_t kb32, f32x16_t (&S)[C::NB]) {
-                uint32_t ka[8];
+            for (int s8 = 0; s8 < 8; ++s8) ka[s8] = ring32 + (uint32_t)swz(l32, 2 * s8 + h32);
 #pragma unroll
-                for (int s8 = 0; s8 < 8; ++s8) ka[s8] = kb32 + k_off[s8];
-                if constexpr (C::NB == 2) {
-                    u32x4_t kf[2][C::KS];
-                    lds_read_b128_x16<32 * kRowBytes>(ka, kf[0], kf[1]);
+            for (int k = 0; k < 8; ++k) va[k] = ring32 + v_lane_off[k];
+            // S^T of a tile = K Q^T: the K fragments are read in one batch,
+            // then eight MFMAs accumulate over the head dimension.
+            auto qk_at = [&](auto off_c, f32x16_t (&S)[C::NB]) {
+                constexpr int OFF = decltype(off_c)::value;
+                u32x4_t kf[C::KS];
+                lds_read_b128_x8<OFF>(ka, kf);
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) {
+                for (int i = 0; i < 16; ++i) S[0][i] = 0.f;
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) S[nb][i] = 0.f;
-                    }
-#pragma unroll
-                    for (int s8 = 0; s8 < C::KS; ++s8) {
-                        S[0] = mma32<QT>(kf[0][s8], qreg[s8], S[0]);
-                        S[1] = mma32<QT>(kf[1][s8], qreg[s8], S[1]);
-                    }
-                } else {
-                    u32x4_t kf[C::KS];
-                    lds_read_b128_x8<0>(ka, kf);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) S[0][i] = 0.f;
-#pragma unroll
-                    for (int s8 = 0; s8 < C::KS; ++s8) S[0] = mma32<QT>(kf[s8], qreg[s8], S[0]);
-                }
+                for (int s8 = 0; s8 < C::KS; ++s8) S[0] = mma32<QT>(kf[s8], qreg[s8], S[0]);
             };
             // dead V rows of tile k (range edges only) are zeroed in its buffer
             auto zero_dead_v_pipe = [&](int k) {
@@ -895,26 +881,48 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 1) * 2 * C::DMA_PER_WAVE));   // tile 0 landed
                 __syncthreads();
                 if (zero_dead_v_pipe(0)) __syncthreads();
-                f32x16_t S[C::NB];
-                qk(k_lds(0), S);
                 u32x4_t pb[C::TS], pl[C::TS];
                 bool split = false;
-                for (int k = 0; k < n_it; ++k) {
-                    mask_scores(ig.t_begin + k, S);
-                    if (k > 0) pv(v_lds(k - 1), pb, pl, split);
-                    raise_max(S);
+                // Iteration k (J = k % NKB): P.V of tile k-1, then (after tile
+                // k+1 has landed) the scores of tile k+1 on the matrix cores
+                // while the VALU turns tile k's scores (cur) into P.  Tile k+1's
+                // scores land in nxt; the unrolled loop alternates the two.
+                auto step = [&](auto j_c, int k, f32x16_t (&cur)[C::NB], f32x16_t (&nxt)[C::NB]) {
+                    constexpr int J = decltype(j_c)::value;
+                    constexpr int KOFF = ((J + 1) % C::NKB) * C::TILE;                     // K of tile k+1
+                    constexpr int VOFF = (C::NKB + (J + C::NVB - 1) % C::NVB) * C::TILE;   // V of tile k-1
+                    mask_scores(ig.t_begin + k, cur);
+                    if (J != 0 || k > 0) {
+                        pv_frags(va, std::integral_constant<int, VOFF>{}, pb);
+                        if (split) pv_frags(va, std::integral_constant<int, VOFF>{}, pl);
+                    }
+                    raise_max(cur);
                     // tile k+1 landed for this wave (tile k+2 may still be in flight) ...
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 2) * 2 * C::DMA_PER_WAVE));
                     // ... and for every wave; every wave is past P.V of tile k-1
                     __syncthreads();
                     if (zero_dead_v_pipe(k + 1)) __syncthreads();
                     dma_pipe(k + C::LEAD);
-                    f32x16_t Sn[C::NB];
-                    qk(k_lds(k + 1), Sn);
-                    split = exp_pack(S, pb, pl);
-#pragma unroll
-                    for (int nb = 0; nb < C::NB; ++nb) S[nb] = Sn[nb];
+                    qk_at(std::integral_constant<int, KOFF>{}, nxt);
+                    split = exp_pack(cur, pb, pl);
+                };
+                using I0 = std::integral_constant<int, 0>;
+                using I1 = std::integral_constant<int, 1>;
+                using I2 = std::integral_constant<int, 2>;
+                using I3 = std::integral_constant<int, 3>;
+                static_assert(C::NKB == 4, "the loop below is unrolled four times");
+                f32x16_t S0[C::NB], S1[C::NB];
+                qk_at(I0{}, S0);
+                int k = 0;
+                for (; k + 4 <= n_it; k += 4) {
+                    step(I0{}, k, S0, S1);
+                    step(I1{}, k + 1, S1, S0);
+                    step(I2{}, k + 2, S0, S1);
+                    step(I3{}, k + 3, S1, S0);
                 }
+                if (k < n_it) step(I0{}, k, S0, S1);
+                if (k + 1 < n_it) step(I1{}, k + 1, S1, S0);
+                if (k + 2 < n_it) step(I2{}, k + 2, S0, S1);
                 pv(v_lds(n_it - 1), pb, pl, split);
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the clamped prefetches past the end
                 __syncthreads();
@@ -1073,61 +1081,63 @@ static hipError_t launch_t(const DecodeArgs& a, int grid, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int WR>
-static hipError_t launch_wr(const DecodeArgs& a, int kvt, int qt, int grid, hipStream_t st) {
-    if (kvt == PA_DTYPE_F16) return launch_t<128, PA_DTYPE_F16, PA_DTYPE_F16, WR>(a, grid, st);
-    if (kvt == PA_DTYPE_BF16) return launch_t<128, PA_DTYPE_BF16, PA_DTYPE_BF16, WR>(a, grid, st);
-    if (qt == PA_DTYPE_BF16) return launch_t<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, WR>(a, grid, st);
-    return launch_t<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, WR>(a, grid, st);
+template <int D, int KVT, int QT, int WR>
+static int blocks_per_cu_t(size_t dyn_lds) {
+    int n = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<D, KVT, QT, WR>,
+                                                                      Cfg<D, KVT, QT, WR>::NTH, dyn_lds);
+    return (e == hipSuccess && n > 0) ? n : 1;
+}
+
+// Instantiations by rows per item: 32-row items (WR = 1) for every cache type;
+// 128-row items (WR = 4) for fp8 caches; 256-row items (WR = 8) for 16-bit
+// caches.  f(tag) is called with the kernel's template arguments as types.
+template <int KVT, int QT, int WR>
+struct KernelTag {
+    static constexpr int kvt = KVT, qt = QT, wr = WR;
+};
+
+template <typename F>
+static bool with_kernel(int kv_dtype, int q_dtype, int wr, F&& f) {
+    const bool fp8 = kv_dtype == PA_DTYPE_FP8_E4M3;
+    if (wr == 1) {
+        if (kv_dtype == PA_DTYPE_F16) return f(KernelTag<PA_DTYPE_F16, PA_DTYPE_F16, 1>{}), true;
+        if (kv_dtype == PA_DTYPE_BF16) return f(KernelTag<PA_DTYPE_BF16, PA_DTYPE_BF16, 1>{}), true;
+        if (q_dtype == PA_DTYPE_BF16) return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, 1>{}), true;
+        return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, 1>{}), true;
+    }
+    if (wr == 4 && fp8) {
+        if (q_dtype == PA_DTYPE_BF16) return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, 4>{}), true;
+        return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, 4>{}), true;
+    }
+    if (wr == 8 && !fp8) {
+        if (kv_dtype == PA_DTYPE_F16) return f(KernelTag<PA_DTYPE_F16, PA_DTYPE_F16, 8>{}), true;
+        return f(KernelTag<PA_DTYPE_BF16, PA_DTYPE_BF16, 8>{}), true;
+    }
+    return false;
 }
 
 int mfma_rows_per_item(int wr) { return 32 * wr; }
 
-template <int WR>
-static int blocks_per_cu_wr(int kvt, int qt, size_t dyn_lds) {
-    int n = 0;
-    hipError_t e;
-    if (kvt == PA_DTYPE_F16)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_F16, PA_DTYPE_F16, WR>,
-                                                          Cfg<128, PA_DTYPE_F16, PA_DTYPE_F16, WR>::NTH, dyn_lds);
-    else if (kvt == PA_DTYPE_BF16)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_BF16, PA_DTYPE_BF16, WR>,
-                                                          Cfg<128, PA_DTYPE_BF16, PA_DTYPE_BF16, WR>::NTH, dyn_lds);
-    else if (qt == PA_DTYPE_BF16)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, WR>,
-                                                          Cfg<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, WR>::NTH, dyn_lds);
-    else
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, WR>,
-                                                          Cfg<128, PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, WR>::NTH, dyn_lds);
-    return (e == hipSuccess && n > 0) ? n : 1;
-}
-
 int mfma_blocks_per_cu(int kv_dtype, int q_dtype, int wr, int max_num_seqs) {
     const size_t dyn = plan_lds_bytes(max_num_seqs);
-    if (wr == 8) {
-        if (kv_dtype == PA_DTYPE_FP8_E4M3) return 1;
-        int n = 0;
-        const hipError_t e =
-            kv_dtype == PA_DTYPE_F16
-                ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_F16, PA_DTYPE_F16, 8>,
-                                                               Cfg<128, PA_DTYPE_F16, PA_DTYPE_F16, 8>::NTH, dyn)
-                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_attn_kernel<128, PA_DTYPE_BF16, PA_DTYPE_BF16, 8>,
-                                                               Cfg<128, PA_DTYPE_BF16, PA_DTYPE_BF16, 8>::NTH, dyn);
-        return (e == hipSuccess && n > 0) ? n : 1;
-    }
-    return wr == 4 ? blocks_per_cu_wr<4>(kv_dtype, q_dtype, dyn) : blocks_per_cu_wr<1>(kv_dtype, q_dtype, dyn);
+    int n = 1;
+    with_kernel(kv_dtype, q_dtype, wr, [&](auto tag) {
+        using T = decltype(tag);
+        n = blocks_per_cu_t<128, T::kvt, T::qt, T::wr>(dyn);
+    });
+    return n;
 }
 
 hipError_t launch_mfma_attn(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int wr, int grid,
                             hipStream_t stream) {
     if (head_dim != 128) return hipErrorInvalidValue;
-    if (wr == 8) {   // 256-row items: 16-bit caches only
-        if (kv_dtype == PA_DTYPE_F16) return launch_t<128, PA_DTYPE_F16, PA_DTYPE_F16, 8>(a, grid, stream);
-        if (kv_dtype == PA_DTYPE_BF16) return launch_t<128, PA_DTYPE_BF16, PA_DTYPE_BF16, 8>(a, grid, stream);
-        return hipErrorInvalidValue;
-    }
-    if (wr == 4) return launch_wr<4>(a, kv_dtype, q_dtype, grid, stream);
-    return launch_wr<1>(a, kv_dtype, q_dtype, grid, stream);
+    hipError_t e = hipErrorInvalidValue;
+    with_kernel(kv_dtype, q_dtype, wr, [&](auto tag) {
+        using T = decltype(tag);
+        e = launch_t<128, T::kvt, T::qt, T::wr>(a, grid, stream);
+    });
+    return e;
 }
 
 }  // namespace pa
