@@ -569,6 +569,10 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
 #pragma unroll
             for (int i = 0; i < 16; ++i) o_acc[db][i] = 0.f;
         float m_run = kNegInf, m_true = kNegInf, l_exact = 0.f;
+        // Derived from m_run and m_true, refreshed only when one of them moves:
+        // the exponent offset -m_run (0 while a row has seen no visible key)
+        // and the split threshold kSplitBelow * 2^(m_true - m_run).
+        float neg_m = 0.f, split_thr = kSplitBelow;
 
         // ------------------------------------------------------------ tile staging
         // Tile t covers logical pages pg_first + t*PPT ...; a page past the
@@ -686,16 +690,21 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
 #pragma unroll
                 for (int i = 0; i < 16; ++i) tmax = fmax_nan(tmax, S[nb][i]);
             tmax = half_swap_max(tmax) * s2;
-            m_true = fmax_nan(m_true, tmax);
-            if (wave_any(tmax > m_run + kTau)) {
-                const float mn = m_true;
-                const float al = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - mn);
-                m_run = mn;
-                l_exact *= al;
+            // m_true <= m_run + kTau holds on entry, so a rescale needs a new maximum
+            if (wave_any(tmax > m_true)) {
+                m_true = fmax_nan(m_true, tmax);
+                if (wave_any(tmax > m_run + kTau)) {
+                    const float mn = m_true;
+                    const float al = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - mn);
+                    m_run = mn;
+                    neg_m = (m_run == kNegInf) ? 0.f : -m_run;
+                    l_exact *= al;
 #pragma unroll
-                for (int db = 0; db < C::DB; ++db)
+                    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) o_acc[db][i] *= al;
+                        for (int i = 0; i < 16; ++i) o_acc[db][i] *= al;
+                }
+                split_thr = kSplitBelow * ((m_run == kNegInf) ? 1.f : fast_exp2(m_true - m_run));
             }
         };
         // P = 2^(s*s2 - m_run) rounded to the P.V operand type; while a row has
@@ -703,7 +712,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
         // rounding error of P goes into pl as a second operand.
         auto exp_pack = [&](f32x16_t (&S)[C::NB], u32x4_t (&pb)[C::TS], u32x4_t (&pl)[C::TS]) {
             // a row that has seen no visible key yet keeps m_run = -inf; its p are 0
-            const float nm = (m_run == kNegInf) ? 0.f : -m_run;
+            const float nm = neg_m;
 #pragma unroll
             for (int ts = 0; ts < C::TS; ++ts) {
                 const int nb = ts / 2, i0 = 8 * (ts % 2);
@@ -717,8 +726,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                     pb[ts][j] = pack2<C::PVT>(p0, p1);
                 }
             }
-            const float p_top = (m_run == kNegInf) ? 1.f : fast_exp2(m_true - m_run);
-            const bool split = C::PSPLIT || wave_any(l_exact < kSplitBelow * p_top);
+            const bool split = C::PSPLIT || wave_any(l_exact < split_thr);
             if (split) {
 #pragma unroll
                 for (int ts = 0; ts < C::TS; ++ts) {
