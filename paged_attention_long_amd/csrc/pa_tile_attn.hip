@@ -99,6 +99,18 @@ PA_DEVINLINE float half_swap_max(float x) {
     return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// Workgroup barrier without the memory fence of __syncthreads(): that fence
+// waits for every asynchronous tile load still in flight (they write LDS).
+// Callers make the data they hand over complete themselves (the LDS read
+// helpers wait inside their asm blocks; tile loads are waited for by count).
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+PA_DEVINLINE void barrier_no_fence() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // s_waitcnt immediates (gfx9 layout: vmcnt[3:0] in bits 3:0, expcnt in 6:4,
 // lgkmcnt in 11:8, vmcnt[5:4] in 15:14); a field at its maximum is not waited on.
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
@@ -908,7 +920,8 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                     // tile k+1 landed for this wave (tile k+2 may still be in flight) ...
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 2) * 2 * C::DMA_PER_WAVE));
                     // ... and for every wave; every wave is past P.V of tile k-1
-                    __syncthreads();
+                    // (K of tile k-1 and V of tile k-1 are free for tile k+3)
+                    barrier_no_fence();
                     if (zero_dead_v_pipe(k + 1)) __syncthreads();
                     dma_pipe(k + C::LEAD);
                     qk_at(std::integral_constant<int, KOFF>{}, nxt);
