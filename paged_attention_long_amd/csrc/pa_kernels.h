@@ -63,7 +63,9 @@ struct MergeArgs {
     int num_q_heads, group, max_rows;
     int desc_cap;              // descriptors the workspace holds
 };
-hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, hipStream_t stream);
+// many_groups: a variant with fewer partial rows in flight per thread and many
+// resident workgroups, for launches that publish many groups (prefill).
+hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, bool many_groups, hipStream_t stream);
 int merge_rows_per_unit(int head_dim);
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int rw, int grid,

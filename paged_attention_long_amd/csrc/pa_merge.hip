@@ -13,10 +13,14 @@ namespace pa {
 namespace {
 
 constexpr int kMergeThreads = 256;
-constexpr int kMergeBatch = 32;   // partial rows in flight per thread
 
-template <int D>
+// BATCH: partial rows in flight per thread.  32 covers the split counts of
+// decode and verification in one round trip (one workgroup per CU at that
+// register count); 8 keeps the registers low enough for many resident
+// workgroups when there are many groups to merge (prefill).
+template <int D, int BATCH>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
+    constexpr int kMergeBatch = BATCH;
     constexpr int EPR = D / 4;                    // float4 columns per row
     constexpr int RPU = kMergeThreads / EPR;      // rows per unit
     constexpr int NW = kMergeThreads / kWave;
@@ -107,11 +111,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
 
 int merge_rows_per_unit(int head_dim) { return kMergeThreads / (head_dim / 4); }
 
-hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, hipStream_t stream) {
-    if (head_dim == 64)
-        hipLaunchKernelGGL((merge_kernel<64>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
-    else
-        hipLaunchKernelGGL((merge_kernel<128>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, bool many_groups, hipStream_t stream) {
+    if (head_dim == 64) {
+        if (many_groups) hipLaunchKernelGGL((merge_kernel<64, 8>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+        else hipLaunchKernelGGL((merge_kernel<64, 32>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+    } else {
+        if (many_groups) hipLaunchKernelGGL((merge_kernel<128, 8>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+        else hipLaunchKernelGGL((merge_kernel<128, 32>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+    }
     return hipGetLastError();
 }
 

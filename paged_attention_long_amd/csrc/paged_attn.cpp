@@ -372,7 +372,7 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     if (need_merge_valu || run_mfma) {
         // Merges whatever split groups the launches above published.  Grid:
         // enough workgroups for the most units those launches can publish
-        // (each group is merged in units of a few rows), at most two per CU.
+        // (each group is merged in units of a few rows).
         const int64_t upg = (h->merge_rows + pa::merge_rows_per_unit(c.head_dim) - 1) / pa::merge_rows_per_unit(c.head_dim);
         int64_t groups = 0;
         if (need_merge_valu) groups += (int64_t)num_seqs * c.num_kv_heads;
@@ -380,10 +380,14 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
             const int bm = pa::mfma_rows_per_item(h->mfma_wr);
             groups += (int64_t)c.num_kv_heads * ((num_tokens * G + bm - 1) / bm + num_seqs);
         }
-        const int mgrid = (int)std::max<int64_t>(1, std::min<int64_t>(2 * h->cu_count, groups * upg));
+        // Many units (prefill): the low-register variant, up to eight
+        // workgroups per CU; otherwise at most two per CU.
+        const int64_t units = groups * upg;
+        const bool many = units > 4 * (int64_t)h->cu_count;
+        const int mgrid = (int)std::max<int64_t>(1, std::min<int64_t>((many ? 8 : 2) * (int64_t)h->cu_count, units));
         pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, out, lse, c.num_q_heads, G, h->merge_rows,
                         h->desc_cap};
-        hipError_t e = pa::launch_merge(m, c.head_dim, mgrid, st);
+        hipError_t e = pa::launch_merge(m, c.head_dim, mgrid, many, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
     }
     return PA_OK;
