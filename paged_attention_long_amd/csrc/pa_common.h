@@ -100,16 +100,46 @@ PA_DEVINLINE float group_sum(float x) {
 
 PA_DEVINLINE float shfl_xor(float x, int m) { return __shfl_xor(x, m, kWave); }
 
+// Returns {x[l], x[l ^ O]} (in some order) on every lane l.  O = 16 and 32 use
+// the gfx950 row and half-wave swaps (VALU, no LDS round trip); smaller O a
+// cross-lane permute.
+template <int O>
+PA_DEVINLINE f32x2_t xor_pair(float x) {
+    if constexpr (O == 16 || O == 32) {
+        const uint32_t u = __float_as_uint(x);
+        const auto r = (O == 16) ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                                 : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        return f32x2_t{__uint_as_float(r[0]), __uint_as_float(r[1])};
+    } else {
+        return f32x2_t{x, __shfl_xor(x, O, kWave)};
+    }
+}
+template <int O>
+PA_DEVINLINE float xor_sum(float x) {
+    const f32x2_t p = xor_pair<O>(x);
+    return p.x + p.y;
+}
+template <int O>
+PA_DEVINLINE float xor_max(float x) {
+    const f32x2_t p = xor_pair<O>(x);
+    return fmaxf(p.x, p.y);
+}
+
 PA_DEVINLINE float wave_max(float x) {
+    x = xor_max<32>(x);
+    x = xor_max<16>(x);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
+    for (int o = 8; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, kWave));
     return x;
 }
 PA_DEVINLINE float wave_sum(float x) {
+    x = xor_sum<32>(x);
+    x = xor_sum<16>(x);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
+    for (int o = 8; o > 0; o >>= 1) x += __shfl_xor(x, o, kWave);
     return x;
 }
+
 
 PA_DEVINLINE bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 

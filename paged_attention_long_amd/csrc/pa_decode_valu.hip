@@ -282,22 +282,24 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
             }
 
             // merge the TPR token lanes of this wave (lanes ch, ch+LPT, ...)
+            auto lanes_max = [](float x) {
+                if constexpr (LPT <= 8) x = xor_max<8>(x);
+                x = xor_max<16>(x);
+                return xor_max<32>(x);
+            };
+            auto lanes_sum = [](float x) {
+                if constexpr (LPT <= 8) x = xor_sum<8>(x);
+                x = xor_sum<16>(x);
+                return xor_sum<32>(x);
+            };
+            static_assert(LPT == 8 || LPT == 16, "token lanes differ in lane bits 3..5 or 4..5");
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
-                float M = m[r];
-#pragma unroll
-                for (int o = LPT; o < kWave; o <<= 1) M = fmaxf(M, shfl_xor(M, o));
+                const float M = lanes_max(m[r]);
                 const float al = (m[r] == kNegInf) ? 0.f : fast_exp2(m[r] - M);
-                float lr = l[r] * al;
+                const float lr = lanes_sum(l[r] * al);
 #pragma unroll
-                for (int o = LPT; o < kWave; o <<= 1) lr += shfl_xor(lr, o);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float x = acc[r][e] * al;
-#pragma unroll
-                    for (int o = LPT; o < kWave; o <<= 1) x += shfl_xor(x, o);
-                    acc[r][e] = x;
-                }
+                for (int e = 0; e < 8; ++e) acc[r][e] = lanes_sum(acc[r][e] * al);
                 m[r] = M;
                 l[r] = lr;
             }

@@ -92,11 +92,10 @@ PA_DEVINLINE float unpack_hi(uint32_t u) {
 // three-operand instruction with no canonicalising of its inputs.
 PA_DEVINLINE float fmax_nan(float x, float y) { return __builtin_elementwise_maximum(x, y); }
 
-// max(x[l], x[l ^ 32]) for every lane l: the two halves of the wave swap
-// through one cross-half permute (gfx950), no LDS round trip.
+// max(x[l], x[l ^ 32]) for every lane l (NaN-propagating)
 PA_DEVINLINE float half_swap_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const f32x2_t p = xor_pair<32>(x);
+    return fmax_nan(p.x, p.y);
 }
 
 // Workgroup barrier without the memory fence of __syncthreads(): that fence
