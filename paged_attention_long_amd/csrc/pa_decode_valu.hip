@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
                                 s[r] = vis ? s[r] * s2 : kNegInf;
                                 need |= s[r] > m[r] + kTau;
                             }
-                            if (wave_any(need)) {
+                            if (__builtin_expect(wave_any(need), 0)) {
 #pragma unroll
                                 for (int r = 0; r < RW; ++r) {
                                     const bool nd = s[r] > m[r] + kTau;
