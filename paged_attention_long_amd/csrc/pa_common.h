@@ -81,6 +81,9 @@ constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;   // reverse within each 8-lane half row
 constexpr int kDppRowMirror = 0x140;    // reverse within each 16-lane row
+constexpr int kDppRowShr = 0x110;       // + n: shift right by n lanes within each row
+constexpr int kDppRowBcast15 = 0x142;   // lane 15 of each row to the next row
+constexpr int kDppRowBcast31 = 0x143;   // lane 31 to rows 2 and 3
 
 template <int CTRL>
 PA_DEVINLINE float dpp(float x) {
@@ -143,14 +146,76 @@ PA_DEVINLINE float wave_sum(float x) {
 
 PA_DEVINLINE bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 
+// Inclusive prefix sum over the wave without LDS: shifts by 1, 2, 4, 8 within
+// each 16-lane row (zeros shifted in), then the last lane of row 0 is added to
+// rows 1 and 3 and the last lane of row 1 (now rows 0-1) to rows 2 and 3.
 PA_DEVINLINE int wave_inclusive_scan(int x) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        int y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-    }
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 1, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 2, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 4, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowShr + 8, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast15, 0xA, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0, x, kDppRowBcast31, 0xC, 0xF, false);
     return x;
+}
+
+// Sum / maximum over the wave without LDS; every lane gets the result.
+// Quads, half rows and rows combine through DPP (each step pairs two groups
+// that already hold their own totals), then rows and wave halves through the
+// lane swaps.
+template <int CTRL>
+PA_DEVINLINE int dpp_i32(int x) { return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false); }
+template <int O>
+PA_DEVINLINE void xor_pair_u32(uint32_t x, uint32_t& a, uint32_t& b) {
+    const auto r = (O == 16) ? __builtin_amdgcn_permlane16_swap(x, x, false, false)
+                             : __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    a = r[0];
+    b = r[1];
+}
+PA_DEVINLINE int wave_max_i32(int x) {
+    x = max(x, dpp_i32<kDppQuadXor1>(x));
+    x = max(x, dpp_i32<kDppQuadXor2>(x));
+    x = max(x, dpp_i32<kDppHalfMirror>(x));
+    x = max(x, dpp_i32<kDppRowMirror>(x));
+    uint32_t a, b;
+    xor_pair_u32<16>((uint32_t)x, a, b);
+    x = max((int)a, (int)b);
+    xor_pair_u32<32>((uint32_t)x, a, b);
+    return max((int)a, (int)b);
+}
+// 64-bit sum: each lane's value is split into 32-bit halves that travel
+// through the same lane moves; the halves are recombined before each add.
+PA_DEVINLINE long long wave_sum_i64(long long v) {
+    auto join = [](uint32_t lo, uint32_t hi) { return (long long)(((unsigned long long)hi << 32) | lo); };
+    auto step_dpp = [&](auto ctrl_c) {
+        constexpr int C = decltype(ctrl_c)::value;
+        const uint32_t lo = (uint32_t)dpp_i32<C>((int)(uint32_t)v);
+        const uint32_t hi = (uint32_t)dpp_i32<C>((int)(uint32_t)((unsigned long long)v >> 32));
+        v += join(lo, hi);
+    };
+    step_dpp(std::integral_constant<int, kDppQuadXor1>{});
+    step_dpp(std::integral_constant<int, kDppQuadXor2>{});
+    step_dpp(std::integral_constant<int, kDppHalfMirror>{});
+    step_dpp(std::integral_constant<int, kDppRowMirror>{});
+    auto step_swap = [&](auto o_c) {
+        constexpr int O = decltype(o_c)::value;
+        uint32_t la, lb, ha, hb;
+        xor_pair_u32<O>((uint32_t)v, la, lb);
+        xor_pair_u32<O>((uint32_t)((unsigned long long)v >> 32), ha, hb);
+        v = join(la, ha) + join(lb, hb);
+    };
+    step_swap(std::integral_constant<int, 16>{});
+    step_swap(std::integral_constant<int, 32>{});
+    return v;
+}
+
+// ceil(a / b) for 0 <= a, 0 < b; 32-bit division when both fit (uniform branch)
+PA_DEVINLINE long long div_ceil_i64(long long a, long long b) {
+    if (((unsigned long long)a | (unsigned long long)b) >> 31 == 0) {
+        const uint32_t ua = (uint32_t)a, ub = (uint32_t)b;
+        return (long long)((ua + ub - 1u) / ub);
+    }
+    return (a + b - 1) / b;
 }
 
 PA_DEVINLINE float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -277,12 +342,7 @@ PA_DEVINLINE void build_plan(Plan& pl, int* dyn, const DecodeArgs& a, const int3
         const int ex = block_exclusive_scan(ql, pl.red, &tot);
         if (b < num_seqs) pl.q_off[b] = carry_q + ex;
         carry_q += tot;
-        int npw = np, npm = np;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            npw += __shfl_xor(npw, o, kWave);
-            npm = max(npm, __shfl_xor(npm, o, kWave));
-        }
+        const int npw = (int)wave_sum_i64(np), npm = wave_max_i32(np);
         if (lane == 0) { pl.red[wid] = npw; pl.red[16 + wid] = npm; }
         __syncthreads();
         for (int w = 0; w < nwaves; ++w) { pages_total += pl.red[w]; max_np = max(max_np, pl.red[16 + w]); }
@@ -294,7 +354,7 @@ PA_DEVINLINE void build_plan(Plan& pl, int* dyn, const DecodeArgs& a, const int3
         pps = forced_pps;
     } else {
         const long long t = target_items > 0 ? target_items : 1;
-        pps = (int)((pages_total + t - 1) / t);
+        pps = (int)div_ceil_i64(pages_total, t);
         pps = max(pps, min_pps);
     }
     // at most kMaxSplits splits per (sequence, KV head)
@@ -303,7 +363,7 @@ PA_DEVINLINE void build_plan(Plan& pl, int* dyn, const DecodeArgs& a, const int3
     {
         long long cap = (long long)max_items - (long long)num_seqs * num_kv_heads;
         if (cap < 1) cap = 1;
-        const long long need = (pages_total + cap - 1) / cap;
+        const long long need = div_ceil_i64(pages_total, cap);
         if (pps < need) pps = (int)need;
         if (pps < 1) pps = 1;
     }

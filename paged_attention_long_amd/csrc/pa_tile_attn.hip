@@ -336,6 +336,8 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
     __shared__ float red_m[4][32];
     __shared__ float red_e[4][32];
     __shared__ long long redw[8], redq[8];
+    __shared__ long long red_items[4][8];
+    __shared__ int red_big[4][8];
     extern __shared__ int dyn_lds[];
 
     const int tid = threadIdx.x;
@@ -412,14 +414,8 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             const int ex = block_exclusive_scan(ql, pl.red, &tot);
             if (b < a.num_seqs) pl.q_off[b] = carry_q + ex;
             carry_q += tot;
-            long long w = (long long)nqt * tub, nq = nqt;
-            int mt = tub;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                w += __shfl_xor(w, o, 64);
-                nq += __shfl_xor(nq, o, 64);
-                mt = max(mt, __shfl_xor(mt, o, 64));
-            }
+            const long long w = wave_sum_i64((long long)nqt * tub), nq = wave_sum_i64(nqt);
+            const int mt = wave_max_i32(tub);
             if (lane == 0) { redw[wid] = w; redq[wid] = nq; pl.red[16 + wid] = mt; }
             __syncthreads();
             for (int ww = 0; ww < (int)(blockDim.x / 64); ++ww) {
@@ -437,7 +433,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
         {
             long long cap = (long long)a.max_items - qtiles;
             if (cap < 1) cap = 1;
-            tmin = max(tmin, (int)((work + cap - 1) / cap));
+            tmin = max(tmin, (int)div_ceil_i64(work, cap));
         }
         int tps;
         if (a.forced_pps > 0) {
@@ -448,36 +444,47 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             // keep the one whose rounds x largest item is smallest (split sizes
             // are equalised within a sequence).
             const long long t = a.target_items > 0 ? a.target_items : 1;
-            long long best = -1;
-            tps = tmin;
-            for (int k = 1; k <= 4; ++k) {
-                const int c = max(tmin, (int)((work + t * k - 1) / (t * k)));
-                long long items = 0;
-                int big = 0;
-                for (int b = tid; b < a.num_seqs; b += nthr) {
-                    const int tub = pl.aux[b];
-                    if (tub > 0) {
-                        const int S = (tub + c - 1) / c;
-                        items += (long long)pl.item_base[b] * S;
-                        big = max(big, (tub + S - 1) / S);
+            constexpr int NC = 4;
+            int cand[NC];
+            long long items[NC];
+            int big[NC];
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+                cand[k] = max(tmin, (int)div_ceil_i64(work, t * (k + 1)));
+                items[k] = 0;
+                big[k] = 0;
+            }
+            // one pass over the sequences for all candidates
+            for (int b = tid; b < a.num_seqs; b += nthr) {
+                const int tub = pl.aux[b];
+                if (tub > 0) {
+#pragma unroll
+                    for (int k = 0; k < NC; ++k) {
+                        const int S = (tub + cand[k] - 1) / cand[k];
+                        items[k] += (long long)pl.item_base[b] * S;
+                        big[k] = max(big[k], (tub + S - 1) / S);
                     }
                 }
+            }
 #pragma unroll
-                for (int o = 32; o > 0; o >>= 1) {
-                    items += __shfl_xor(items, o, 64);
-                    big = max(big, __shfl_xor(big, o, 64));
-                }
-                if (lane == 0) { redw[wid] = items; redq[wid] = big; }
-                __syncthreads();
-                items = 0;
-                big = 0;
+            for (int k = 0; k < NC; ++k) {
+                const long long it_w = wave_sum_i64(items[k]);
+                const int big_w = wave_max_i32(big[k]);
+                if (lane == 0) { red_items[k][wid] = it_w; red_big[k][wid] = big_w; }
+            }
+            __syncthreads();
+            long long best = -1;
+            tps = tmin;
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+                long long it_k = 0;
+                int big_k = 0;
                 for (int ww = 0; ww < (int)(blockDim.x / 64); ++ww) {
-                    items += redw[ww];
-                    big = max(big, (int)redq[ww]);
+                    it_k += red_items[k][ww];
+                    big_k = max(big_k, red_big[k][ww]);
                 }
-                __syncthreads();
-                const long long cost = (items * a.num_kv_heads + t - 1) / t * big;
-                if (best < 0 || cost < best) { best = cost; tps = c; }
+                const long long cost = div_ceil_i64(it_k * a.num_kv_heads, t) * big_k;
+                if (best < 0 || cost < best) { best = cost; tps = cand[k]; }
             }
         }
         int carry_i = 0;
