@@ -243,20 +243,24 @@ PA_DEVINLINE int64_t kv_offset(int64_t page, int g, int slot, int64_t page_strid
 
 // Per-sequence plan arrays live in dynamic LDS, sized from num_seqs by the
 // host (plan_lds_bytes).
+// The per-sequence arrays live in dynamic LDS; typed as LDS pointers so that
+// accesses through them are LDS instructions, not generic (flat) ones.
+typedef __attribute__((address_space(3))) int lds_int_t;
 struct Plan {
     int pps;        // pages (or tiles) per split
     int n_items;
     int red[32];
-    int* item_base;  // [num_seqs + 1] items before sequence b; [num_seqs] = n_items
-    int* q_off;      // [num_seqs + 1] first query row of sequence b
-    int* seq_len;    // [num_seqs]
-    int* q_len;      // [num_seqs]
-    int* aux;        // [num_seqs] kernel-specific per-sequence value
+    lds_int_t* item_base;  // [num_seqs + 1] items before sequence b; [num_seqs] = n_items
+    lds_int_t* q_off;      // [num_seqs + 1] first query row of sequence b
+    lds_int_t* seq_len;    // [num_seqs]
+    lds_int_t* q_len;      // [num_seqs]
+    lds_int_t* aux;        // [num_seqs] kernel-specific per-sequence value
 };
 
 inline __host__ __device__ size_t plan_lds_bytes(int num_seqs) { return (size_t)(5 * num_seqs + 2) * sizeof(int); }
 
-PA_DEVINLINE void plan_bind(Plan& pl, int* dyn, int num_seqs) {
+PA_DEVINLINE void plan_bind(Plan& pl, int* dyn_generic, int num_seqs) {
+    lds_int_t* dyn = (lds_int_t*)dyn_generic;   // the caller's extern __shared__ array
     pl.item_base = dyn;
     pl.q_off = dyn + (num_seqs + 1);
     pl.seq_len = dyn + 2 * (num_seqs + 1);
