@@ -394,7 +394,34 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
         const int nthr = blockDim.x;
         long long work = 0, qtiles = 0;
         int max_tiles = 0, carry_q = 0;
-        for (int b0 = 0; b0 < a.num_seqs; b0 += nthr) {
+        // row blocks and widest tile count of a sequence (0, 0 if not in this launch)
+        auto seq_stats = [&](int sl, int ql, int& nqt, int& tub) {
+            nqt = 0;
+            tub = 0;
+            const int rows = ql * a.group;
+            if (ql > 0 && in_launch(a, rows, sl - seq_visible_lo(sl, ql, a.window))) {
+                nqt = (rows + BM - 1) / BM;
+                tub = widest_tiles(sl, ql);
+            }
+        };
+        // A single sequence (verification, prefill) is planned with uniform
+        // scalar code: no scans or reductions across the workgroup.
+        const bool one = a.num_seqs == 1;
+        int one_nqt = 0, one_tub = 0;
+        if (one) {
+            const int sl = a.seq_lens[0], ql = a.q_lens[0];
+            seq_stats(sl, ql, one_nqt, one_tub);
+            if (tid == 0) {
+                pl.seq_len[0] = sl;
+                pl.q_len[0] = ql;
+                pl.q_off[0] = 0;
+            }
+            carry_q = ql;
+            work = (long long)one_nqt * one_tub;
+            qtiles = one_nqt;
+            max_tiles = one_tub;
+        }
+        for (int b0 = 0; !one && b0 < a.num_seqs; b0 += nthr) {
             const int b = b0 + tid;
             int ql = 0, nqt = 0, tub = 0;
             if (b < a.num_seqs) {
@@ -402,11 +429,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 ql = a.q_lens[b];
                 pl.seq_len[b] = sl;
                 pl.q_len[b] = ql;
-                const int rows = ql * a.group;
-                if (ql > 0 && in_launch(a, rows, sl - seq_visible_lo(sl, ql, a.window))) {
-                    nqt = (rows + BM - 1) / BM;
-                    tub = widest_tiles(sl, ql);
-                }
+                seq_stats(sl, ql, nqt, tub);
                 pl.aux[b] = tub;
                 pl.item_base[b] = nqt;   // temporary
             }
@@ -455,7 +478,19 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 big[k] = 0;
             }
             // one pass over the sequences for all candidates
-            for (int b = tid; b < a.num_seqs; b += nthr) {
+            long long best = -1;
+            tps = tmin;
+            if (one) {
+#pragma unroll
+                for (int k = 0; k < NC; ++k) {
+                    const int S = one_tub > 0 ? (one_tub + cand[k] - 1) / cand[k] : 0;
+                    const long long it_k = (long long)one_nqt * S;
+                    const int big_k = S > 0 ? (one_tub + S - 1) / S : 0;
+                    const long long cost = div_ceil_i64(it_k * a.num_kv_heads, t) * big_k;
+                    if (best < 0 || cost < best) { best = cost; tps = cand[k]; }
+                }
+            }
+            for (int b = tid; !one && b < a.num_seqs; b += nthr) {
                 const int tub = pl.aux[b];
                 if (tub > 0) {
 #pragma unroll
@@ -467,16 +502,14 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 }
             }
 #pragma unroll
-            for (int k = 0; k < NC; ++k) {
+            for (int k = 0; !one && k < NC; ++k) {
                 const long long it_w = wave_sum_i64(items[k]);
                 const int big_w = wave_max_i32(big[k]);
                 if (lane == 0) { red_items[k][wid] = it_w; red_big[k][wid] = big_w; }
             }
-            __syncthreads();
-            long long best = -1;
-            tps = tmin;
+            if (!one) __syncthreads();
 #pragma unroll
-            for (int k = 0; k < NC; ++k) {
+            for (int k = 0; !one && k < NC; ++k) {
                 long long it_k = 0;
                 int big_k = 0;
                 for (int ww = 0; ww < (int)(blockDim.x / 64); ++ww) {
@@ -488,7 +521,15 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             }
         }
         int carry_i = 0;
-        for (int b0 = 0; b0 < a.num_seqs; b0 += nthr) {
+        if (one) {
+            const int S = (one_tub + tps - 1) / tps;
+            carry_i = one_nqt * a.num_kv_heads * S;
+            if (tid == 0) {
+                pl.aux[0] = S;
+                pl.item_base[0] = 0;
+            }
+        }
+        for (int b0 = 0; !one && b0 < a.num_seqs; b0 += nthr) {
             const int b = b0 + tid;
             int it = 0;
             if (b < a.num_seqs) {
