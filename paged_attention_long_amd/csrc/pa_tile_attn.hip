@@ -1051,13 +1051,19 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
 #pragma unroll
             for (int w = 0; w < C::WK; ++w) Mx = fmaxf(Mx, red_m[w][l32]);
             const float al = (M == kNegInf) ? 0.f : fast_exp2(M - Mx);
-            float* accbuf = reinterpret_cast<float*>(tiles);   // [WK][32][D]
+            // [WK][32][D]; the 16-byte chunks of row r are XOR-ed with r so that
+            // the 32 rows a half-wave writes at once (512 B apart) do not all
+            // land in the same bank
+            static_assert(C::WK * 32 * D * 4 <= C::TILES_LDS, "accumulator exchange fits the tile buffers");
+            static_assert(D / 4 == 32, "32 chunks per row");
+            float* accbuf = reinterpret_cast<float*>(tiles);
+            auto acc_at = [&](int row, int col) { return accbuf + row * D + (((col >> 2) ^ (row & 31)) << 2); };
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
                     const int d = db * 32 + 8 * jj + 4 * h32;
-                    *reinterpret_cast<float4*>(accbuf + (wid * 32 + l32) * D + d) =
+                    *reinterpret_cast<float4*>(acc_at(wid * 32 + l32, d)) =
                         make_float4(o_acc[db][4 * jj] * al, o_acc[db][4 * jj + 1] * al, o_acc[db][4 * jj + 2] * al,
                                     o_acc[db][4 * jj + 3] * al);
                 }
@@ -1080,7 +1086,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             for (int w = 0; w < C::WK; ++w)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const float4 v = *reinterpret_cast<const float4*>(accbuf + (w * 32 + r) * D + c0 + 4 * q);
+                    const float4 v = *reinterpret_cast<const float4*>(acc_at(w * 32 + r, c0 + 4 * q));
                     sum[q].x += v.x; sum[q].y += v.y; sum[q].z += v.z; sum[q].w += v.w;
                 }
             if (r < ig.rows) {
