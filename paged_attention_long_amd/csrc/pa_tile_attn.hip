@@ -473,7 +473,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             int big[NC];
 #pragma unroll
             for (int k = 0; k < NC; ++k) {
-                cand[k] = max(tmin, (int)div_ceil_i64(work, t * (k + 1)));
+                cand[k] = one ? tmin : max(tmin, (int)div_ceil_i64(work, t * (k + 1)));
                 items[k] = 0;
                 big[k] = 0;
             }
@@ -481,13 +481,23 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             long long best = -1;
             tps = tmin;
             if (one) {
-#pragma unroll
-                for (int k = 0; k < NC; ++k) {
-                    const int S = one_tub > 0 ? (one_tub + cand[k] - 1) / cand[k] : 0;
+                // lane k evaluates candidate k (the divisions run once, side by
+                // side); the smallest cost wins, ties to the fewer rounds
+                long long cost = 0;
+                int ck = tmin;
+                if (lane < NC) {
+                    ck = max(tmin, (int)div_ceil_i64(work, t * (lane + 1)));
+                    const int S = one_tub > 0 ? (one_tub + ck - 1) / ck : 0;
                     const long long it_k = (long long)one_nqt * S;
                     const int big_k = S > 0 ? (one_tub + S - 1) / S : 0;
-                    const long long cost = div_ceil_i64(it_k * a.num_kv_heads, t) * big_k;
-                    if (best < 0 || cost < best) { best = cost; tps = cand[k]; }
+                    cost = div_ceil_i64(it_k * a.num_kv_heads, t) * big_k;
+                }
+#pragma unroll
+                for (int k = 0; k < NC; ++k) {
+                    const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)cost, k);
+                    const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((unsigned long long)cost >> 32), k);
+                    const long long c_k = (long long)(((unsigned long long)hi << 32) | lo);
+                    if (best < 0 || c_k < best) { best = c_k; tps = __builtin_amdgcn_readlane(ck, k); }
                 }
             }
             for (int b = tid; !one && b < a.num_seqs; b += nthr) {
