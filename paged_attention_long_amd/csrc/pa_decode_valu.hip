@@ -345,8 +345,17 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
             __syncthreads();
         }
 
-        if (!direct && it == first_item && tid == 0)
-            publish_merge(a, MergeDesc{(int)first_item, n_splits, rows, a.r_max, si.q_off, g, 0, vscale});
+        if (!direct && it == first_item && tid == 0) {
+            const MergeDesc d{(int)first_item, n_splits, rows, a.r_max, si.q_off, g, 0, vscale};
+            if (a.sdesc != nullptr) {
+                // fixed slots, one per merge unit the group's rows cover
+                MergeDesc* slot = a.sdesc + (int64_t)(b * a.num_kv_heads + g) * a.sdesc_upg;
+                const int units = (rows + merge_rpu(D) - 1) / merge_rpu(D);
+                for (int u = 0; u < units; ++u) slot[u] = d;
+            } else {
+                publish_merge(a, d);
+            }
+        }
     };
 
     if (a.static_pps > 0) {

@@ -8,6 +8,9 @@ namespace pa {
 
 constexpr int kMaxSplits = 64;        // splits per (sequence, KV head) the merge reads in one pass
 constexpr int kPidChunkPages = 1024;  // page ids a workgroup stages in LDS at a time
+constexpr int kMergeThreads = 256;    // threads of a merge workgroup
+// Rows of one merge unit: a merge thread owns a float4 column of one row.
+constexpr int merge_rpu(int head_dim) { return kMergeThreads / (head_dim / 4); }
 
 // One group of split partials to merge: rows [0, rows) of items
 // first_item .. first_item + n_splits - 1 (row stride rstride in the partial
@@ -38,6 +41,12 @@ struct DecodeArgs {
     float* ws_lse;             // [max_items][r_max] (log2 domain)
     MergeDesc* mdesc;          // merge groups published by this forward
     int* mcount;               // [0]: groups published, [1]: merge workgroups done
+    // Fixed merge slots (static splits, VALU kernel only): when set, the group
+    // of (sequence b, KV head g) writes its descriptor to slots
+    // (b * Hkv + g) * sdesc_upg + u for each merge unit u its rows cover,
+    // instead of appending to mdesc.
+    MergeDesc* sdesc;
+    int sdesc_upg;
     int64_t page_stride, head_stride, token_stride;   // elements
     int num_seqs, bt_stride;
     int num_q_heads, num_kv_heads, group;
@@ -62,6 +71,11 @@ struct MergeArgs {
     float* lse;
     int num_q_heads, group, max_rows;
     int desc_cap;              // descriptors the workspace holds
+    // Fixed slots: > 0 selects them; workgroup u merges the unit whose
+    // descriptor is in sdesc[u] (units per group: sdesc_upg), if one was
+    // written this forward, and clears it.  mdesc and mcount are then unused.
+    MergeDesc* sdesc;
+    int static_units, sdesc_upg;
 };
 // many_groups: a variant with fewer partial rows in flight per thread and many
 // resident workgroups, for launches that publish many groups (prefill).

@@ -12,8 +12,6 @@ namespace pa {
 
 namespace {
 
-constexpr int kMergeThreads = 256;
-
 // BATCH: partial rows in flight per thread.  32 covers the split counts of
 // decode and verification in one round trip (one workgroup per CU at that
 // register count); 8 keeps the registers low enough for many resident
@@ -31,6 +29,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
     const int lane = tid & (kWave - 1);
     const int wid = tid / kWave;
 
+    static_assert(RPU == merge_rpu(D), "unit size shared with the publishers");
     const int upg = (m.max_rows + RPU - 1) / RPU;   // units per group
     // The attention kernels' writes are visible across the kernel boundary.
     // This workgroup's first group descriptor is read together with the count
@@ -107,11 +106,85 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
     }
 }
 
+// Fixed slots (static splits): workgroup u merges the unit whose descriptor is
+// in m.sdesc[u], if one was written this forward, and clears the slot once
+// every thread has its copy, so a group merged directly in a later forward
+// finds it empty.  No count and no arrival counter.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_slots_kernel(MergeArgs m) {
+    constexpr int EPR = D / 4;                    // float4 columns per row
+    constexpr int RPU = kMergeThreads / EPR;      // rows per unit
+    constexpr int NW = kMergeThreads / kWave;
+    constexpr int B = 32;                         // partial rows in flight per thread
+    static_assert(RPU == merge_rpu(D), "unit size shared with the publishers");
+    __shared__ float w_sh[RPU][kMaxSplits];
+    __shared__ float lse_sh[RPU];
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wid = tid / kWave;
+    const MergeDesc d = m.sdesc[blockIdx.x];
+    __syncthreads();
+    if (d.n_splits == 0) return;
+    if (tid == 0) m.sdesc[blockIdx.x].n_splits = 0;
+    const int r0 = (int)(blockIdx.x % m.sdesc_upg) * RPU;
+    const int rl = tid / EPR;
+    const int col = (tid - rl * EPR) * 4;
+    MergeTarget tgt{m.out, m.lse, m.num_q_heads, m.group, 1.0f};
+    const int nr = min(RPU, d.rows - r0);
+    const int S = d.n_splits;
+    const bool act = rl < nr;
+    const int64_t sstride = (int64_t)d.rstride * D;
+    const float* src = m.ws_o + ((int64_t)d.first_item * d.rstride + r0 + rl) * D + col;
+    float4 o[B];
+    auto issue = [&](int s0) {
+#pragma unroll
+        for (int k = 0; k < B; ++k)
+            o[k] = (act && s0 + k < S) ? *reinterpret_cast<const float4*>(src + (int64_t)(s0 + k) * sstride)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    };
+    issue(0);
+    for (int r = wid; r < nr; r += NW) {
+        const float ls = (lane < S) ? m.ws_lse[((int64_t)d.first_item + lane) * d.rstride + r0 + r] : kNegInf;
+        const float M = wave_max(ls);
+        const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
+        const float L = wave_sum(w);
+        w_sh[r][lane] = (L > 0.f) ? w / L : 0.f;
+        if (lane == 0) lse_sh[r] = (L > 0.f) ? M + fast_log2(L) : kNegInf;
+    }
+    __syncthreads();
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s0 = 0; s0 < S; s0 += B) {
+        if (s0 > 0) issue(s0);
+#pragma unroll
+        for (int k = 0; k < B; ++k) {
+            const float w = (s0 + k < S) ? w_sh[rl][s0 + k] : 0.f;
+            acc.x = fmaf(w, o[k].x, acc.x);
+            acc.y = fmaf(w, o[k].y, acc.y);
+            acc.z = fmaf(w, o[k].z, acc.z);
+            acc.w = fmaf(w, o[k].w, acc.w);
+        }
+    }
+    if (act) {
+        const int64_t orow = out_row(tgt, d.q_off, d.g, d.row0 + r0 + rl);
+        const float sc = d.out_scale;
+        *reinterpret_cast<float4*>(m.out + orow * D + col) = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+        if (m.lse != nullptr && col == 0) {
+            const float l2 = lse_sh[rl];
+            m.lse[orow] = (l2 == kNegInf) ? kNegInf : l2 * kLn2;
+        }
+    }
+}
+
 }  // namespace
 
-int merge_rows_per_unit(int head_dim) { return kMergeThreads / (head_dim / 4); }
+int merge_rows_per_unit(int head_dim) { return merge_rpu(head_dim); }
 
 hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, bool many_groups, hipStream_t stream) {
+    if (m.static_units > 0) {
+        if (head_dim == 64) hipLaunchKernelGGL((merge_slots_kernel<64>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+        else hipLaunchKernelGGL((merge_slots_kernel<128>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+        return hipGetLastError();
+    }
     if (head_dim == 64) {
         if (many_groups) hipLaunchKernelGGL((merge_kernel<64, 8>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
         else hipLaunchKernelGGL((merge_kernel<64, 32>), dim3(grid), dim3(kMergeThreads), 0, stream, m);

@@ -32,6 +32,9 @@ struct pa_handle {
     float* ws_o = nullptr;
     float* ws_lse = nullptr;
     pa::MergeDesc* mdesc = nullptr;   // merge groups published by the attention kernels
+    pa::MergeDesc* sdesc = nullptr;   // fixed merge slots for static splits (zeroed; each merge clears what it used)
+    int sdesc_upg = 1;                // merge units per (sequence, KV head) group in sdesc
+    int64_t sdesc_groups = 0;         // groups sdesc holds
     int* mcount = nullptr;            // [0] groups published, [1] merge workgroups done
     void* ws = nullptr;
     size_t ws_bytes = 0;
@@ -173,8 +176,13 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
     h->desc_cap = (int)std::max<size_t>(1, ((size_t)h->max_items_valu + (D == 128 ? (size_t)h->max_items_mfma : 0)) / 2);
     const size_t d_bytes = (size_t)h->desc_cap * sizeof(pa::MergeDesc);
     const size_t c_bytes = 2 * sizeof(int);
+    // Fixed slots for the VALU kernel's static splits (at most 8 workgroups
+    // per CU, so at most that many (sequence, KV head) groups).
+    h->sdesc_upg = (h->r_max_valu + pa::merge_rows_per_unit(D) - 1) / pa::merge_rows_per_unit(D);
+    h->sdesc_groups = std::min<int64_t>((int64_t)cfg->max_num_seqs * cfg->num_kv_heads, (int64_t)8 * h->cu_count);
+    const size_t s_bytes = (size_t)h->sdesc_groups * h->sdesc_upg * sizeof(pa::MergeDesc);
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    h->ws_bytes = up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes);
+    h->ws_bytes = up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes) + up(s_bytes);
     if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
         const size_t want = h->ws_bytes;
         delete h;
@@ -186,7 +194,8 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
     h->ws_lse = reinterpret_cast<float*>(p + up(o_bytes));
     h->mdesc = reinterpret_cast<pa::MergeDesc*>(p + up(o_bytes) + up(l_bytes));
     h->mcount = reinterpret_cast<int*>(p + up(o_bytes) + up(l_bytes) + up(d_bytes));
-    if (hipMemset(h->mcount, 0, c_bytes) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    h->sdesc = reinterpret_cast<pa::MergeDesc*>(p + up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes));
+    if (hipMemset(h->mcount, 0, up(c_bytes) + up(s_bytes)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(h->ws);
         delete h;
         return fail(nullptr, PA_ERR_HIP, "workspace clear failed");
@@ -277,6 +286,8 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     a.ws_lse = h->ws_lse;
     a.mdesc = h->mdesc;
     a.mcount = h->mcount;
+    a.sdesc = nullptr;
+    a.sdesc_upg = h->sdesc_upg;
     a.page_stride = layout->page_stride;
     a.head_stride = layout->head_stride;
     a.token_stride = layout->token_stride;
@@ -349,15 +360,19 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
                 a.static_pps = (int)pps;
                 a.static_splits = (int)S;
                 vgrid = (int)items;
+                // alone on the stream, the groups go to fixed merge slots
+                if (!run_mfma && S > 1 && (int64_t)num_seqs * c.num_kv_heads <= h->sdesc_groups) a.sdesc = h->sdesc;
             }
         }
         hipError_t e = pa::launch_decode_valu(a, c.head_dim, c.kv_dtype, c.q_dtype, rw, vgrid, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
         if (a.static_pps > 0 && a.static_splits == 1) need_merge_valu = false;
     }
+    const bool static_merge = a.sdesc != nullptr;
     if (run_mfma) {
         a.static_pps = 0;
         a.static_splits = 0;
+        a.sdesc = nullptr;
         a.cls_side = 1;
         a.min_pps = 1;
         a.forced_pps = h->tune.kv_tiles_per_split;
@@ -369,7 +384,14 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         hipError_t e = pa::launch_mfma_attn(a, c.head_dim, c.kv_dtype, c.q_dtype, h->mfma_wr, tgrid, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "tile launch failed: %s", hipGetErrorString(e));
     }
-    if (need_merge_valu || run_mfma) {
+    if (static_merge && need_merge_valu) {
+        // one workgroup per fixed slot; empty slots leave at once
+        const int64_t su = (int64_t)num_seqs * c.num_kv_heads * h->sdesc_upg;
+        pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, out, lse, c.num_q_heads, G, h->merge_rows,
+                        h->desc_cap, h->sdesc, (int)su, h->sdesc_upg};
+        hipError_t e = pa::launch_merge(m, c.head_dim, (int)su, false, st);
+        if (e != hipSuccess) return fail(h, PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
+    } else if (need_merge_valu || run_mfma) {
         // Merges whatever split groups the launches above published.  Grid:
         // enough workgroups for the most units those launches can publish
         // (each group is merged in units of a few rows).
@@ -386,7 +408,7 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         const bool many = units > 4 * (int64_t)h->cu_count;
         const int mgrid = (int)std::max<int64_t>(1, std::min<int64_t>((many ? 8 : 2) * (int64_t)h->cu_count, units));
         pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, out, lse, c.num_q_heads, G, h->merge_rows,
-                        h->desc_cap};
+                        h->desc_cap, nullptr, 0, 1};
         hipError_t e = pa::launch_merge(m, c.head_dim, mgrid, many, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
     }
