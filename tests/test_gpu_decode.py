@@ -282,3 +282,23 @@ def test_host_argument_errors():
             pal.paged_attn_set_tuning(c.h, grid=10 ** 7)
     finally:
         c.close()
+
+
+def test_fixed_merge_slots_do_not_leak_between_forwards():
+    """Static splits publish to fixed merge slots.  A (sequence, KV head) group
+    merged from several splits, then the same group short enough for a single
+    split on the same handle: the slot must have been emptied by the first
+    merge, or the second forward's direct output would be overwritten."""
+    long = generate(_spec(seq_lens=(4097,), q_lens=(1,)))[0]
+    short = generate(_spec(seq_lens=(40,), q_lens=(1,), seed=9))[0]
+    a = GpuCase([long], split_mode=1)
+    b = GpuCase([short], handle=a.h)
+    try:
+        for i, (inp, case) in enumerate(((long, a), (short, b), (long, a), (short, b))):
+            progress(f"fixed merge slots, forward {i}: seq_len {int(inp.seq_lens[0])}")
+            ref_o, ref_l = oracle.attention(inp)
+            out, lse = case.run()
+            compare(f"forward{i}", inp.kv_dtype, out, lse, ref_o, ref_l)
+    finally:
+        b.close()
+        a.close()
