@@ -879,30 +879,36 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             // k's scores into P.  Tile k's K sits in K buffer k % NKB from its
             // load (issued at iteration k - LEAD) to its QK (iteration k - 1); its
             // V in V buffer k % NVB until its P.V (iteration k + 1).
-            const int n_pid = max(0, min(C::PID_CAP, (ig.t_end - ig.t_begin) * PPT));
+            // Page ids of the item's tiles and of the LEAD tiles prefetched past
+            // its end (those read the last visible page: in bounds, unused),
+            // staged in LDS when they fit; otherwise scalar loads per tile.
+            const int n_pid = (ig.t_end - ig.t_begin + C::LEAD) * PPT;
+            const bool staged = n_pid <= C::PID_CAP;
             const int pid0 = ig.pg_first + ig.t_begin * PPT;
-            for (int k = tid; k < n_pid; k += blockDim.x) ipid[k] = bt[min(pid0 + k, ig.pg_end - 1)];
+            if (staged)
+                for (int k = tid; k < n_pid; k += blockDim.x) ipid[k] = bt[min(pid0 + k, ig.pg_end - 1)];
             __syncthreads();
+            // tiles t_begin + k with k in [k_live, k_live + n_live) have no dead V rows
+            int k_live, n_live;
+            {
+                const int kb0 = ig.pg_first * kPage;
+                const int key_b = min(ig.si.seq_len, ig.pg_end * kPage);
+                const int t_lo = ig.si.lo <= kb0 ? 0 : (ig.si.lo - kb0 + BN - 1) / BN;
+                const int t_hi = key_b < kb0 ? 0 : (key_b - kb0) / BN;
+                k_live = t_lo - ig.t_begin;
+                n_live = max(0, t_hi - t_lo);
+            }
             const uint32_t ring32 = (uint32_t)(uintptr_t)(lds_void_t*)tiles;
             auto v_lds = [&](int k) { return ring32 + (uint32_t)((C::NKB + k % C::NVB) * C::TILE); };
             auto dma_pipe = [&](int k) {
-                const int t = min(ig.t_begin + k, ig.t_end - 1);
                 int pid[PPT];
-                const int q0 = (t - ig.t_begin) * PPT;
-                if (q0 + PPT <= n_pid) {
-                    if constexpr (PPT == 4) {
-                        const int4 w = *reinterpret_cast<const int4*>(ipid + q0);
-                        pid[0] = __builtin_amdgcn_readfirstlane(w.x);
-                        pid[1] = __builtin_amdgcn_readfirstlane(w.y);
-                        pid[2] = __builtin_amdgcn_readfirstlane(w.z);
-                        pid[3] = __builtin_amdgcn_readfirstlane(w.w);
-                    } else {
-                        static_assert(PPT == 2, "tiles of 2 or 4 pages");
-                        const int2 w = *reinterpret_cast<const int2*>(ipid + q0);
-                        pid[0] = __builtin_amdgcn_readfirstlane(w.x);
-                        pid[1] = __builtin_amdgcn_readfirstlane(w.y);
-                    }
+                if (staged) {
+                    static_assert(PPT == 2, "tiles of two pages");
+                    const int2 w = *reinterpret_cast<const int2*>(ipid + k * PPT);
+                    pid[0] = __builtin_amdgcn_readfirstlane(w.x);
+                    pid[1] = __builtin_amdgcn_readfirstlane(w.y);
                 } else {
+                    const int t = min(ig.t_begin + k, ig.t_end - 1);
 #pragma unroll
                     for (int p = 0; p < PPT; ++p) pid[p] = tile_pid(t, p);
                 }
@@ -938,10 +944,9 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             };
             // dead V rows of tile k (range edges only) are zeroed in its buffer
             auto zero_dead_v_pipe = [&](int k) {
+                if ((unsigned)(k - k_live) < (unsigned)n_live) return false;
                 const int t = ig.t_begin + k;
                 const int k0 = key_pos(t, 0);
-                const bool edge = (k0 < ig.si.lo) || (k0 + BN > ig.si.seq_len) || (ig.pg_first + (t + 1) * PPT > ig.pg_end);
-                if (!edge) return false;
                 uint8_t* vb = tiles + (C::NKB + k % C::NVB) * C::TILE;
                 for (int e = tid; e < BN * 16; e += blockDim.x) {
                     const int key = e >> 4, c = e & 15;
