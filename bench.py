@@ -228,7 +228,7 @@ def cpu_baseline(workload: str, base, budget_s: float = 12.0):
 
 
 COPY_KERNEL_TAG = "neg_kernel"     # torch.neg: reads N bytes, writes N bytes
-OUR_KERNEL_TAGS = ("decode_valu_kernel", "tile_attn_kernel", "merge_kernel")
+OUR_KERNEL_TAGS = ("decode_valu_kernel", "tile_attn_kernel", "merge_kernel", "merge_slots_kernel")
 
 
 def calibrate_copy(mib: int) -> None:
