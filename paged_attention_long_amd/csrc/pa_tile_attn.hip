@@ -161,6 +161,36 @@ PA_DEVINLINE void lds_read_b128_x8(const uint32_t (&addr)[8], u32x4_t (&r)[8]) {
         : "memory");
 }
 
+// Eight paired 64-bit LDS reads: r[c] = {8 bytes at addr + 512c, 8 bytes at
+// addr + 4096 + 512c} (one raw fp8 K chunk and the matching V chunk), completed
+// inside the block.  The reads are invisible to the compiler's wait insertion,
+// so the caller orders them after the asynchronous loads that fill the slot.
+PA_DEVINLINE void lds_read_raw_kv(uint32_t addr, u32x4_t (&r)[8]) {
+    asm volatile(
+        "ds_read2st64_b64 %0, %8 offset0:0 offset1:8\n\t"
+        "ds_read2st64_b64 %1, %8 offset0:1 offset1:9\n\t"
+        "ds_read2st64_b64 %2, %8 offset0:2 offset1:10\n\t"
+        "ds_read2st64_b64 %3, %8 offset0:3 offset1:11\n\t"
+        "ds_read2st64_b64 %4, %8 offset0:4 offset1:12\n\t"
+        "ds_read2st64_b64 %5, %8 offset0:5 offset1:13\n\t"
+        "ds_read2st64_b64 %6, %8 offset0:6 offset1:14\n\t"
+        "ds_read2st64_b64 %7, %8 offset0:7 offset1:15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(addr)
+        : "memory");
+}
+
+// A widened K chunk at addr and the matching V chunk at addr + VOFF.  Inline
+// asm for the same reason as the reads: the compiler's alias tracking can lose
+// the LDS object of these stores and wait for every asynchronous load in
+// flight.  Stores take their data at issue; the caller orders later reads.
+template <int VOFF>
+PA_DEVINLINE void lds_write_kv(uint32_t addr, const u32x4_t& k, const u32x4_t& v) {
+    asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:%3" : : "v"(addr), "v"(k), "v"(v), "i"(VOFF)
+                 : "memory");
+}
+
 // Sixteen 128-bit LDS reads: addr[k] (into r0) and addr[k] + OFF (into r1),
 // completed inside the block.
 template <int OFF>
@@ -268,20 +298,29 @@ struct Cfg {
     static constexpr bool FP8 = (KVT == PA_DTYPE_FP8_E4M3);
     static constexpr int EB = FP8 ? 1 : 2;
     static constexpr int PVT = FP8 ? PA_DTYPE_F16 : KVT;   // P.V operand type
-    static constexpr bool PSPLIT = (WR == 1);              // memory-bound: P.V always on the split P
+    // memory-bound 16-bit caches: P.V always on the split P (fp8 caches never
+    // split P: their own error is far larger than P's f16 rounding)
+    static constexpr bool PSPLIT = (WR == 1) && !FP8;
     static constexpr int TILE = BN * kRowBytes;            // bytes of one K (or V) tile in LDS
     static constexpr int NBUF = FP8 ? 1 : 2;               // LDS buffers per wave group
     static constexpr int GROUP_LDS = NBUF * 2 * TILE;
     static constexpr int DMA_PER_WAVE = BN * kRowBytes / 1024 / WR;   // 1 KB async loads per wave per tile
     // fp8 register staging: 8-element chunks per thread per tile
     static constexpr int FCH = BN * (D / 8) / NT;
+    // fp8 at WR = 1: raw tiles reach LDS by asynchronous loads into two
+    // staging slots (two LDS objects), each wave widening its own tiles from
+    // there; RAW_DMA 1 KB loads per wave per tile (K and V).
+    static constexpr bool FSTAGE = FP8 && (WR == 1);
+    static constexpr int RAW_TILE = BN * D;                // bytes of one raw fp8 K (or V) tile
+    static constexpr int RAW_DMA = 2 * RAW_TILE / 1024;
+    static constexpr int STAGE_LDS = FSTAGE ? WK * 2 * RAW_TILE : 16;
     // 256-row items on 16-bit caches run a software pipeline: K tiles in a
     // ring of NKB buffers, V tiles in a ring of NVB, loads issued LEAD tiles
     // ahead; the item's page ids are staged in LDS (PID_CAP of them).  The
     // loop is unrolled over the ring, so buffer offsets are immediates.
     static constexpr bool PIPE = (WR == 8) && !FP8;
     static constexpr int NKB = 4, NVB = 4, LEAD = 3;
-    static constexpr int PID_CAP = PIPE ? 4096 : 1;
+    static constexpr int PID_CAP = PIPE ? 4096 : (WR == 1 ? 1024 : 1);
     static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : WK * GROUP_LDS / NBUF;
     static constexpr int TILES2_LDS = (PIPE || NBUF == 1) ? 16 : WK * GROUP_LDS / NBUF;
 };
@@ -295,19 +334,20 @@ struct Raw<PA_DTYPE_BF16> { using T = u32x4_t; };
 template <>
 struct Raw<PA_DTYPE_FP8_E4M3> { using T = u32x2_t; };
 
+// Eight fp8 e4m3 values to eight 16-bit values, exactly (both targets hold
+// every e4m3 value): the gfx950 scaled conversion with scale 1 turns two fp8
+// bytes of a word (low or high half) into a packed pair in one instruction.
 template <int T>
 PA_DEVINLINE u32x4_t widen_fp8x8(const u32x2_t& c) {
     u32x4_t r;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const f32x2_t lo = fp8x2_to_f32(c[i], false);
-        const f32x2_t hi = fp8x2_to_f32(c[i], true);
         if constexpr (T == PA_DTYPE_BF16) {
-            r[2 * i] = f32x2_to_bf16x2(lo);
-            r[2 * i + 1] = f32x2_to_bf16x2(hi);
+            r[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, false));
+            r[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[i], 1.0f, true));
         } else {
-            r[2 * i] = f32x2_to_f16x2(lo);
-            r[2 * i + 1] = f32x2_to_f16x2(hi);
+            r[2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[i], 1.0f, false));
+            r[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c[i], 1.0f, true));
         }
     }
     return r;
@@ -333,6 +373,8 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[C::TILES_LDS];
     __shared__ __attribute__((aligned(1024))) uint8_t tiles2[C::TILES2_LDS];
     __shared__ __attribute__((aligned(16))) int ipid[C::PID_CAP];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage0[C::STAGE_LDS];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage1[C::STAGE_LDS];
     __shared__ float red_m[4][32];
     __shared__ float red_e[4][32];
     __shared__ long long redw[8], redq[8];
@@ -601,8 +643,11 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             ig.t_begin = min(ig.n_tiles, ig.split * tpsb);
             ig.t_end = min(ig.n_tiles, ig.t_begin + tpsb);
         }
-        const float kscale = C::FP8 ? a.kv_scale[ig.g] : 1.0f;
-        const float vscale = C::FP8 ? a.kv_scale[a.num_kv_heads + ig.g] : 1.0f;
+        // the scales are read-only and uniform: scalar loads (a vector load
+        // would sit in the same in-order counter as the tile loads issued next)
+        const __attribute__((address_space(4))) float* ksc = (const __attribute__((address_space(4))) float*)a.kv_scale;
+        const float kscale = C::FP8 ? ksc[ig.g] : 1.0f;
+        const float vscale = C::FP8 ? ksc[a.num_kv_heads + ig.g] : 1.0f;
         const float s2 = a.scale * kLog2e * kscale;
         const int32_t* bt = a.block_table + (int64_t)ig.b * a.bt_stride;
         const bool direct = (ig.splits == 1);
@@ -671,10 +716,26 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             const int c = (lane & 15) ^ swz_key(row);
             dma_off[ii] = (uint32_t)(head_off + (int64_t)(row % kPage) * tok_bytes + c * 16);
         }
-        auto dma_tile = [&](int t, int buf) {
-            int pid[PPT];
+        // WR = 1: the item's page ids are staged in LDS when they fit (set
+        // before the tile loop), so a tile's loads do not wait behind a
+        // scalar block-table load that missed its cache.
+        bool pid_staged = false;
+        auto tile_pids = [&](int t, int (&pid)[PPT]) {
+            if constexpr (WR == 1) {
+                static_assert(PPT == 2, "tiles of two pages");
+                if (pid_staged) {
+                    const int2 w = *reinterpret_cast<const int2*>(ipid + (t - ig.t_begin) * PPT);
+                    pid[0] = __builtin_amdgcn_readfirstlane(w.x);
+                    pid[1] = __builtin_amdgcn_readfirstlane(w.y);
+                    return;
+                }
+            }
 #pragma unroll
             for (int p = 0; p < PPT; ++p) pid[p] = tile_pid(t, p);
+        };
+        auto dma_tile = [&](int t, int buf) {
+            int pid[PPT];
+            tile_pids(t, pid);
 #pragma unroll
             for (int ii = 0; ii < C::DMA_PER_WAVE; ++ii) {
                 const int i = ii * WR + wig;
@@ -707,6 +768,50 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 if constexpr (C::FP8) {
                     *reinterpret_cast<u32x4_t*>(kbuf(buf) + swz(key, e)) = widen_fp8x8<QT>(fk[c]);
                     *reinterpret_cast<u32x4_t*>(vbuf(buf) + swz(key, e)) = widen_fp8x8<C::PVT>(fv[c]);
+                }
+            }
+        };
+        // fp8 staging (FSTAGE): async load i of a raw tile covers rows 8i ..
+        // 8i+7 (128 B each), lane l row 8i + l/8, 16-byte chunk l%8; the raw
+        // tile sits row-major in the slot, K then V.
+        uint32_t raw_off[C::FSTAGE ? 4 : 1];
+        if constexpr (C::FSTAGE) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 8 * i + (lane >> 3);
+                raw_off[i] = (uint32_t)(head_off + (int64_t)(row % kPage) * tok_bytes + (lane & 7) * 16);
+            }
+        }
+        auto stage_slot = [&](auto slot_c) {
+            return (decltype(slot_c)::value == 0 ? stage0 : stage1) + gi * 2 * C::RAW_TILE;
+        };
+        auto raw_dma = [&](auto slot_c, int t) {
+            if constexpr (C::FSTAGE) {
+                uint8_t* st = stage_slot(slot_c);
+                int pid[PPT];
+                tile_pids(t, pid);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t pb = (int64_t)pid[(8 * i) / kPage] * page_bytes;
+                    async_load16(kbase + pb + raw_off[i], (lds_void_t*)(st + i * 1024));
+                    async_load16(vbase + pb + raw_off[i], (lds_void_t*)(st + C::RAW_TILE + i * 1024));
+                }
+            }
+        };
+        // widen a staged raw tile into the group's K/V buffer (same layout as
+        // fp8_store): chunk ch = gtid + 64c of the raw tile is bytes 8ch .. 8ch+7
+        auto raw_widen = [&](auto slot_c) {
+            if constexpr (C::FSTAGE) {
+                static_assert(C::NT == 64 && C::FCH == 8 && C::RAW_TILE == 4096, "lds_read_raw_kv offsets");
+                u32x4_t r[8];
+                lds_read_raw_kv((uint32_t)(uintptr_t)(lds_void_t*)(stage_slot(slot_c) + gtid * 8), r);
+                const uint32_t kb32 = (uint32_t)(uintptr_t)(lds_void_t*)kbuf(0);
+#pragma unroll
+                for (int c = 0; c < C::FCH; ++c) {
+                    const int ch = gtid + c * C::NT;
+                    const int key = ch / (D / 8), e = ch % (D / 8);
+                    lds_write_kv<C::TILE>(kb32 + (uint32_t)swz(key, e), widen_fp8x8<QT>(u32x2_t{r[c][0], r[c][1]}),
+                                          widen_fp8x8<C::PVT>(u32x2_t{r[c][2], r[c][3]}));
                 }
             }
         };
@@ -795,7 +900,9 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                     pb[ts][j] = pack2<C::PVT>(p0, p1);
                 }
             }
-            const bool split = C::PSPLIT || wave_any(l_exact < split_thr);
+            // fp8 caches: P's f16 rounding (relative 2^-11) stays far inside
+            // the error the cache format already carries, so no split
+            const bool split = C::PSPLIT || (!C::FP8 && wave_any(l_exact < split_thr));
             if (split) {
 #pragma unroll
                 for (int ts = 0; ts < C::TS; ++ts) {
@@ -873,6 +980,15 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
         // ------------------------------------------------------------ tile loop
         const int my_first = ig.t_begin + gi;
         const int n_iter = (ig.t_end - ig.t_begin + C::WK - 1) / C::WK;
+        if constexpr (WR == 1) {
+            // every tile a wave loads (clamped to the item's last) is staged
+            const int n_pid = (ig.t_end - ig.t_begin) * PPT;
+            pid_staged = n_pid <= C::PID_CAP;
+            const int pid0 = ig.pg_first + ig.t_begin * PPT;
+            if (pid_staged)
+                for (int k = tid; k < n_pid; k += blockDim.x) ipid[k] = bt[min(pid0 + k, ig.pg_end - 1)];
+            __syncthreads();
+        }
         if constexpr (C::PIPE) {
             // Iteration k: P.V of tile k-1, then (after tile k+1 has landed) the
             // scores of tile k+1 on the matrix cores while the VALU turns tile
@@ -1033,6 +1149,37 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                         if (itn + 2 < n_iter) dma_tile(min(t + 2 * C::WK, ig.t_end - 1), half);
                     }
                 }
+            }
+        } else if constexpr (C::FSTAGE) {
+            // Tile itn of this wave is staged in slot itn % 2, loaded two tiles
+            // ahead; a slot is reloaded as soon as it has been widened, so two
+            // raw tiles are in flight while one is computed.  Every load is
+            // issued, past the end too (clamped to the last tile: in bounds,
+            // unused); an odd count ends with one uncomputed iteration.
+            if (n_iter > 0) {
+                using I0 = std::integral_constant<int, 0>;
+                using I1 = std::integral_constant<int, 1>;
+                raw_dma(I0{}, min(my_first, ig.t_end - 1));
+                raw_dma(I1{}, min(my_first + C::WK, ig.t_end - 1));
+                auto fstep = [&](auto slot_c, int itn) {
+                    const int t = my_first + itn * C::WK;
+                    const bool have = t < ig.t_end;
+                    // this slot's loads are the older ones in flight
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::RAW_DMA));
+                    raw_widen(slot_c);
+                    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // slot read out; K/V buffer written
+                    raw_dma(slot_c, min(t + 2 * C::WK, ig.t_end - 1));
+                    if (have) {
+                        if (zero_dead_v(t, 0)) group_sync();
+                        compute_tile(t, kbuf(0), vbuf(0));
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                };
+                for (int iter = 0; iter < n_iter; iter += 2) {
+                    fstep(I0{}, iter);
+                    fstep(I1{}, iter + 1);
+                }
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the clamped loads past the end
             }
         } else {
             if (n_iter > 0) fp8_load(min(my_first, ig.t_end - 1));
