@@ -71,13 +71,24 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
                                            : make_float4(0.f, 0.f, 0.f, 0.f);
         };
         issue(0);
-        for (int r = wid; r < nr; r += NW) {
-            const float ls = (lane < S) ? m.ws_lse[((int64_t)d.first_item + lane) * d.rstride + r0 + r] : kNegInf;
-            const float M = wave_max(ls);
-            const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
-            const float L = wave_sum(w);
-            w_sh[r][lane] = (L > 0.f) ? w / L : 0.f;
-            if (lane == 0) lse_sh[r] = (L > 0.f) ? M + fast_log2(L) : kNegInf;
+        // each wave weighs rows wid, wid + NW, ...: their LSE loads first, together
+        constexpr int RPW = (RPU + NW - 1) / NW;
+        float ls[RPW];
+#pragma unroll
+        for (int k = 0; k < RPW; ++k) {
+            const int r = wid + k * NW;
+            ls[k] = (r < nr && lane < S) ? m.ws_lse[((int64_t)d.first_item + lane) * d.rstride + r0 + r] : kNegInf;
+        }
+#pragma unroll
+        for (int k = 0; k < RPW; ++k) {
+            const int r = wid + k * NW;
+            if (r < nr) {
+                const float M = wave_max(ls[k]);
+                const float w = (ls[k] == kNegInf) ? 0.f : fast_exp2(ls[k] - M);
+                const float L = wave_sum(w);
+                w_sh[r][lane] = (L > 0.f) ? w / L : 0.f;
+                if (lane == 0) lse_sh[r] = (L > 0.f) ? M + fast_log2(L) : kNegInf;
+            }
         }
         __syncthreads();
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -143,13 +154,23 @@ __global__ __launch_bounds__(kMergeThreads) void merge_slots_kernel(MergeArgs m)
                                        : make_float4(0.f, 0.f, 0.f, 0.f);
     };
     issue(0);
-    for (int r = wid; r < nr; r += NW) {
-        const float ls = (lane < S) ? m.ws_lse[((int64_t)d.first_item + lane) * d.rstride + r0 + r] : kNegInf;
-        const float M = wave_max(ls);
-        const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
-        const float L = wave_sum(w);
-        w_sh[r][lane] = (L > 0.f) ? w / L : 0.f;
-        if (lane == 0) lse_sh[r] = (L > 0.f) ? M + fast_log2(L) : kNegInf;
+    constexpr int RPW = (RPU + NW - 1) / NW;
+    float ls[RPW];
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+        const int r = wid + k * NW;
+        ls[k] = (r < nr && lane < S) ? m.ws_lse[((int64_t)d.first_item + lane) * d.rstride + r0 + r] : kNegInf;
+    }
+#pragma unroll
+    for (int k = 0; k < RPW; ++k) {
+        const int r = wid + k * NW;
+        if (r < nr) {
+            const float M = wave_max(ls[k]);
+            const float w = (ls[k] == kNegInf) ? 0.f : fast_exp2(ls[k] - M);
+            const float L = wave_sum(w);
+            w_sh[r][lane] = (L > 0.f) ? w / L : 0.f;
+            if (lane == 0) lse_sh[r] = (L > 0.f) ? M + fast_log2(L) : kNegInf;
+        }
     }
     __syncthreads();
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);

@@ -161,34 +161,45 @@ PA_DEVINLINE void lds_read_b128_x8(const uint32_t (&addr)[8], u32x4_t (&r)[8]) {
         : "memory");
 }
 
-// Eight paired 64-bit LDS reads: r[c] = {8 bytes at addr + 512c, 8 bytes at
-// addr + 4096 + 512c} (one raw fp8 K chunk and the matching V chunk), completed
-// inside the block.  The reads are invisible to the compiler's wait insertion,
-// so the caller orders them after the asynchronous loads that fill the slot.
-PA_DEVINLINE void lds_read_raw_kv(uint32_t addr, u32x4_t (&r)[8]) {
-    asm volatile(
-        "ds_read2st64_b64 %0, %8 offset0:0 offset1:8\n\t"
-        "ds_read2st64_b64 %1, %8 offset0:1 offset1:9\n\t"
-        "ds_read2st64_b64 %2, %8 offset0:2 offset1:10\n\t"
-        "ds_read2st64_b64 %3, %8 offset0:3 offset1:11\n\t"
-        "ds_read2st64_b64 %4, %8 offset0:4 offset1:12\n\t"
-        "ds_read2st64_b64 %5, %8 offset0:5 offset1:13\n\t"
-        "ds_read2st64_b64 %6, %8 offset0:6 offset1:14\n\t"
-        "ds_read2st64_b64 %7, %8 offset0:7 offset1:15\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
-        : "v"(addr)
-        : "memory");
+// One staged raw fp8 tile of slot SLOT (8 KB apart), completed inside the
+// block: eight 64-bit K reads at ka[s] (the K operand layout) and eight 64-bit
+// V chunks, two per read, at va + 4096 + 512c (c = 0 .. 7; v[j] holds chunks 2j
+// and 2j+1).  The reads are invisible to the compiler's wait insertion, so the
+// caller orders them after the asynchronous loads that fill the slot.
+#define PA_RAW_TILE_READS(K0, V0, V1, V2, V3, V4, V5, V6, V7)                                        \
+    asm volatile("ds_read_b64 %0, %12 offset:" #K0 "\n\t"                                          \
+                 "ds_read_b64 %1, %13 offset:" #K0 "\n\t"                                          \
+                 "ds_read_b64 %2, %14 offset:" #K0 "\n\t"                                          \
+                 "ds_read_b64 %3, %15 offset:" #K0 "\n\t"                                          \
+                 "ds_read_b64 %4, %16 offset:" #K0 "\n\t"                                          \
+                 "ds_read_b64 %5, %17 offset:" #K0 "\n\t"                                          \
+                 "ds_read_b64 %6, %18 offset:" #K0 "\n\t"                                          \
+                 "ds_read_b64 %7, %19 offset:" #K0 "\n\t"                                          \
+                 "ds_read2st64_b64 %8, %20 offset0:" #V0 " offset1:" #V1 "\n\t"                    \
+                 "ds_read2st64_b64 %9, %20 offset0:" #V2 " offset1:" #V3 "\n\t"                    \
+                 "ds_read2st64_b64 %10, %20 offset0:" #V4 " offset1:" #V5 "\n\t"                   \
+                 "ds_read2st64_b64 %11, %20 offset0:" #V6 " offset1:" #V7 "\n\t"                   \
+                 "s_waitcnt lgkmcnt(0)"                                                              \
+                 : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),     \
+                   "=&v"(k[6]), "=&v"(k[7]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])      \
+                 : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), \
+                   "v"(ka[7]), "v"(va)                                                               \
+                 : "memory")
+template <int SLOT>
+PA_DEVINLINE void lds_read_raw_tile(const uint32_t (&ka)[8], uint32_t va, u32x2_t (&k)[8], u32x4_t (&v)[4]) {
+    static_assert(SLOT == 0 || SLOT == 1, "two staging slots");
+    if constexpr (SLOT == 0) PA_RAW_TILE_READS(0, 8, 9, 10, 11, 12, 13, 14, 15);
+    else PA_RAW_TILE_READS(8192, 24, 25, 26, 27, 28, 29, 30, 31);
 }
+#undef PA_RAW_TILE_READS
 
-// A widened K chunk at addr and the matching V chunk at addr + VOFF.  Inline
-// asm for the same reason as the reads: the compiler's alias tracking can lose
-// the LDS object of these stores and wait for every asynchronous load in
-// flight.  Stores take their data at issue; the caller orders later reads.
-template <int VOFF>
-PA_DEVINLINE void lds_write_kv(uint32_t addr, const u32x4_t& k, const u32x4_t& v) {
-    asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %2 offset:%3" : : "v"(addr), "v"(k), "v"(v), "i"(VOFF)
-                 : "memory");
+// One 128-bit LDS store at addr + OFF.  Inline asm for the same reason as the
+// reads: the compiler's alias tracking can lose the LDS object of such stores
+// and wait for every asynchronous load in flight.  A store takes its data at
+// issue; the caller orders later reads.
+template <int OFF>
+PA_DEVINLINE void lds_store_b128(uint32_t addr, const u32x4_t& d) {
+    asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(addr), "v"(d), "i"(OFF) : "memory");
 }
 
 // Sixteen 128-bit LDS reads: addr[k] (into r0) and addr[k] + OFF (into r1),
@@ -308,12 +319,13 @@ struct Cfg {
     // fp8 register staging: 8-element chunks per thread per tile
     static constexpr int FCH = BN * (D / 8) / NT;
     // fp8 at WR = 1: raw tiles reach LDS by asynchronous loads into two
-    // staging slots (two LDS objects), each wave widening its own tiles from
-    // there; RAW_DMA 1 KB loads per wave per tile (K and V).
+    // staging slots per wave (K then V, 8 KB a slot); K is widened in
+    // registers at its use, V into one of two 16-bit V buffers per wave.
+    // RAW_DMA 1 KB loads per wave per tile (K and V).
     static constexpr bool FSTAGE = FP8 && (WR == 1);
     static constexpr int RAW_TILE = BN * D;                // bytes of one raw fp8 K (or V) tile
     static constexpr int RAW_DMA = 2 * RAW_TILE / 1024;
-    static constexpr int STAGE_LDS = FSTAGE ? WK * 2 * RAW_TILE : 16;
+    static constexpr int STAGE_LDS = FSTAGE ? WK * 2 * 2 * RAW_TILE : 16;
     // 256-row items on 16-bit caches run a software pipeline: K tiles in a
     // ring of NKB buffers, V tiles in a ring of NVB, loads issued LEAD tiles
     // ahead; the item's page ids are staged in LDS (PID_CAP of them).  The
@@ -373,8 +385,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[C::TILES_LDS];
     __shared__ __attribute__((aligned(1024))) uint8_t tiles2[C::TILES2_LDS];
     __shared__ __attribute__((aligned(16))) int ipid[C::PID_CAP];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage0[C::STAGE_LDS];
-    __shared__ __attribute__((aligned(1024))) uint8_t stage1[C::STAGE_LDS];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage[C::STAGE_LDS];
     __shared__ float red_m[4][32];
     __shared__ float red_e[4][32];
     __shared__ long long redw[8], redq[8];
@@ -771,52 +782,37 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 }
             }
         };
-        // fp8 staging (FSTAGE): async load i of a raw tile covers rows 8i ..
-        // 8i+7 (128 B each), lane l row 8i + l/8, 16-byte chunk l%8; the raw
-        // tile sits row-major in the slot, K then V.
-        uint32_t raw_off[C::FSTAGE ? 4 : 1];
+        // fp8 staging (FSTAGE): async load i of a raw K or V tile covers rows
+        // 8i .. 8i+7 (128 B each), lane l row 8i + l/8.  V rows sit as they
+        // are (lane l brings 16-byte unit l%8); K rows are stored with unit u
+        // at position u ^ (row & 7), so the K operand reads (one unit per row
+        // and lane) spread over the banks: lane l brings unit
+        // (l%8) ^ ((l/8) & 7).  A wave's two slots: [K 4 KB | V 4 KB] each.
+        uint32_t raw_off_k[C::FSTAGE ? 4 : 1], raw_off_v[C::FSTAGE ? 4 : 1];
         if constexpr (C::FSTAGE) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 8 * i + (lane >> 3);
-                raw_off[i] = (uint32_t)(head_off + (int64_t)(row % kPage) * tok_bytes + (lane & 7) * 16);
+                const int64_t row_off = head_off + (int64_t)(row % kPage) * tok_bytes;
+                raw_off_k[i] = (uint32_t)(row_off + (((lane & 7) ^ ((lane >> 3) & 7)) << 4));
+                raw_off_v[i] = (uint32_t)(row_off + (lane & 7) * 16);
             }
         }
-        auto stage_slot = [&](auto slot_c) {
-            return (decltype(slot_c)::value == 0 ? stage0 : stage1) + gi * 2 * C::RAW_TILE;
-        };
         auto raw_dma = [&](auto slot_c, int t) {
             if constexpr (C::FSTAGE) {
-                uint8_t* st = stage_slot(slot_c);
+                uint8_t* st = stage + gi * 4 * C::RAW_TILE + decltype(slot_c)::value * 2 * C::RAW_TILE;
                 int pid[PPT];
                 tile_pids(t, pid);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int64_t pb = (int64_t)pid[(8 * i) / kPage] * page_bytes;
-                    async_load16(kbase + pb + raw_off[i], (lds_void_t*)(st + i * 1024));
-                    async_load16(vbase + pb + raw_off[i], (lds_void_t*)(st + C::RAW_TILE + i * 1024));
-                }
-            }
-        };
-        // widen a staged raw tile into the group's K/V buffer (same layout as
-        // fp8_store): chunk ch = gtid + 64c of the raw tile is bytes 8ch .. 8ch+7
-        auto raw_widen = [&](auto slot_c) {
-            if constexpr (C::FSTAGE) {
-                static_assert(C::NT == 64 && C::FCH == 8 && C::RAW_TILE == 4096, "lds_read_raw_kv offsets");
-                u32x4_t r[8];
-                lds_read_raw_kv((uint32_t)(uintptr_t)(lds_void_t*)(stage_slot(slot_c) + gtid * 8), r);
-                const uint32_t kb32 = (uint32_t)(uintptr_t)(lds_void_t*)kbuf(0);
-#pragma unroll
-                for (int c = 0; c < C::FCH; ++c) {
-                    const int ch = gtid + c * C::NT;
-                    const int key = ch / (D / 8), e = ch % (D / 8);
-                    lds_write_kv<C::TILE>(kb32 + (uint32_t)swz(key, e), widen_fp8x8<QT>(u32x2_t{r[c][0], r[c][1]}),
-                                          widen_fp8x8<C::PVT>(u32x2_t{r[c][2], r[c][3]}));
+                    async_load16(kbase + pb + raw_off_k[i], (lds_void_t*)(st + i * 1024));
+                    async_load16(vbase + pb + raw_off_v[i], (lds_void_t*)(st + C::RAW_TILE + i * 1024));
                 }
             }
         };
         // Zero the V rows of dead keys (only tiles that touch a range edge).
-        auto zero_dead_v = [&](int t, int buf) {
+        auto zero_dead_v_in = [&](int t, uint8_t* vb) {
             const int k0 = key_pos(t, 0);
             const bool edge = (k0 < ig.si.lo) || (k0 + BN > ig.si.seq_len) || (ig.pg_first + (t + 1) * PPT > ig.pg_end);
             if (!edge) return false;
@@ -824,10 +820,11 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 const int key = e >> 4, c = e & 15;
                 const int j = k0 + key;
                 const bool live = (j >= ig.si.lo) && (j < ig.si.seq_len) && (ig.pg_first + t * PPT + key / kPage < ig.pg_end);
-                if (!live) *reinterpret_cast<u32x4_t*>(vbuf(buf) + swz(key, c)) = u32x4_t{0u, 0u, 0u, 0u};
+                if (!live) *reinterpret_cast<u32x4_t*>(vb + swz(key, c)) = u32x4_t{0u, 0u, 0u, 0u};
             }
             return true;
         };
+        auto zero_dead_v = [&](int t, int buf) { return zero_dead_v_in(t, vbuf(buf)); };
         // Synchronise the wave group after LDS writes (WR == 1: one wave).
         auto group_sync = [&]() {
             if constexpr (WR == 1) __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wave's LDS writes are done
@@ -1151,33 +1148,92 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 }
             }
         } else if constexpr (C::FSTAGE) {
-            // Tile itn of this wave is staged in slot itn % 2, loaded two tiles
-            // ahead; a slot is reloaded as soon as it has been widened, so two
-            // raw tiles are in flight while one is computed.  Every load is
-            // issued, past the end too (clamped to the last tile: in bounds,
-            // unused); an odd count ends with one uncomputed iteration.
+            // Software pipeline over this wave's tiles (iteration k: tile
+            // my_first + k*WK).  Raw tile k sits in staging slot k % 2 (loaded
+            // two iterations ahead), its widened V in V buffer k % 2.  Step k:
+            // P.V of tile k-1, then tile k+1 is read out of its slot (which is
+            // reloaded at once), its V widened into V buffer (k+1) % 2 and its
+            // K widened in registers for its scores on the matrix cores, while
+            // the VALU turns tile k's scores into P.  Every load is issued,
+            // past the end too (clamped to the last tile: in bounds, unused).
             if (n_iter > 0) {
                 using I0 = std::integral_constant<int, 0>;
                 using I1 = std::integral_constant<int, 1>;
-                raw_dma(I0{}, min(my_first, ig.t_end - 1));
-                raw_dma(I1{}, min(my_first + C::WK, ig.t_end - 1));
-                auto fstep = [&](auto slot_c, int itn) {
-                    const int t = my_first + itn * C::WK;
-                    const bool have = t < ig.t_end;
-                    // this slot's loads are the older ones in flight
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::RAW_DMA));
-                    raw_widen(slot_c);
-                    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // slot read out; K/V buffer written
-                    raw_dma(slot_c, min(t + 2 * C::WK, ig.t_end - 1));
-                    if (have) {
-                        if (zero_dead_v(t, 0)) group_sync();
-                        compute_tile(t, kbuf(0), vbuf(0));
+                static_assert(C::NB == 1 && C::NT == 64 && C::FCH == 8 && C::RAW_TILE == 4096 && C::TILE == 8192,
+                              "lds_read_raw_tile offsets");
+                uint8_t* st = stage + gi * 4 * C::RAW_TILE;
+                uint8_t* vw = tiles + gi * 2 * C::TILE;   // V buffer J at vw + J * TILE
+                const uint32_t st32 = (uint32_t)(uintptr_t)(lds_void_t*)st;
+                const uint32_t vw32 = (uint32_t)(uintptr_t)(lds_void_t*)vw;
+                uint32_t ka[8], vt[8];
+#pragma unroll
+                for (int s8 = 0; s8 < 8; ++s8) ka[s8] = st32 + l32 * 128 + ((s8 ^ (l32 & 7)) << 4) + h32 * 8;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) vt[k] = vw32 + v_lane_off[k];
+                const uint32_t va = st32 + gtid * 8;
+                auto tile_of = [&](int k) { return my_first + k * C::WK; };
+                raw_dma(I0{}, min(tile_of(0), ig.t_end - 1));
+                raw_dma(I1{}, min(tile_of(1), ig.t_end - 1));
+                // tile k from slot J: read out, slot reloaded with tile k+2, V
+                // widened into V buffer J, scores into S
+                auto load_tile = [&](auto j_c, int k, f32x16_t (&S)[C::NB]) {
+                    constexpr int J = decltype(j_c)::value;
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::RAW_DMA));   // slot J's tile is the older in flight
+                    u32x2_t kr[8];
+                    u32x4_t vr[4];
+                    lds_read_raw_tile<J>(ka, va, kr, vr);
+                    raw_dma(j_c, min(tile_of(k + 2), ig.t_end - 1));
+#pragma unroll
+                    for (int c = 0; c < C::FCH; ++c) {
+                        const int key = gtid / 16 + 4 * c, e = gtid % 16;
+                        const u32x4_t& w = vr[c / 2];
+                        const u32x2_t raw = (c % 2) ? u32x2_t{w[2], w[3]} : u32x2_t{w[0], w[1]};
+                        lds_store_b128<J * C::TILE>(vw32 + (uint32_t)swz(key, e), widen_fp8x8<C::PVT>(raw));
                     }
-                    __builtin_amdgcn_wave_barrier();
+                    const int t = tile_of(k);
+                    if (t < ig.t_end) zero_dead_v_in(t, vw + J * C::TILE);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) S[0][i] = 0.f;
+#pragma unroll
+                    for (int s8 = 0; s8 < C::KS; ++s8) S[0] = mma32<QT>(widen_fp8x8<QT>(kr[s8]), qreg[s8], S[0]);
                 };
-                for (int iter = 0; iter < n_iter; iter += 2) {
-                    fstep(I0{}, iter);
-                    fstep(I1{}, iter + 1);
+                u32x4_t pb[C::TS], pl[C::TS];
+                // Step k < n_iter - 1 (tiles k and k+1 are the item's: only a
+                // wave's last tile can lie past the end): no branches around
+                // the pieces, so tile k+1's matrix ops and tile k's exponentials
+                // share one block and interleave.
+                auto step = [&](auto j_c, int k, f32x16_t (&cur)[C::NB], f32x16_t (&nxt)[C::NB]) {
+                    constexpr int J = decltype(j_c)::value;
+                    mask_scores(tile_of(k), cur);
+                    if (k > 0) pv_frags(vt, std::integral_constant<int, (1 - J) * C::TILE>{}, pb);   // tile k-1
+                    raise_max(cur);
+                    load_tile(std::integral_constant<int, 1 - J>{}, k + 1, nxt);
+                    exp_pack(cur, pb, pl);
+                };
+                // the last step: no tile to load; its tile may lie past the end
+                auto last_step = [&](auto j_c, int k, f32x16_t (&cur)[C::NB]) {
+                    constexpr int J = decltype(j_c)::value;
+                    const bool have = tile_of(k) < ig.t_end;
+                    if (have) mask_scores(tile_of(k), cur);
+                    if (k > 0) pv_frags(vt, std::integral_constant<int, (1 - J) * C::TILE>{}, pb);
+                    if (have) {
+                        raise_max(cur);
+                        exp_pack(cur, pb, pl);
+                        pv_frags(vt, std::integral_constant<int, J * C::TILE>{}, pb);
+                    }
+                };
+                f32x16_t S0[C::NB], S1[C::NB];
+                load_tile(I0{}, 0, S0);
+                int k = 0;
+                for (; k + 2 < n_iter; k += 2) {
+                    step(I0{}, k, S0, S1);
+                    step(I1{}, k + 1, S1, S0);
+                }
+                if (k + 1 < n_iter) {
+                    step(I0{}, k, S0, S1);
+                    last_step(I1{}, k + 1, S1);
+                } else {
+                    last_step(I0{}, k, S0);
                 }
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the clamped loads past the end
             }
