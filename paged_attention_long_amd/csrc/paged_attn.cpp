@@ -321,6 +321,14 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         a.cls_rows = kValuRowsMax; a.cls_len = kValuMaxKeys;
         run_valu = rows_min <= kValuRowsMax;
         run_mfma = rows_max > kValuRowsMax || cap_tokens > kValuMaxKeys;
+        // A tile launch with 32-row items takes the few-row sequences as well:
+        // a VALU launch before it on the same stream would add its whole
+        // latency, and per key the tile kernel costs less.  (With prefill-sized
+        // items a few-row sequence would fill a small part of each tile.)
+        if (run_mfma && h->mfma_wr == 1) {
+            run_valu = false;
+            a.cls_rows = 0; a.cls_len = 0;
+        }
     }
     bool need_merge_valu = run_valu;
     if (run_valu) {

@@ -74,6 +74,11 @@ VERIFY = {
                           kv_dtype="f16", window=300, poison_out_of_window=True),
     "fp8_q4_q8": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(3000, 999), q_lens=(4, 8), kv_dtype="fp8_e4m3"),
     "bf16_q3_g6": dict(seq_lens=(1234,), q_lens=(3,)),
+    # fp8 verification widths on the tile kernel: a poisoned window (dead
+    # rows zeroed in the widened V buffer) and sequences of one and two tiles
+    "fp8_q8_window": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(4000,), q_lens=(8,), kv_dtype="fp8_e4m3",
+                          window=200, poison_out_of_window=True, k_outlier_frac=0.01),
+    "fp8_short": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(20, 50, 33), q_lens=(8, 2, 4), kv_dtype="fp8_e4m3"),
 }
 
 
@@ -102,6 +107,22 @@ def test_tile_split_invariance(tps):
     finally:
         c.close()
     compare(f"tps={tps}", inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("tps", [1, 2, 3, 5])
+def test_fp8_tile_split_invariance(tps):
+    # 1 .. 5 tiles per item: a wave gets zero, one or two tiles, so each of the
+    # fp8 pipeline's endings (one step, an even and an odd count) is taken
+    inp = generate(_spec(num_q_heads=32, num_kv_heads=8, seq_lens=(2100, 700), q_lens=(8, 4),
+                         kv_dtype="fp8_e4m3"))[0]
+    progress(f"fp8 tile split tps={tps}")
+    ref_o, ref_l = oracle.attention(inp)
+    c = GpuCase([inp], kv_tiles_per_split=tps, path=pal.PA_PATH_MFMA)
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare(f"fp8 tps={tps}", inp.kv_dtype, out, lse, ref_o, ref_l)
 
 
 def test_mfma_deterministic():
