@@ -74,12 +74,18 @@ struct MergeArgs {
     // Fixed slots: > 0 selects them; workgroup u merges the unit whose
     // descriptor is in sdesc[u] (units per group: sdesc_upg), if one was
     // written this forward, and clears it.  mdesc and mcount are then unused.
+    // The groups' items are numbered as in the static split mode (group
+    // q = b * Hkv + g owns items q * static_splits ..., static_rstride rows
+    // each), so the partials are requested together with the descriptor.
     MergeDesc* sdesc;
-    int static_units, sdesc_upg;
+    int static_units, sdesc_upg, static_splits, static_rstride;
 };
-// many_groups: a variant with fewer partial rows in flight per thread and many
-// resident workgroups, for launches that publish many groups (prefill).
-hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, bool many_groups, hipStream_t stream);
+// batch: partial rows in flight per thread (8, 16 or 32).  32 covers the
+// split counts of decode and verification in one round trip at one resident
+// workgroup per CU; 16 and 8 keep the registers low enough for several
+// resident workgroups, for grids wider than the CUs and for launches with
+// many groups (prefill).
+hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, int batch, hipStream_t stream);
 int merge_rows_per_unit(int head_dim);
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int rw, int grid,

@@ -12,10 +12,7 @@ namespace pa {
 
 namespace {
 
-// BATCH: partial rows in flight per thread.  32 covers the split counts of
-// decode and verification in one round trip (one workgroup per CU at that
-// register count); 8 keeps the registers low enough for many resident
-// workgroups when there are many groups to merge (prefill).
+// BATCH: partial rows in flight per thread (see launch_merge).
 template <int D, int BATCH>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
     constexpr int kMergeBatch = BATCH;
@@ -120,12 +117,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
 // Fixed slots (static splits): workgroup u merges the unit whose descriptor is
 // in m.sdesc[u], if one was written this forward, and clears the slot once
 // every thread has its copy, so a group merged directly in a later forward
-// finds it empty.  No count and no arrival counter.
+// finds it empty.  No count and no arrival counter.  The partials and LSEs of
+// every split the group can own are requested together with the descriptor
+// (one round trip); splits outside the descriptor's range are skipped.
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_slots_kernel(MergeArgs m) {
     constexpr int EPR = D / 4;                    // float4 columns per row
     constexpr int RPU = kMergeThreads / EPR;      // rows per unit
     constexpr int NW = kMergeThreads / kWave;
+    constexpr int RPW = (RPU + NW - 1) / NW;
     constexpr int B = 32;                         // partial rows in flight per thread
     static_assert(RPU == merge_rpu(D), "unit size shared with the publishers");
     __shared__ float w_sh[RPU][kMaxSplits];
@@ -133,40 +133,44 @@ __global__ __launch_bounds__(kMergeThreads) void merge_slots_kernel(MergeArgs m)
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = tid / kWave;
-    const MergeDesc d = m.sdesc[blockIdx.x];
-    __syncthreads();
-    if (d.n_splits == 0) return;
-    if (tid == 0) m.sdesc[blockIdx.x].n_splits = 0;
+    const int q = (int)(blockIdx.x / m.sdesc_upg);            // group b * Hkv + g
     const int r0 = (int)(blockIdx.x % m.sdesc_upg) * RPU;
     const int rl = tid / EPR;
     const int col = (tid - rl * EPR) * 4;
-    MergeTarget tgt{m.out, m.lse, m.num_q_heads, m.group, 1.0f};
-    const int nr = min(RPU, d.rows - r0);
-    const int S = d.n_splits;
-    const bool act = rl < nr;
-    const int64_t sstride = (int64_t)d.rstride * D;
-    const float* src = m.ws_o + ((int64_t)d.first_item * d.rstride + r0 + rl) * D + col;
+    const int S_all = m.static_splits;
+    const int rs = m.static_rstride;
+    const int64_t item0 = (int64_t)q * S_all;
+    const int64_t sstride = (int64_t)rs * D;
+    // requests that do not wait for the descriptor (rows past the item's row
+    // stride are not requested: they belong to the next item)
+    const bool in_rows = r0 + rl < rs;
+    const float* src = m.ws_o + (item0 * rs + r0 + rl) * D + col;
     float4 o[B];
-    auto issue = [&](int s0) {
 #pragma unroll
-        for (int k = 0; k < B; ++k)
-            o[k] = (act && s0 + k < S) ? *reinterpret_cast<const float4*>(src + (int64_t)(s0 + k) * sstride)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-    };
-    issue(0);
-    constexpr int RPW = (RPU + NW - 1) / NW;
+    for (int k = 0; k < B; ++k)
+        o[k] = (in_rows && k < S_all) ? *reinterpret_cast<const float4*>(src + (int64_t)k * sstride)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
     float ls[RPW];
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
         const int r = wid + k * NW;
-        ls[k] = (r < nr && lane < S) ? m.ws_lse[((int64_t)d.first_item + lane) * d.rstride + r0 + r] : kNegInf;
+        ls[k] = (r0 + r < rs && lane < S_all) ? m.ws_lse[(item0 + lane) * rs + r0 + r] : kNegInf;
     }
+    const MergeDesc d = m.sdesc[blockIdx.x];
+    __syncthreads();
+    if (d.n_splits == 0) return;
+    if (tid == 0) m.sdesc[blockIdx.x].n_splits = 0;
+    // the group's splits are items d.first_item .. d.first_item + n_splits - 1
+    const int s0 = (int)(d.first_item - item0), S = d.n_splits;
+    const int nr = min(RPU, d.rows - r0);
+    const bool act = rl < nr;
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
         const int r = wid + k * NW;
         if (r < nr) {
-            const float M = wave_max(ls[k]);
-            const float w = (ls[k] == kNegInf) ? 0.f : fast_exp2(ls[k] - M);
+            const float l = (lane >= s0 && lane < s0 + S) ? ls[k] : kNegInf;
+            const float M = wave_max(l);
+            const float w = (l == kNegInf) ? 0.f : fast_exp2(l - M);
             const float L = wave_sum(w);
             w_sh[r][lane] = (L > 0.f) ? w / L : 0.f;
             if (lane == 0) lse_sh[r] = (L > 0.f) ? M + fast_log2(L) : kNegInf;
@@ -174,18 +178,28 @@ __global__ __launch_bounds__(kMergeThreads) void merge_slots_kernel(MergeArgs m)
     }
     __syncthreads();
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s0 = 0; s0 < S; s0 += B) {
-        if (s0 > 0) issue(s0);
+    for (int b0 = 0; b0 < s0 + S; b0 += B) {
+        if (b0 > 0) {
+#pragma unroll
+            for (int k = 0; k < B; ++k)
+                o[k] = (in_rows && b0 + k < S_all) ? *reinterpret_cast<const float4*>(src + (int64_t)(b0 + k) * sstride)
+                                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
         for (int k = 0; k < B; ++k) {
-            const float w = (s0 + k < S) ? w_sh[rl][s0 + k] : 0.f;
-            acc.x = fmaf(w, o[k].x, acc.x);
-            acc.y = fmaf(w, o[k].y, acc.y);
-            acc.z = fmaf(w, o[k].z, acc.z);
-            acc.w = fmaf(w, o[k].w, acc.w);
+            const int s = b0 + k;
+            // outside the group's range the partial may be stale: skipped, not weighted by 0
+            if (s >= s0 && s < s0 + S) {
+                const float w = w_sh[rl][s];
+                acc.x = fmaf(w, o[k].x, acc.x);
+                acc.y = fmaf(w, o[k].y, acc.y);
+                acc.z = fmaf(w, o[k].z, acc.z);
+                acc.w = fmaf(w, o[k].w, acc.w);
+            }
         }
     }
     if (act) {
+        MergeTarget tgt{m.out, m.lse, m.num_q_heads, m.group, 1.0f};
         const int64_t orow = out_row(tgt, d.q_off, d.g, d.row0 + r0 + rl);
         const float sc = d.out_scale;
         *reinterpret_cast<float4*>(m.out + orow * D + col) = make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
@@ -200,19 +214,20 @@ __global__ __launch_bounds__(kMergeThreads) void merge_slots_kernel(MergeArgs m)
 
 int merge_rows_per_unit(int head_dim) { return merge_rpu(head_dim); }
 
-hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, bool many_groups, hipStream_t stream) {
+hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, int batch, hipStream_t stream) {
     if (m.static_units > 0) {
         if (head_dim == 64) hipLaunchKernelGGL((merge_slots_kernel<64>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
         else hipLaunchKernelGGL((merge_slots_kernel<128>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
         return hipGetLastError();
     }
-    if (head_dim == 64) {
-        if (many_groups) hipLaunchKernelGGL((merge_kernel<64, 8>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
-        else hipLaunchKernelGGL((merge_kernel<64, 32>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
-    } else {
-        if (many_groups) hipLaunchKernelGGL((merge_kernel<128, 8>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
-        else hipLaunchKernelGGL((merge_kernel<128, 32>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
-    }
+    auto go = [&](auto d_c) {
+        constexpr int D = decltype(d_c)::value;
+        if (batch <= 8) hipLaunchKernelGGL((merge_kernel<D, 8>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+        else if (batch <= 16) hipLaunchKernelGGL((merge_kernel<D, 16>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+        else hipLaunchKernelGGL((merge_kernel<D, 32>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+    };
+    if (head_dim == 64) go(std::integral_constant<int, 64>{});
+    else go(std::integral_constant<int, 128>{});
     return hipGetLastError();
 }
 

@@ -377,6 +377,7 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         if (a.static_pps > 0 && a.static_splits == 1) need_merge_valu = false;
     }
     const bool static_merge = a.sdesc != nullptr;
+    const int static_splits = a.static_splits;
     if (run_mfma) {
         a.static_pps = 0;
         a.static_splits = 0;
@@ -395,9 +396,10 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     if (static_merge && need_merge_valu) {
         // one workgroup per fixed slot; empty slots leave at once
         const int64_t su = (int64_t)num_seqs * c.num_kv_heads * h->sdesc_upg;
-        pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, out, lse, c.num_q_heads, G, h->merge_rows,
-                        h->desc_cap, h->sdesc, (int)su, h->sdesc_upg};
-        hipError_t e = pa::launch_merge(m, c.head_dim, (int)su, false, st);
+        pa::MergeArgs m{h->ws_o,   h->ws_lse,   h->mdesc,     h->mcount,    out,         lse,
+                        c.num_q_heads, G,       h->merge_rows, h->desc_cap, h->sdesc, (int)su,
+                        h->sdesc_upg,  static_splits, h->r_max_valu};
+        hipError_t e = pa::launch_merge(m, c.head_dim, (int)su, 32, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
     } else if (need_merge_valu || run_mfma) {
         // Merges whatever split groups the launches above published.  Grid:
@@ -411,13 +413,15 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
             groups += (int64_t)c.num_kv_heads * ((num_tokens * G + bm - 1) / bm + num_seqs);
         }
         // Many units (prefill): the low-register variant, up to eight
-        // workgroups per CU; otherwise at most two per CU.
+        // workgroups per CU; otherwise at most two per CU, with fewer rows in
+        // flight per thread once the grid is wider than the CUs.
         const int64_t units = groups * upg;
         const bool many = units > 4 * (int64_t)h->cu_count;
         const int mgrid = (int)std::max<int64_t>(1, std::min<int64_t>((many ? 8 : 2) * (int64_t)h->cu_count, units));
+        const int batch = many ? 8 : (mgrid > h->cu_count ? 16 : 32);
         pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, out, lse, c.num_q_heads, G, h->merge_rows,
-                        h->desc_cap, nullptr, 0, 1};
-        hipError_t e = pa::launch_merge(m, c.head_dim, mgrid, many, st);
+                        h->desc_cap, nullptr, 0, 1, 0, 0};
+        hipError_t e = pa::launch_merge(m, c.head_dim, mgrid, batch, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
     }
     return PA_OK;
