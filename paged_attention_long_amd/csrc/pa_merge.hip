@@ -59,13 +59,15 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
         const int S = d.n_splits;
         const bool act = rl < nr;
         const int64_t sstride = (int64_t)d.rstride * D;
-        const float* src = m.ws_o + ((int64_t)d.first_item * d.rstride + r0 + rl) * D + col;
+        // Branch-free requests: a thread past the unit's rows reads row r0 and
+        // a split past the group's last reads the last one (both written by
+        // this group in this forward, so finite); their weights are 0.
+        const float* src = m.ws_o + ((int64_t)d.first_item * d.rstride + r0 + (act ? rl : 0)) * D + col;
         float4 o[kMergeBatch];
         auto issue = [&](int s0) {
 #pragma unroll
             for (int k = 0; k < kMergeBatch; ++k)
-                o[k] = (act && s0 + k < S) ? *reinterpret_cast<const float4*>(src + (int64_t)(s0 + k) * sstride)
-                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+                o[k] = *reinterpret_cast<const float4*>(src + (int64_t)min(s0 + k, S - 1) * sstride);
         };
         issue(0);
         // each wave weighs rows wid, wid + NW, ...: their LSE loads first, together
@@ -89,11 +91,12 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
         }
         __syncthreads();
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        static_assert(kMaxSplits % kMergeBatch == 0, "weights of a whole batch are in w_sh");
         for (int s0 = 0; s0 < S; s0 += kMergeBatch) {
             if (s0 > 0) issue(s0);
 #pragma unroll
             for (int k = 0; k < kMergeBatch; ++k) {
-                const float w = (s0 + k < S) ? w_sh[rl][s0 + k] : 0.f;
+                const float w = w_sh[rl][s0 + k];   // 0 past the group's splits
                 acc.x = fmaf(w, o[k].x, acc.x);
                 acc.y = fmaf(w, o[k].y, acc.y);
                 acc.z = fmaf(w, o[k].z, acc.z);

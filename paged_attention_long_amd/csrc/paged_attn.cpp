@@ -412,12 +412,14 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
             const int bm = pa::mfma_rows_per_item(h->mfma_wr);
             groups += (int64_t)c.num_kv_heads * ((num_tokens * G + bm - 1) / bm + num_seqs);
         }
-        // Many units (prefill): the low-register variant, up to eight
-        // workgroups per CU; otherwise at most two per CU, with fewer rows in
-        // flight per thread once the grid is wider than the CUs.
+        // Many units (prefill): the low-register variant, four workgroups per
+        // CU (every workgroup also takes one turn on the shared arrival
+        // counter, so a wider grid costs more than it gains); otherwise at
+        // most two per CU, with fewer rows in flight per thread once the grid
+        // is wider than the CUs.
         const int64_t units = groups * upg;
         const bool many = units > 4 * (int64_t)h->cu_count;
-        const int mgrid = (int)std::max<int64_t>(1, std::min<int64_t>((many ? 8 : 2) * (int64_t)h->cu_count, units));
+        const int mgrid = (int)std::max<int64_t>(1, std::min<int64_t>((many ? 4 : 2) * (int64_t)h->cu_count, units));
         const int batch = many ? 8 : (mgrid > h->cu_count ? 16 : 32);
         pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, out, lse, c.num_q_heads, G, h->merge_rows,
                         h->desc_cap, nullptr, 0, 1, 0, 0};
