@@ -313,8 +313,7 @@ struct Cfg {
     // split P: their own error is far larger than P's f16 rounding)
     static constexpr bool PSPLIT = (WR == 1) && !FP8;
     static constexpr int TILE = BN * kRowBytes;            // bytes of one K (or V) tile in LDS
-    static constexpr int NBUF = FP8 ? 1 : 2;               // LDS buffers per wave group
-    static constexpr int GROUP_LDS = NBUF * 2 * TILE;
+    static constexpr int GROUP_LDS = 2 * TILE;             // a wave group's K and V tile in LDS
     static constexpr int DMA_PER_WAVE = BN * kRowBytes / 1024 / WR;   // 1 KB async loads per wave per tile
     // fp8 register staging: 8-element chunks per thread per tile
     static constexpr int FCH = BN * (D / 8) / NT;
@@ -333,8 +332,7 @@ struct Cfg {
     static constexpr bool PIPE = (WR == 8) && !FP8;
     static constexpr int NKB = 4, NVB = 4, LEAD = 3;
     static constexpr int PID_CAP = PIPE ? 4096 : (WR == 1 ? 1024 : 1);
-    static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : WK * GROUP_LDS / NBUF;
-    static constexpr int TILES2_LDS = (PIPE || NBUF == 1) ? 16 : WK * GROUP_LDS / NBUF;
+    static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : WK * GROUP_LDS;
 };
 
 template <int KVT>
@@ -379,11 +377,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
     constexpr int BM = C::BM, BN = C::BN, PPT = C::PPT;
 
     __shared__ Plan pl;
-    // Two distinct LDS objects for the two buffers: the compiler tracks
-    // asynchronous LDS loads per object, so reading one buffer does not wait
-    // for the loads still in flight into the other.
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[C::TILES_LDS];
-    __shared__ __attribute__((aligned(1024))) uint8_t tiles2[C::TILES2_LDS];
     __shared__ __attribute__((aligned(16))) int ipid[C::PID_CAP];
     __shared__ __attribute__((aligned(1024))) uint8_t stage[C::STAGE_LDS];
     __shared__ float red_m[4][32];
@@ -420,9 +414,9 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             }
     }
 
-    // buffer b of wave group gi: K tile then V tile
-    auto kbuf = [&](int buf) { return (buf == 0 ? tiles : tiles2) + gi * 2 * C::TILE; };
-    auto vbuf = [&](int buf) { return (buf == 0 ? tiles : tiles2) + gi * 2 * C::TILE + C::TILE; };
+    // the LDS tile of wave group gi (outside the pipelined paths): K then V
+    auto kbuf = [&](int) { return tiles + gi * 2 * C::TILE; };
+    auto vbuf = [&](int) { return tiles + gi * 2 * C::TILE + C::TILE; };
 
     // ---------------------------------------------------------------- plan
     // A sequence is in this launch if in_launch() says so.  Its
@@ -716,10 +710,11 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
         auto row_src = [&](const uint8_t* base, const int (&pid)[PPT], int key) -> const uint8_t* {
             return base + (int64_t)pid[key / kPage] * page_bytes + head_off + (int64_t)(key % kPage) * tok_bytes;
         };
-        // 16-bit caches: asynchronous loads straight into LDS.  Async load i of a
-        // group covers tile rows 4i .. 4i+3; lane l fills row 4i + l/16, physical
-        // chunk l%16, which holds logical chunk (l%16) ^ (row & 15).
-        // Per-lane byte offset inside its page for async load ii (constant per item).
+        // 16-bit caches: 1 KB loads of tile rows (asynchronous into LDS on the
+        // pipelined path, through registers at 32-row items).  Load i of a
+        // group covers tile rows 4i .. 4i+3; lane l fills row 4i + l/16,
+        // physical chunk l%16, which holds logical chunk (l%16) ^ (row & 15).
+        // Per-lane byte offset inside its page for load ii (constant per item).
         uint32_t dma_off[C::DMA_PER_WAVE];
 #pragma unroll
         for (int ii = 0; ii < C::DMA_PER_WAVE; ++ii) {
@@ -743,17 +738,6 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             }
 #pragma unroll
             for (int p = 0; p < PPT; ++p) pid[p] = tile_pid(t, p);
-        };
-        auto dma_tile = [&](int t, int buf) {
-            int pid[PPT];
-            tile_pids(t, pid);
-#pragma unroll
-            for (int ii = 0; ii < C::DMA_PER_WAVE; ++ii) {
-                const int i = ii * WR + wig;
-                const int64_t pb = (int64_t)pid[(4 * i) / kPage] * page_bytes;   // page of rows 4i .. 4i+3
-                async_load16(kbase + pb + dma_off[ii], (lds_void_t*)(kbuf(buf) + i * 1024));
-                async_load16(vbase + pb + dma_off[ii], (lds_void_t*)(vbuf(buf) + i * 1024));
-            }
         };
         // fp8 caches: registers, widened, then written in the same layout.
         typename Raw<KVT>::T fk[C::FCH], fv[C::FCH];
@@ -1124,27 +1108,42 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 __syncthreads();
             }
         } else if constexpr (!C::FP8) {
-            // double-buffered asynchronous loads; buffers alternate by iteration parity
-            if (n_iter > 0) dma_tile(min(my_first, ig.t_end - 1), 0);
-            if (n_iter > 1) dma_tile(min(my_first + C::WK, ig.t_end - 1), 1);
-            for (int iter = 0; iter < n_iter; iter += 2) {
+            // Register-staged tiles (32-row items, 16-bit caches): the next tile's K and V rows are in flight
+            // in registers while this one is computed from the wave's LDS
+            // buffer; then they are written there and the tile after is
+            // requested.  Every load is issued, past the end too (clamped).
+            static_assert(WR == 1, "one wave per tile stream");
+            u32x4_t rk[C::DMA_PER_WAVE], rv[C::DMA_PER_WAVE];
+            auto reg_load = [&](int t) {
+                int pid[PPT];
+                tile_pids(t, pid);
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int itn = iter + half;
-                    if (itn < n_iter) {
-                        const int t = my_first + itn * C::WK;
-                        const bool have = t < ig.t_end;
-                        // this buffer's loads are the older ones in flight
-                        if (itn + 1 < n_iter) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * C::DMA_PER_WAVE));
-                        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-                        if constexpr (WR > 1) __syncthreads();
-                        if (have) {
-                            if (zero_dead_v(t, half)) group_sync();
-                            compute_tile(t, kbuf(half), vbuf(half));
-                        }
-                        if constexpr (WR > 1) __syncthreads();    // everyone is done with this buffer
-                        if (itn + 2 < n_iter) dma_tile(min(t + 2 * C::WK, ig.t_end - 1), half);
+                for (int ii = 0; ii < C::DMA_PER_WAVE; ++ii) {
+                    const int64_t pb = (int64_t)pid[(4 * ii) / kPage] * page_bytes;
+                    rk[ii] = load_b128(kbase + pb + dma_off[ii]);
+                    rv[ii] = load_b128(vbase + pb + dma_off[ii]);
+                }
+            };
+            const uint32_t kb32 = (uint32_t)(uintptr_t)(lds_void_t*)kbuf(0);
+            auto reg_store = [&]() {
+#pragma unroll
+                for (int ii = 0; ii < C::DMA_PER_WAVE; ++ii)
+                {
+                    lds_store_b128<0>(kb32 + ii * 1024 + lane * 16, rk[ii]);
+                    lds_store_b128<C::TILE>(kb32 + ii * 1024 + lane * 16, rv[ii]);
+                }
+            };
+            if (n_iter > 0) {
+                reg_load(min(my_first, ig.t_end - 1));
+                for (int itn = 0; itn < n_iter; ++itn) {
+                    const int t = my_first + itn * C::WK;
+                    reg_store();
+                    reg_load(min(t + C::WK, ig.t_end - 1));
+                    if (t < ig.t_end) {
+                        if (zero_dead_v(t, 0)) group_sync();
+                        compute_tile(t, kbuf(0), vbuf(0));
                     }
+                    __builtin_amdgcn_wave_barrier();
                 }
             }
         } else if constexpr (C::FSTAGE) {
