@@ -161,37 +161,60 @@ PA_DEVINLINE void lds_read_b128_x8(const uint32_t (&addr)[8], u32x4_t (&r)[8]) {
         : "memory");
 }
 
-// One staged raw fp8 tile of slot SLOT (8 KB apart), completed inside the
-// block: eight 64-bit K reads at ka[s] (the K operand layout) and eight 64-bit
-// V chunks, two per read, at va + 4096 + 512c (c = 0 .. 7; v[j] holds chunks 2j
-// and 2j+1).  The reads are invisible to the compiler's wait insertion, so the
-// caller orders them after the asynchronous loads that fill the slot.
-#define PA_RAW_TILE_READS(K0, V0, V1, V2, V3, V4, V5, V6, V7)                                        \
-    asm volatile("ds_read_b64 %0, %12 offset:" #K0 "\n\t"                                          \
-                 "ds_read_b64 %1, %13 offset:" #K0 "\n\t"                                          \
-                 "ds_read_b64 %2, %14 offset:" #K0 "\n\t"                                          \
-                 "ds_read_b64 %3, %15 offset:" #K0 "\n\t"                                          \
-                 "ds_read_b64 %4, %16 offset:" #K0 "\n\t"                                          \
-                 "ds_read_b64 %5, %17 offset:" #K0 "\n\t"                                          \
-                 "ds_read_b64 %6, %18 offset:" #K0 "\n\t"                                          \
-                 "ds_read_b64 %7, %19 offset:" #K0 "\n\t"                                          \
-                 "ds_read2st64_b64 %8, %20 offset0:" #V0 " offset1:" #V1 "\n\t"                    \
-                 "ds_read2st64_b64 %9, %20 offset0:" #V2 " offset1:" #V3 "\n\t"                    \
-                 "ds_read2st64_b64 %10, %20 offset0:" #V4 " offset1:" #V5 "\n\t"                   \
-                 "ds_read2st64_b64 %11, %20 offset0:" #V6 " offset1:" #V7 "\n\t"                   \
+// Raw fp8 K operand fragments of staging slot SLOT (slots 8 KB apart): eight
+// 64-bit reads at ka[s], completed inside the block.  These reads (and the V
+// reads below) are invisible to the compiler's wait insertion, so the caller
+// orders them after the asynchronous loads that fill the slot.
+#define PA_RAW_K_READS(OFF)                                                                          \
+    asm volatile("ds_read_b64 %0, %8 offset:" #OFF "\n\t"                                           \
+                 "ds_read_b64 %1, %9 offset:" #OFF "\n\t"                                           \
+                 "ds_read_b64 %2, %10 offset:" #OFF "\n\t"                                          \
+                 "ds_read_b64 %3, %11 offset:" #OFF "\n\t"                                          \
+                 "ds_read_b64 %4, %12 offset:" #OFF "\n\t"                                          \
+                 "ds_read_b64 %5, %13 offset:" #OFF "\n\t"                                          \
+                 "ds_read_b64 %6, %14 offset:" #OFF "\n\t"                                          \
+                 "ds_read_b64 %7, %15 offset:" #OFF "\n\t"                                          \
                  "s_waitcnt lgkmcnt(0)"                                                              \
                  : "=&v"(k[0]), "=&v"(k[1]), "=&v"(k[2]), "=&v"(k[3]), "=&v"(k[4]), "=&v"(k[5]),     \
-                   "=&v"(k[6]), "=&v"(k[7]), "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])      \
+                   "=&v"(k[6]), "=&v"(k[7])                                                          \
                  : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "v"(ka[4]), "v"(ka[5]), "v"(ka[6]), \
-                   "v"(ka[7]), "v"(va)                                                               \
+                   "v"(ka[7])                                                                        \
                  : "memory")
 template <int SLOT>
-PA_DEVINLINE void lds_read_raw_tile(const uint32_t (&ka)[8], uint32_t va, u32x2_t (&k)[8], u32x4_t (&v)[4]) {
+PA_DEVINLINE void lds_read_raw_k(const uint32_t (&ka)[8], u32x2_t (&k)[8]) {
     static_assert(SLOT == 0 || SLOT == 1, "two staging slots");
-    if constexpr (SLOT == 0) PA_RAW_TILE_READS(0, 8, 9, 10, 11, 12, 13, 14, 15);
-    else PA_RAW_TILE_READS(8192, 24, 25, 26, 27, 28, 29, 30, 31);
+    if constexpr (SLOT == 0) PA_RAW_K_READS(0);
+    else PA_RAW_K_READS(8192);
 }
-#undef PA_RAW_TILE_READS
+#undef PA_RAW_K_READS
+
+// Raw fp8 V^T operand fragments of slot SLOT by 8-bit transposing reads
+// (ds_read_b64_tr_b8: within 16 lanes, the 8-byte pieces of lanes 2r, 2r+1
+// form row r of an 8 x 16-byte block and lane j receives byte j of every
+// row).  v[ts * 4 + db] for 16-key step ts and 32-column block db: va[db]
+// addresses the block's rows of step 0, step 1 is 2 KB further; V is 4 KB
+// into the slot.  Completed inside the block.
+#define PA_RAW_V_READS(O0, O1)                                                                       \
+    asm volatile("ds_read_b64_tr_b8 %0, %8 offset:" #O0 "\n\t"                                      \
+                 "ds_read_b64_tr_b8 %1, %9 offset:" #O0 "\n\t"                                      \
+                 "ds_read_b64_tr_b8 %2, %10 offset:" #O0 "\n\t"                                     \
+                 "ds_read_b64_tr_b8 %3, %11 offset:" #O0 "\n\t"                                     \
+                 "ds_read_b64_tr_b8 %4, %8 offset:" #O1 "\n\t"                                      \
+                 "ds_read_b64_tr_b8 %5, %9 offset:" #O1 "\n\t"                                      \
+                 "ds_read_b64_tr_b8 %6, %10 offset:" #O1 "\n\t"                                     \
+                 "ds_read_b64_tr_b8 %7, %11 offset:" #O1 "\n\t"                                     \
+                 "s_waitcnt lgkmcnt(0)"                                                              \
+                 : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),     \
+                   "=&v"(v[6]), "=&v"(v[7])                                                          \
+                 : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3])                                    \
+                 : "memory")
+template <int SLOT>
+PA_DEVINLINE void lds_read_raw_vt(const uint32_t (&va)[4], u32x2_t (&v)[8]) {
+    static_assert(SLOT == 0 || SLOT == 1, "two staging slots");
+    if constexpr (SLOT == 0) PA_RAW_V_READS(4096, 6144);
+    else PA_RAW_V_READS(12288, 14336);
+}
+#undef PA_RAW_V_READS
 
 // One 128-bit LDS store at addr + OFF.  Inline asm for the same reason as the
 // reads: the compiler's alias tracking can lose the LDS object of such stores
@@ -318,9 +341,9 @@ struct Cfg {
     // fp8 register staging: 8-element chunks per thread per tile
     static constexpr int FCH = BN * (D / 8) / NT;
     // fp8 at WR = 1: raw tiles reach LDS by asynchronous loads into two
-    // staging slots per wave (K then V, 8 KB a slot); K is widened in
-    // registers at its use, V into one of two 16-bit V buffers per wave.
-    // RAW_DMA 1 KB loads per wave per tile (K and V).
+    // staging slots per wave (K then V, 8 KB a slot); both operands are read
+    // raw (V by 8-bit transposing reads) and widened in registers at their
+    // matrix ops.  RAW_DMA 1 KB loads per wave per tile (K and V).
     static constexpr bool FSTAGE = FP8 && (WR == 1);
     static constexpr int RAW_TILE = BN * D;                // bytes of one raw fp8 K (or V) tile
     static constexpr int RAW_DMA = 2 * RAW_TILE / 1024;
@@ -332,7 +355,7 @@ struct Cfg {
     static constexpr bool PIPE = (WR == 8) && !FP8;
     static constexpr int NKB = 4, NVB = 4, LEAD = 3;
     static constexpr int PID_CAP = PIPE ? 4096 : (WR == 1 ? 1024 : 1);
-    static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : WK * GROUP_LDS;
+    static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : (FSTAGE ? 16 : WK * GROUP_LDS);
 };
 
 template <int KVT>
@@ -767,19 +790,17 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             }
         };
         // fp8 staging (FSTAGE): async load i of a raw K or V tile covers rows
-        // 8i .. 8i+7 (128 B each), lane l row 8i + l/8.  V rows sit as they
-        // are (lane l brings 16-byte unit l%8); K rows are stored with unit u
-        // at position u ^ (row & 7), so the K operand reads (one unit per row
-        // and lane) spread over the banks: lane l brings unit
+        // 8i .. 8i+7 (128 B each), lane l row 8i + l/8.  Rows are stored with
+        // 16-byte unit u at position u ^ (row & 7), so the operand reads (one
+        // unit of many rows at once) spread over the banks: lane l brings unit
         // (l%8) ^ ((l/8) & 7).  A wave's two slots: [K 4 KB | V 4 KB] each.
-        uint32_t raw_off_k[C::FSTAGE ? 4 : 1], raw_off_v[C::FSTAGE ? 4 : 1];
+        uint32_t raw_off[C::FSTAGE ? 4 : 1];
         if constexpr (C::FSTAGE) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int row = 8 * i + (lane >> 3);
-                const int64_t row_off = head_off + (int64_t)(row % kPage) * tok_bytes;
-                raw_off_k[i] = (uint32_t)(row_off + (((lane & 7) ^ ((lane >> 3) & 7)) << 4));
-                raw_off_v[i] = (uint32_t)(row_off + (lane & 7) * 16);
+                raw_off[i] = (uint32_t)(head_off + (int64_t)(row % kPage) * tok_bytes +
+                                        (((lane & 7) ^ ((lane >> 3) & 7)) << 4));
             }
         }
         auto raw_dma = [&](auto slot_c, int t) {
@@ -790,8 +811,8 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int64_t pb = (int64_t)pid[(8 * i) / kPage] * page_bytes;
-                    async_load16(kbase + pb + raw_off_k[i], (lds_void_t*)(st + i * 1024));
-                    async_load16(vbase + pb + raw_off_v[i], (lds_void_t*)(st + C::RAW_TILE + i * 1024));
+                    async_load16(kbase + pb + raw_off[i], (lds_void_t*)(st + i * 1024));
+                    async_load16(vbase + pb + raw_off[i], (lds_void_t*)(st + C::RAW_TILE + i * 1024));
                 }
             }
         };
@@ -1147,92 +1168,88 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 }
             }
         } else if constexpr (C::FSTAGE) {
-            // Software pipeline over this wave's tiles (iteration k: tile
-            // my_first + k*WK).  Raw tile k sits in staging slot k % 2 (loaded
-            // two iterations ahead), its widened V in V buffer k % 2.  Step k:
-            // P.V of tile k-1, then tile k+1 is read out of its slot (which is
-            // reloaded at once), its V widened into V buffer (k+1) % 2 and its
-            // K widened in registers for its scores on the matrix cores, while
-            // the VALU turns tile k's scores into P.  Every load is issued,
-            // past the end too (clamped to the last tile: in bounds, unused).
+            // Tile k of this wave (tile my_first + k*WK) sits in staging slot
+            // k % 2, loaded two tiles ahead; its K and V operand fragments are
+            // read raw and widened in registers right at their matrix ops, so
+            // the slot is free once the tile is done.  The small LDS footprint
+            // leaves room for two workgroups per CU, whose waves hide each
+            // other's latencies.  Every load is issued, past the end too
+            // (clamped to the last tile: in bounds, unused); an odd count ends
+            // with one uncomputed step.
             if (n_iter > 0) {
                 using I0 = std::integral_constant<int, 0>;
                 using I1 = std::integral_constant<int, 1>;
-                static_assert(C::NB == 1 && C::NT == 64 && C::FCH == 8 && C::RAW_TILE == 4096 && C::TILE == 8192,
-                              "lds_read_raw_tile offsets");
+                static_assert(C::NB == 1 && C::TS == 2 && C::DB == 4 && C::RAW_TILE == 4096, "raw read offsets");
                 uint8_t* st = stage + gi * 4 * C::RAW_TILE;
-                uint8_t* vw = tiles + gi * 2 * C::TILE;   // V buffer J at vw + J * TILE
                 const uint32_t st32 = (uint32_t)(uintptr_t)(lds_void_t*)st;
-                const uint32_t vw32 = (uint32_t)(uintptr_t)(lds_void_t*)vw;
-                uint32_t ka[8], vt[8];
+                // K fragment s of lane (l32, h32): row l32, unit s, half h32
+                uint32_t ka[8];
 #pragma unroll
                 for (int s8 = 0; s8 < 8; ++s8) ka[s8] = st32 + l32 * 128 + ((s8 ^ (l32 & 7)) << 4) + h32 * 8;
+                // V^T fragment (ts, db): in each 16 lanes, lanes 2r, 2r+1 point
+                // at the two halves of unit 2db + (lane/16)%2 of key row kr(r) of
+                // step 0, where kr(r) = 4 (lane/32) + r for r < 4 and
+                // 4 (lane/32) + r + 4 above (the key order of P's packed pairs)
+                uint32_t va[4];
+                {
+                    const int s16 = lane & 15, r = s16 >> 1, hh = s16 & 1, g16 = lane >> 4;
+                    const int krow = 4 * (g16 >> 1) + (r < 4 ? r : r + 4);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) vt[k] = vw32 + v_lane_off[k];
-                const uint32_t va = st32 + gtid * 8;
+                    for (int db = 0; db < 4; ++db) {
+                        const int u = 2 * db + (g16 & 1);
+                        va[db] = st32 + krow * 128 + ((u ^ (krow & 7)) << 4) + hh * 8;
+                    }
+                }
                 auto tile_of = [&](int k) { return my_first + k * C::WK; };
                 raw_dma(I0{}, min(tile_of(0), ig.t_end - 1));
                 raw_dma(I1{}, min(tile_of(1), ig.t_end - 1));
-                // tile k from slot J: read out, slot reloaded with tile k+2, V
-                // widened into V buffer J, scores into S
-                auto load_tile = [&](auto j_c, int k, f32x16_t (&S)[C::NB]) {
-                    constexpr int J = decltype(j_c)::value;
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::RAW_DMA));   // slot J's tile is the older in flight
-                    u32x2_t kr[8];
-                    u32x4_t vr[4];
-                    lds_read_raw_tile<J>(ka, va, kr, vr);
-                    raw_dma(j_c, min(tile_of(k + 2), ig.t_end - 1));
-#pragma unroll
-                    for (int c = 0; c < C::FCH; ++c) {
-                        const int key = gtid / 16 + 4 * c, e = gtid % 16;
-                        const u32x4_t& w = vr[c / 2];
-                        const u32x2_t raw = (c % 2) ? u32x2_t{w[2], w[3]} : u32x2_t{w[0], w[1]};
-                        lds_store_b128<J * C::TILE>(vw32 + (uint32_t)swz(key, e), widen_fp8x8<C::PVT>(raw));
-                    }
-                    const int t = tile_of(k);
-                    if (t < ig.t_end) zero_dead_v_in(t, vw + J * C::TILE);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) S[0][i] = 0.f;
-#pragma unroll
-                    for (int s8 = 0; s8 < C::KS; ++s8) S[0] = mma32<QT>(widen_fp8x8<QT>(kr[s8]), qreg[s8], S[0]);
-                };
                 u32x4_t pb[C::TS], pl[C::TS];
-                // Step k < n_iter - 1 (tiles k and k+1 are the item's: only a
-                // wave's last tile can lie past the end): no branches around
-                // the pieces, so tile k+1's matrix ops and tile k's exponentials
-                // share one block and interleave.
-                auto step = [&](auto j_c, int k, f32x16_t (&cur)[C::NB], f32x16_t (&nxt)[C::NB]) {
+                auto fstep = [&](auto j_c, int k) {
                     constexpr int J = decltype(j_c)::value;
-                    mask_scores(tile_of(k), cur);
-                    if (k > 0) pv_frags(vt, std::integral_constant<int, (1 - J) * C::TILE>{}, pb);   // tile k-1
-                    raise_max(cur);
-                    load_tile(std::integral_constant<int, 1 - J>{}, k + 1, nxt);
-                    exp_pack(cur, pb, pl);
-                };
-                // the last step: no tile to load; its tile may lie past the end
-                auto last_step = [&](auto j_c, int k, f32x16_t (&cur)[C::NB]) {
-                    constexpr int J = decltype(j_c)::value;
-                    const bool have = tile_of(k) < ig.t_end;
-                    if (have) mask_scores(tile_of(k), cur);
-                    if (k > 0) pv_frags(vt, std::integral_constant<int, (1 - J) * C::TILE>{}, pb);
-                    if (have) {
-                        raise_max(cur);
-                        exp_pack(cur, pb, pl);
-                        pv_frags(vt, std::integral_constant<int, J * C::TILE>{}, pb);
+                    const int t = tile_of(k);
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::RAW_DMA));   // slot J's tile is the older in flight
+                    if (t < ig.t_end) {
+                        // dead keys' V rows (range edges only) are zeroed in the slot
+                        {
+                            const int k0 = key_pos(t, 0);
+                            const bool edge = (k0 < ig.si.lo) || (k0 + BN > ig.si.seq_len) ||
+                                              (ig.pg_first + (t + 1) * PPT > ig.pg_end);
+                            if (edge) {
+                                uint8_t* vrows = st + J * 2 * C::RAW_TILE + C::RAW_TILE;
+                                for (int e = gtid; e < BN * 8; e += C::NT) {
+                                    const int key = e >> 3, c = e & 7;
+                                    const int j = k0 + key;
+                                    const bool live = (j >= ig.si.lo) && (j < ig.si.seq_len) &&
+                                                      (ig.pg_first + t * PPT + key / kPage < ig.pg_end);
+                                    if (!live) *reinterpret_cast<u32x4_t*>(vrows + key * 128 + c * 16) = u32x4_t{0u, 0u, 0u, 0u};
+                                }
+                                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                            }
+                        }
+                        u32x2_t kr[8];
+                        lds_read_raw_k<J>(ka, kr);
+                        f32x16_t S[C::NB];
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) S[0][i] = 0.f;
+#pragma unroll
+                        for (int s8 = 0; s8 < C::KS; ++s8) S[0] = mma32<QT>(widen_fp8x8<QT>(kr[s8]), qreg[s8], S[0]);
+                        mask_scores(t, S);
+                        raise_max(S);
+                        exp_pack(S, pb, pl);
+                        u32x2_t vr[8];
+                        lds_read_raw_vt<J>(va, vr);
+#pragma unroll
+                        for (int ts = 0; ts < C::TS; ++ts)
+#pragma unroll
+                            for (int db = 0; db < C::DB; ++db)
+                                o_acc[db] = mma32<C::PVT>(widen_fp8x8<C::PVT>(vr[ts * 4 + db]), pb[ts], o_acc[db]);
                     }
+                    raw_dma(j_c, min(tile_of(k + 2), ig.t_end - 1));   // the slot's reads are complete
+                    __builtin_amdgcn_wave_barrier();
                 };
-                f32x16_t S0[C::NB], S1[C::NB];
-                load_tile(I0{}, 0, S0);
-                int k = 0;
-                for (; k + 2 < n_iter; k += 2) {
-                    step(I0{}, k, S0, S1);
-                    step(I1{}, k + 1, S1, S0);
-                }
-                if (k + 1 < n_iter) {
-                    step(I0{}, k, S0, S1);
-                    last_step(I1{}, k + 1, S1);
-                } else {
-                    last_step(I0{}, k, S0);
+                for (int k = 0; k < n_iter; k += 2) {
+                    fstep(I0{}, k);
+                    fstep(I1{}, k + 1);
                 }
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the clamped loads past the end
             }
@@ -1271,9 +1288,11 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             // [WK][32][D]; the 16-byte chunks of row r are XOR-ed with r so that
             // the 32 rows a half-wave writes at once (512 B apart) do not all
             // land in the same bank
-            static_assert(C::WK * 32 * D * 4 <= C::TILES_LDS, "accumulator exchange fits the tile buffers");
+            // (the fp8 staging path exchanges through its staging slots)
+            static_assert(C::WK * 32 * D * 4 <= (C::FSTAGE ? C::STAGE_LDS : C::TILES_LDS),
+                          "accumulator exchange fits the tile buffers");
             static_assert(D / 4 == 32, "32 chunks per row");
-            float* accbuf = reinterpret_cast<float*>(tiles);
+            float* accbuf = reinterpret_cast<float*>(C::FSTAGE ? stage : tiles);
             auto acc_at = [&](int row, int col) { return accbuf + row * D + (((col >> 2) ^ (row & 31)) << 2); };
 #pragma unroll
             for (int db = 0; db < C::DB; ++db)
