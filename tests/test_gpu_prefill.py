@@ -110,6 +110,23 @@ def test_tile_split_invariance(tps):
 
 
 @pytest.mark.parametrize("tps", [1, 2, 3, 5])
+def test_f16_verify_tile_split_invariance(tps):
+    # verification widths on 16-bit caches (register-staged tiles): 1 .. 5
+    # tiles per item give each wave zero, one or two tiles; outliers and a
+    # window edge put dead rows and large scores inside the items
+    inp = generate(_spec(num_q_heads=32, num_kv_heads=8, seq_lens=(2100, 700), q_lens=(8, 4), q_dtype="f16",
+                         kv_dtype="f16", window=600, poison_out_of_window=True, k_outlier_frac=0.01))[0]
+    progress(f"f16 verify tile split tps={tps}")
+    ref_o, ref_l = oracle.attention(inp)
+    c = GpuCase([inp], kv_tiles_per_split=tps, path=pal.PA_PATH_MFMA)
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare(f"f16 tps={tps}", inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("tps", [1, 2, 3, 5])
 def test_fp8_tile_split_invariance(tps):
     # 1 .. 5 tiles per item: a wave gets zero, one or two tiles, so each of the
     # fp8 pipeline's endings (one step, an even and an odd count) is taken
