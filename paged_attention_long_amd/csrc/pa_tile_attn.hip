@@ -10,34 +10,42 @@
 // "Prefill: teach the fork's fast kernel to read the int8 cache": 16 to 64
 // query rows per tile was 1.8x there).
 //
-// Two shapes share the code:
-//   * WR = 4 (prefill): four waves own 32 rows each (BM = 128) and share
-//     64-key tiles in LDS;
-//   * WR = 1 (verification widths, <= 64 rows per KV head): each wave owns the
-//     same 32 rows and streams its own 32-key tiles through its own LDS
-//     buffers, so the tile loop has no workgroup barrier; the four waves'
-//     softmax states are merged at the end.
+// Three shapes share the code:
+//   * WR = 8 (prefill, 16-bit caches): eight waves own 32 rows each
+//     (BM = 256), two per SIMD, and share 32-key tiles in a four-slot LDS
+//     ring filled three tiles ahead by asynchronous global->LDS loads; a
+//     software pipeline runs P.V of tile k-1, then the scores of tile k+1 on
+//     the matrix cores while the VALU turns tile k's scores into P;
+//   * WR = 4 (prefill, fp8 caches): four waves own 32 rows each (BM = 128)
+//     and share 64-key tiles, loaded to registers, widened exactly (K to the
+//     query type, V to fp16) and written to LDS;
+//   * WR = 1 (verification widths and few-row sequences, <= 64 rows per KV
+//     head): each wave owns the same 32 rows and streams its own 32-key
+//     tiles, so the tile loop has no workgroup barrier; the four waves'
+//     softmax states are merged at the end.  16-bit tiles are staged through
+//     registers into the wave's LDS tile; fp8 tiles go by asynchronous loads
+//     into two raw staging slots and both operands are read raw (K by 64-bit
+//     reads, V by 8-bit transposing reads) and widened in registers.
 //
 // Per tile of BN keys (BN/16 pages gathered through the block table):
-//   * 16-bit K and V arrive by asynchronous global->LDS loads (no staging
-//     registers), double-buffered, row-major with the 16-byte chunks of a row
-//     XOR-swizzled by the row index so that both operand reads are free of
-//     bank conflicts; fp8 (E4M3FN) K/V are loaded to registers, widened
-//     exactly (K to the query type, V to fp16) and written in the same layout;
-//   * S^T = K Q^T with v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q^T held
-//     in registers): each lane then holds 16 keys of one query row;
+//   * LDS rows have their 16-byte chunks XOR-swizzled by the row index, so
+//     that the operand reads (one chunk of many rows at once) are free of
+//     bank conflicts;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16 (A = K rows, B = Q^T held in
+//     registers): each lane then holds 16 keys of one query row;
 //   * V^T operands come straight from the row-major V tile through the
-//     gfx950 transposing LDS read (ds_read_b64_tr_b16): four lanes' 8-byte
-//     reads of four key rows come back as four keys of one head-dim column;
+//     gfx950 transposing LDS reads (ds_read_b64_tr_b16, or _tr_b8 on raw
+//     fp8): the 8-byte pieces of several key rows come back as several keys
+//     of one head-dim column;
 //   * online softmax in fp32 against a lazily raised reference max (moved
 //     only when a score passes it by 2^8, so weights stay <= 256 and the
-//     accumulators are rarely rescaled); masked keys are set to -inf by select and dead keys' V rows are zeroed in LDS, so NaN in
-//     freed pages never reaches a product;
+//     accumulators are rarely rescaled); masked keys are set to -inf by
+//     select and dead keys' V rows are zeroed in LDS, so NaN in freed pages
+//     never reaches a product;
 //   * P^T is rounded to the MFMA input type and output and lse are
-//     normalised by the fp32 weight sum; at verification widths
-//     (memory-bound) and while a row has few effective keys, a second MFMA
-//     adds P's rounding error, so rows dominated by a few keys keep full
-//     precision.
+//     normalised by the fp32 weight sum; with 16-bit caches at verification
+//     widths, and while a row has few effective keys, a second MFMA adds P's
+//     rounding error, so rows dominated by a few keys keep full precision.
 // Splits are combined by the merge launch that follows (pa_merge.h).
 #include "pa_common.h"
 #include "pa_merge.h"
