@@ -345,7 +345,69 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
             __syncthreads();
         }
 
-        if (!direct && it == first_item && tid == 0) {
+        if (!direct && a.arrive != nullptr) {
+            // In-kernel merge (static splits, small grids).  Every thread
+            // releases its partial stores at device scope, the barrier joins
+            // them, and one device-scope acquire-release increment counts the
+            // workgroup in.  The workgroup that completes the count acquires
+            // every other workgroup's partials, merges the group (splits in
+            // index order, an online max) and clears the counter.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __syncthreads();
+            if (tid == 0) {
+                int* cnt = a.arrive + b * a.num_kv_heads + g;
+                const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+                const int last = (old == n_splits - 1);
+                if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sm.stat[3] = last;
+            }
+            __syncthreads();
+            if (sm.stat[3]) {
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                constexpr int EPR = D / 4;                 // float4 columns per row
+                constexpr int NB = 16;                     // partials in flight per thread
+                for (int r0 = 0; r0 < rows; r0 += kThreads / EPR) {
+                    const int rl = r0 + tid / EPR;
+                    const int col = (tid % EPR) * 4;
+                    if (rl < rows) {
+                        float M = kNegInf, L = 0.f;
+                        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+                        for (int s0 = 0; s0 < n_splits; s0 += NB) {
+                            float ls[NB];
+                            float4 o[NB];
+#pragma unroll
+                            for (int k = 0; k < NB; ++k) {
+                                const int64_t slot = (first_item + min(s0 + k, n_splits - 1)) * a.r_max + rl;
+                                ls[k] = a.ws_lse[slot];
+                                o[k] = *reinterpret_cast<const float4*>(a.ws_o + slot * D + col);
+                            }
+#pragma unroll
+                            for (int k = 0; k < NB; ++k) {
+                                if (s0 + k < n_splits && ls[k] != kNegInf) {
+                                    if (ls[k] > M) {
+                                        const float sc = (M == kNegInf) ? 0.f : fast_exp2(M - ls[k]);
+                                        L *= sc;
+                                        acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
+                                        M = ls[k];
+                                    }
+                                    const float w = fast_exp2(ls[k] - M);
+                                    L += w;
+                                    acc.x = fmaf(w, o[k].x, acc.x);
+                                    acc.y = fmaf(w, o[k].y, acc.y);
+                                    acc.z = fmaf(w, o[k].z, acc.z);
+                                    acc.w = fmaf(w, o[k].w, acc.w);
+                                }
+                            }
+                        }
+                        const int64_t orow = out_row(tgt, si.q_off, g, rl);
+                        const float sc = (L > 0.f) ? vscale / L : 0.f;
+                        *reinterpret_cast<float4*>(a.out + orow * D + col) =
+                            make_float4(acc.x * sc, acc.y * sc, acc.z * sc, acc.w * sc);
+                        if (a.lse != nullptr && col == 0) a.lse[orow] = (L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
+                    }
+                }
+            }
+        } else if (!direct && it == first_item && tid == 0) {
             const MergeDesc d{(int)first_item, n_splits, rows, a.r_max, si.q_off, g, 0, vscale};
             if (a.sdesc != nullptr) {
                 // fixed slots, one per merge unit the group's rows cover

@@ -47,6 +47,10 @@ struct DecodeArgs {
     // instead of appending to mdesc.
     MergeDesc* sdesc;
     int sdesc_upg;
+    // Arrival counters (static splits, VALU kernel only): when set, the
+    // workgroups of group (b, g) count their arrivals in arrive[b * Hkv + g]
+    // and the last one merges the group's partials itself (no merge launch).
+    int* arrive;
     int64_t page_stride, head_stride, token_stride;   // elements
     int num_seqs, bt_stride;
     int num_q_heads, num_kv_heads, group;

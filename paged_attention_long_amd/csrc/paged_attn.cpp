@@ -33,6 +33,7 @@ struct pa_handle {
     float* ws_lse = nullptr;
     pa::MergeDesc* mdesc = nullptr;   // merge groups published by the attention kernels
     pa::MergeDesc* sdesc = nullptr;   // fixed merge slots for static splits (zeroed; each merge clears what it used)
+    int* arrive = nullptr;            // per-group arrival counters for static splits merged in-kernel (zeroed; the last arrival clears its own)
     int sdesc_upg = 1;                // merge units per (sequence, KV head) group in sdesc
     int64_t sdesc_groups = 0;         // groups sdesc holds
     int* mcount = nullptr;            // [0] groups published, [1] merge workgroups done
@@ -181,8 +182,9 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
     h->sdesc_upg = (h->r_max_valu + pa::merge_rows_per_unit(D) - 1) / pa::merge_rows_per_unit(D);
     h->sdesc_groups = std::min<int64_t>((int64_t)cfg->max_num_seqs * cfg->num_kv_heads, (int64_t)8 * h->cu_count);
     const size_t s_bytes = (size_t)h->sdesc_groups * h->sdesc_upg * sizeof(pa::MergeDesc);
+    const size_t a_bytes = (size_t)h->sdesc_groups * sizeof(int);
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    h->ws_bytes = up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes) + up(s_bytes);
+    h->ws_bytes = up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes) + up(s_bytes) + up(a_bytes);
     if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
         const size_t want = h->ws_bytes;
         delete h;
@@ -195,7 +197,9 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
     h->mdesc = reinterpret_cast<pa::MergeDesc*>(p + up(o_bytes) + up(l_bytes));
     h->mcount = reinterpret_cast<int*>(p + up(o_bytes) + up(l_bytes) + up(d_bytes));
     h->sdesc = reinterpret_cast<pa::MergeDesc*>(p + up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes));
-    if (hipMemset(h->mcount, 0, up(c_bytes) + up(s_bytes)) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    h->arrive = reinterpret_cast<int*>(p + up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes) + up(s_bytes));
+    if (hipMemset(h->mcount, 0, up(c_bytes) + up(s_bytes) + up(a_bytes)) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
         (void)hipFree(h->ws);
         delete h;
         return fail(nullptr, PA_ERR_HIP, "workspace clear failed");
@@ -288,6 +292,7 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     a.mcount = h->mcount;
     a.sdesc = nullptr;
     a.sdesc_upg = h->sdesc_upg;
+    a.arrive = nullptr;
     a.page_stride = layout->page_stride;
     a.head_stride = layout->head_stride;
     a.token_stride = layout->token_stride;
@@ -368,13 +373,19 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
                 a.static_pps = (int)pps;
                 a.static_splits = (int)S;
                 vgrid = (int)items;
-                // alone on the stream, the groups go to fixed merge slots
-                if (!run_mfma && S > 1 && (int64_t)num_seqs * c.num_kv_heads <= h->sdesc_groups) a.sdesc = h->sdesc;
+                // Alone on the stream, the groups are merged without a merge
+                // launch by the last workgroup of each to arrive (small grids:
+                // measured faster up to about half the CUs), or else through
+                // fixed merge slots.
+                if (!run_mfma && S > 1 && (int64_t)num_seqs * c.num_kv_heads <= h->sdesc_groups) {
+                    if (vgrid <= h->cu_count / 2) a.arrive = h->arrive;
+                    else a.sdesc = h->sdesc;
+                }
             }
         }
         hipError_t e = pa::launch_decode_valu(a, c.head_dim, c.kv_dtype, c.q_dtype, rw, vgrid, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
-        if (a.static_pps > 0 && a.static_splits == 1) need_merge_valu = false;
+        if (a.static_pps > 0 && (a.static_splits == 1 || a.arrive != nullptr)) need_merge_valu = false;
     }
     const bool static_merge = a.sdesc != nullptr;
     const int static_splits = a.static_splits;
@@ -382,6 +393,7 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         a.static_pps = 0;
         a.static_splits = 0;
         a.sdesc = nullptr;
+        a.arrive = nullptr;
         a.cls_side = 1;
         a.min_pps = 1;
         a.forced_pps = h->tune.kv_tiles_per_split;

@@ -302,3 +302,43 @@ def test_fixed_merge_slots_do_not_leak_between_forwards():
     finally:
         b.close()
         a.close()
+
+
+def test_static_splits_merged_in_kernel_and_through_slots():
+    """Static splits of a small grid are merged inside the attention kernel by
+    the last workgroup of each group to arrive; a larger grid goes through the
+    fixed merge slots.  Both alternate on one handle, so the arrival counters
+    and the slots must each be left clear by the forward that used them."""
+    big = generate(_spec(seq_lens=(1000, 977, 1003, 640, 999, 1001, 850, 1003), q_lens=(1,) * 8))[0]
+    small = generate(_spec(seq_lens=(1003,), q_lens=(1,), seed=9))[0]
+    a = GpuCase([big], path=pal.PA_PATH_VALU, split_mode=1, pages_per_split=4)
+    b = GpuCase([small], handle=a.h)
+    try:
+        for i, (inp, case) in enumerate(((big, a), (small, b), (small, b), (big, a), (small, b))):
+            progress(f"static merges, forward {i}: {inp.num_seqs} sequences")
+            ref_o, ref_l = oracle.attention(inp)
+            out, lse = case.run()
+            compare(f"forward{i}", inp.kv_dtype, out, lse, ref_o, ref_l)
+    finally:
+        b.close()
+        a.close()
+
+
+@pytest.mark.parametrize("q_len", [1, 3])
+def test_in_kernel_merge_at_split_limit(q_len):
+    """64 static splits per group (the most one merge reads) merged inside
+    the attention kernel, rows spanning more than one merge pass; run twice
+    on one handle, bit-identical."""
+    inp = generate(_spec(num_q_heads=8, num_kv_heads=2, seq_lens=(4090,), q_lens=(q_len,), q_dtype="f16",
+                         kv_dtype="f16", window=0))[0]
+    progress(f"in-kernel merge at 64 splits, q_len {q_len}")
+    ref_o, ref_l = oracle.attention(inp)
+    c = GpuCase([inp], path=pal.PA_PATH_VALU, split_mode=1, pages_per_split=4)
+    try:
+        o1, l1 = c.run()
+        o2, l2 = c.run()
+    finally:
+        c.close()
+    compare("splits64", inp.kv_dtype, o1, l1, ref_o, ref_l)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
