@@ -191,10 +191,25 @@ def test_nhd_layout_through_strides():
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
-def test_graph_replay_matches_eager():
+GRAPH_CASES = {
+    # static splits on 176 workgroups: fixed merge slots
+    "decode_merge_slots": dict(seq_lens=(4097,), q_lens=(1,)),
+    # static splits on a small grid: merged inside the attention kernel
+    "decode_in_kernel_merge": dict(seq_lens=(1003,), q_lens=(1,)),
+    # verification width: tile kernel, published groups, merge launch
+    "verify_merge_launch": dict(seq_lens=(3000,), q_lens=(8,), q_dtype="f16", kv_dtype="f16"),
+}
+
+
+@pytest.mark.parametrize("name", list(GRAPH_CASES))
+def test_graph_replay_matches_eager(name):
+    """A captured forward replayed several times (eager work in between)
+    equals the eager forward bit for bit: every counter and merge slot the
+    forward uses is back at zero when it ends."""
     import torch
 
-    inp = generate(_spec(seq_lens=(4097,), q_lens=(1,)))[0]
+    inp = generate(_spec(**GRAPH_CASES[name]))[0]
+    progress(f"graph replay {name}")
     c = GpuCase([inp])
     try:
         eager_o, eager_l = c.run()
