@@ -67,13 +67,15 @@ extern "C" {
 
 /* execution paths (pa_tuning_t.path) */
 #define PA_PATH_AUTO   0   /* VALU split-KV kernel for rows-per-KV-head <= 8, MFMA tile kernel above */
-#define PA_PATH_VALU   1   /* every sequence through the VALU split-KV kernel */
-#define PA_PATH_MFMA   2   /* every sequence through the MFMA tile kernel */
+#define PA_PATH_VALU   1   /* every sequence through the VALU split-KV kernel (handles whose
+                              max_q_len * Hq / Hkv is at most 64; else PA_ERR_UNSUPPORTED) */
+#define PA_PATH_MFMA   2   /* every sequence through the MFMA tile kernel (head_dim 128 only) */
 
 typedef struct pa_config {
     int32_t num_q_heads;     /* Hq >= 1 */
     int32_t num_kv_heads;    /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 16 */
-    int32_t head_dim;        /* D: 64 or 128 */
+    int32_t head_dim;        /* D: 64 or 128; 64 runs on the VALU kernel only and needs
+                                max_q_len * Hq / Hkv <= 64 (else PA_ERR_UNSUPPORTED at create) */
     int32_t page_size;       /* P: tokens per page; 16 */
     int32_t q_dtype;         /* PA_DTYPE_F16 or PA_DTYPE_BF16 */
     int32_t kv_dtype;        /* PA_DTYPE_F16, PA_DTYPE_BF16 (== q_dtype) or PA_DTYPE_FP8_E4M3 */
@@ -102,7 +104,8 @@ typedef struct pa_cache_layout {
 typedef struct pa_tuning {
     int32_t path;             /* PA_PATH_* */
     int32_t pages_per_split;  /* VALU kernel: KV pages per split (0: sized from the live context) */
-    int32_t kv_tiles_per_split; /* MFMA kernel: 64-key tiles per split (0: automatic) */
+    int32_t kv_tiles_per_split; /* MFMA kernel: key tiles per split (32-key tiles; 64-key for
+                                   fp8 caches at prefill widths; 0: automatic) */
     int32_t grid;             /* workgroups per launch (0: from the CU count) */
     int32_t split_mode;       /* VALU kernel: 0 automatic, 1 static splits from the block-table
                                  width (one round trip to start), 2 splits planned on the device

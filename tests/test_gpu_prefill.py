@@ -28,6 +28,11 @@ PREFILL = {
     "f16_outliers_g4": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(3000,), q_lens=(48,), q_dtype="f16",
                             kv_dtype="f16", k_outlier_frac=0.01),
     "mixed_lengths": dict(seq_lens=(513, 70, 2049), q_lens=(33, 70, 5), num_q_heads=8, num_kv_heads=2),
+    # head_dim 64 (VALU kernel only) at its limit of 64 rows per KV head
+    "f16_d64_max_rows": dict(num_q_heads=8, num_kv_heads=2, head_dim=64, seq_lens=(700, 16), q_lens=(16, 16),
+                             q_dtype="f16", kv_dtype="f16"),
+    "fp8_d64_window": dict(num_q_heads=8, num_kv_heads=2, head_dim=64, seq_lens=(900,), q_lens=(16,),
+                           kv_dtype="fp8_e4m3", window=120, poison_out_of_window=True, k_outlier_frac=0.01),
 }
 
 
