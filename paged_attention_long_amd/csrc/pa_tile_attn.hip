@@ -543,15 +543,20 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             // The grid is one round of resident workgroups (t of them) and each
             // takes items it, it + t, ...  Try splits sized for 1..4 rounds and
             // keep the one whose rounds x largest item is smallest (split sizes
-            // are equalised within a sequence).
+            // are equalised within a sequence).  An item's tiles are shared by
+            // the WK waves of its workgroup, so an item takes ceil(tiles / WK)
+            // wave steps: candidates are rounded up to a multiple of WK (the
+            // same steps, fewer items and partials) and costed in wave steps.
             const long long t = a.target_items > 0 ? a.target_items : 1;
+            auto round_wk = [](int c) { return (c + C::WK - 1) / C::WK * C::WK; };
+            auto wave_steps = [](int tiles) { return (tiles + C::WK - 1) / C::WK; };
             constexpr int NC = 4;
             int cand[NC];
             long long items[NC];
             int big[NC];
 #pragma unroll
             for (int k = 0; k < NC; ++k) {
-                cand[k] = one ? tmin : max(tmin, (int)div_ceil_i64(work, t * (k + 1)));
+                cand[k] = one ? tmin : round_wk(max(tmin, (int)div_ceil_i64(work, t * (k + 1))));
                 items[k] = 0;
                 big[k] = 0;
             }
@@ -564,11 +569,11 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 long long cost = 0;
                 int ck = tmin;
                 if (lane < NC) {
-                    ck = max(tmin, (int)div_ceil_i64(work, t * (lane + 1)));
+                    ck = round_wk(max(tmin, (int)div_ceil_i64(work, t * (lane + 1))));
                     const int S = one_tub > 0 ? (one_tub + ck - 1) / ck : 0;
                     const long long it_k = (long long)one_nqt * S;
                     const int big_k = S > 0 ? (one_tub + S - 1) / S : 0;
-                    cost = div_ceil_i64(it_k * a.num_kv_heads, t) * big_k;
+                    cost = div_ceil_i64(it_k * a.num_kv_heads, t) * wave_steps(big_k);
                 }
 #pragma unroll
                 for (int k = 0; k < NC; ++k) {
@@ -604,7 +609,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                     it_k += red_items[k][ww];
                     big_k = max(big_k, red_big[k][ww]);
                 }
-                const long long cost = div_ceil_i64(it_k * a.num_kv_heads, t) * big_k;
+                const long long cost = div_ceil_i64(it_k * a.num_kv_heads, t) * wave_steps(big_k);
                 if (best < 0 || cost < best) { best = cost; tps = cand[k]; }
             }
         }
