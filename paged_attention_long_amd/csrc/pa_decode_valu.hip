@@ -24,7 +24,8 @@
 //     section "Bug 2: the drafter read freed memory");
 //   * the context of each (sequence, KV head) is split across workgroups
 //     sized from the live lengths; the partials are combined by the merge
-//     launch that follows (log-sum-exp merge, pa_merge.h).
+//     launch that follows (log-sum-exp merge, pa_merge.h), or, for static
+//     splits on a small grid, by the last workgroup of the group to finish.
 #include "pa_common.h"
 #include "pa_merge.h"
 #include "pa_kernels.h"

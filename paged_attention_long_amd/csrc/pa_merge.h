@@ -12,9 +12,12 @@
 // The workgroup that runs a group's first split publishes a descriptor; a
 // separate merge launch, ordered after the attention kernels on the stream,
 // merges every published group with all of its threads.  The kernel boundary
-// makes the partials visible, so the attention kernels need no device-wide
-// fences or arrival counters.  Splits are visited in index order, so results
-// are deterministic.  A group has at most kMaxSplits splits.
+// makes the partials visible, so those attention kernels need no device-wide
+// fences or arrival counters.  The one exception is static-split decode on
+// a small grid, where the last workgroup of each group to arrive (a
+// device-scope acquire-release count) merges the group inside the decode
+// kernel.  Splits are visited in index order, so results are deterministic.
+// A group has at most kMaxSplits splits.
 #pragma once
 
 #include "pa_common.h"
