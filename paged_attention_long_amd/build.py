@@ -19,12 +19,13 @@ ARCH = "gfx950"
 
 SOURCES = ["paged_attn.cpp", "pa_decode_valu.hip", "pa_tile_attn.hip", "pa_merge.hip", "pa_gather.hip"]
 
+OBJ_DIR = os.path.join(PKG, "_build")
+
 FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wno-unused-function",
     "-Wno-unused-variable",
@@ -37,6 +38,15 @@ FLAGS = [
 ]
 
 
+# Flags of single sources.  The decode kernel (a short chain of dependent
+# page loads per wave, a few rows of softmax state) schedules better with the
+# ILP-oriented machine scheduler: about 0.4 us less per 4k-token decode
+# forward, measured; the tile kernels are no faster with it.
+SOURCE_FLAGS = {
+    "pa_decode_valu.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -45,21 +55,38 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = True, extra=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-o", tmp, *srcs]
+    """Compile every source to an object (in parallel, each with its own
+    flags), link the shared library and check that it loads."""
+    os.makedirs(OBJ_DIR, exist_ok=True)
     t0 = time.time()
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    cc = hipcc()
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
+        cmd = [cc, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, f"-I{INCLUDE}", f"-I{CSRC}", "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        jobs.append((src, obj, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    errs, objs = [], []
+    for src, obj, proc in jobs:
+        out, err = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out + err)
+            raise RuntimeError(f"hipcc failed on {src} ({proc.returncode})")
+        errs.append(err)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    link = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    res = subprocess.run(link, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed ({res.returncode})")
+        raise RuntimeError(f"link failed ({res.returncode})")
     # a library with an unresolved symbol must fail the build, not the first caller
     import ctypes
 
     ctypes.CDLL(os.path.abspath(tmp))
     os.replace(tmp, LIB)
     if verbose:
-        warn = [l for l in res.stderr.splitlines() if "warning" in l and "packed-fp32-ops" not in l]
+        warn = [l for e in errs for l in e.splitlines() if "warning" in l and "packed-fp32-ops" not in l]
         for l in warn[:20]:
             print(l)
         print(f"built {LIB} in {time.time() - t0:.1f}s")
