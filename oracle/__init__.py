@@ -23,6 +23,7 @@ It shares no code with the HIP path; its only inputs are the storage bits and
 integer metadata that the seeded generator produces.
 """
 from .codec import decode_bits, fp8_e4m3_table  # noqa: F401
+from .append import append_kv, e4m3_encode, new_row_positions  # noqa: F401
 from .attention import (  # noqa: F401
     attention,
     attention_rows,

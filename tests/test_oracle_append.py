@@ -1,0 +1,101 @@
+"""Pins of the oracle's cache append and its E4M3FN encoder (CPU).
+
+The encoder is checked against what fixes it from outside: torch's own
+float8_e4m3fn cast (round to nearest even) on in-range values and on every
+midpoint between neighbouring codes, the exact round trip of every finite
+code, the format's saturation and NaN rules, and a brute-force nearest-value
+search.  The append is checked by brute force on small caches."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.append import append_kv, e4m3_encode
+
+TABLE = oracle.fp8_e4m3_table()
+
+
+def _torch_codes(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_matches_torch_cast_in_range():
+    rng = np.random.default_rng(1)
+    x = np.concatenate([rng.standard_normal(50000) * s for s in (1e-3, 0.1, 1.0, 30.0, 150.0)]).astype(np.float32)
+    x = x[np.abs(x) <= 448]
+    assert np.array_equal(e4m3_encode(x), _torch_codes(x))
+
+
+def test_midpoints_round_to_even_code():
+    pos = TABLE[:0x7F]
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (pos[:-1] + pos[1:]) / 2)   # exact in fp32
+    codes = e4m3_encode(mids)
+    assert np.all(codes % 2 == 0)
+    assert np.all((codes == np.arange(0, 0x7E)) | (codes == np.arange(1, 0x7F)))
+    assert np.array_equal(codes, _torch_codes(mids))
+    assert np.array_equal(e4m3_encode(-mids), codes | 0x80)
+
+
+def test_every_finite_code_round_trips():
+    codes = np.array([c for c in range(256) if not np.isnan(TABLE[c])], dtype=np.uint8)
+    vals = TABLE[codes].astype(np.float32)
+    got = e4m3_encode(vals)
+    # +0 and -0 keep their sign bits
+    assert np.array_equal(got, codes)
+
+
+def test_saturation_nan_and_sign():
+    x = np.array([448.0, 449.0, 463.9, 464.0, 1e30, np.inf, -500.0, -np.inf, np.nan, -np.nan, 0.0, -0.0],
+                 dtype=np.float32)
+    assert e4m3_encode(x).tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F, 0xFF, 0x00, 0x80]
+
+
+def test_brute_force_nearest():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal(2000) * rng.choice([1e-3, 1.0, 100.0], 2000)).astype(np.float32)
+    codes = e4m3_encode(x)
+    finite = TABLE[~np.isnan(TABLE)]
+    for xi, ci in zip(x.tolist(), codes.tolist()):
+        best = np.min(np.abs(finite - xi))
+        assert abs(TABLE[ci] - xi) == best
+
+
+@pytest.mark.parametrize("cache_dtype", ["f16", "fp8_e4m3"])
+def test_append_brute_force(cache_dtype):
+    rng = np.random.default_rng(3)
+    P, hkv, D, pages = 16, 2, 8, 12
+    seq_lens, q_lens = np.array([20, 5, 16, 33]), np.array([3, 5, 0, 17])
+    bt = rng.permutation(pages)[:12].reshape(4, 3).astype(np.int32)     # distinct pages per sequence
+    T = int(q_lens.sum())
+    k_new = rng.standard_normal((T, hkv, D)).astype(np.float16).view(np.uint16)
+    v_new = rng.standard_normal((T, hkv, D)).astype(np.float16).view(np.uint16)
+    st = np.uint16 if cache_dtype == "f16" else np.uint8
+    k_pool = rng.integers(0, 255, (pages, hkv, P, D)).astype(st)
+    v_pool = rng.integers(0, 255, (pages, hkv, P, D)).astype(st)
+    scale = np.array([[0.5, 2.0], [0.25, 3.0]], dtype=np.float32)
+    k_out, v_out = append_kv(k_new, v_new, "f16", k_pool, v_pool, cache_dtype, bt, seq_lens, q_lens, scale, P)
+    touched = np.zeros((pages, P), dtype=bool)
+    t = 0
+    for b in range(4):
+        for i in range(int(q_lens[b])):
+            p = int(seq_lens[b] - q_lens[b] + i)
+            pg, sl = int(bt[b, p // P]), p % P
+            touched[pg, sl] = True
+            for g in range(hkv):
+                for which, new, out in ((0, k_new, k_out), (1, v_new, v_out)):
+                    if cache_dtype == "f16":
+                        assert np.array_equal(out[pg, g, sl], new[t + i, g])
+                    else:
+                        x = new[t + i, g].view(np.float16).astype(np.float64)
+                        vals = TABLE[out[pg, g, sl]] * scale[which, g]
+                        # nearest representable after scaling (fp32 quotient: within half a step)
+                        step = np.abs(TABLE[out[pg, g, sl] ^ 1] - TABLE[out[pg, g, sl]]) * scale[which, g]
+                        assert np.all(np.abs(vals - x) <= step / 2 * (1 + 1e-6))
+        t += int(q_lens[b])
+    # nothing else changed
+    for pg in range(pages):
+        for sl in range(P):
+            if not touched[pg, sl]:
+                assert np.array_equal(k_out[pg, :, sl], k_pool[pg, :, sl])
+                assert np.array_equal(v_out[pg, :, sl], v_pool[pg, :, sl])
