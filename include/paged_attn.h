@@ -203,6 +203,38 @@ int paged_attn_debug_gather(pa_handle_t* h,
                             const int32_t* seq_lens, const int32_t* q_lens, int32_t window,
                             int64_t* slots_out, void* rows_out, int64_t capacity, void* stream);
 
+/*
+ * paged_attn_append: write a step's new K and V rows into their pages, the
+ * step just before attention reads them ("Dual MI50, part 2", sections
+ * "Bug 2: the drafter read freed memory" and "Prefill: teach the fork's
+ * fast kernel to read the int8 cache").  Sequence b's rows are its last
+ * q_len_b positions (seq_len_b counts them): its row i is logical position
+ * p = seq_len_b - q_len_b + i, stored in page block_table[b][p / P], slot
+ * p % P, for every KV head.  A 16-bit cache receives the input bits
+ * unchanged; an fp8 E4M3FN cache receives, per element, the code nearest to
+ * x / s (s = kv_scale[0][g] for K, kv_scale[1][g] for V; the quotient
+ * rounded once in fp32), ties to the even code, magnitudes of 448 and more
+ * (and infinities) stored as 448, NaN as NaN, the sign kept.
+ *
+ *  k_new, v_new  device, q_dtype, contiguous [num_tokens][Hkv][D], rows of
+ *                sequence 0 first; 16-byte aligned.  Read only.
+ *  k_cache, v_cache, layout, block_table, num_seqs, block_table_stride,
+ *  seq_lens, q_lens, kv_scale, stream: as in paged_attn_forward (the caches
+ *                are written; kv_scale is required for an fp8 cache and must
+ *                be NULL otherwise).
+ *
+ * Only the addressed slots are written.  A sequence with q_len <= 0,
+ * q_len > seq_len, or rows past num_tokens writes nothing; a row whose
+ * position lies past the block table's width, or whose page id is outside
+ * [0, num_pages), is skipped.  Asynchronous on `stream`; allocates nothing.
+ * Returns PA_OK or PA_ERR_INVALID_ARGUMENT / PA_ERR_UNSUPPORTED (host
+ * checks, nothing enqueued) or PA_ERR_HIP.
+ */
+int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int64_t num_tokens,
+                      void* k_cache, void* v_cache, const pa_cache_layout_t* layout,
+                      const int32_t* block_table, int32_t num_seqs, int32_t block_table_stride,
+                      const int32_t* seq_lens, const int32_t* q_lens, const float* kv_scale, void* stream);
+
 /* paged_attn_version: library version, e.g. "0.1.0". */
 const char* paged_attn_version(void);
 

@@ -104,6 +104,10 @@ def load_library() -> ctypes.CDLL:
     lib.paged_attn_debug_gather.argtypes = [
         vp, vp, ctypes.POINTER(pa_cache_layout_t), vp, i32, i32, vp, vp, i32, vp, vp, i64, vp]
     lib.paged_attn_debug_gather.restype = ctypes.c_int
+    lib.paged_attn_append.argtypes = [
+        vp, vp, vp, ctypes.c_int64, vp, vp, ctypes.POINTER(pa_cache_layout_t), vp, ctypes.c_int32, ctypes.c_int32,
+        vp, vp, vp, vp]
+    lib.paged_attn_append.restype = ctypes.c_int
     lib.paged_attn_version.argtypes = []
     lib.paged_attn_version.restype = ctypes.c_char_p
     _lib = lib
@@ -231,6 +235,30 @@ def paged_attn_debug_gather(h: Handle, k_cache, block_table, seq_lens, q_lens, w
     rc = load_library().paged_attn_debug_gather(
         h.ptr, _ptr(k_cache), ctypes.byref(layout), _ptr(block_table), seq_lens.shape[0], block_table.stride(0),
         _ptr(seq_lens), _ptr(q_lens), int(window), _ptr(slots_out), _ptr(rows_out), slots_out.shape[0],
+        _stream_ptr(stream))
+    _check(rc, h.ptr)
+
+
+def paged_attn_append(h: Handle, k_new, v_new, k_cache, v_cache, block_table, seq_lens, q_lens, kv_scale=None,
+                      stream=None) -> None:
+    """Enqueue the cache append; see include/paged_attn.h for the contract."""
+    c = h.cfg
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.dim() != 3 or tuple(t.shape[1:]) != (c.num_kv_heads, c.head_dim) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [T, Hkv, D] tensor")
+        if t.element_size() != 2:
+            raise ValueError(f"{name} must have 2-byte elements")
+    if v_new.shape != k_new.shape:
+        raise ValueError("v_new must match k_new")
+    _check_cache(h, k_cache)
+    if v_cache.shape != k_cache.shape or v_cache.stride() != k_cache.stride():
+        raise ValueError("v_cache must match k_cache in shape and strides")
+    if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.element_size() != 4:
+        raise ValueError("block_table must be int32 [num_seqs, width] with unit column stride")
+    layout = cache_layout(k_cache)
+    rc = load_library().paged_attn_append(
+        h.ptr, _ptr(k_new), _ptr(v_new), k_new.shape[0], _ptr(k_cache), _ptr(v_cache), ctypes.byref(layout),
+        _ptr(block_table), seq_lens.shape[0], block_table.stride(0), _ptr(seq_lens), _ptr(q_lens), _ptr(kv_scale),
         _stream_ptr(stream))
     _check(rc, h.ptr)
 

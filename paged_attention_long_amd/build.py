@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpaged_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["paged_attn.cpp", "pa_decode_valu.hip", "pa_tile_attn.hip", "pa_merge.hip", "pa_gather.hip"]
+SOURCES = ["paged_attn.cpp", "pa_decode_valu.hip", "pa_tile_attn.hip", "pa_merge.hip", "pa_gather.hip", "pa_append.hip"]
 
 OBJ_DIR = os.path.join(PKG, "_build")
 

@@ -1,0 +1,133 @@
+// Writing a step's new K/V rows into the paged cache (quantise-on-write for
+// fp8 caches).  Sequence b's new rows are its last q_len_b positions
+// (seq_len_b counts them), so row i lands at logical position
+// p = seq_len_b - q_len_b + i: page block_table[b][p / 16], slot p % 16, the
+// same addressing the attention kernels read with (kv_offset).  A 16-bit
+// cache receives the input bits; an fp8 E4M3FN cache receives the code
+// nearest to x / s (s the KV head's K or V scale, the quotient rounded once
+// in fp32), ties to the even code, magnitudes from 448 up saturated to 448,
+// NaN kept as NaN, sign kept.  The pages quantise their own (int8) cache on
+// write in the same place of the step ("Dual MI50, part 2", section
+// "Prefill: teach the fork's fast kernel to read the int8 cache").
+//
+// Bandwidth-bound and tiny per row: one thread per 8 elements (16 B in,
+// 16 B or 8 B out), workgroups along the sequence's rows.  Every store is
+// checked against the cache and the block table; rows whose position or page
+// falls outside them are skipped.
+#include "pa_common.h"
+#include "pa_kernels.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kAppendThreads = 256;
+
+// E4M3FN code of an fp32 value by integer rounding of its bits: the
+// mantissa is cut to 3 bits (exponent >= -6) or the significand is shifted
+// to units of 2^-9 (subnormal codes), rounding to nearest, ties to even.
+// Codes are ordered like the values they stand for, so a round-up that
+// carries into the exponent lands on the next code.
+PA_DEVINLINE uint32_t e4m3_code(float q) {
+    const uint32_t u = __float_as_uint(q);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7fffffffu;
+    if (a > 0x7f800000u) return sign | 0x7fu;          // NaN
+    if (a >= 0x43e00000u) return sign | 0x7eu;         // >= 448 (and infinity): saturate
+    if (a < 0x00800000u) return sign;                  // zero and fp32 subnormals (< 2^-126)
+    const int e = (int)(a >> 23) - 127;
+    uint32_t code;
+    if (e >= -6) {
+        const uint32_t m = a & 0x7fffffu;
+        const uint32_t base = ((uint32_t)(e + 7) << 3) | (m >> 20);
+        const uint32_t rem = m & 0xfffffu;
+        code = base + ((rem > 0x80000u || (rem == 0x80000u && (base & 1u))) ? 1u : 0u);
+    } else {
+        const int sh = 14 - e;                         // significand in units of 2^-9
+        if (sh >= 32) return sign;
+        const uint32_t sig = (a & 0x7fffffu) | 0x800000u;
+        const uint32_t base = sig >> sh;
+        const uint32_t rem = sig & ((1u << sh) - 1u);
+        const uint32_t half = 1u << (sh - 1);
+        code = base + ((rem > half || (rem == half && (base & 1u))) ? 1u : 0u);
+    }
+    return sign | min(code, 0x7eu);
+}
+
+template <int IT>
+PA_DEVINLINE float to_f32(uint32_t bits16) {
+    if constexpr (IT == PA_DTYPE_BF16) return __uint_as_float(bits16 << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+template <int KVT, int IT>
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
+    const int b = blockIdx.x;
+    __shared__ int red[kAppendThreads / kWave];
+    // this sequence's first input row: sum of the earlier q_lens
+    int part = 0;
+    for (int s = threadIdx.x; s < b; s += kAppendThreads) part += max(a.q_lens[s], 0);
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) part += __shfl_xor(part, o, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = part;
+    __syncthreads();
+    int q_off = 0;
+#pragma unroll
+    for (int w = 0; w < kAppendThreads / kWave; ++w) q_off += red[w];
+    const int ql = a.q_lens[b], sl = a.seq_lens[b];
+    if (ql <= 0 || ql > sl || q_off + ql > a.num_tokens) return;
+    const int cpr = a.head_dim / 8;                                // 8-element chunks per head row
+    const int64_t per_side = (int64_t)ql * a.num_kv_heads * cpr;
+    const int64_t stride = (int64_t)gridDim.y * kAppendThreads;
+    for (int64_t c = (int64_t)blockIdx.y * kAppendThreads + threadIdx.x; c < 2 * per_side; c += stride) {
+        const int which = c >= per_side;                           // 0: K, 1: V
+        const int64_t r = c - which * per_side;
+        const int ch = (int)(r % cpr);
+        const int64_t rg = r / cpr;
+        const int g = (int)(rg % a.num_kv_heads);
+        const int i = (int)(rg / a.num_kv_heads);
+        const int p = sl - ql + i;
+        if (p / kAppendPage >= a.bt_stride) continue;
+        const int pid = a.block_table[(int64_t)b * a.bt_stride + p / kAppendPage];
+        if (pid < 0 || pid >= a.num_pages) continue;
+        const uint16_t* src = static_cast<const uint16_t*>(which ? a.v_new : a.k_new) +
+                              ((int64_t)(q_off + i) * a.num_kv_heads + g) * a.head_dim + ch * 8;
+        const uint4 in = *reinterpret_cast<const uint4*>(src);
+        const int64_t off = (int64_t)pid * a.page_stride + (int64_t)g * a.head_stride +
+                            (int64_t)(p % kAppendPage) * a.token_stride + ch * 8;
+        if constexpr (KVT != PA_DTYPE_FP8_E4M3) {
+            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(which ? a.v_cache : a.k_cache) + off) = in;
+        } else {
+            const float s = a.kv_scale[which * a.num_kv_heads + g];
+            const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t bits = (w[k / 2] >> (16 * (k & 1))) & 0xffffu;
+                const uint32_t code = e4m3_code(__fdiv_rn(to_f32<IT>(bits), s));
+                if (k < 4) lo |= code << (8 * k);
+                else hi |= code << (8 * (k - 4));
+            }
+            *reinterpret_cast<uint2*>(static_cast<uint8_t*>(which ? a.v_cache : a.k_cache) + off) = make_uint2(lo, hi);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, int kv_dtype, int in_dtype, int max_rows, hipStream_t stream) {
+    const int64_t chunks = 2LL * max_rows * a.num_kv_heads * (a.head_dim / 8);
+    const int gy = (int)std::min<int64_t>(256, std::max<int64_t>(1, (chunks + kAppendThreads - 1) / kAppendThreads));
+    const dim3 grid(a.num_seqs, gy);
+    if (kv_dtype == PA_DTYPE_FP8_E4M3) {
+        if (in_dtype == PA_DTYPE_BF16)
+            hipLaunchKernelGGL((append_kernel<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16>), grid, dim3(kAppendThreads), 0, stream, a);
+        else
+            hipLaunchKernelGGL((append_kernel<PA_DTYPE_FP8_E4M3, PA_DTYPE_F16>), grid, dim3(kAppendThreads), 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((append_kernel<PA_DTYPE_F16, PA_DTYPE_F16>), grid, dim3(kAppendThreads), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace pa

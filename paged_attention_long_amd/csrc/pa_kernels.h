@@ -118,4 +118,24 @@ struct GatherArgs {
 
 hipError_t launch_debug_gather(const GatherArgs& a, hipStream_t stream);
 
+constexpr int kAppendPage = 16;   // tokens per cache page
+
+// Arguments of the cache append (new K/V rows written into their pages).
+struct AppendArgs {
+    const void* k_new;         // [num_tokens][Hkv][D], 16-bit
+    const void* v_new;
+    void* k_cache;
+    void* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const int32_t* q_lens;
+    const float* kv_scale;     // [2][Hkv] (fp8 caches)
+    int64_t num_pages, page_stride, head_stride, token_stride;   // elements
+    int64_t num_tokens;
+    int num_seqs, bt_stride, num_kv_heads, head_dim;
+};
+
+// max_rows: the largest q_len of the call (sizes the grid along the rows).
+hipError_t launch_append(const AppendArgs& a, int kv_dtype, int in_dtype, int max_rows, hipStream_t stream);
+
 }  // namespace pa

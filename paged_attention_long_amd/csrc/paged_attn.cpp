@@ -479,4 +479,49 @@ int paged_attn_debug_gather(pa_handle_t* h, const void* k_cache, const pa_cache_
     return PA_OK;
 }
 
+int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int64_t num_tokens, void* k_cache,
+                      void* v_cache, const pa_cache_layout_t* layout, const int32_t* block_table, int32_t num_seqs,
+                      int32_t block_table_stride, const int32_t* seq_lens, const int32_t* q_lens,
+                      const float* kv_scale, void* stream) {
+    if (!h) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "handle is NULL");
+    const pa_config_t& c = h->cfg;
+    int rc = validate_cache(h, layout, k_cache, v_cache);
+    if (rc != PA_OK) return rc;
+    if (!k_new || !v_new || !block_table || !seq_lens || !q_lens)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "k_new, v_new, block_table, seq_lens and q_lens must be non-NULL");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(h, PA_ERR_INVALID_ARGUMENT, "k_new and v_new must be 16-byte aligned");
+    if (num_tokens < 1 || num_tokens > c.max_num_tokens)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "num_tokens %lld outside 1..%lld", (long long)num_tokens,
+                    (long long)c.max_num_tokens);
+    if (num_seqs < 1 || num_seqs > c.max_num_seqs)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "num_seqs %d outside 1..%d", num_seqs, c.max_num_seqs);
+    if (block_table_stride < 1) return fail(h, PA_ERR_INVALID_ARGUMENT, "block_table_stride must be >= 1");
+    if ((c.kv_dtype == PA_DTYPE_FP8_E4M3) != (kv_scale != nullptr))
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "kv_scale is required for an fp8 cache and must be NULL otherwise");
+    if (c.page_size != pa::kAppendPage) return fail(h, PA_ERR_UNSUPPORTED, "page_size must be 16");
+    DeviceGuard guard(c.device);
+    if (!guard.ok) return fail(h, PA_ERR_HIP, "hipSetDevice(%d) failed", c.device);
+    pa::AppendArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.q_lens = q_lens;
+    a.kv_scale = kv_scale;
+    a.num_pages = layout->num_pages;
+    a.page_stride = layout->page_stride;
+    a.head_stride = layout->head_stride;
+    a.token_stride = layout->token_stride;
+    a.num_tokens = num_tokens;
+    a.num_seqs = num_seqs;
+    a.bt_stride = block_table_stride;
+    a.num_kv_heads = c.num_kv_heads;
+    a.head_dim = c.head_dim;
+    hipError_t e = pa::launch_append(a, c.kv_dtype, c.q_dtype, c.max_q_len, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(h, PA_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
+    return PA_OK;
+}
+
 }  // extern "C"
