@@ -41,6 +41,7 @@ WORKLOADS = {
     "verify_window": "speculative verify, 2048-token window, out-of-window pages NaN (61,448 tokens, fp16 KV)",
     "prefill": "chunked prefill: 2,048-token chunk on 65,536 cached, 24/4 heads, D 128, bf16 KV",
     "mixed_fp8": "mixed batch: 4 seqs, 200,001/131,076/32,776/4,097 tokens, q_len 1/4/8/1, 32/8 heads, fp8 e4m3 KV",
+    "append_fp8": "cache append: 64 seqs x 256 new rows, 8 KV heads, D 128, bf16 rows quantised into fp8 e4m3 pages",
 }
 # inputs as stored; every product is accumulated, and every softmax step computed, in fp32
 DTYPE_NAME = {"f16": "f16 in / f32 accumulate", "bf16": "bf16 in / f32 accumulate",
@@ -356,6 +357,119 @@ def reduce_profiles(prof_dir: str, workload: str, calib_mib: int, commands: list
     return data[workload]
 
 
+APPEND_SHAPE = dict(num_seqs=64, rows=256, hkv=8, head_dim=128)
+
+
+def _append_inputs(seed: int = 7):
+    """Seeded append workload: each sequence's last `rows` positions get new
+    rows; its block table maps those pages to distinct pool pages."""
+    import numpy as np
+
+    sh = APPEND_SHAPE
+    rng = np.random.default_rng(seed)
+    seq_lens = rng.integers(sh["rows"], 60000, sh["num_seqs"]).astype(np.int32)
+    q_lens = np.full(sh["num_seqs"], sh["rows"], dtype=np.int32)
+    width = int((seq_lens.max() + 15) // 16)
+    per = sh["rows"] // 16 + 1
+    pages = sh["num_seqs"] * per
+    perm = rng.permutation(pages).astype(np.int32)
+    bt = np.zeros((sh["num_seqs"], width), dtype=np.int32)
+    for b, sl in enumerate(seq_lens.tolist()):
+        first = (sl - sh["rows"]) // 16
+        last = (sl - 1) // 16
+        bt[b, first:last + 1] = perm[b * per:b * per + (last - first + 1)]
+    T = int(q_lens.sum())
+    x = rng.standard_normal((2, T, sh["hkv"], sh["head_dim"])).astype(np.float32)
+    scale = rng.uniform(0.01, 0.05, (2, sh["hkv"])).astype(np.float32)
+    return seq_lens, q_lens, bt, pages, x, scale
+
+
+def measure_append(steps: int, warmup: int, use_graph: bool = True):
+    import numpy as np
+    import torch
+
+    import paged_attention_long_amd as pal
+
+    sh = APPEND_SHAPE
+    seq_lens, q_lens, bt, pages, x, scale = _append_inputs()
+    T = int(q_lens.sum())
+    dev = torch.device("cuda")
+    kn = torch.from_numpy(x[0]).to(dev).to(torch.bfloat16).contiguous()
+    vn = torch.from_numpy(x[1]).to(dev).to(torch.bfloat16).contiguous()
+    kc = torch.zeros((pages, sh["hkv"], 16, sh["head_dim"]), dtype=torch.uint8, device=dev)
+    vc = torch.zeros_like(kc)
+    d_bt, d_sl, d_ql = (torch.from_numpy(a).to(dev) for a in (bt, seq_lens, q_lens))
+    d_sc = torch.from_numpy(scale.reshape(-1)).to(dev)
+    cfg = pal.make_config(sh["hkv"] * 4, sh["hkv"], sh["head_dim"], "bf16", "fp8_e4m3", sh["num_seqs"], sh["rows"], T)
+    h = pal.paged_attn_create(cfg)
+    stream = torch.cuda.current_stream()
+
+    def step(st=None):
+        pal.paged_attn_append(h, kn, vn, kc, vc, d_bt, d_sl, d_ql, d_sc, stream=st or stream)
+
+    try:
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(); [step() for _ in range(steps)]; e1.record(); torch.cuda.synchronize()
+        eager_us = e0.elapsed_time(e1) * 1e3 / steps
+        us = eager_us
+        timing = "eager launches"
+        if use_graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(steps):
+                    step(torch.cuda.current_stream())
+            g.replay(); torch.cuda.synchronize()
+            e0.record(); g.replay(); e1.record(); torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            timing = "graph replay of the timed steps"
+    finally:
+        pal.paged_attn_destroy(h)
+    nbytes = 2 * T * sh["hkv"] * sh["head_dim"] * (2 + 1)     # read the 16-bit rows, write the fp8 codes
+    gbs = nbytes / us / 1e3
+    print(f"[bench] append_fp8: {gbs:.1f} GB/s ({timing}), {us:.2f} us per call = {100 * gbs / HBM_PEAK_GBS:.1f}% of peak",
+          file=sys.stderr, flush=True)
+    res = {
+        "value": gbs, "unit": "GB/s", "ms_per_step": us / 1e3, "dtype": "bf16 in / fp8 e4m3 out",
+        "kv_bytes_per_step": nbytes, "flops_per_step": 0, "rotating_copies": 1,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": None, "scope": "one append call (new K and V rows read, fp8 codes written)"},
+        "timing": timing, "forward_us": {"events": us, "eager_events": eager_us},
+        "eager_value": nbytes / eager_us / 1e3, "forwards_run": warmup + steps * (2 if use_graph else 1) + 1,
+    }
+    return res, (seq_lens, q_lens, bt, pages, x, scale)
+
+
+def cpu_baseline_append(base):
+    """The oracle's append on the host cores, on the first sequences' rows."""
+    import numpy as np
+
+    import oracle
+
+    seq_lens, q_lens, bt, pages, x, scale = base
+    sh = APPEND_SHAPE
+    bits = np.stack([x[w].astype(np.float32) for w in range(2)])
+    import torch
+    b16 = torch.from_numpy(bits).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    pool = np.zeros((pages, sh["hkv"], 16, sh["head_dim"]), dtype=np.uint8)
+    n_seq = 2
+    rows = n_seq * sh["rows"]
+    t0 = time.time()
+    reps = 0
+    while True:
+        oracle.append_kv(b16[0, :rows], b16[1, :rows], "bf16", pool, pool, "fp8_e4m3", bt[:n_seq], seq_lens[:n_seq],
+                         q_lens[:n_seq], scale, 16)
+        reps += 1
+        if time.time() - t0 > 10:
+            break
+    sec = time.time() - t0
+    nbytes = reps * 2 * rows * sh["hkv"] * sh["head_dim"] * 3
+    return {"value": nbytes / sec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} rows of {n_seq} sequences, {reps} repetitions", "seconds": sec}
+
+
 def profile_commands(workload: str, calib_mib: int = 512) -> list:
     """The rocprofv3 runs behind profiles/<kernel>_<workload>.md, from the
     repository root $REPO (counters in passes of their own, as the profiler
@@ -405,7 +519,10 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
-    res, base = measure(args.workload, args.steps, args.warmup, use_graph=not args.eager)
+    if args.workload == "append_fp8":
+        res, base = measure_append(args.steps, args.warmup, use_graph=not args.eager)
+    else:
+        res, base = measure(args.workload, args.steps, args.warmup, use_graph=not args.eager)
     line = {
         "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -429,7 +546,8 @@ def main():
                 per[w] = {"error": repr(e)}
         line["per_config"] = per
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(args.workload, base)
+        line["cpu_baseline"] = (cpu_baseline_append(base) if args.workload == "append_fp8"
+                                else cpu_baseline(args.workload, base))
     text = json.dumps(line)
     print(text, flush=True)
     if args.json_out:
