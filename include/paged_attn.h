@@ -235,7 +235,39 @@ int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int6
                       const int32_t* block_table, int32_t num_seqs, int32_t block_table_stride,
                       const int32_t* seq_lens, const int32_t* q_lens, const float* kv_scale, void* stream);
 
-/* paged_attn_version: library version, e.g. "0.1.0". */
+/*
+ * paged_attn_forward_noalloc: paged_attn_forward for callers that cannot
+ * allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It takes the configuration
+ * instead of a handle and allocates nothing: its split partials, merge
+ * descriptors and counters live in one fixed device array of
+ * PA_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends (set up on the first call on a device).
+ *
+ *  cfg          host, validated as in paged_attn_create (default tuning).
+ *  other arguments as in paged_attn_forward; the result is the same as a
+ *               handle created from cfg would give.
+ *
+ * Each call first zeroes, with a small kernel on `stream`, the counters the
+ * kernels expect at zero.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (concurrent streams, threads) race and give
+ * wrong results; serialise them.  A configuration whose workspace exceeds
+ * the array -- prefill-sized row counts, large batches -- is rejected with
+ * PA_ERR_UNSUPPORTED and a message naming the size it needs; decode and
+ * verification widths of the usual head counts fit.  Errors are reported by
+ * paged_attn_last_error(NULL) on the calling thread.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int paged_attn_forward_noalloc(const pa_config_t* cfg,
+                               const void* q, int64_t num_tokens,
+                               const void* k_cache, const void* v_cache,
+                               const pa_cache_layout_t* layout,
+                               const int32_t* block_table, int32_t num_seqs, int32_t block_table_stride,
+                               const int32_t* seq_lens, const int32_t* q_lens,
+                               int32_t window, float scale, const float* kv_scale,
+                               float* out, float* lse, void* stream);
+
+/* paged_attn_version: library version, e.g. "0.2.0". */
 const char* paged_attn_version(void);
 
 #ifdef __cplusplus

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     paged_attn_append,
     paged_attn_destroy,
     paged_attn_forward,
+    paged_attn_forward_noalloc,
     paged_attn_last_error,
     paged_attn_set_tuning,
     paged_attn_version,

@@ -108,6 +108,10 @@ def load_library() -> ctypes.CDLL:
         vp, vp, vp, ctypes.c_int64, vp, vp, ctypes.POINTER(pa_cache_layout_t), vp, ctypes.c_int32, ctypes.c_int32,
         vp, vp, vp, vp]
     lib.paged_attn_append.restype = ctypes.c_int
+    lib.paged_attn_forward_noalloc.argtypes = [
+        ctypes.POINTER(pa_config_t), vp, i64, vp, vp, ctypes.POINTER(pa_cache_layout_t), vp, i32, i32, vp, vp, i32,
+        f32, vp, vp, vp, vp]
+    lib.paged_attn_forward_noalloc.restype = ctypes.c_int
     lib.paged_attn_version.argtypes = []
     lib.paged_attn_version.restype = ctypes.c_char_p
     _lib = lib
@@ -194,6 +198,20 @@ def cache_layout(k_cache) -> pa_cache_layout_t:
     return pa_cache_layout_t(k_cache.shape[0], k_cache.stride(0), k_cache.stride(1), k_cache.stride(2))
 
 
+_FLOAT16_NAMES = {PA_DTYPE_F16: "float16", PA_DTYPE_BF16: "bfloat16"}
+
+
+def _check_16bit(name: str, t, q_dtype: int):
+    """A 16-bit input must be raw 16-bit storage (int16/uint16 bits) or the
+    handle's own floating type: f16 rows given to a bf16 handle (or the
+    reverse) would be reinterpreted, so they are refused."""
+    if t.element_size() != 2:
+        raise ValueError(f"{name} must have 2-byte elements")
+    kind = str(t.dtype).replace("torch.", "")
+    if kind in ("float16", "bfloat16") and kind != _FLOAT16_NAMES[q_dtype]:
+        raise ValueError(f"{name} is {kind} but the handle's q_dtype is {_FLOAT16_NAMES[q_dtype]}")
+
+
 def _check_cache(h: Handle, k_cache):
     c = h.cfg
     if k_cache.element_size() != ELEM_BYTES[c.kv_dtype]:
@@ -203,14 +221,11 @@ def _check_cache(h: Handle, k_cache):
                          f"{c.page_size}, {c.head_dim}]")
 
 
-def paged_attn_forward(h: Handle, q, k_cache, v_cache, block_table, seq_lens, q_lens, window: int, scale: float,
-                       kv_scale, out, lse=None, stream=None) -> None:
-    """Enqueue paged attention; see include/paged_attn.h for the contract."""
+def _check_forward_args(h, q, k_cache, v_cache, block_table, out, lse):
     c = h.cfg
     if q.dim() != 3 or tuple(q.shape[1:]) != (c.num_q_heads, c.head_dim) or not q.is_contiguous():
         raise ValueError("q must be a contiguous [T, Hq, D] tensor")
-    if q.element_size() != 2:
-        raise ValueError("q must have 2-byte elements")
+    _check_16bit("q", q, c.q_dtype)
     if tuple(out.shape) != tuple(q.shape) or not out.is_contiguous() or out.element_size() != 4:
         raise ValueError("out must be a contiguous fp32 [T, Hq, D] tensor")
     if lse is not None and (tuple(lse.shape) != tuple(q.shape[:2]) or not lse.is_contiguous()):
@@ -220,12 +235,39 @@ def paged_attn_forward(h: Handle, q, k_cache, v_cache, block_table, seq_lens, q_
         raise ValueError("v_cache must match k_cache in shape and strides")
     if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.element_size() != 4:
         raise ValueError("block_table must be int32 [num_seqs, width] with unit column stride")
+
+
+def paged_attn_forward(h: Handle, q, k_cache, v_cache, block_table, seq_lens, q_lens, window: int, scale: float,
+                       kv_scale, out, lse=None, stream=None) -> None:
+    """Enqueue paged attention; see include/paged_attn.h for the contract."""
+    _check_forward_args(h, q, k_cache, v_cache, block_table, out, lse)
     layout = cache_layout(k_cache)
     rc = load_library().paged_attn_forward(
         h.ptr, _ptr(q), q.shape[0], _ptr(k_cache), _ptr(v_cache), ctypes.byref(layout), _ptr(block_table),
         seq_lens.shape[0], block_table.stride(0), _ptr(seq_lens), _ptr(q_lens), int(window), float(scale),
         _ptr(kv_scale), _ptr(out), _ptr(lse), _stream_ptr(stream))
     _check(rc, h.ptr)
+
+
+class _CfgView:
+    """What the argument checks read from a handle: its configuration."""
+
+    def __init__(self, cfg: pa_config_t):
+        self.cfg = cfg
+        self.ptr = None
+
+
+def paged_attn_forward_noalloc(cfg: pa_config_t, q, k_cache, v_cache, block_table, seq_lens, q_lens, window: int,
+                               scale: float, kv_scale, out, lse=None, stream=None) -> None:
+    """Enqueue the forward that allocates nothing (fixed device array); see
+    include/paged_attn.h.  Errors come from paged_attn_last_error(None)."""
+    _check_forward_args(_CfgView(cfg), q, k_cache, v_cache, block_table, out, lse)
+    layout = cache_layout(k_cache)
+    rc = load_library().paged_attn_forward_noalloc(
+        ctypes.byref(cfg), _ptr(q), q.shape[0], _ptr(k_cache), _ptr(v_cache), ctypes.byref(layout),
+        _ptr(block_table), seq_lens.shape[0], block_table.stride(0), _ptr(seq_lens), _ptr(q_lens), int(window),
+        float(scale), _ptr(kv_scale), _ptr(out), _ptr(lse), _stream_ptr(stream))
+    _check(rc, None)
 
 
 def paged_attn_debug_gather(h: Handle, k_cache, block_table, seq_lens, q_lens, window: int, slots_out, rows_out,
@@ -246,8 +288,7 @@ def paged_attn_append(h: Handle, k_new, v_new, k_cache, v_cache, block_table, se
     for name, t in (("k_new", k_new), ("v_new", v_new)):
         if t.dim() != 3 or tuple(t.shape[1:]) != (c.num_kv_heads, c.head_dim) or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [T, Hkv, D] tensor")
-        if t.element_size() != 2:
-            raise ValueError(f"{name} must have 2-byte elements")
+        _check_16bit(name, t, c.q_dtype)
     if v_new.shape != k_new.shape:
         raise ValueError("v_new must match k_new")
     _check_cache(h, k_cache)

@@ -10,52 +10,16 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
-#include <string>
 
 #include "paged_attn.h"
+#include "pa_host.h"
 #include "pa_kernels.h"
 
-struct pa_handle {
-    pa_config_t cfg;
-    pa_tuning_t tune;
-    int cu_count = 0;
-    int grid_default = 0;
-    int max_items_valu = 0;  // split-partial slots of the VALU kernel
-    int r_max_valu = 0;      // rows per VALU slot (largest rows-per-KV-head it may handle)
-    bool valu_all_ok = false;  // the VALU kernel's slots hold every sequence's rows
-    int mfma_wr = 1;         // MFMA kernel: waves along rows (rows per item = 32 * mfma_wr)
-    int max_items_mfma = 0;
-    int mfma_grid = 0;       // tile-kernel workgroups: one per resident slot
-    int merge_rows = 0;      // largest row count of one merge group
-    int mfma_item_off = 0;   // first partial item of the tile kernel
-    int desc_cap = 0;        // merge descriptors the workspace holds
-    float* ws_o = nullptr;
-    float* ws_lse = nullptr;
-    pa::MergeDesc* mdesc = nullptr;   // merge groups published by the attention kernels
-    pa::MergeDesc* sdesc = nullptr;   // fixed merge slots for static splits (zeroed; each merge clears what it used)
-    int* arrive = nullptr;            // per-group arrival counters for static splits merged in-kernel (zeroed; the last arrival clears its own)
-    int sdesc_upg = 1;                // merge units per (sequence, KV head) group in sdesc
-    int64_t sdesc_groups = 0;         // groups sdesc holds
-    int* mcount = nullptr;            // [0] groups published, [1] merge workgroups done
-    void* ws = nullptr;
-    size_t ws_bytes = 0;
-    std::string err;
-};
+namespace pa {
 
 namespace {
 
-thread_local std::string g_err;
-
-int fail(pa_handle* h, int code, const char* fmt, ...) __attribute__((format(printf, 3, 4)));
-int fail(pa_handle* h, int code, const char* fmt, ...) {
-    char buf[512];
-    va_list ap;
-    va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
-    va_end(ap);
-    if (h) h->err = buf; else g_err = buf;
-    return code;
-}
+thread_local char g_err[512];
 
 int elem_bytes(int dt) { return dt == PA_DTYPE_FP8_E4M3 ? 1 : 2; }
 
@@ -71,9 +35,25 @@ constexpr int kMinPagesPerSplit = 4;
 constexpr int kValuRowsMax = 8;   // rows per KV head handled by the VALU kernel under PA_PATH_AUTO
 constexpr int kValuMaxKeys = 16384;   // and visible keys (longer contexts go to the tile kernel)
 
-int validate_config(const pa_config_t* c, std::string* why) {
-    char buf[256];
-    auto bad = [&](int code, const char* msg) { *why = msg; return code; };
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+int fail(pa_handle* h, int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(h ? h->err : g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+const char* thread_error() { return g_err; }
+
+int validate_config(const pa_config_t* c, char* why, size_t why_len) {
+    auto bad = [&](int code, const char* msg) {
+        snprintf(why, why_len, "%s", msg);
+        return code;
+    };
     if (!c) return bad(PA_ERR_INVALID_ARGUMENT, "config is NULL");
     if (c->num_q_heads < 1 || c->num_kv_heads < 1) return bad(PA_ERR_INVALID_ARGUMENT, "head counts must be >= 1");
     if (c->num_q_heads % c->num_kv_heads) return bad(PA_ERR_INVALID_ARGUMENT, "num_q_heads % num_kv_heads != 0");
@@ -98,52 +78,14 @@ int validate_config(const pa_config_t* c, std::string* why) {
         return bad(PA_ERR_UNSUPPORTED, "max_q_len * group too large");
     if (c->flags != 0) return bad(PA_ERR_INVALID_ARGUMENT, "flags must be 0");
     if (c->device < 0) return bad(PA_ERR_INVALID_ARGUMENT, "device must be >= 0");
-    (void)buf;
     return PA_OK;
 }
 
-struct DeviceGuard {
-    int prev = -1;
-    bool ok = false;
-    explicit DeviceGuard(int dev) {
-        if (hipGetDevice(&prev) != hipSuccess) return;
-        ok = hipSetDevice(dev) == hipSuccess;
-    }
-    ~DeviceGuard() {
-        if (prev >= 0) (void)hipSetDevice(prev);
-    }
-};
-
-}  // namespace
-
-extern "C" {
-
-const char* paged_attn_version(void) { return "0.1.0"; }
-
-const char* paged_attn_last_error(const pa_handle_t* h) { return h ? h->err.c_str() : g_err.c_str(); }
-
-int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
-    if (!out) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "out is NULL");
-    *out = nullptr;
-    std::string why;
-    int rc = validate_config(cfg, &why);
-    if (rc != PA_OK) return fail(nullptr, rc, "%s", why.c_str());
-
-    int ndev = 0;
-    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= cfg->device)
-        return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "device %d not present (%d devices)", cfg->device, ndev);
-    DeviceGuard guard(cfg->device);
-    if (!guard.ok) return fail(nullptr, PA_ERR_HIP, "hipSetDevice(%d) failed", cfg->device);
-
-    pa_handle* h = new (std::nothrow) pa_handle();
-    if (!h) return fail(nullptr, PA_ERR_OUT_OF_MEMORY, "host allocation failed");
+void size_handle(pa_handle* h, const pa_config_t* cfg, int cu_count) {
     h->cfg = *cfg;
     std::memset(&h->tune, 0, sizeof h->tune);
-    if (hipDeviceGetAttribute(&h->cu_count, hipDeviceAttributeMultiprocessorCount, cfg->device) != hipSuccess ||
-        h->cu_count <= 0)
-        h->cu_count = 256;
+    h->cu_count = cu_count > 0 ? cu_count : 256;
     h->grid_default = 2 * h->cu_count;
-
     const int G = cfg->num_q_heads / cfg->num_kv_heads;
     const int D = cfg->head_dim;
     const int64_t rows_max = (int64_t)cfg->max_q_len * G;
@@ -159,81 +101,70 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
     h->mfma_wr = rows_max > 64 ? (cfg->kv_dtype == PA_DTYPE_FP8_E4M3 ? 4 : 8) : 1;
     // The tile kernel launches exactly one round of resident workgroups; its
     // in-kernel plan sizes the splits for that many items.
-    h->mfma_grid = D == 128 ? h->cu_count * pa::mfma_blocks_per_cu(cfg->kv_dtype, cfg->q_dtype, h->mfma_wr,
-                                                                    cfg->max_num_seqs)
+    h->mfma_grid = D == 128 ? h->cu_count * mfma_blocks_per_cu(cfg->kv_dtype, cfg->q_dtype, h->mfma_wr,
+                                                                cfg->max_num_seqs)
                             : h->cu_count;
     const int bm = 32 * h->mfma_wr;
     const int64_t qblocks = ((int64_t)cfg->max_num_tokens * G + bm - 1) / bm + cfg->max_num_seqs;
     h->max_items_mfma = (int)std::min<int64_t>((int64_t)1 << 30, grid_cap + qblocks * cfg->num_kv_heads);
     h->merge_rows = (int)std::max<int64_t>(h->r_max_valu, D == 128 ? bm : 0);
+    // Fixed slots for the VALU kernel's static splits (at most 8 workgroups
+    // per CU, so at most that many (sequence, KV head) groups).
+    h->sdesc_upg = (h->r_max_valu + merge_rows_per_unit(D) - 1) / merge_rows_per_unit(D);
+    h->sdesc_groups = std::min<int64_t>((int64_t)cfg->max_num_seqs * cfg->num_kv_heads, (int64_t)8 * h->cu_count);
+}
+
+WsLayout layout_workspace(const pa_handle* h, bool valu, bool mfma) {
+    const int D = h->cfg.head_dim;
+    mfma = mfma && D == 128;
+    const int bm = 32 * h->mfma_wr;
+    WsLayout L{};
     // The two kernels' partials live side by side until the merge launch: VALU
     // slots first, then the tile kernel's, starting at a whole tile item.
-    const size_t valu_slots = ((size_t)h->max_items_valu * h->r_max_valu + bm - 1) / bm * bm;
-    h->mfma_item_off = (int)(valu_slots / bm);
-    const size_t slots = valu_slots + (D == 128 ? (size_t)h->max_items_mfma * bm : (size_t)0);
+    const size_t valu_slots = valu ? ((size_t)h->max_items_valu * h->r_max_valu + bm - 1) / bm * bm : 0;
+    L.mfma_item_off = (int)(valu_slots / bm);
+    const size_t slots = valu_slots + (mfma ? (size_t)h->max_items_mfma * bm : (size_t)0);
     const size_t o_bytes = slots * D * sizeof(float);
     const size_t l_bytes = slots * sizeof(float);
     // a merge group has at least two items
-    h->desc_cap = (int)std::max<size_t>(1, ((size_t)h->max_items_valu + (D == 128 ? (size_t)h->max_items_mfma : 0)) / 2);
-    const size_t d_bytes = (size_t)h->desc_cap * sizeof(pa::MergeDesc);
+    L.desc_cap = (int)std::max<size_t>(
+        1, ((valu ? (size_t)h->max_items_valu : 0) + (mfma ? (size_t)h->max_items_mfma : 0)) / 2);
+    const size_t d_bytes = (size_t)L.desc_cap * sizeof(MergeDesc);
     const size_t c_bytes = 2 * sizeof(int);
-    // Fixed slots for the VALU kernel's static splits (at most 8 workgroups
-    // per CU, so at most that many (sequence, KV head) groups).
-    h->sdesc_upg = (h->r_max_valu + pa::merge_rows_per_unit(D) - 1) / pa::merge_rows_per_unit(D);
-    h->sdesc_groups = std::min<int64_t>((int64_t)cfg->max_num_seqs * cfg->num_kv_heads, (int64_t)8 * h->cu_count);
-    const size_t s_bytes = (size_t)h->sdesc_groups * h->sdesc_upg * sizeof(pa::MergeDesc);
-    const size_t a_bytes = (size_t)h->sdesc_groups * sizeof(int);
-    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    h->ws_bytes = up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes) + up(s_bytes) + up(a_bytes);
-    if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
-        const size_t want = h->ws_bytes;
-        delete h;
-        (void)hipGetLastError();
-        return fail(nullptr, PA_ERR_OUT_OF_MEMORY, "workspace of %zu bytes could not be allocated", want);
-    }
-    char* p = static_cast<char*>(h->ws);
-    h->ws_o = reinterpret_cast<float*>(p);
-    h->ws_lse = reinterpret_cast<float*>(p + up(o_bytes));
-    h->mdesc = reinterpret_cast<pa::MergeDesc*>(p + up(o_bytes) + up(l_bytes));
-    h->mcount = reinterpret_cast<int*>(p + up(o_bytes) + up(l_bytes) + up(d_bytes));
-    h->sdesc = reinterpret_cast<pa::MergeDesc*>(p + up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes));
-    h->arrive = reinterpret_cast<int*>(p + up(o_bytes) + up(l_bytes) + up(d_bytes) + up(c_bytes) + up(s_bytes));
-    if (hipMemset(h->mcount, 0, up(c_bytes) + up(s_bytes) + up(a_bytes)) != hipSuccess ||
-        hipDeviceSynchronize() != hipSuccess) {
-        (void)hipFree(h->ws);
-        delete h;
-        return fail(nullptr, PA_ERR_HIP, "workspace clear failed");
-    }
-    *out = h;
-    return PA_OK;
+    const size_t s_bytes = valu ? (size_t)h->sdesc_groups * h->sdesc_upg * sizeof(MergeDesc) : 0;
+    const size_t a_bytes = valu ? (size_t)h->sdesc_groups * sizeof(int) : 0;
+    const size_t e_bytes = sizeof(int);
+    L.o_off = 0;
+    L.l_off = L.o_off + up256(o_bytes);
+    L.d_off = L.l_off + up256(l_bytes);
+    L.c_off = L.d_off + up256(d_bytes);
+    L.s_off = L.c_off + up256(c_bytes);
+    L.a_off = L.s_off + up256(s_bytes);
+    L.e_off = L.a_off + up256(a_bytes);
+    L.total = L.e_off + up256(e_bytes);
+    L.zero_begin = L.c_off;
+    L.zero_end = L.total;
+    return L;
 }
 
-void paged_attn_destroy(pa_handle_t* h) {
-    if (!h) return;
-    if (h->ws) {
-        DeviceGuard guard(h->cfg.device);
-        (void)hipFree(h->ws);
-    }
-    delete h;
+void bind_workspace(pa_handle* h, void* base, const WsLayout& L) {
+    char* p = static_cast<char*>(base);
+    h->ws_o = reinterpret_cast<float*>(p + L.o_off);
+    h->ws_lse = reinterpret_cast<float*>(p + L.l_off);
+    h->mdesc = reinterpret_cast<MergeDesc*>(p + L.d_off);
+    h->mcount = reinterpret_cast<int*>(p + L.c_off);
+    h->sdesc = reinterpret_cast<MergeDesc*>(p + L.s_off);
+    h->arrive = reinterpret_cast<int*>(p + L.a_off);
+    h->err_word = reinterpret_cast<int*>(p + L.e_off);
+    h->mfma_item_off = L.mfma_item_off;
+    h->desc_cap = L.desc_cap;
 }
 
-int paged_attn_set_tuning(pa_handle_t* h, const pa_tuning_t* t) {
-    if (!h) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "handle is NULL");
-    if (!t) {
-        std::memset(&h->tune, 0, sizeof h->tune);
-        return PA_OK;
-    }
-    if (t->path < PA_PATH_AUTO || t->path > PA_PATH_MFMA) return fail(h, PA_ERR_INVALID_ARGUMENT, "bad path %d", t->path);
-    if (t->path == PA_PATH_MFMA && h->cfg.head_dim != 128)
-        return fail(h, PA_ERR_UNSUPPORTED, "the MFMA path needs head_dim 128");
-    if (t->path == PA_PATH_VALU && !h->valu_all_ok)
-        return fail(h, PA_ERR_UNSUPPORTED, "the VALU path holds at most 64 rows per KV head");
-    if (t->pages_per_split < 0 || t->kv_tiles_per_split < 0 || t->grid < 0 || t->grid > 8 * h->cu_count ||
-        t->split_mode < 0 || t->split_mode > 2)
-        return fail(h, PA_ERR_INVALID_ARGUMENT, "tuning values out of range (grid <= %d)", 8 * h->cu_count);
-    h->tune = *t;
-    return PA_OK;
-}
+}  // namespace pa
+
+using namespace pa;
+
+namespace pa {
 
 static int validate_cache(pa_handle* h, const pa_cache_layout_t* L, const void* k, const void* v) {
     const pa_config_t& c = h->cfg;
@@ -250,42 +181,67 @@ static int validate_cache(pa_handle* h, const pa_cache_layout_t* L, const void* 
     return PA_OK;
 }
 
-int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const void* k_cache, const void* v_cache,
-                       const pa_cache_layout_t* layout, const int32_t* block_table, int32_t num_seqs,
-                       int32_t block_table_stride, const int32_t* seq_lens, const int32_t* q_lens, int32_t window,
-                       float scale, const float* kv_scale, float* out, float* lse, void* stream) {
-    if (!h) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "handle is NULL");
+int check_forward(pa_handle* h, const ForwardCall& f) {
     const pa_config_t& c = h->cfg;
-    if (!q || !out || !block_table || !seq_lens || !q_lens)
+    if (!f.q || !f.out || !f.block_table || !f.seq_lens || !f.q_lens)
         return fail(h, PA_ERR_INVALID_ARGUMENT, "q, out, block_table, seq_lens and q_lens must be non-NULL");
-    if (!aligned16(q) || !aligned16(out)) return fail(h, PA_ERR_INVALID_ARGUMENT, "q and out must be 16-byte aligned");
-    if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(h, PA_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
-    if (num_tokens < 1 || num_tokens > c.max_num_tokens)
-        return fail(h, PA_ERR_INVALID_ARGUMENT, "num_tokens %lld outside 1..%lld", (long long)num_tokens,
+    if (!aligned16(f.q) || !aligned16(f.out)) return fail(h, PA_ERR_INVALID_ARGUMENT, "q and out must be 16-byte aligned");
+    if (f.lse && (reinterpret_cast<uintptr_t>(f.lse) & 3u)) return fail(h, PA_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+    if (f.num_tokens < 1 || f.num_tokens > c.max_num_tokens)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "num_tokens %lld outside 1..%lld", (long long)f.num_tokens,
                     (long long)c.max_num_tokens);
-    if (num_seqs < 1 || num_seqs > c.max_num_seqs)
-        return fail(h, PA_ERR_INVALID_ARGUMENT, "num_seqs %d outside 1..%d", num_seqs, c.max_num_seqs);
-    if (block_table_stride < 1) return fail(h, PA_ERR_INVALID_ARGUMENT, "block_table_stride must be >= 1");
-    if (!std::isfinite(scale) || !(scale > 0.f)) return fail(h, PA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
-    if ((c.kv_dtype == PA_DTYPE_FP8_E4M3) != (kv_scale != nullptr))
+    if (f.num_seqs < 1 || f.num_seqs > c.max_num_seqs)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "num_seqs %d outside 1..%d", f.num_seqs, c.max_num_seqs);
+    if (f.bt_stride < 1) return fail(h, PA_ERR_INVALID_ARGUMENT, "block_table_stride must be >= 1");
+    if (!std::isfinite(f.scale) || !(f.scale > 0.f)) return fail(h, PA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
+    if ((c.kv_dtype == PA_DTYPE_FP8_E4M3) != (f.kv_scale != nullptr))
         return fail(h, PA_ERR_INVALID_ARGUMENT, "kv_scale is required for an fp8 cache and must be NULL otherwise");
-    int rc = validate_cache(h, layout, k_cache, v_cache);
-    if (rc != PA_OK) return rc;
+    return validate_cache(h, f.layout, f.k_cache, f.v_cache);
+}
 
-    DeviceGuard guard(c.device);
-    if (!guard.ok) return fail(h, PA_ERR_HIP, "hipSetDevice(%d) failed", c.device);
-
+// Each sequence goes to one kernel, decided on the device from its lengths:
+// a few rows per KV head over a short context stream K/V through the vector
+// ALUs (lowest latency); verification widths, prefill chunks and long
+// contexts go to the MFMA tile kernel, whose per-key VALU work is several
+// times smaller.  The host launches a kernel only if some sequence can
+// belong to it.
+LaunchPlan plan_launches(const pa_handle* h, const ForwardCall& f) {
+    const pa_config_t& c = h->cfg;
     const int G = c.num_q_heads / c.num_kv_heads;
-    pa::DecodeArgs a{};
-    a.q = q;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.block_table = block_table;
-    a.seq_lens = seq_lens;
-    a.q_lens = q_lens;
-    a.kv_scale = kv_scale;
-    a.out = out;
-    a.lse = lse;
+    const int rows_min = c.min_q_len * G, rows_max = c.max_q_len * G;
+    const int64_t cap_tokens = (int64_t)f.bt_stride * c.page_size;
+    LaunchPlan lp{};
+    if (c.head_dim != 128 || h->tune.path == PA_PATH_VALU) {
+        lp.run_valu = true;
+        lp.run_mfma = false;
+    } else if (h->tune.path == PA_PATH_MFMA) {
+        lp.run_valu = false;
+        lp.run_mfma = true;
+    } else {
+        lp.run_valu = rows_min <= kValuRowsMax;
+        lp.run_mfma = rows_max > kValuRowsMax || cap_tokens > kValuMaxKeys;
+        // A tile launch with 32-row items takes the few-row sequences as well:
+        // a VALU launch before it on the same stream would add its whole
+        // latency, and per key the tile kernel costs less.  (With prefill-sized
+        // items a few-row sequence would fill a small part of each tile.)
+        if (lp.run_mfma && h->mfma_wr == 1) lp.run_valu = false;
+    }
+    return lp;
+}
+
+int enqueue_forward(pa_handle* h, const ForwardCall& f, const LaunchPlan& lp) {
+    const pa_config_t& c = h->cfg;
+    const int G = c.num_q_heads / c.num_kv_heads;
+    DecodeArgs a{};
+    a.q = f.q;
+    a.k_cache = f.k_cache;
+    a.v_cache = f.v_cache;
+    a.block_table = f.block_table;
+    a.seq_lens = f.seq_lens;
+    a.q_lens = f.q_lens;
+    a.kv_scale = f.kv_scale;
+    a.out = f.out;
+    a.lse = f.lse;
     a.ws_o = h->ws_o;
     a.ws_lse = h->ws_lse;
     a.mdesc = h->mdesc;
@@ -293,47 +249,29 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     a.sdesc = nullptr;
     a.sdesc_upg = h->sdesc_upg;
     a.arrive = nullptr;
-    a.page_stride = layout->page_stride;
-    a.head_stride = layout->head_stride;
-    a.token_stride = layout->token_stride;
-    a.num_seqs = num_seqs;
-    a.bt_stride = block_table_stride;
+    a.page_stride = f.layout->page_stride;
+    a.head_stride = f.layout->head_stride;
+    a.token_stride = f.layout->token_stride;
+    a.num_seqs = f.num_seqs;
+    a.bt_stride = f.bt_stride;
     a.num_q_heads = c.num_q_heads;
     a.num_kv_heads = c.num_kv_heads;
     a.group = G;
-    a.window = window;
-    a.scale = scale;
+    a.window = f.window;
+    a.scale = f.scale;
     const int grid = h->tune.grid > 0 ? h->tune.grid : h->grid_default;
     a.target_items = grid;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-
-    // Each sequence goes to one kernel, decided on the device from its
-    // lengths: a few rows per KV head over a short context stream K/V through
-    // the vector ALUs (lowest latency); verification widths, prefill chunks
-    // and long contexts go to the MFMA tile kernel, whose per-key VALU work is
-    // several times smaller.  The host launches a kernel only if some
-    // sequence can belong to it.
-    const int rows_min = c.min_q_len * G, rows_max = c.max_q_len * G;
-    const int64_t cap_tokens = (int64_t)block_table_stride * c.page_size;
-    bool run_valu, run_mfma;
+    hipStream_t st = f.stream;
+    const int num_seqs = f.num_seqs;
+    const int window = f.window;
+    const int32_t block_table_stride = f.bt_stride;
+    const bool run_valu = lp.run_valu, run_mfma = lp.run_mfma;
     if (c.head_dim != 128 || h->tune.path == PA_PATH_VALU) {
-        run_valu = true; run_mfma = false;
         a.cls_rows = 1 << 30; a.cls_len = 1 << 30;
-    } else if (h->tune.path == PA_PATH_MFMA) {
-        run_valu = false; run_mfma = true;
+    } else if (h->tune.path == PA_PATH_MFMA || (run_mfma && h->mfma_wr == 1)) {
         a.cls_rows = 0; a.cls_len = 0;
     } else {
         a.cls_rows = kValuRowsMax; a.cls_len = kValuMaxKeys;
-        run_valu = rows_min <= kValuRowsMax;
-        run_mfma = rows_max > kValuRowsMax || cap_tokens > kValuMaxKeys;
-        // A tile launch with 32-row items takes the few-row sequences as well:
-        // a VALU launch before it on the same stream would add its whole
-        // latency, and per key the tile kernel costs less.  (With prefill-sized
-        // items a few-row sequence would fill a small part of each tile.)
-        if (run_mfma && h->mfma_wr == 1) {
-            run_valu = false;
-            a.cls_rows = 0; a.cls_len = 0;
-        }
     }
     bool need_merge_valu = run_valu;
     if (run_valu) {
@@ -408,7 +346,7 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
     if (static_merge && need_merge_valu) {
         // one workgroup per fixed slot; empty slots leave at once
         const int64_t su = (int64_t)num_seqs * c.num_kv_heads * h->sdesc_upg;
-        pa::MergeArgs m{h->ws_o,   h->ws_lse,   h->mdesc,     h->mcount,    out,         lse,
+        pa::MergeArgs m{h->ws_o,   h->ws_lse,   h->mdesc,     h->mcount,    f.out,       f.lse,
                         c.num_q_heads, G,       h->merge_rows, h->desc_cap, h->sdesc, (int)su,
                         h->sdesc_upg,  static_splits, h->r_max_valu};
         hipError_t e = pa::launch_merge(m, c.head_dim, (int)su, 32, st);
@@ -422,7 +360,7 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         if (need_merge_valu) groups += (int64_t)num_seqs * c.num_kv_heads;
         if (run_mfma) {
             const int bm = pa::mfma_rows_per_item(h->mfma_wr);
-            groups += (int64_t)c.num_kv_heads * ((num_tokens * G + bm - 1) / bm + num_seqs);
+            groups += (int64_t)c.num_kv_heads * ((f.num_tokens * G + bm - 1) / bm + num_seqs);
         }
         // Many units (prefill): the low-register variant, four workgroups per
         // CU (every workgroup also takes one turn on the shared arrival
@@ -433,12 +371,99 @@ int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const 
         const bool many = units > 4 * (int64_t)h->cu_count;
         const int mgrid = (int)std::max<int64_t>(1, std::min<int64_t>((many ? 4 : 2) * (int64_t)h->cu_count, units));
         const int batch = many ? 8 : (mgrid > h->cu_count ? 16 : 32);
-        pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, out, lse, c.num_q_heads, G, h->merge_rows,
+        pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, f.out, f.lse, c.num_q_heads, G, h->merge_rows,
                         h->desc_cap, nullptr, 0, 1, 0, 0};
         hipError_t e = pa::launch_merge(m, c.head_dim, mgrid, batch, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
     }
     return PA_OK;
+}
+
+}  // namespace pa
+
+extern "C" {
+
+const char* paged_attn_version(void) { return "0.2.0"; }
+
+const char* paged_attn_last_error(const pa_handle_t* h) { return h ? h->err : pa::thread_error(); }
+
+int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
+    if (!out) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "out is NULL");
+    *out = nullptr;
+    char why[256];
+    int rc = validate_config(cfg, why, sizeof why);
+    if (rc != PA_OK) return fail(nullptr, rc, "%s", why);
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= cfg->device)
+        return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "device %d not present (%d devices)", cfg->device, ndev);
+    DeviceGuard guard(cfg->device);
+    if (!guard.ok) return fail(nullptr, PA_ERR_HIP, "hipSetDevice(%d) failed", cfg->device);
+
+    pa_handle* h = new (std::nothrow) pa_handle();
+    if (!h) return fail(nullptr, PA_ERR_OUT_OF_MEMORY, "host allocation failed");
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, cfg->device) != hipSuccess) cu = 0;
+    size_handle(h, cfg, cu);
+    // The handle's workspace holds the partials of both kernels.
+    const WsLayout L = layout_workspace(h, true, true);
+    h->ws_bytes = L.total;
+    if (hipMalloc(&h->ws, h->ws_bytes) != hipSuccess) {
+        const size_t want = h->ws_bytes;
+        delete h;
+        (void)hipGetLastError();
+        return fail(nullptr, PA_ERR_OUT_OF_MEMORY, "workspace of %zu bytes could not be allocated", want);
+    }
+    bind_workspace(h, h->ws, L);
+    if (hipMemset(static_cast<char*>(h->ws) + L.zero_begin, 0, L.zero_end - L.zero_begin) != hipSuccess ||
+        hipDeviceSynchronize() != hipSuccess) {
+        (void)hipFree(h->ws);
+        delete h;
+        return fail(nullptr, PA_ERR_HIP, "workspace clear failed");
+    }
+    *out = h;
+    return PA_OK;
+}
+
+void paged_attn_destroy(pa_handle_t* h) {
+    if (!h) return;
+    if (h->ws) {
+        DeviceGuard guard(h->cfg.device);
+        (void)hipFree(h->ws);
+    }
+    delete h;
+}
+
+int paged_attn_set_tuning(pa_handle_t* h, const pa_tuning_t* t) {
+    if (!h) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "handle is NULL");
+    if (!t) {
+        std::memset(&h->tune, 0, sizeof h->tune);
+        return PA_OK;
+    }
+    if (t->path < PA_PATH_AUTO || t->path > PA_PATH_MFMA) return fail(h, PA_ERR_INVALID_ARGUMENT, "bad path %d", t->path);
+    if (t->path == PA_PATH_MFMA && h->cfg.head_dim != 128)
+        return fail(h, PA_ERR_UNSUPPORTED, "the MFMA path needs head_dim 128");
+    if (t->path == PA_PATH_VALU && !h->valu_all_ok)
+        return fail(h, PA_ERR_UNSUPPORTED, "the VALU path holds at most 64 rows per KV head");
+    if (t->pages_per_split < 0 || t->kv_tiles_per_split < 0 || t->grid < 0 || t->grid > 8 * h->cu_count ||
+        t->split_mode < 0 || t->split_mode > 2)
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "tuning values out of range (grid <= %d)", 8 * h->cu_count);
+    h->tune = *t;
+    return PA_OK;
+}
+
+int paged_attn_forward(pa_handle_t* h, const void* q, int64_t num_tokens, const void* k_cache, const void* v_cache,
+                       const pa_cache_layout_t* layout, const int32_t* block_table, int32_t num_seqs,
+                       int32_t block_table_stride, const int32_t* seq_lens, const int32_t* q_lens, int32_t window,
+                       float scale, const float* kv_scale, float* out, float* lse, void* stream) {
+    if (!h) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "handle is NULL");
+    const ForwardCall f{q,        num_tokens, k_cache,  v_cache, layout, block_table, num_seqs, block_table_stride,
+                        seq_lens, q_lens,     window,   scale,   kv_scale, out,       lse,      static_cast<hipStream_t>(stream)};
+    int rc = check_forward(h, f);
+    if (rc != PA_OK) return rc;
+    DeviceGuard guard(h->cfg.device);
+    if (!guard.ok) return fail(h, PA_ERR_HIP, "hipSetDevice(%d) failed", h->cfg.device);
+    return enqueue_forward(h, f, plan_launches(h, f));
 }
 
 int paged_attn_debug_gather(pa_handle_t* h, const void* k_cache, const pa_cache_layout_t* layout,

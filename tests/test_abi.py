@@ -23,7 +23,7 @@ def test_exports_every_declared_function():
 
 
 def test_version():
-    assert pal.paged_attn_version() == "0.1.0"
+    assert pal.paged_attn_version() == "0.2.0"
 
 
 def _cfg(**kw):
