@@ -76,123 +76,191 @@ def load_traffic(workload: str):
     return ent.get("hbm_bytes_per_launch")
 
 
-def measure(workload: str, steps: int, warmup: int, use_graph: bool = True):
-    import numpy as np
+PATHS = {"auto": 0, "valu": 1, "mfma": 2}
+# Workloads measured on the VALU path as well as on the automatic (MFMA tile) one.
+ALT_PATH_WORKLOADS = ("verify", "mixed_fp8")
+# Timed regions per measurement: the median is reported, and the spread
+# (max - min) / median across them ("run it three times, watch the drift").
+REPEATS = 3
+WARM_REPLAYS = 3   # untimed replays of the captured graph before the timed ones (clocks settle)
+
+
+class Prepared:
+    """One workload's inputs on the device: rotating copies of the batch at
+    disjoint physical pages in one pool."""
+
+    def __init__(self, workload: str):
+        import torch
+
+        from synth import named
+        from synth.gen import replicate
+        from synth.torch_upload import upload_batch, upload_pool
+
+        t0 = time.time()
+        self.workload = workload
+        self.base = named(workload)[0]
+        self.kv_bytes = self.base.kv_bytes()
+        self.flops = self.base.flops()
+        self.copies = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / self.kv_bytes)))
+        batches = replicate(self.base, self.copies, seed=1)
+        self.pools = upload_pool(batches)
+        self.devs = [upload_batch(b) for b in batches]
+        b = self.base
+        self.out = torch.empty((b.num_tokens, b.num_q_heads, b.head_dim), dtype=torch.float32, device="cuda")
+        self.lse = torch.empty((b.num_tokens, b.num_q_heads), dtype=torch.float32, device="cuda")
+        log(f"[bench] {workload}: inputs ready in {time.time() - t0:.1f}s ({self.copies} rotating copies, "
+            f"{self.kv_bytes / 1e6:.2f} MB KV per step)")
+
+    def handle(self, path: str = "auto"):
+        import paged_attention_long_amd as pal
+
+        b = self.base
+        pos = b.q_lens[b.q_lens > 0]
+        cfg = pal.make_config(b.num_q_heads, b.num_kv_heads, b.head_dim, b.q_dtype, b.kv_dtype, b.num_seqs,
+                              int(b.q_lens.max()), b.num_tokens, min_q_len=int(pos.min()))
+        h = pal.paged_attn_create(cfg)
+        if path != "auto":
+            pal.paged_attn_set_tuning(h, path=PATHS[path])
+        return h
+
+    def step(self, h, i: int):
+        import torch
+
+        import paged_attention_long_amd as pal
+
+        d = self.devs[i % self.copies]
+        pal.paged_attn_forward(h, d["q"], self.pools["k"], self.pools["v"], d["block_table"], d["seq_lens"],
+                               d["q_lens"], self.base.window, self.base.scale, d["kv_scale"], self.out, self.lse,
+                               stream=torch.cuda.current_stream())
+
+    def free(self):
+        import torch
+
+        self.pools = self.devs = self.out = self.lse = None
+        torch.cuda.empty_cache()
+
+
+def _timed(fn):
+    """Wall clock and HIP-event time of fn(), synchronised on both sides; the
+    events are recorded on the stream the forwards are launched on."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return time.perf_counter() - w0, e0.elapsed_time(e1) * 1e-3
+
+
+def time_path(prep: Prepared, path: str, steps: int, warmup: int, repeats: int = REPEATS, graph: bool = True):
+    """Warm-up forwards, one eager timed region, then `repeats` timed replays
+    of a HIP graph holding `steps` forwards (no host launch cost between
+    them); with graph=False, `repeats` eager timed regions instead.  Returns
+    per-forward times in microseconds."""
     import torch
 
     import paged_attention_long_amd as pal
-    from synth import named
-    from synth.gen import replicate
-    from synth.torch_upload import upload_batch, upload_pool
 
-    t0 = time.time()
-    base = named(workload)[0]
-    kv_bytes = base.kv_bytes()
-    flops = base.flops()
-    copies = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / kv_bytes)))
-    batches = replicate(base, copies, seed=1)
-    pools = upload_pool(batches)
-    devs = [upload_batch(b) for b in batches]
-    log(f"[bench] {workload}: inputs ready in {time.time() - t0:.1f}s ({copies} rotating copies, "
-        f"{kv_bytes / 1e6:.2f} MB KV per step)")
-
-    pos = base.q_lens[base.q_lens > 0]
-    cfg = pal.make_config(base.num_q_heads, base.num_kv_heads, base.head_dim, base.q_dtype, base.kv_dtype,
-                          base.num_seqs, int(base.q_lens.max()), base.num_tokens, min_q_len=int(pos.min()))
-    h = pal.paged_attn_create(cfg)
-    out = torch.empty((base.num_tokens, base.num_q_heads, base.head_dim), dtype=torch.float32, device="cuda")
-    lse = torch.empty((base.num_tokens, base.num_q_heads), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        d = devs[i % copies]
-        pal.paged_attn_forward(h, d["q"], pools["k"], pools["v"], d["block_table"], d["seq_lens"], d["q_lens"],
-                               base.window, base.scale, d["kv_scale"], out, lse,
-                               stream=torch.cuda.current_stream())
-
-    def timed(fn):
-        """Wall clock and HIP-event time of fn(), synchronised on both sides."""
-        stream = torch.cuda.current_stream()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    h = prep.handle(path)
+    try:
+        for i in range(warmup):
+            prep.step(h, i)
         torch.cuda.synchronize()
-        w0 = time.perf_counter()
-        e0.record(stream)
-        fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return time.perf_counter() - w0, e0.elapsed_time(e1) * 1e-3
-
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # Eager: one launch per step from Python.
-    eager_wall, eager_ev = timed(lambda: [step(warmup + i) for i in range(steps)])
-    graph_wall = graph_ev = None
-    if use_graph:
-        # The same K steps captured once into a HIP graph and replayed: no
-        # host launch cost between the forwards.
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(steps):
-                step(i)
-        g.replay()
-        torch.cuda.synchronize()
-        graph_wall, graph_ev = timed(g.replay)
-    pal.paged_attn_destroy(h)
-    assert torch.isfinite(out).all().item(), "non-finite output"
-
-    wall = graph_wall if use_graph else eager_wall
-    k_mean = (graph_ev if use_graph else eager_ev) / steps
-    if workload == "prefill":
-        unit = "TFLOP/s"
-        value = flops * steps / wall / 1e12
-        achieved = flops / k_mean / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": achieved / BF16_MFMA_PEAK_TFS}
-    else:
-        unit = "GB/s"
-        value = kv_bytes * steps / wall / 1e9
-        achieved = kv_bytes / k_mean / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBS}
-    roof["traffic"] = load_traffic(workload)
-    # A forward is the attention launch(es) plus the split-merge launch; the
-    # events bracket whole forwards, so achieved and traffic are per forward.
-    roof["scope"] = "one forward: attention kernel(s) + split-merge kernel, HIP events over the timed region / steps"
-    work = flops if workload == "prefill" else kv_bytes
-    res = {
-        "value": value, "unit": unit, "ms_per_step": wall / steps * 1e3, "roofline": roof,
-        "forward_us": {"graph_events": graph_ev / steps * 1e6 if use_graph else None,
-                       "eager_events": eager_ev / steps * 1e6, "eager_wall": eager_wall / steps * 1e6},
-        "eager_value": work * steps / eager_wall / (1e12 if workload == "prefill" else 1e9),
-        "timing": "graph replay of the timed steps" if use_graph else "eager launches",
-        "forwards_run": warmup + steps + (2 * steps if use_graph else 0),
-        "kv_bytes_per_step": kv_bytes, "flops_per_step": flops, "rotating_copies": copies,
-        "dtype": DTYPE_NAME[base.kv_dtype],
+        eager_wall, eager_ev = _timed(lambda: [prep.step(h, warmup + i) for i in range(steps)])
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    prep.step(h, i)
+            for _ in range(WARM_REPLAYS):
+                g.replay()
+            torch.cuda.synchronize()
+            runs = [_timed(g.replay) for _ in range(repeats)]
+            del g
+        else:
+            runs = [(eager_wall, eager_ev)] + [
+                _timed(lambda: [prep.step(h, i) for i in range(steps)]) for _ in range(repeats - 1)]
+    finally:
+        pal.paged_attn_destroy(h)
+    assert torch.isfinite(prep.out).all().item(), f"{prep.workload}/{path}: non-finite output"
+    walls = sorted(w / steps * 1e6 for w, _ in runs)
+    evs = [e / steps * 1e6 for _, e in runs]
+    ev_sorted = sorted(evs)
+    med_ev = ev_sorted[len(ev_sorted) // 2]
+    return {
+        "path": path,
+        "graph_event_us": med_ev,
+        "graph_event_runs_us": evs,
+        "graph_wall_us": walls[len(walls) // 2],
+        "spread": (ev_sorted[-1] - ev_sorted[0]) / med_ev,
+        "eager_event_us": eager_ev / steps * 1e6,
+        "eager_wall_us": eager_wall / steps * 1e6,
+        "timing": "graph replay of the timed steps" if graph else "eager launches",
+        "forwards_run": warmup + steps + steps * (WARM_REPLAYS + repeats) if graph else warmup + steps * repeats,
     }
-    log(f"[bench] {workload}: {value:.1f} {unit} ({res['timing']}, wall), {k_mean * 1e6:.2f} us per forward "
-        f"(events) -> {achieved:.1f} {roof['unit']} = {roof['frac'] * 100:.1f}% of peak; eager "
-        f"{res['eager_value']:.1f} {unit}")
-    return res, base
 
 
-def cpu_baseline(workload: str, base, budget_s: float = 12.0):
-    """The fp64 oracle on this host: full attention of the workload's batch
-    (decode-sized workloads) or a bounded slice of its rows, repeated until
-    the time budget is spent."""
+def rates(prep: Prepared, t: dict) -> dict:
+    """Throughput and roofline of one timing (prefill in TFLOP/s against the
+    bf16 MFMA peak, the others in KV GB/s against HBM)."""
+    if prep.workload == "prefill":
+        work, unit, peak, bound, scale = prep.flops, "TFLOP/s", BF16_MFMA_PEAK_TFS, "mfma", 1e-6
+    else:
+        work, unit, peak, bound, scale = prep.kv_bytes, "GB/s", HBM_PEAK_GBS, "hbm", 1e-3
+    value = work / t["graph_wall_us"] * scale
+    achieved = work / t["graph_event_us"] * scale
+    return {
+        "value": value, "unit": unit,
+        "roofline": {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+                     "traffic": load_traffic(prep.workload),
+                     "scope": "one forward (every kernel it launches), HIP events on the launch stream over "
+                              f"the timed region ({t['timing']}) / steps, median of the repeats"},
+        "eager_value": work / t["eager_wall_us"] * scale,
+    }
+
+
+def measure(workload: str, steps: int, warmup: int, paths=("auto",), repeats: int = REPEATS, graph: bool = True):
+    prep = Prepared(workload)
+    try:
+        res = {}
+        for path in paths:
+            t = time_path(prep, path, steps, warmup, repeats, graph)
+            r = rates(prep, t)
+            r["timing"] = t
+            res[path] = r
+            log(f"[bench] {workload}/{path}: {r['value']:.1f} {r['unit']} ({t['timing']}, wall); "
+                f"{t['graph_event_us']:.2f} us per forward (events, median of {repeats}, spread "
+                f"{100 * t['spread']:.2f}%) -> {r['roofline']['frac'] * 100:.1f}% of peak")
+        return res, prep.base
+    finally:
+        prep.free()
+
+
+def cpu_baseline(workload: str, base, budget_s: float = 10.0):
+    """The fp64 oracle, unmodified, on this host: full attention of the
+    workload's batch (decode-sized workloads) or all rows of some query heads
+    (larger ones, scaled by the head count), repeated until the budget is
+    spent.  cores: the CPUs this process may run on; blas_threads: the
+    threads numpy's BLAS uses."""
     import numpy as np
 
     import oracle
 
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        blas = None
     kv_bytes = base.kv_bytes()
     t0 = time.perf_counter()
     reps = 0
+    common = {"cores": cores, "blas_threads": blas, "kind": "oracle"}
     if workload in ("tiny_decode", "decode", "verify_window"):
         while True:
             oracle.attention(base)
@@ -201,20 +269,16 @@ def cpu_baseline(workload: str, base, budget_s: float = 12.0):
                 break
         el = time.perf_counter() - t0
         sample = f"full {workload} batch (all {base.num_tokens * base.num_q_heads} rows), {reps} repetitions"
-        return {"value": kv_bytes * reps / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-                "sample": sample, "seconds": el}
-    # Larger workloads: rows of one KV head at a time, scaled by the head count.
+        return {"value": kv_bytes * reps / el / 1e9, "unit": "GB/s", **common, "sample": sample, "seconds": el}
+    # Larger workloads: all tokens of one query head at a time, scaled by the head count.
     Hk, G = base.num_kv_heads, base.group
-    rows = []
     cu = np.concatenate([[0], np.cumsum(base.q_lens)])
-    for b in range(base.num_seqs):
-        for t in range(int(cu[b]), int(cu[b + 1])):
-            rows.append((t, 0))
+    toks = [t for b in range(base.num_seqs) for t in range(int(cu[b]), int(cu[b + 1]))]
     done_heads = 0
     while True:
         g = done_heads % Hk
         hh = g * G + (done_heads // Hk) % G
-        oracle.attention_rows(base, [(t, hh) for t, _ in rows])
+        oracle.attention_rows(base, [(t, hh) for t in toks])
         done_heads += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -222,14 +286,143 @@ def cpu_baseline(workload: str, base, budget_s: float = 12.0):
     frac = done_heads / base.num_q_heads
     sample = f"all tokens of {done_heads} query head(s) of {base.num_q_heads}; scaled by heads"
     if workload == "prefill":
-        return {"value": base.flops() * frac / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-                "sample": sample, "seconds": el}
-    return {"value": kv_bytes * frac / el / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "seconds": el}
+        return {"value": base.flops() * frac / el / 1e12, "unit": "TFLOP/s", **common, "sample": sample,
+                "seconds": el}
+    return {"value": kv_bytes * frac / el / 1e9, "unit": "GB/s", **common, "sample": sample, "seconds": el}
+
+
+# ------------------------------------------------------------------ kernel trace of the replayed forwards
+MARKER_TAG = "bitwise_not"     # a torch kernel launched between workloads in the traced child run
+
+
+def _marker():
+    import torch
+
+    x = torch.zeros(64, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    x.bitwise_not_()
+    torch.cuda.synchronize()
+
+
+def trace_child(workloads, steps: int, warmup: int, replays: int) -> None:
+    """Runs inside rocprofv3 --kernel-trace: per workload, warm-up forwards,
+    then a marker kernel, `replays` replays of a graph of `steps` forwards,
+    and a marker again, so the replayed dispatches can be told apart."""
+    import torch
+
+    import paged_attention_long_amd as pal
+
+    for w in workloads:
+        prep = Prepared(w)
+        h = prep.handle("auto")
+        try:
+            for i in range(warmup):
+                prep.step(h, i)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(steps):
+                    prep.step(h, i)
+            torch.cuda.synchronize()
+            _marker()
+            for _ in range(replays):
+                g.replay()
+            torch.cuda.synchronize()
+            _marker()
+            del g
+        finally:
+            pal.paged_attn_destroy(h)
+            prep.free()
+        log(f"[bench] traced {w}: {replays} x {steps} replayed forwards")
+
+
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def parse_kernel_trace(csv_path: str, workloads, forwards: int) -> dict:
+    """Per workload, the replayed dispatches between its two markers: per
+    kernel the dispatches per forward and the median duration; the kernel
+    time of one forward and its dominant kernel."""
+    import csv
+
+    with open(csv_path) as f:
+        rows = list(csv.DictReader(f))
+    ev = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]) for r in rows)
+    marks = [i for i, e in enumerate(ev) if MARKER_TAG in e[2]]
+    if len(marks) != 2 * len(workloads):
+        raise RuntimeError(f"expected {2 * len(workloads)} marker dispatches, found {len(marks)}")
+    out = {}
+    for k, w in enumerate(workloads):
+        # the library's kernels only (the markers' own fill kernels fall in between)
+        seg = [e for e in ev[marks[2 * k] + 1:marks[2 * k + 1]] if any(t in e[2] for t in OUR_KERNEL_TAGS)]
+        per = {}
+        for s0, s1, name in seg:
+            per.setdefault(_short(name), []).append((s1 - s0) * 1e-3)
+        kern = {n: {"per_forward": len(d) / forwards, "median_us": _median(d), "min_us": min(d), "max_us": max(d)}
+                for n, d in per.items()}
+        total = sum(v["median_us"] * v["per_forward"] for v in kern.values())
+        dom = max(kern, key=lambda n: kern[n]["median_us"] * kern[n]["per_forward"]) if kern else None
+        out[w] = {"kernels": kern, "kernel_us_per_forward": total, "dominant": dom}
+    return out
+
+
+def kernel_trace(workloads, steps: int = 10, warmup: int = 3, replays: int = 5, timeout_s: int = 300):
+    """Runs this file under rocprofv3 --kernel-trace in a child process (the
+    profiler runs the program itself, after --) and returns the parsed
+    replayed-dispatch durations, or {"error": ...}."""
+    import glob
+    import shutil
+    import subprocess
+    import tempfile
+
+    prof = shutil.which("rocprofv3") or "/opt/rocm/bin/rocprofv3"
+    if not os.path.exists(prof):
+        return {"error": "rocprofv3 not found"}
+    tmp = tempfile.mkdtemp(prefix="pa_ktrace_", dir="/tmp")
+    cmd = [prof, "--kernel-trace", "--output-format", "csv", "-d", tmp, "-o", "run", "--",
+           sys.executable, os.path.abspath(__file__), "--trace-child", ",".join(workloads), "--steps", str(steps),
+           "--warmup", str(warmup), "--replays", str(replays)]
+    env = dict(os.environ, TMPDIR="/tmp")
+    t0 = time.time()
+    try:
+        r = subprocess.run(cmd, cwd="/tmp", env=env, timeout=timeout_s, stdout=subprocess.PIPE,
+                           stderr=subprocess.STDOUT, text=True)
+        rc = r.returncode
+        tail = r.stdout[-2000:]
+    except subprocess.TimeoutExpired:
+        return {"error": f"rocprofv3 child timed out after {timeout_s}s"}
+    files = glob.glob(os.path.join(tmp, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        return {"error": f"no kernel trace (rocprofv3 rc {rc})", "tail": tail}
+    try:
+        res = parse_kernel_trace(files[0], workloads, steps * replays)
+    except Exception as e:  # report, do not hide
+        return {"error": repr(e), "rc": rc}
+    shutil.rmtree(tmp, ignore_errors=True)
+    log(f"[bench] kernel trace of {len(workloads)} workloads in {time.time() - t0:.1f}s (rocprofv3 rc {rc})")
+    return {"command": "rocprofv3 --kernel-trace --output-format csv -- python3 bench.py --trace-child "
+                       f"{','.join(workloads)} --steps {steps} --warmup {warmup} --replays {replays}",
+            "profiler_rc": rc, "replayed_forwards": steps * replays, "workloads": res}
+
+
+def kernel_roofline(prep_like: dict, tr: dict) -> dict:
+    """Roofline of the dominant kernel from its replayed-dispatch median, and
+    the kernel-only time of the whole forward."""
+    dom = tr["dominant"]
+    k = tr["kernels"][dom]
+    work, unit, peak, scale = prep_like["work"], prep_like["unit"], prep_like["peak"], prep_like["scale"]
+    return {"kernel": dom, "median_us": k["median_us"], "per_forward": k["per_forward"],
+            "achieved": work / (k["median_us"] * k["per_forward"]) * scale, "unit": unit, "peak": peak,
+            "frac": work / (k["median_us"] * k["per_forward"]) * scale / peak,
+            "forward_kernels_us": tr["kernel_us_per_forward"],
+            "forward_kernels_frac": work / tr["kernel_us_per_forward"] * scale / peak}
 
 
 COPY_KERNEL_TAG = "neg_kernel"     # torch.neg: reads N bytes, writes N bytes
-OUR_KERNEL_TAGS = ("decode_valu_kernel", "tile_attn_kernel", "merge_kernel", "merge_slots_kernel")
+OUR_KERNEL_TAGS = ("decode_valu_kernel", "tile_attn_kernel", "merge_kernel", "merge_slots_kernel", "append_kernel",
+                   "zero_words_kernel")
 
 
 def calibrate_copy(mib: int) -> None:
@@ -316,12 +509,28 @@ def reduce_profiles(prof_dir: str, workload: str, calib_mib: int, commands: list
     lines = [f"# {', '.join(kern) or 'kernels'}: {workload}", "",
              f"Workload: {WORKLOADS[workload]}.", "", "Commands (run from the repository root):", ""]
     lines += [f"    {c}" for c in commands]
+    # The timed graph replays are the last steps x repeats dispatches of each
+    # kernel in the traced run (warm-up and eager dispatches come first).
+    trace_rows = _csv_rows(os.path.join(prof_dir, "kt", "**", "*kernel_trace.csv"))
+    replayed = n_fwd.get("steps", 0) * n_fwd.get("repeats", REPEATS)
+    by_kernel = collections.defaultdict(list)
+    for r in sorted(trace_rows, key=lambda r: int(r["Start_Timestamp"])):
+        if any(t in r["Kernel_Name"] for t in OUR_KERNEL_TAGS):
+            by_kernel[_short(r["Kernel_Name"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
     lines += ["", "## Kernel trace (rocprofv3 --kernel-trace --stats)", "",
+              "All dispatches of the run (warm-up, eager and replayed forwards):", "",
               "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
     for r in stats:
         if any(t in r["Name"] for t in OUR_KERNEL_TAGS):
             lines.append(f"| {_short(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                          f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    if replayed and by_kernel:
+        lines += ["", f"The timed graph replays only (the last {replayed} dispatches of each kernel):", "",
+                  "| kernel | dispatches | median us | average us | min us | max us |", "|---|---|---|---|---|---|"]
+        for k, d in sorted(by_kernel.items()):
+            d = d[-replayed:]
+            lines.append(f"| {k} | {len(d)} | {_median(d):.2f} | {sum(d) / len(d):.2f} | {min(d):.2f} | "
+                         f"{max(d):.2f} |")
     lines += ["", f"The traced bench.py run: {n_fwd['timing']}, forward time from HIP events "
               f"{json.dumps(n_fwd['forward_us'])} us, roofline {json.dumps(n_fwd['roofline'])}.", "",
               "## HBM traffic (FETCH_SIZE, WRITE_SIZE passes)", "",
@@ -384,7 +593,10 @@ def _append_inputs(seed: int = 7):
     return seq_lens, q_lens, bt, pages, x, scale
 
 
-def measure_append(steps: int, warmup: int, use_graph: bool = True):
+def measure_append(steps: int, warmup: int, use_graph: bool = True, repeats: int = REPEATS):
+    """Times the cache append over rotating copies: each copy has its own new
+    rows and its own page range, about 1 GiB in all, so every call reads its
+    rows from HBM and writes pages no recent call touched."""
     import numpy as np
     import torch
 
@@ -393,51 +605,64 @@ def measure_append(steps: int, warmup: int, use_graph: bool = True):
     sh = APPEND_SHAPE
     seq_lens, q_lens, bt, pages, x, scale = _append_inputs()
     T = int(q_lens.sum())
+    nbytes = 2 * T * sh["hkv"] * sh["head_dim"] * (2 + 1)     # read the 16-bit rows, write the fp8 codes
+    copies = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / nbytes)))
     dev = torch.device("cuda")
-    kn = torch.from_numpy(x[0]).to(dev).to(torch.bfloat16).contiguous()
-    vn = torch.from_numpy(x[1]).to(dev).to(torch.bfloat16).contiguous()
-    kc = torch.zeros((pages, sh["hkv"], 16, sh["head_dim"]), dtype=torch.uint8, device=dev)
+    kn0 = torch.from_numpy(x[0]).to(dev).to(torch.bfloat16).contiguous()
+    vn0 = torch.from_numpy(x[1]).to(dev).to(torch.bfloat16).contiguous()
+    kns = [kn0] + [kn0.clone() for _ in range(copies - 1)]
+    vns = [vn0] + [vn0.clone() for _ in range(copies - 1)]
+    kc = torch.zeros((pages * copies, sh["hkv"], 16, sh["head_dim"]), dtype=torch.uint8, device=dev)
     vc = torch.zeros_like(kc)
-    d_bt, d_sl, d_ql = (torch.from_numpy(a).to(dev) for a in (bt, seq_lens, q_lens))
+    d_bts = [torch.from_numpy(bt + np.int32(c * pages)).to(dev) for c in range(copies)]
+    d_sl, d_ql = (torch.from_numpy(a).to(dev) for a in (seq_lens, q_lens))
     d_sc = torch.from_numpy(scale.reshape(-1)).to(dev)
     cfg = pal.make_config(sh["hkv"] * 4, sh["hkv"], sh["head_dim"], "bf16", "fp8_e4m3", sh["num_seqs"], sh["rows"], T)
     h = pal.paged_attn_create(cfg)
-    stream = torch.cuda.current_stream()
 
-    def step(st=None):
-        pal.paged_attn_append(h, kn, vn, kc, vc, d_bt, d_sl, d_ql, d_sc, stream=st or stream)
+    def step(i):
+        c = i % copies
+        pal.paged_attn_append(h, kns[c], vns[c], kc, vc, d_bts[c], d_sl, d_ql, d_sc,
+                              stream=torch.cuda.current_stream())
 
     try:
-        for _ in range(warmup):
-            step()
+        for i in range(warmup):
+            step(i)
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(); [step() for _ in range(steps)]; e1.record(); torch.cuda.synchronize()
-        eager_us = e0.elapsed_time(e1) * 1e3 / steps
-        us = eager_us
-        timing = "eager launches"
+        eager_wall, eager_ev = _timed(lambda: [step(warmup + i) for i in range(steps)])
         if use_graph:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                for _ in range(steps):
-                    step(torch.cuda.current_stream())
-            g.replay(); torch.cuda.synchronize()
-            e0.record(); g.replay(); e1.record(); torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 1e3 / steps
+                for i in range(steps):
+                    step(i)
+            g.replay()
+            torch.cuda.synchronize()
+            runs = [_timed(g.replay) for _ in range(repeats)]
             timing = "graph replay of the timed steps"
+        else:
+            runs = [(eager_wall, eager_ev)] + [_timed(lambda: [step(i) for i in range(steps)])
+                                              for _ in range(repeats - 1)]
+            timing = "eager launches"
     finally:
         pal.paged_attn_destroy(h)
-    nbytes = 2 * T * sh["hkv"] * sh["head_dim"] * (2 + 1)     # read the 16-bit rows, write the fp8 codes
+    evs = sorted(e / steps * 1e6 for _, e in runs)
+    walls = sorted(w / steps * 1e6 for w, _ in runs)
+    us, wall_us = evs[len(evs) // 2], walls[len(walls) // 2]
     gbs = nbytes / us / 1e3
-    print(f"[bench] append_fp8: {gbs:.1f} GB/s ({timing}), {us:.2f} us per call = {100 * gbs / HBM_PEAK_GBS:.1f}% of peak",
-          file=sys.stderr, flush=True)
+    log(f"[bench] append_fp8: {nbytes / wall_us / 1e3:.1f} GB/s ({timing}, wall), {us:.2f} us per call "
+        f"(events) = {100 * gbs / HBM_PEAK_GBS:.1f}% of peak, {copies} rotating copies")
     res = {
-        "value": gbs, "unit": "GB/s", "ms_per_step": us / 1e3, "dtype": "bf16 in / fp8 e4m3 out",
-        "kv_bytes_per_step": nbytes, "flops_per_step": 0, "rotating_copies": 1,
+        "value": nbytes / wall_us / 1e3, "unit": "GB/s", "ms_per_step": wall_us / 1e3,
+        "dtype": "bf16 in / fp8 e4m3 out", "kv_bytes_per_step": nbytes, "flops_per_step": 0,
+        "rotating_copies": copies,
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                     "traffic": None, "scope": "one append call (new K and V rows read, fp8 codes written)"},
-        "timing": timing, "forward_us": {"events": us, "eager_events": eager_us},
-        "eager_value": nbytes / eager_us / 1e3, "forwards_run": warmup + steps * (2 if use_graph else 1) + 1,
+                     "traffic": load_traffic("append_fp8"),
+                     "scope": "one append call (new K and V rows read, fp8 codes written), HIP events"},
+        "timing": {"timing": timing, "graph_event_us": us, "graph_event_runs_us": [e / steps * 1e6 for _, e in runs],
+                   "spread": (evs[-1] - evs[0]) / us, "eager_event_us": eager_ev / steps * 1e6,
+                   "eager_wall_us": eager_wall / steps * 1e6},
+        "eager_value": nbytes / (eager_wall / steps * 1e6) / 1e3,
+        "forwards_run": warmup + steps + (steps * (1 + repeats) if use_graph else steps * (repeats - 1)),
     }
     return res, (seq_lens, q_lens, bt, pages, x, scale)
 
@@ -466,7 +691,9 @@ def cpu_baseline_append(base):
             break
     sec = time.time() - t0
     nbytes = reps * 2 * rows * sh["hkv"] * sh["head_dim"] * 3
-    return {"value": nbytes / sec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+    # elementwise numpy code: one thread does the work whatever the affinity
+    return {"value": nbytes / sec / 1e9, "unit": "GB/s", "cores": 1, "affinity_cores": len(os.sched_getaffinity(0)),
+            "kind": "oracle",
             "sample": f"{rows} rows of {n_seq} sequences, {reps} repetitions", "seconds": sec}
 
 
@@ -475,33 +702,74 @@ def profile_commands(workload: str, calib_mib: int = 512) -> list:
     repository root $REPO (counters in passes of their own, as the profiler
     collects them)."""
     out = f"$REPO/gpurun_out/prof/{workload}"
-    run = f"python3 $REPO/bench.py --workload {workload} --no-cpu-baseline"
+    run = (f"python3 $REPO/bench.py --workload {workload} --no-cpu-baseline --no-per-config --no-kernel-trace "
+           f"--path auto")
     return [
         "cd /tmp && export TMPDIR=/tmp",
         f"rocprofv3 --kernel-trace --stats --output-format csv -d {out}/kt -o run -- "
         f"{run} --steps 50 --warmup 5 --json-out {out}/kt/bench.json",
         f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d {out}/fetch -o run -- "
-        f"{run} --steps 5 --warmup 1 --eager --calibrate-copy {calib_mib} --json-out {out}/fetch/bench.json",
+        f"{run} --steps 5 --warmup 1 --repeats 1 --eager --calibrate-copy {calib_mib} --json-out {out}/fetch/bench.json",
         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/write -o run -- "
-        f"{run} --steps 5 --warmup 1 --eager --calibrate-copy {calib_mib} --json-out {out}/write/bench.json",
+        f"{run} --steps 5 --warmup 1 --repeats 1 --eager --calibrate-copy {calib_mib} --json-out {out}/write/bench.json",
         f"python3 bench.py --workload {workload} --reduce-profiles gpurun_out/prof/{workload}   # on any host",
     ]
+
+
+# Per-configuration entries of the default run: steps sized so each timed
+# region lasts a few milliseconds.
+PER_CONFIG = {"tiny_decode": 300, "decode": 200, "verify": 60, "verify_window": 200, "prefill": 20}
+CPU_BUDGET_HEADLINE_S = 10.0
+CPU_BUDGET_PER_CONFIG_S = 3.0
+
+
+def _entry(workload: str, res: dict, base, trace: dict, cpu: dict = None) -> dict:
+    auto = res["auto"]
+    t = auto["timing"]
+    e = {"value": auto["value"], "unit": auto["unit"], "path": "auto", "roofline": auto["roofline"],
+         "forward_us": {"graph_event_median": t["graph_event_us"], "graph_event_runs": t["graph_event_runs_us"],
+                        "spread": t["spread"], "graph_wall_median": t["graph_wall_us"],
+                        "eager_events": t["eager_event_us"], "eager_wall": t["eager_wall_us"]},
+         "eager_value": auto["eager_value"], "kv_bytes_per_step": base.kv_bytes(), "flops_per_step": base.flops()}
+    tr = (trace or {}).get("workloads", {}).get(workload)
+    if tr:
+        work = base.flops() if workload == "prefill" else base.kv_bytes()
+        unit = e["unit"]
+        peak = BF16_MFMA_PEAK_TFS if workload == "prefill" else HBM_PEAK_GBS
+        e["roofline"] = dict(e["roofline"], kernel=kernel_roofline(
+            {"work": work, "unit": unit, "peak": peak, "scale": 1e-6 if workload == "prefill" else 1e-3}, tr),
+            kernels=tr["kernels"])
+    for path, r in res.items():
+        if path != "auto":
+            e.setdefault("alt_paths", {})[path] = {
+                "value": r["value"], "unit": r["unit"], "frac": r["roofline"]["frac"],
+                "forward_us": {"graph_event_median": r["timing"]["graph_event_us"], "spread": r["timing"]["spread"]}}
+    if cpu is not None:
+        e["cpu_baseline"] = cpu
+    return e
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--all", action="store_true", help="also measure every other workload (per_config)")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--repeats", type=int, default=REPEATS, help="timed regions per measurement (median, spread)")
+    ap.add_argument("--workload", default="mixed_fp8", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="headline workload only (the default run also measures every other config)")
+    ap.add_argument("--no-kernel-trace", action="store_true", help="skip the rocprofv3 kernel-trace child run")
     ap.add_argument("--eager", action="store_true", help="time eager launches only (no graph replay)")
+    ap.add_argument("--path", default=None, choices=sorted(PATHS),
+                    help="time this path only (default: auto, plus valu for verify and mixed_fp8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a copy kernel of known size (for counter scaling)")
     ap.add_argument("--profile-commands", action="store_true", help="print the rocprofv3 commands and exit")
     ap.add_argument("--reduce-profiles", default=None, metavar="DIR",
                     help="summarise the rocprofv3 runs in DIR into profiles/ (no GPU needed)")
+    ap.add_argument("--trace-child", default=None, metavar="WORKLOADS", help=argparse.SUPPRESS)
+    ap.add_argument("--replays", type=int, default=5, help=argparse.SUPPRESS)
     ap.add_argument("--json-out", default=None)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -517,42 +785,93 @@ def main():
     import torch
 
     torch.cuda.set_device(0)
+    if args.trace_child:
+        trace_child(args.trace_child.split(","), args.steps, args.warmup, args.replays)
+        return
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
-    if args.workload == "append_fp8":
-        res, base = measure_append(args.steps, args.warmup, use_graph=not args.eager)
+    w = args.workload
+    if w == "append_fp8":
+        head, base = measure_append(args.steps, args.warmup, use_graph=not args.eager, repeats=args.repeats)
+        t = head["timing"]
+        line = {
+            "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",
+            "config": {"workload": WORKLOADS[w], "name": w, "kv_bytes_per_step": head["kv_bytes_per_step"],
+                       "rotating_copies": head["rotating_copies"], "parallelism": "single GPU"},
+            "roofline": head["roofline"], "timing": t["timing"], "forward_us": t,
+            "eager_value": head["eager_value"], "forwards_run": head["forwards_run"],
+        }
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_append(base)
+        _emit(line, args.json_out)
+        return
+
+    per_config = (w == "mixed_fp8") and not args.no_per_config and not args.eager
+    if args.path:
+        paths = (args.path,)
     else:
-        res, base = measure(args.workload, args.steps, args.warmup, use_graph=not args.eager)
+        paths = ("auto", "valu") if (w in ALT_PATH_WORKLOADS and not args.eager) else ("auto",)
+    res, base = measure(w, args.steps, args.warmup, paths, args.repeats, graph=not args.eager)
+    if "auto" not in res:
+        res = {"auto": res[paths[0]]}
+    auto = res["auto"]
+    t = auto["timing"]
+    kinds = {"f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3"}
     line = {
-        "metric": METRIC, "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.workload], "name": args.workload,
-                   "kv_bytes_per_step": res["kv_bytes_per_step"], "flops_per_step": res["flops_per_step"],
-                   "rotating_copies": res["rotating_copies"], "parallelism": "single GPU"},
-        "roofline": res["roofline"], "timing": res["timing"], "forward_us": res["forward_us"],
-        "eager_value": res["eager_value"], "forwards_run": res["forwards_run"],
+        "metric": METRIC, "value": auto["value"], "unit": auto["unit"], "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": t["graph_wall_us"] / 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAME[kinds[base.kv_dtype]], "data": "synthetic",
+        "config": {"workload": WORKLOADS[w], "name": w, "kv_bytes_per_step": base.kv_bytes(),
+                   "flops_per_step": base.flops(), "parallelism": "single GPU", "path": paths[0]},
+        "roofline": auto["roofline"], "timing": t["timing"],
+        "forward_us": {"graph_event_median": t["graph_event_us"], "graph_event_runs": t["graph_event_runs_us"],
+                       "spread": t["spread"], "graph_wall_median": t["graph_wall_us"],
+                       "eager_events": t["eager_event_us"], "eager_wall": t["eager_wall_us"]},
+        "eager_value": auto["eager_value"], "forwards_run": t["forwards_run"], "repeats": args.repeats,
     }
-    if args.all:
-        per = {}
-        for w in ("decode", "verify", "verify_window", "prefill", "mixed_fp8"):
-            if w == args.workload:
-                continue
+    line["config"]["rotating_copies"] = max(1, min(MAX_COPIES, math.ceil(ROTATE_BYTES / base.kv_bytes())))
+    cpu_budget = CPU_BUDGET_HEADLINE_S
+    per, bases = {}, {}
+    if per_config:
+        for pw, steps in PER_CONFIG.items():
             try:
-                r, _ = measure(w, max(20, args.steps // 4), max(5, args.warmup // 2), use_graph=not args.eager)
-                per[w] = {"value": r["value"], "unit": r["unit"], "roofline": r["roofline"],
-                          "forward_us": r["forward_us"], "eager_value": r["eager_value"]}
+                r, b = measure(pw, steps, max(5, args.warmup),
+                               ("auto", "valu") if pw in ALT_PATH_WORKLOADS else ("auto",), args.repeats)
+                per[pw], bases[pw] = r, b
             except Exception as e:  # report, do not hide
-                per[w] = {"error": repr(e)}
-        line["per_config"] = per
+                per[pw] = {"error": repr(e)}
+    trace = None
+    if not args.no_kernel_trace and not args.eager:
+        trace = kernel_trace([w] + [pw for pw in per if "error" not in per[pw]])
+        line["kernel_trace"] = {k: v for k, v in trace.items() if k != "workloads"}
+        if "error" in trace:
+            log(f"[bench] kernel trace failed: {trace['error']}")
+    head = _entry(w, res, base, trace)
+    line["roofline"] = head["roofline"]
+    if "alt_paths" in head:
+        line["alt_paths"] = head["alt_paths"]
+    if per_config:
+        line["per_config"] = {}
+        for pw, r in per.items():
+            if "error" in r:
+                line["per_config"][pw] = r
+                continue
+            cpu = None if args.no_cpu_baseline else cpu_baseline(pw, bases[pw], CPU_BUDGET_PER_CONFIG_S)
+            line["per_config"][pw] = dict(_entry(pw, r, bases[pw], trace, cpu), config=WORKLOADS[pw],
+                                          steps=PER_CONFIG[pw])
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = (cpu_baseline_append(base) if args.workload == "append_fp8"
-                                else cpu_baseline(args.workload, base))
+        line["cpu_baseline"] = cpu_baseline(w, base, cpu_budget)
+    _emit(line, args.json_out)
+
+
+def _emit(line: dict, json_out) -> None:
     text = json.dumps(line)
     print(text, flush=True)
-    if args.json_out:
-        os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
-        with open(args.json_out, "w") as f:
+    if json_out:
+        os.makedirs(os.path.dirname(os.path.abspath(json_out)), exist_ok=True)
+        with open(json_out, "w") as f:
             f.write(text + "\n")
 
 

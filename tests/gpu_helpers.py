@@ -14,8 +14,10 @@ import paged_attention_long_amd as pal
 from synth.torch_upload import upload_batch, upload_pool
 
 # Tolerances (max abs error against the fp64 oracle): fp16/bf16 caches with
-# fp32 accumulation 2e-3 on out and 1e-3 on lse; fp8 caches 2e-2.
-TOL = {"f16": (2e-3, 1e-3), "bf16": (2e-3, 1e-3), "fp8_e4m3": (2e-2, 2e-2)}
+# fp32 accumulation 2e-3 on out and 1e-3 on lse; fp8 caches 2e-2 on out and
+# 1e-3 on lse (the oracle reads the same stored codes and scales, which
+# enter the scores exactly in fp32, so the lse carries no format error).
+TOL = {"f16": (2e-3, 1e-3), "bf16": (2e-3, 1e-3), "fp8_e4m3": (2e-2, 1e-3)}
 
 
 def progress(msg: str) -> None:

@@ -69,3 +69,35 @@ def test_kernel_source_hash_covers_every_source_file(tmp_path, monkeypatch):
         assert bench.kernel_source_hash() != h0, name
         p.write_bytes(orig)
     assert bench.kernel_source_hash() == h0
+
+
+def test_kernel_trace_parser_takes_dispatches_between_markers(tmp_path):
+    """Replayed dispatches are those between each workload's two marker
+    kernels; per kernel the median duration and dispatches per forward."""
+    rows = [("warm tile_attn_kernel<128, 3, 2, 1>(pa::DecodeArgs)", 0, 500)]
+    t = 1000
+    names = ["tile_attn_kernel<128, 3, 2, 1>(pa::DecodeArgs)", "merge_kernel<128, 32>(pa::MergeArgs)"]
+    for w, durs in (("mixed_fp8", (100, 10)), ("decode", (12, 5))):
+        rows.append(("void at::native::bitwise_not_kernel(x)", t, t + 1)); t += 10
+        for k in range(4):
+            for n, d in zip(names, durs):
+                rows.append((n, t, t + d * 1000 + k)); t += d * 1000 + 50
+        rows.append(("void at::native::bitwise_not_kernel(x)", t, t + 1)); t += 10
+    p = tmp_path / "run_kernel_trace.csv"
+    with open(p, "w") as f:
+        f.write("Kind,Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for n, a, b in rows:
+            f.write(f'KERNEL_DISPATCH,"{n}",{a},{b}\n')
+    res = bench.parse_kernel_trace(str(p), ["mixed_fp8", "decode"], forwards=4)
+    m = res["mixed_fp8"]
+    assert m["dominant"] == "tile_attn_kernel<128, 3, 2, 1>"
+    assert m["kernels"]["tile_attn_kernel<128, 3, 2, 1>"]["per_forward"] == 1.0
+    assert abs(m["kernels"]["tile_attn_kernel<128, 3, 2, 1>"]["median_us"] - 100.0015) < 1e-6
+    assert abs(m["kernel_us_per_forward"] - (100.0015 + 10.0015)) < 1e-6
+    assert res["decode"]["kernels"]["merge_kernel<128, 32>"]["median_us"] < 6
+
+
+def test_default_run_is_the_mixed_batch():
+    src = open(os.path.join(ROOT, "bench.py")).read()
+    assert 'ap.add_argument("--workload", default="mixed_fp8"' in src
+    assert set(bench.PER_CONFIG) == {"tiny_decode", "decode", "verify", "verify_window", "prefill"}

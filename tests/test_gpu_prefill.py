@@ -50,19 +50,16 @@ def test_prefill_small_parity(name):
     compare(name, inp.kv_dtype, out, lse, ref_o, ref_l)
 
 
-def test_prefill_named_sampled_rows():
-    """The 2,048-token chunk on 65,536 cached tokens, checked on sampled rows
-    (first, last and random tokens; every head of a few tokens)."""
+def test_prefill_named_dense_rows():
+    """The 2,048-token chunk on 65,536 cached tokens: every 16th token and the
+    last, with all 24 query heads (3,096 rows).  A 256-row item spans about
+    43 tokens, so every item, and within it every split of the key range,
+    reaches the comparison."""
     inp = named("prefill")[0]
-    progress("prefill named sampled rows")
-    rng = np.random.default_rng(3)
-    toks = sorted(set([0, 1, 127, 128, 1023, 2046, 2047] + rng.choice(2048, 9, replace=False).tolist()))
-    rows = []
-    for t in toks:
-        for h in rng.choice(inp.num_q_heads, size=4, replace=False):
-            rows.append((int(t), int(h)))
-    rows += [(2047, h) for h in range(inp.num_q_heads)]
-    ref = oracle.attention_rows(inp, sorted(set(rows)))
+    progress("prefill named dense rows")
+    toks = sorted(set(list(range(0, 2048, 16)) + [1, 2047]))
+    rows = [(t, h) for t in toks for h in range(inp.num_q_heads)]
+    ref = oracle.attention_rows(inp, rows)
     c = GpuCase([inp])
     try:
         out, lse = c.run()
@@ -84,6 +81,21 @@ VERIFY = {
     "fp8_q8_window": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(4000,), q_lens=(8,), kv_dtype="fp8_e4m3",
                           window=200, poison_out_of_window=True, k_outlier_frac=0.01),
     "fp8_short": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(20, 50, 33), q_lens=(8, 2, 4), kv_dtype="fp8_e4m3"),
+    # 9..16 new tokens at four query heads per KV head: 33..64 rows, two
+    # 32-row tiles per (sequence, KV head) on the tile kernel (the 15 drafts
+    # + 1 verification width of "tps-maxxing on amd gpu", section
+    # "Speculative decoding: native MTP vs. DFlash")
+    "f16_q16_window_outliers": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(5000,), q_lens=(16,), q_dtype="f16",
+                                    kv_dtype="f16", window=700, poison_out_of_window=True, k_outlier_frac=0.01),
+    "f16_q9_q16_outliers": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(7001, 2500), q_lens=(9, 16),
+                                q_dtype="f16", kv_dtype="f16", k_outlier_frac=0.01),
+    "bf16_q12_q16_window": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(6100, 900), q_lens=(12, 16),
+                                window=1000, poison_out_of_window=True, k_outlier_frac=0.01),
+    "bf16_q16_long": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(20011,), q_lens=(16,), k_outlier_frac=0.01),
+    "fp8_q16_window_outliers": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(4500,), q_lens=(16,),
+                                    kv_dtype="fp8_e4m3", window=900, poison_out_of_window=True, k_outlier_frac=0.01),
+    "fp8_q9_q13_q16": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(3000, 1200, 16), q_lens=(9, 13, 16),
+                           kv_dtype="fp8_e4m3", k_outlier_frac=0.01),
 }
 
 
@@ -99,6 +111,20 @@ def test_paths_agree_with_oracle(name, path):
     finally:
         c.close()
     compare(f"{name}/path{path}", inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+def test_verify_named_on_valu_path():
+    """The 61,448-token verification batch in full on the vector-ALU path
+    (every sequence through the split-KV decode kernel)."""
+    inp = named("verify")[0]
+    progress("named verify full oracle, VALU path")
+    ref_o, ref_l = oracle.attention(inp)
+    c = GpuCase([inp], path=pal.PA_PATH_VALU)
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare("verify/valu", inp.kv_dtype, out, lse, ref_o, ref_l)
 
 
 @pytest.mark.parametrize("tps", [1, 3, 1000])
