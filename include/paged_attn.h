@@ -76,7 +76,13 @@ typedef struct pa_config {
     int32_t num_kv_heads;    /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 16 */
     int32_t head_dim;        /* D: 64 or 128; 64 runs on the VALU kernel only and needs
                                 max_q_len * Hq / Hkv <= 64 (else PA_ERR_UNSUPPORTED at create) */
-    int32_t page_size;       /* P: tokens per page; 16 */
+    int32_t page_size;       /* P: tokens per page, a multiple of 16 in 16..65536 (the cache is read in
+                                place at any such block size: "Dual MI50, part 2", section "Prefill:
+                                teach the fork's fast kernel to read the int8 cache"; the pages use
+                                1,056- and 1,584-token pages).  With P > 16 the layout's page stride
+                                must be a multiple of 16 token rows (true of HND and NHD), num_pages
+                                x page_stride / (16 x token_stride) below 2^31, and
+                                block_table_stride x P below 2^28 (else PA_ERR_UNSUPPORTED). */
     int32_t q_dtype;         /* PA_DTYPE_F16 or PA_DTYPE_BF16 */
     int32_t kv_dtype;        /* PA_DTYPE_F16, PA_DTYPE_BF16 (== q_dtype) or PA_DTYPE_FP8_E4M3 */
     int32_t max_num_seqs;    /* largest num_seqs passed to forward, 1..1024 */
@@ -136,8 +142,8 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out);
  *  layout       host, see pa_cache_layout_t.
  *  block_table  device int32 [num_seqs][block_table_stride]: entry
  *               [b][i] is the physical page holding tokens i*P .. i*P+P-1
- *               of sequence b; entries past the sequence's last page are
- *               never read.
+ *               of sequence b (P = cfg.page_size); entries past the
+ *               sequence's last page are never read.
  *  num_seqs     host int, 1..cfg.max_num_seqs.
  *  seq_lens     device int32 [num_seqs]: cached tokens incl. the new ones.
  *  q_lens       device int32 [num_seqs]: new rows, 0 <= q_len <= min(seq_len,

@@ -1,7 +1,7 @@
 // Writing a step's new K/V rows into the paged cache (quantise-on-write for
 // fp8 caches).  Sequence b's new rows are its last q_len_b positions
 // (seq_len_b counts them), so row i lands at logical position
-// p = seq_len_b - q_len_b + i: page block_table[b][p / 16], slot p % 16, the
+// p = seq_len_b - q_len_b + i: page block_table[b][p / P], slot p % P, the
 // same addressing the attention kernels read with (kv_offset).  A 16-bit
 // cache receives the input bits; an fp8 E4M3FN cache receives the code
 // nearest to x / s (s the KV head's K or V scale, the quotient rounded once
@@ -87,14 +87,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         const int g = (int)(rg % a.num_kv_heads);
         const int i = (int)(rg / a.num_kv_heads);
         const int p = sl - ql + i;
-        if (p / kAppendPage >= a.bt_stride) continue;
-        const int pid = a.block_table[(int64_t)b * a.bt_stride + p / kAppendPage];
+        const int lp = p / a.page_size;
+        if (lp >= a.bt_stride) continue;
+        const int pid = a.block_table[(int64_t)b * a.bt_stride + lp];
         if (pid < 0 || pid >= a.num_pages) continue;
         const uint16_t* src = static_cast<const uint16_t*>(which ? a.v_new : a.k_new) +
                               ((int64_t)(q_off + i) * a.num_kv_heads + g) * a.head_dim + ch * 8;
         const uint4 in = *reinterpret_cast<const uint4*>(src);
         const int64_t off = (int64_t)pid * a.page_stride + (int64_t)g * a.head_stride +
-                            (int64_t)(p % kAppendPage) * a.token_stride + ch * 8;
+                            (int64_t)(p - lp * a.page_size) * a.token_stride + ch * 8;
         if constexpr (KVT != PA_DTYPE_FP8_E4M3) {
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(which ? a.v_cache : a.k_cache) + off) = in;
         } else {

@@ -234,6 +234,22 @@ PA_DEVINLINE int64_t kv_offset(int64_t page, int g, int slot, int64_t page_strid
     return page * page_stride + (int64_t)g * head_stride + (int64_t)slot * token_stride;
 }
 
+// Virtual page holding 16-token chunk c of the sequence whose block-table row
+// is bt (c < 2^24).  With 16-token pages it is the page id itself.  A page of
+// P = 16 * cpp tokens is cut into cpp virtual pages of 16 token rows each:
+// chunk c is virtual page bt[c / cpp] * vr + c % cpp, and the kernels address
+// virtual pages with a stride of 16 token rows, so every kernel keeps its
+// 16-token loops for any page size that is a multiple of 16 ("Dual MI50,
+// part 2", section "Prefill: teach the fork's fast kernel to read the int8
+// cache": the cache is read in place at any block size).  The quotient is a
+// multiply-high and a shift with a magic number from the host.
+template <typename BT>
+PA_DEVINLINE int chunk_page(BT bt, int c, const DecodeArgs& a) {
+    if (a.cpp == 1) return bt[c];
+    const int q = (int)(__umulhi((uint32_t)c, a.cpp_magic) >> a.cpp_shift);
+    return bt[q] * a.vr + (c - q * a.cpp);
+}
+
 // ----------------------------------------------------------------- split plan
 
 // Work items of one launch, computed identically by every workgroup from the

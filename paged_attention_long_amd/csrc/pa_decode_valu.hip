@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
                 const int c1 = min(p_end, c0 + kPidChunk);
                 if (!(pid_ready && c0 == p_begin && rg0 == 0)) {
                     __syncthreads();
-                    for (int k = tid; k < c1 - c0; k += kThreads) sm.pid[k] = bt[c0 + k];
+                    for (int k = tid; k < c1 - c0; k += kThreads) sm.pid[k] = chunk_page(bt, c0 + k, a);
                 }
                 __syncthreads();
                 if (active) {
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         const int pps = a.static_pps;
         const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
         for (int k = tid; k < pps; k += kThreads)
-            sm.pid[k] = (split * pps + k < a.bt_stride) ? bt[split * pps + k] : 0;
+            sm.pid[k] = (split * pps + k < a.bt_chunks) ? chunk_page(bt, split * pps + k, a) : 0;
         if (wid == 0) {
             int qs = 0;
             for (int b0 = 0; b0 < b; b0 += kWave) qs += (b0 + lane < b) ? a.q_lens[b0 + lane] : 0;
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         const int p_end = min((split + 1) * pps, last_page + 1);
         if (p_begin > split * pps) {   // window start inside this split: realign the staged ids
             __syncthreads();
-            for (int k = tid; k < p_end - p_begin; k += kThreads) sm.pid[k] = bt[p_begin + k];
+            for (int k = tid; k < p_end - p_begin; k += kThreads) sm.pid[k] = chunk_page(bt, p_begin + k, a);
             __syncthreads();
         }
         const int64_t first_item = (int64_t)(b * a.num_kv_heads + g) * S + s_first;

@@ -51,8 +51,17 @@ struct DecodeArgs {
     // workgroups of group (b, g) count their arrivals in arrive[b * Hkv + g]
     // and the last one merges the group's partials itself (no merge launch).
     int* arrive;
+    // Pages of P = 16 * cpp tokens are addressed as cpp virtual pages of 16
+    // tokens: 16-token chunk c of a sequence lives in virtual page
+    // block_table[c / cpp] * vr + c % cpp, whose rows start page_stride
+    // elements apart (16 * token_stride when cpp > 1; see chunk_page()).
     int64_t page_stride, head_stride, token_stride;   // elements
     int num_seqs, bt_stride;
+    int cpp;                   // 16-token chunks per page (1: 16-token pages)
+    uint32_t cpp_magic;        // c / cpp == umulhi(c, cpp_magic) >> cpp_shift for c < 2^24 (cpp > 1)
+    int cpp_shift;
+    int vr;                    // virtual pages per physical page (cpp > 1)
+    int bt_chunks;             // 16-token chunks the block-table row covers (bt_stride * cpp)
     int num_q_heads, num_kv_heads, group;
     int window;
     float scale;
@@ -118,8 +127,6 @@ struct GatherArgs {
 
 hipError_t launch_debug_gather(const GatherArgs& a, hipStream_t stream);
 
-constexpr int kAppendPage = 16;   // tokens per cache page
-
 // Arguments of the cache append (new K/V rows written into their pages).
 struct AppendArgs {
     const void* k_new;         // [num_tokens][Hkv][D], 16-bit
@@ -132,7 +139,7 @@ struct AppendArgs {
     const float* kv_scale;     // [2][Hkv] (fp8 caches)
     int64_t num_pages, page_stride, head_stride, token_stride;   // elements
     int64_t num_tokens;
-    int num_seqs, bt_stride, num_kv_heads, head_dim;
+    int num_seqs, bt_stride, num_kv_heads, head_dim, page_size;
 };
 
 // max_rows: the largest q_len of the call (sizes the grid along the rows).

@@ -740,7 +740,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             (const __attribute__((address_space(4))) int32_t*)bt;
         auto tile_pid = [&](int t, int p) {
             const int pg = __builtin_amdgcn_readfirstlane(min(ig.pg_first + t * PPT + p, ig.pg_end - 1));
-            return bt_c[pg];
+            return chunk_page(bt_c, pg, a);
         };
         auto key_pos = [&](int t, int key) { return (ig.pg_first + t * PPT) * kPage + key; };
         auto row_src = [&](const uint8_t* base, const int (&pid)[PPT], int key) -> const uint8_t* {
@@ -1001,7 +1001,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             pid_staged = n_pid <= C::PID_CAP;
             const int pid0 = ig.pg_first + ig.t_begin * PPT;
             if (pid_staged)
-                for (int k = tid; k < n_pid; k += blockDim.x) ipid[k] = bt[min(pid0 + k, ig.pg_end - 1)];
+                for (int k = tid; k < n_pid; k += blockDim.x) ipid[k] = chunk_page(bt, min(pid0 + k, ig.pg_end - 1), a);
             __syncthreads();
         }
         if constexpr (C::PIPE) {
@@ -1017,7 +1017,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             const bool staged = n_pid <= C::PID_CAP;
             const int pid0 = ig.pg_first + ig.t_begin * PPT;
             if (staged)
-                for (int k = tid; k < n_pid; k += blockDim.x) ipid[k] = bt[min(pid0 + k, ig.pg_end - 1)];
+                for (int k = tid; k < n_pid; k += blockDim.x) ipid[k] = chunk_page(bt, min(pid0 + k, ig.pg_end - 1), a);
             __syncthreads();
             // tiles t_begin + k with k in [k_live, k_live + n_live) have no dead V rows
             int k_live, n_live;

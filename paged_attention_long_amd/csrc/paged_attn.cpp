@@ -37,6 +37,22 @@ constexpr int kValuMaxKeys = 16384;   // and visible keys (longer contexts go to
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// c / d == umulhi(c, magic) >> shift for every c < 2^24 and 2 <= d <= 4096:
+// with 2^shift < d <= 2^(shift+1) and magic = ceil(2^(32+shift) / d) < 2^32,
+// c * magic / 2^(32+shift) exceeds c / d by less than 2^24 / 2^(32+shift),
+// which is below 1/d, so the floor is unchanged.
+void chunk_magic(int d, uint32_t* magic, int* shift) {
+    if (d <= 1) {
+        *magic = 0;
+        *shift = 0;
+        return;
+    }
+    int s = 0;
+    while ((1 << (s + 1)) < d) ++s;
+    *shift = s;
+    *magic = (uint32_t)((((uint64_t)1 << (32 + s)) + (uint64_t)d - 1) / (uint64_t)d);
+}
+
 }  // namespace
 
 int fail(pa_handle* h, int code, const char* fmt, ...) {
@@ -59,7 +75,8 @@ int validate_config(const pa_config_t* c, char* why, size_t why_len) {
     if (c->num_q_heads % c->num_kv_heads) return bad(PA_ERR_INVALID_ARGUMENT, "num_q_heads % num_kv_heads != 0");
     if (c->num_q_heads / c->num_kv_heads > 16) return bad(PA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
     if (c->head_dim != 64 && c->head_dim != 128) return bad(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
-    if (c->page_size != 16) return bad(PA_ERR_UNSUPPORTED, "page_size must be 16");
+    if (c->page_size < 16 || c->page_size > 65536 || c->page_size % 16)
+        return bad(PA_ERR_UNSUPPORTED, "page_size must be a multiple of 16 in 16..65536");
     if (c->q_dtype != PA_DTYPE_F16 && c->q_dtype != PA_DTYPE_BF16)
         return bad(PA_ERR_UNSUPPORTED, "q_dtype must be F16 or BF16");
     if (c->kv_dtype != PA_DTYPE_F16 && c->kv_dtype != PA_DTYPE_BF16 && c->kv_dtype != PA_DTYPE_FP8_E4M3)
@@ -178,6 +195,15 @@ static int validate_cache(pa_handle* h, const pa_cache_layout_t* L, const void* 
     if ((L->page_stride * eb) % 16 || (L->head_stride * eb) % 16 || (L->token_stride * eb) % 16)
         return fail(h, PA_ERR_INVALID_ARGUMENT, "every stride must be a multiple of 16 bytes");
     if (L->num_pages > ((int64_t)1 << 31)) return fail(h, PA_ERR_INVALID_ARGUMENT, "num_pages must fit in int32");
+    const int cpp = c.page_size / 16;
+    if (cpp > 1) {
+        // pages of more than 16 tokens are addressed as 16-token virtual pages
+        if (L->page_stride % (16 * L->token_stride))
+            return fail(h, PA_ERR_UNSUPPORTED,
+                        "with pages of %d tokens the page stride must be a multiple of 16 token rows", c.page_size);
+        if (L->num_pages * (L->page_stride / (16 * L->token_stride)) >= ((int64_t)1 << 31))
+            return fail(h, PA_ERR_UNSUPPORTED, "num_pages x %d-token pages exceeds 2^31 virtual pages", c.page_size);
+    }
     return PA_OK;
 }
 
@@ -193,6 +219,8 @@ int check_forward(pa_handle* h, const ForwardCall& f) {
     if (f.num_seqs < 1 || f.num_seqs > c.max_num_seqs)
         return fail(h, PA_ERR_INVALID_ARGUMENT, "num_seqs %d outside 1..%d", f.num_seqs, c.max_num_seqs);
     if (f.bt_stride < 1) return fail(h, PA_ERR_INVALID_ARGUMENT, "block_table_stride must be >= 1");
+    if ((int64_t)f.bt_stride * (c.page_size / 16) >= ((int64_t)1 << 24))
+        return fail(h, PA_ERR_UNSUPPORTED, "block_table_stride x page_size must be below 2^28 tokens");
     if (!std::isfinite(f.scale) || !(f.scale > 0.f)) return fail(h, PA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
     if ((c.kv_dtype == PA_DTYPE_FP8_E4M3) != (f.kv_scale != nullptr))
         return fail(h, PA_ERR_INVALID_ARGUMENT, "kv_scale is required for an fp8 cache and must be NULL otherwise");
@@ -249,11 +277,15 @@ int enqueue_forward(pa_handle* h, const ForwardCall& f, const LaunchPlan& lp) {
     a.sdesc = nullptr;
     a.sdesc_upg = h->sdesc_upg;
     a.arrive = nullptr;
-    a.page_stride = f.layout->page_stride;
+    a.cpp = c.page_size / 16;
+    chunk_magic(a.cpp, &a.cpp_magic, &a.cpp_shift);
+    a.page_stride = a.cpp > 1 ? 16 * f.layout->token_stride : f.layout->page_stride;
+    a.vr = a.cpp > 1 ? (int)(f.layout->page_stride / (16 * f.layout->token_stride)) : 1;
     a.head_stride = f.layout->head_stride;
     a.token_stride = f.layout->token_stride;
     a.num_seqs = f.num_seqs;
     a.bt_stride = f.bt_stride;
+    a.bt_chunks = f.bt_stride * a.cpp;
     a.num_q_heads = c.num_q_heads;
     a.num_kv_heads = c.num_kv_heads;
     a.group = G;
@@ -289,11 +321,10 @@ int enqueue_forward(pa_handle* h, const ForwardCall& f, const LaunchPlan& lp) {
         a.static_pps = 0;
         a.static_splits = 0;
         {
-            // Pages a VALU-class sequence can reach (static splits count from
-            // page 0): without a window its visible keys start at 0.
+            // 16-token chunks a VALU-class sequence can reach (static splits
+            // count from chunk 0): without a window its visible keys start at 0.
             const int64_t cap_pages =
-                window > 0 ? (int64_t)block_table_stride
-                           : std::min<int64_t>(block_table_stride, (int64_t)a.cls_len / c.page_size + 1);
+                window > 0 ? (int64_t)a.bt_chunks : std::min<int64_t>(a.bt_chunks, (int64_t)a.cls_len / 16 + 1);
             const int64_t units = (int64_t)num_seqs * c.num_kv_heads * cap_pages;
             // one workgroup per CU: a second resident workgroup on some CUs
             // would double their share of the bytes
@@ -523,7 +554,6 @@ int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int6
     if (block_table_stride < 1) return fail(h, PA_ERR_INVALID_ARGUMENT, "block_table_stride must be >= 1");
     if ((c.kv_dtype == PA_DTYPE_FP8_E4M3) != (kv_scale != nullptr))
         return fail(h, PA_ERR_INVALID_ARGUMENT, "kv_scale is required for an fp8 cache and must be NULL otherwise");
-    if (c.page_size != pa::kAppendPage) return fail(h, PA_ERR_UNSUPPORTED, "page_size must be 16");
     DeviceGuard guard(c.device);
     if (!guard.ok) return fail(h, PA_ERR_HIP, "hipSetDevice(%d) failed", c.device);
     pa::AppendArgs a{};
@@ -544,6 +574,7 @@ int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int6
     a.bt_stride = block_table_stride;
     a.num_kv_heads = c.num_kv_heads;
     a.head_dim = c.head_dim;
+    a.page_size = c.page_size;
     hipError_t e = pa::launch_append(a, c.kv_dtype, c.q_dtype, c.max_q_len, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(h, PA_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
     return PA_OK;

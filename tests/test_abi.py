@@ -52,11 +52,35 @@ def test_create_rejects_bad_config_on_host(kw, code):
     assert pal.paged_attn_last_error(None) != ""
 
 
-def test_page_size_and_flags_rejected():
+@pytest.mark.parametrize("page_size", [0, 8, 24, 40, 65552])
+def test_page_size_not_a_multiple_of_16_rejected(page_size):
     cfg = _cfg()
-    cfg.page_size = 32
-    with pytest.raises(pal.PagedAttnError):
+    cfg.page_size = page_size
+    with pytest.raises(pal.PagedAttnError) as e:
         pal.paged_attn_create(cfg)
+    assert e.value.code == B.PA_ERR_UNSUPPORTED
+    assert "page_size" in pal.paged_attn_last_error(None)
+
+
+def test_page_chunk_division_by_multiply_high():
+    """The kernels find a 16-token chunk's page as umulhi(c, magic) >> shift
+    with the host's magic number for d = page_size / 16: exact for every
+    c < 2^24 (checked here on all of them for the pages' block sizes and a
+    few others)."""
+    import numpy as np
+
+    c = np.arange(1 << 24, dtype=np.uint64)
+    for d in (2, 3, 4, 5, 7, 64, 66, 99, 100, 127, 128, 129, 4095, 4096):
+        s = 0
+        while (1 << (s + 1)) < d:
+            s += 1
+        magic = ((1 << (32 + s)) + d - 1) // d
+        assert magic < (1 << 32)
+        q = ((c * np.uint64(magic)) >> np.uint64(32)) >> np.uint64(s)
+        assert np.array_equal(q, c // np.uint64(d)), d
+
+
+def test_flags_rejected():
     cfg = _cfg()
     cfg.flags = 1
     with pytest.raises(pal.PagedAttnError):

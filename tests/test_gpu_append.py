@@ -21,11 +21,16 @@ def _bits16(x: np.ndarray, dtype: str) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def _case(rng, kv_dtype, in_dtype, hkv, D, seq_lens, q_lens, pages, width):
+def _case(rng, kv_dtype, in_dtype, hkv, D, seq_lens, q_lens, pages, width, scales="pow2"):
     T = int(np.sum(q_lens))
     x = rng.standard_normal((2, T, hkv, D)).astype(np.float32)
     scale = None
-    if kv_dtype == "fp8_e4m3":
+    if kv_dtype == "fp8_e4m3" and scales == "arbitrary":
+        # scales as a quantiser derives them (any fp32 value): the quotient
+        # x / s is inexact, so its single fp32 rounding decides many codes
+        scale = rng.uniform(0.004, 0.05, (2, hkv)).astype(np.float32)
+        x *= rng.uniform(0.5, 40.0, (1, 1, hkv, 1)).astype(np.float32)
+    elif kv_dtype == "fp8_e4m3":
         # power-of-two scales keep the planted ties exact through the 16-bit
         # input and the fp32 quotient
         scale = rng.choice([0.125, 0.25, 0.5, 1.0, 2.0], (2, hkv)).astype(np.float32)
@@ -60,6 +65,11 @@ CASES = {
     "bf16_prefill_chunk": dict(kv="bf16", q="bf16", hkv=4, D=128, seq_lens=(700,), q_lens=(300,)),
     "fp8_from_bf16": dict(kv="fp8_e4m3", q="bf16", hkv=8, D=128, seq_lens=(40, 300, 5), q_lens=(8, 130, 5)),
     "fp8_from_f16_d64": dict(kv="fp8_e4m3", q="f16", hkv=2, D=64, seq_lens=(100, 31), q_lens=(16, 16)),
+    # arbitrary fp32 scales and plain data (no planted ties)
+    "fp8_from_bf16_any_scale": dict(kv="fp8_e4m3", q="bf16", hkv=8, D=128, seq_lens=(77, 1000, 16),
+                                    q_lens=(8, 200, 16), scales="arbitrary"),
+    "fp8_from_f16_any_scale": dict(kv="fp8_e4m3", q="f16", hkv=4, D=128, seq_lens=(500, 3), q_lens=(64, 3),
+                                   scales="arbitrary"),
 }
 
 
@@ -73,7 +83,8 @@ def test_append_bit_exact(name, layout):
     seq_lens, q_lens = np.array(cs["seq_lens"], np.int32), np.array(cs["q_lens"], np.int32)
     pages = int(sum((s + P - 1) // P for s in seq_lens)) + 5
     width = max((int(s) + P - 1) // P for s in seq_lens) + 1
-    bits, scale, pools, bt = _case(rng, cs["kv"], cs["q"], cs["hkv"], cs["D"], seq_lens, q_lens, pages, width)
+    bits, scale, pools, bt = _case(rng, cs["kv"], cs["q"], cs["hkv"], cs["D"], seq_lens, q_lens, pages, width,
+                                   cs.get("scales", "pow2"))
     progress(f"append {name} {layout}: seqs={seq_lens.tolist()} q={q_lens.tolist()}")
     T = int(q_lens.sum())
     cfg = pal.make_config(cs["hkv"] * 4, cs["hkv"], cs["D"], cs["q"], cs["kv"], len(seq_lens), int(q_lens.max()),
@@ -137,3 +148,119 @@ def test_append_skips_rows_outside_the_cache():
     # seq 0: positions 16..19 -> block 1 = page 99: outside the pool, skipped
     # seq 1: nothing; seq 2: positions 36..39 -> block 2: past the table width, skipped
     assert np.array_equal(written, expect)
+
+
+def _host_pool(inp, attr):
+    arr = getattr(inp, attr)
+    pool = np.full((inp.num_pages,) + arr.shape[1:], inp.fill_bits, dtype=arr.dtype)
+    pool[inp.live_pages] = arr
+    return pool
+
+
+@pytest.mark.parametrize("kind", ["f16_verify", "fp8_mixed"])
+def test_append_then_forward(kind):
+    """The step a decode loop runs: the new rows' slots start out NaN, the
+    append writes them, and the forward then reads them.  The pools after
+    the append equal the oracle's append bit for bit, and the forward
+    equals the oracle's attention over those pools."""
+    import dataclasses
+
+    import torch
+
+    from synth import Spec, generate
+    from synth.torch_upload import upload_batch, upload_pool
+    from tests.gpu_helpers import compare
+
+    if kind == "f16_verify":
+        spec = Spec(name=kind, num_q_heads=32, num_kv_heads=8, head_dim=128, seq_lens=(3001, 650), q_lens=(8, 5),
+                    q_dtype="f16", kv_dtype="f16", k_outlier_frac=0.01, seed=41)
+    else:
+        spec = Spec(name=kind, num_q_heads=32, num_kv_heads=8, head_dim=128, seq_lens=(9000, 2001, 300),
+                    q_lens=(1, 4, 8), q_dtype="bf16", kv_dtype="fp8_e4m3", seed=42)
+    inp = generate(spec)[0]
+    T, hkv, D = inp.num_tokens, inp.num_kv_heads, inp.head_dim
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal((2, T, hkv, D)).astype(np.float32)
+    new_bits = _bits16(x, inp.q_dtype)
+    # the cache before the step: the new rows' slots hold NaN
+    pools_before = []
+    for attr in ("k_live", "v_live"):
+        pool = _host_pool(inp, attr)
+        t = 0
+        for b in range(inp.num_seqs):
+            sl, ql = int(inp.seq_lens[b]), int(inp.q_lens[b])
+            for p in range(sl - ql, sl):
+                pool[inp.block_table[b, p // P], :, p % P, :] = inp.fill_bits
+        pools_before.append(pool)
+    ref_k, ref_v = oracle.append_kv(new_bits[0], new_bits[1], inp.q_dtype, pools_before[0], pools_before[1],
+                                    inp.kv_dtype, inp.block_table, inp.seq_lens, inp.q_lens, inp.kv_scale, P)
+    after = dataclasses.replace(inp, k_live=ref_k[inp.live_pages], v_live=ref_v[inp.live_pages])
+    before = dataclasses.replace(inp, k_live=pools_before[0][inp.live_pages], v_live=pools_before[1][inp.live_pages])
+    progress(f"append then forward {kind}: seqs={inp.seq_lens.tolist()} q={inp.q_lens.tolist()}")
+    pools = upload_pool([before])
+    d = upload_batch(before)
+    qt = getattr(torch, TORCH_16[inp.q_dtype])
+    kn = torch.from_numpy(new_bits[0].view(np.int16)).cuda().view(qt).contiguous()
+    vn = torch.from_numpy(new_bits[1].view(np.int16)).cuda().view(qt).contiguous()
+    cfg = pal.make_config(inp.num_q_heads, hkv, D, inp.q_dtype, inp.kv_dtype, inp.num_seqs, int(inp.q_lens.max()), T)
+    h = pal.paged_attn_create(cfg)
+    try:
+        out = torch.full((T, inp.num_q_heads, D), float("nan"), device="cuda")
+        lse = torch.full((T, inp.num_q_heads), float("nan"), device="cuda")
+        pal.paged_attn_append(h, kn, vn, pools["k"], pools["v"], d["block_table"], d["seq_lens"], d["q_lens"],
+                              d["kv_scale"])
+        pal.paged_attn_forward(h, d["q"], pools["k"], pools["v"], d["block_table"], d["seq_lens"], d["q_lens"],
+                               inp.window, inp.scale, d["kv_scale"], out, lse)
+        torch.cuda.synchronize()
+        got = [pools[w].cpu().numpy().view(np.uint8 if inp.kv_dtype == "fp8_e4m3" else np.uint16) for w in "kv"]
+        o, l = out.cpu().numpy(), lse.cpu().numpy()
+    finally:
+        pal.paged_attn_destroy(h)
+    assert np.array_equal(got[0], ref_k) and np.array_equal(got[1], ref_v)
+    ref_o, ref_l = oracle.attention(after)
+    compare(f"append then forward {kind}", inp.kv_dtype, o, l, ref_o, ref_l)
+
+
+def test_append_host_argument_errors():
+    """Host checks of paged_attn_append, through the C ABI directly: missing
+    or unexpected kv_scale, misaligned rows, num_tokens outside the handle's
+    range, NULL pointers.  Nothing is launched for a rejected call."""
+    import ctypes
+
+    import torch
+
+    from paged_attention_long_amd import binding as B
+
+    lib = pal.load_library()
+    hkv, D, pages = 2, 128, 4
+    dev = torch.device("cuda")
+    for kv in ("fp8_e4m3", "bf16"):
+        cfg = pal.make_config(8, hkv, D, "bf16", kv, 2, 4, 8)
+        h = pal.paged_attn_create(cfg)
+        try:
+            st = torch.uint8 if kv == "fp8_e4m3" else torch.bfloat16
+            kc = torch.zeros((pages, hkv, P, D), dtype=st, device=dev)
+            layout = B.cache_layout(kc)
+            new = torch.zeros((9, hkv, D), dtype=torch.bfloat16, device=dev)
+            bt = torch.zeros((2, 2), dtype=torch.int32, device=dev)
+            sl = torch.tensor([5, 3], dtype=torch.int32, device=dev)
+            ql = torch.tensor([4, 3], dtype=torch.int32, device=dev)
+            sc = torch.ones(2 * hkv, device=dev)
+            good_scale = sc.data_ptr() if kv == "fp8_e4m3" else None
+            bad_scale = None if kv == "fp8_e4m3" else sc.data_ptr()
+
+            def call(k_new=new.data_ptr(), num_tokens=7, kv_scale=good_scale, k_cache=kc.data_ptr(),
+                     block_table=bt.data_ptr()):
+                return lib.paged_attn_append(h.ptr, k_new, new.data_ptr(), num_tokens, k_cache, kc.data_ptr(),
+                                             ctypes.byref(layout), block_table, 2, 2, sl.data_ptr(), ql.data_ptr(),
+                                             kv_scale, None)
+
+            assert call() == B.PA_OK
+            torch.cuda.synchronize()
+            for kw in (dict(kv_scale=bad_scale), dict(k_new=new.data_ptr() + 2), dict(num_tokens=0),
+                       dict(num_tokens=9), dict(k_new=None), dict(k_cache=None), dict(block_table=None)):
+                rc = call(**kw)
+                assert rc == B.PA_ERR_INVALID_ARGUMENT, (kv, kw, rc)
+                assert pal.paged_attn_last_error(h) != ""
+        finally:
+            pal.paged_attn_destroy(h)

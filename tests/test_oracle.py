@@ -159,6 +159,13 @@ def test_block_table_permutation_is_bitwise_invariant(kv):
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
+def test_block_table_permutation_invariant_with_48_token_pages():
+    inp = _one(seq_lens=(200, 47), q_lens=(4, 2), page_size=48, pool_pages=20)
+    o1, l1 = oracle.attention(inp)
+    o2, l2 = oracle.attention(permute_pool(inp, 5))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 def test_gqa_equals_mha_with_replicated_heads():
     inp = _one(seq_lens=(33,), q_lens=(2,), num_q_heads=6, num_kv_heads=2)
     out, lse = oracle.attention(inp)
@@ -210,6 +217,11 @@ BRUTE = [
     dict(seq_lens=(50,), q_lens=(5,), kv_dtype="bf16", q_dtype="bf16", num_q_heads=4, num_kv_heads=4),
     dict(seq_lens=(70, 12), q_lens=(4, 1), kv_dtype="fp8_e4m3", q_dtype="bf16", window=13),
     dict(seq_lens=(26,), q_lens=(2,), page_size=16, k_outlier_frac=0.1),
+    # pages of 48 and of 1,056 tokens (the pages' hybrid-model block size,
+    # "tps-maxxing on amd gpu", section "Baseline"): a token's page and slot
+    # come from a division by a page size that is no power of two
+    dict(seq_lens=(100, 49), q_lens=(3, 1), page_size=48, window=30),
+    dict(seq_lens=(1100,), q_lens=(2,), page_size=1056, kv_dtype="fp8_e4m3", q_dtype="bf16"),
 ]
 
 
