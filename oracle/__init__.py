@@ -11,7 +11,7 @@ rows against a paged KV cache:
 
 with grouped-query heads (query head h reads KV head h // (Hq/Hkv)), a causal
 mask inside the new rows, an optional sliding window, and a dequantised fp8
-cache.  The cache is first copied out of its pages into a dense, logical
+(per-head scales) or int8 (per-row scales) cache.  The cache is first copied out of its pages into a dense, logical
 token order (an explicit de-paging step), then every sum runs only over the
 keys a row may see, in float64.  Sources: "Dual MI50, part 2" (blog.sbm-labs
 .com), sections "Bug 2: the drafter read freed memory", "Kernels: why the
@@ -23,7 +23,7 @@ It shares no code with the HIP path; its only inputs are the storage bits and
 integer metadata that the seeded generator produces.
 """
 from .codec import decode_bits, fp8_e4m3_table  # noqa: F401
-from .append import append_kv, e4m3_encode, new_row_positions  # noqa: F401
+from .append import append_kv, e4m3_encode, int8_encode_row, new_row_positions  # noqa: F401
 from .attention import (  # noqa: F401
     attention,
     attention_rows,

@@ -55,14 +55,47 @@ def new_row_positions(seq_len: int, q_len: int) -> np.ndarray:
     return np.arange(seq_len - q_len, seq_len, dtype=np.int64)
 
 
+def int8_encode_row(x) -> tuple:
+    """int8 codes (as uint8 bits) and fp32 scale of one row of fp32 values:
+    scale = amax / 127 with amax the largest |x| of the row (NaN if the row
+    holds a NaN, infinity if it holds an infinity), code = x / scale rounded
+    to the nearest integer, ties to even, limited to [-127, 127], both the
+    division and amax / 127 in fp32; a NaN quotient (a zero or non-finite
+    row) stores code 0.  This is the per-row quantisation of the pages' int8
+    cache ("Dual MI50, part 2", section "Prefill: teach the fork's fast kernel
+    to read the int8 cache"), in the plainest reading: symmetric, absolute
+    maximum, round to nearest."""
+    x = np.asarray(x, dtype=np.float32)
+    a = np.abs(x)
+    amax = np.float32(np.nan) if np.isnan(a).any() else a.max()
+    scale = np.float32(amax / np.float32(127.0))
+    codes = np.zeros(x.shape, dtype=np.int8)
+    for i, v in enumerate(x.tolist()):
+        with np.errstate(divide="ignore", invalid="ignore"):
+            q = float(np.float32(v) / scale)        # one fp32 rounding
+        if q != q:
+            continue
+        q = min(max(q, -127.0), 127.0)
+        n = int(np.floor(q))
+        frac = q - n
+        if frac > 0.5 or (frac == 0.5 and n % 2 != 0):
+            n += 1
+        codes[i] = n
+    return codes.view(np.uint8), scale
+
+
 def append_kv(k_new: np.ndarray, v_new: np.ndarray, in_dtype: str, k_pool: np.ndarray, v_pool: np.ndarray,
-              cache_dtype: str, block_table: np.ndarray, seq_lens, q_lens, kv_scale=None, page_size: int = 16):
+              cache_dtype: str, block_table: np.ndarray, seq_lens, q_lens, kv_scale=None, page_size: int = 16,
+              row_scale=None):
     """Pools (storage bits, [num_pages][Hkv][P][D]) after writing the new rows.
 
     k_new, v_new: storage bits [T][Hkv][D] of dtype in_dtype ("f16"/"bf16"),
     rows of sequence 0 first.  kv_scale: fp32 [2][Hkv] (fp8 caches only).
-    Returns new arrays; the inputs are not modified."""
+    row_scale: fp32 [2][num_pages][Hkv][P] row scales (int8 caches only).
+    Returns new arrays (k, v, and for int8 the row scales); the inputs are
+    not modified."""
     k_out, v_out = k_pool.copy(), v_pool.copy()
+    rs_out = None if row_scale is None else np.array(row_scale, dtype=np.float32, copy=True)
     hkv = k_new.shape[1]
     t = 0
     for b, (sl, ql) in enumerate(zip(np.asarray(seq_lens).tolist(), np.asarray(q_lens).tolist())):
@@ -78,7 +111,12 @@ def append_kv(k_new: np.ndarray, v_new: np.ndarray, in_dtype: str, k_pool: np.nd
                         x = decode_bits(bits, in_dtype).astype(np.float32)      # exact: 16-bit values fit fp32
                         s = np.float32(np.asarray(kv_scale, dtype=np.float32).reshape(2, hkv)[which, g])
                         dst[page, g, slot, :] = e4m3_encode(x / s)               # fp32 quotient
+                    elif cache_dtype == "int8":
+                        x = decode_bits(bits, in_dtype).astype(np.float32)
+                        dst[page, g, slot, :], rs_out[which, page, g, slot] = int8_encode_row(x)
                     else:
                         raise ValueError(f"cannot store {in_dtype} rows in a {cache_dtype} cache")
         t += ql
+    if cache_dtype == "int8":
+        return k_out, v_out, rs_out
     return k_out, v_out

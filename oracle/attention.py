@@ -18,7 +18,11 @@ the design notes):
   * query head h reads KV head h // (Hq / Hkv) ("Dual MI50, part 2",
     section "Decode: a new kernel for the shape MTP actually runs": several
     query heads share each KV head);
-  * the fp8 cache value is code * scale[K or V, kv head], and the softmax
+  * the fp8 cache value is code * scale[K or V, kv head]; the int8 cache
+    value is code * (the fp32 scale of its own row: one token of one KV
+    head, K and V separately), the pages' own cache format ("Dual MI50,
+    part 2", section "Prefill: teach the fork's fast kernel to read the int8
+    cache": the cache is read in place with its per-row scales); the softmax
     scale multiplies q.k after that dequantisation;
   * lse is the natural log of the sum of exp over the visible scaled scores.
 """
@@ -64,12 +68,23 @@ def _page_bits(inp, which: str, phys: int, live_index: np.ndarray) -> np.ndarray
     return arr[li]
 
 
+def _page_row_scales(inp, which: str, phys: int, live_index: np.ndarray) -> np.ndarray:
+    """fp32 row scales [Hkv, P] of physical page ``phys`` (int8 caches); a page
+    that holds no live data has NaN scales."""
+    li = live_index[phys]
+    shape = inp.row_scale.shape[2:]
+    if li < 0:
+        return np.full(shape, np.nan, dtype=np.float32)
+    return inp.row_scale[0 if which == "k" else 1, li]
+
+
 def depage(inp, which: str, b: int, g: int, lo: int, hi: int,
            live_index: Optional[np.ndarray] = None) -> np.ndarray:
     """Explicit copy of logical tokens [lo, hi) of sequence b, KV head g.
 
     Token j lives in physical page block_table[b][j // P], slot j % P.
-    Returns float64 [hi - lo, D] holding the dequantised values.  Only the
+    Returns float64 [hi - lo, D] holding the dequantised values (an int8
+    row times its own scale from the same page and slot).  Only the
     requested tokens' pages are touched.
     """
     P = int(inp.page_size)
@@ -85,6 +100,9 @@ def depage(inp, which: str, b: int, g: int, lo: int, hi: int,
         s0 = j % P
         s1 = min(P, s0 + (hi - j))
         outv[j - lo:j - lo + (s1 - s0)] = decode_bits(page[g, s0:s1, :], inp.kv_dtype)
+        if inp.kv_dtype == "int8":
+            rs = _page_row_scales(inp, which, phys, live_index)[g, s0:s1].astype(np.float64)
+            outv[j - lo:j - lo + (s1 - s0)] *= rs[:, None]
         j += s1 - s0
     if inp.kv_dtype == "fp8_e4m3":
         s = float(inp.kv_scale[0 if which == "k" else 1][g])

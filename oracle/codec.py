@@ -9,10 +9,12 @@
   largest finite magnitude is 1.75 * 2^8 = 448.  The table below is built
   from that definition, one code at a time.
 
-Per-KV-head fp32 scales are applied by the caller after decoding
-(BASELINE workload: fp8 e4m3 KV with per-KV-head fp32 scales; the pages'
-own cache used int8 with per-row scales, "Dual MI50, part 2", section
-"Prefill: teach the fork's fast kernel to read the int8 cache").
+* int8: two's-complement signed bytes; the value is the integer itself.
+
+Scales are applied by the caller after decoding: one fp32 scale per KV head
+for fp8 caches, one fp32 scale per cached row (token and KV head) for int8
+caches, the pages' own format ("Dual MI50, part 2", section "Prefill: teach
+the fork's fast kernel to read the int8 cache").
 """
 from __future__ import annotations
 
@@ -48,4 +50,6 @@ def decode_bits(bits: np.ndarray, dtype: str) -> np.ndarray:
             return u32.view(np.float32).astype(np.float64)
     if dtype == "fp8_e4m3":
         return _FP8_TABLE[np.asarray(bits, dtype=np.uint8)]
+    if dtype == "int8":
+        return np.asarray(bits, dtype=np.uint8).view(np.int8).astype(np.float64)
     raise ValueError(f"unknown dtype {dtype!r}")

@@ -25,7 +25,14 @@ Recipe (the same for every workload):
     ``poison_out_of_window`` every page whose tokens all fall before the
     first query row's window holds NaN in K and V (freed-and-reused pages);
   * fp8 (OCP E4M3FN) caches are quantised per (K or V, KV head) with scale
-    ``amax/448`` over that head's live tokens, codes saturated to +-448.
+    ``amax/448`` over that head's live tokens, codes saturated to +-448;
+  * int8 caches carry one fp32 scale per cached row (one token of one KV
+    head, K and V separately), the pages' own cache format ("Dual MI50,
+    part 2", section "Prefill: teach the fork's fast kernel to read the int8
+    cache"): scale ``amax/127`` over the row's D values, code the nearest
+    integer to ``x/scale`` (ties to even, both steps in fp32) within
+    [-127, 127]; a dead slot (tail, unused page, poisoned page) holds code
+    -128 and a NaN scale.
 
 Nothing here computes attention.  The returned arrays are raw storage bits;
 consumers decode them with their own code.
@@ -40,9 +47,12 @@ from typing import List, Optional, Sequence
 import numpy as np
 
 # Canonical quiet-NaN storage patterns.
-NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0, "fp8_e4m3": 0x7F}
-STORAGE_NP = {"f16": np.uint16, "bf16": np.uint16, "fp8_e4m3": np.uint8}
-ELEM_BYTES = {"f16": 2, "bf16": 2, "fp8_e4m3": 1}
+# (int8 has no NaN code: a dead int8 slot holds -128, never produced by the
+# quantiser, and its row scale is NaN.)
+NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0, "fp8_e4m3": 0x7F, "int8": 0x80}
+STORAGE_NP = {"f16": np.uint16, "bf16": np.uint16, "fp8_e4m3": np.uint8, "int8": np.uint8}
+ELEM_BYTES = {"f16": 2, "bf16": 2, "fp8_e4m3": 1, "int8": 1}
+ROW_SCALE_BYTES = {"int8": 4}   # per cached row (token, KV head) of K or of V
 FP8_E4M3_MAX = 448.0
 
 
@@ -101,6 +111,7 @@ class PagedInputs:
     seed: int = 0
     batch: int = 0
     extra: dict = field(default_factory=dict)
+    row_scale: Optional[np.ndarray] = None   # float32 [2, n_live, Hkv, P] (K, then V) for int8, else None
 
     @property
     def num_seqs(self) -> int:
@@ -123,13 +134,15 @@ class PagedInputs:
         return 0, s
 
     def kv_bytes(self) -> int:
-        """K+V bytes of the visible token ranges, once per KV head."""
+        """K+V bytes of the visible token ranges, once per KV head (with each
+        row's scale for int8 caches)."""
         tot = 0
         for b in range(self.num_seqs):
             lo, hi = self.visible_range(b)
             if int(self.q_lens[b]) > 0:
                 tot += (hi - lo)
-        return 2 * tot * self.num_kv_heads * self.head_dim * ELEM_BYTES[self.kv_dtype]
+        row = self.head_dim * ELEM_BYTES[self.kv_dtype] + ROW_SCALE_BYTES.get(self.kv_dtype, 0)
+        return 2 * tot * self.num_kv_heads * row
 
     def pair_count(self) -> int:
         """Visible (query row, key) pairs per query head."""
@@ -146,6 +159,18 @@ class PagedInputs:
     def flops(self) -> int:
         """4*D per visible (row, key) pair per query head (Q.K^T and P.V)."""
         return 4 * self.head_dim * self.pair_count() * self.num_q_heads
+
+
+def _int8_rows(x: np.ndarray):
+    """Codes (uint8 bits of int8) and fp32 scales of rows x[..., D]: scale =
+    amax/127, code = nearest integer to x/scale, ties to even, in [-127, 127];
+    a zero row (scale 0) gets zero codes."""
+    amax = np.abs(x).max(axis=-1)
+    sc = (amax / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        qv = x / sc[..., None]
+    qv = np.where(np.isnan(qv), np.float32(0.0), np.clip(np.rint(qv), -127.0, 127.0))
+    return qv.astype(np.int8).view(np.uint8), sc
 
 
 def _to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
@@ -249,10 +274,18 @@ def generate(spec: Spec, seed: Optional[int] = None, batches: int = 1) -> List[P
                     s_h = np.float32(a) / np.float32(FP8_E4M3_MAX) if a > 0 else np.float32(1.0)
                     kv_scale[which, h] = s_h
                     arr[:, h, :, :] /= s_h
-        kb = _to_bits(kf, spec.kv_dtype)
-        del kf
-        vb = _to_bits(vf, spec.kv_dtype)
-        del vf
+        row_scale = None
+        if spec.kv_dtype == "int8":
+            row_scale = np.empty((2, n_live, Hk, P), dtype=np.float32)
+            kb, row_scale[0] = _int8_rows(kf)
+            del kf
+            vb, row_scale[1] = _int8_rows(vf)
+            del vf
+        else:
+            kb = _to_bits(kf, spec.kv_dtype)
+            del kf
+            vb = _to_bits(vf, spec.kv_dtype)
+            del vf
         qb = _to_bits(qf, spec.q_dtype)
         del qf
 
@@ -261,6 +294,8 @@ def generate(spec: Spec, seed: Optional[int] = None, batches: int = 1) -> List[P
         dead = ~live_mask
         kb[np.nonzero(dead)[0], :, np.nonzero(dead)[1], :] = nanb
         vb[np.nonzero(dead)[0], :, np.nonzero(dead)[1], :] = nanb
+        if row_scale is not None:
+            row_scale[:, np.nonzero(dead)[0], :, np.nonzero(dead)[1]] = np.nan
         poisoned = []
         if spec.poison_out_of_window and spec.window > 0:
             for b in range(B):
@@ -270,6 +305,8 @@ def generate(spec: Spec, seed: Optional[int] = None, batches: int = 1) -> List[P
                 if n_dead:
                     kb[offs[b]:offs[b] + n_dead] = nanb
                     vb[offs[b]:offs[b] + n_dead] = nanb
+                    if row_scale is not None:
+                        row_scale[:, offs[b]:offs[b] + n_dead] = np.nan
                     poisoned.append((b, n_dead))
 
         out.append(PagedInputs(
@@ -277,7 +314,7 @@ def generate(spec: Spec, seed: Optional[int] = None, batches: int = 1) -> List[P
             q_dtype=spec.q_dtype, kv_dtype=spec.kv_dtype, window=int(spec.window), scale=scale,
             seq_lens=seq_lens.astype(np.int32), q_lens=q_lens.astype(np.int32), block_table=bt,
             num_pages=int(pool), live_pages=live, page_offsets=offs, k_live=kb, v_live=vb, q=qb,
-            kv_scale=kv_scale, fill_bits=nanb, nan_page=nan_page, seed=seed, batch=bi,
+            kv_scale=kv_scale, fill_bits=nanb, nan_page=nan_page, seed=seed, batch=bi, row_scale=row_scale,
             extra={"outliers": outl, "poisoned_pages": poisoned, **extra_float},
         ))
     return out
@@ -320,6 +357,12 @@ NAMED_SPECS = {
         name="mixed_fp8", num_q_heads=32, num_kv_heads=8, head_dim=128,
         seq_lens=(200001, 131076, 32776, 4097), q_lens=(1, 4, 8, 1),
         q_dtype="bf16", kv_dtype="fp8_e4m3", pool_pages=32768, seed=1005),
+    # the same long mixed batch on the pages' own cache format: int8 codes
+    # with a fp32 scale per cached row
+    "mixed_int8": Spec(
+        name="mixed_int8", num_q_heads=32, num_kv_heads=8, head_dim=128,
+        seq_lens=(200001, 131076, 32776, 4097), q_lens=(1, 4, 8, 1),
+        q_dtype="bf16", kv_dtype="int8", pool_pages=32768, seed=1006),
 }
 
 

@@ -23,7 +23,7 @@ def _bits_tensor(a: np.ndarray) -> torch.Tensor:
 
 
 def _fill_value(inp: PagedInputs) -> int:
-    if inp.kv_dtype == "fp8_e4m3":
+    if inp.kv_dtype in ("fp8_e4m3", "int8"):
         return int(inp.fill_bits)
     return int(np.array(inp.fill_bits, dtype=np.uint16).view(np.int16))
 
@@ -33,6 +33,8 @@ def upload_pool(batches: List[PagedInputs], device="cuda", layout: str = "hnd") 
 
     layout "hnd": [pages, Hkv, P, D] contiguous; "nhd": storage is
     [pages, P, Hkv, D] and the returned tensors are [pages, Hkv, P, D] views.
+    int8 caches also get "row_scale": the contiguous fp32 row-scale storage
+    (K scales, then V scales), the kv_scale argument of an int8 forward.
     """
     f = batches[0]
     sdtype = torch.int16 if f.kv_dtype in ("f16", "bf16") else torch.uint8
@@ -42,6 +44,17 @@ def upload_pool(batches: List[PagedInputs], device="cuda", layout: str = "hnd") 
     else:
         store = shape
     pools = {}
+    if f.row_scale is not None:
+        # one fp32 scale per cached row, laid out like the cache with rows of
+        # one element: [2][pages][Hkv][P] (HND) or [2][pages][P][Hkv] (NHD);
+        # rows of pages no batch owns hold NaN
+        sstore = (2, f.num_pages, f.page_size, f.num_kv_heads) if layout == "nhd" else (2,) + shape[:3]
+        rs = torch.full(sstore, float("nan"), dtype=torch.float32, device=device)
+        rview = rs.permute(0, 1, 3, 2) if layout == "nhd" else rs
+        for inp in batches:
+            idx = torch.from_numpy(inp.live_pages.astype(np.int64)).to(device)
+            rview[:, idx] = torch.from_numpy(np.ascontiguousarray(inp.row_scale)).to(device)
+        pools["row_scale"] = rs
     for name, attr in (("k", "k_live"), ("v", "v_live")):
         pool = torch.full(store, _fill_value(f), dtype=sdtype, device=device)
         view = pool.permute(0, 2, 1, 3) if layout == "nhd" else pool

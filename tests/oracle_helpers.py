@@ -10,8 +10,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-_TORCH = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8_e4m3": torch.float8_e4m3fn}
-_VIEW = {"f16": torch.int16, "bf16": torch.int16, "fp8_e4m3": torch.uint8}
+_TORCH = {"f16": torch.float16, "bf16": torch.bfloat16, "fp8_e4m3": torch.float8_e4m3fn, "int8": torch.int8}
+_VIEW = {"f16": torch.int16, "bf16": torch.int16, "fp8_e4m3": torch.uint8, "int8": torch.uint8}
 
 
 def torch_decode(bits: np.ndarray, dtype: str) -> np.ndarray:
@@ -36,6 +36,16 @@ def dense_view(inp, b: int):
     if inp.kv_dtype == "fp8_e4m3":
         kk = kk * inp.kv_scale[0][:, None, None].astype(np.float64)
         vv = vv * inp.kv_scale[1][:, None, None].astype(np.float64)
+    if inp.kv_dtype == "int8":
+        # the generator's own per-row scales, in (logical page, slot) order
+        n = (s + P - 1) // P
+        for w, arr in ((0, "kk"), (1, "vv")):
+            rs = inp.row_scale[w, o0:o0 + n].astype(np.float64)          # [pages, Hkv, P]
+            rs = rs.transpose(1, 0, 2).reshape(inp.num_kv_heads, -1)[:, :s]
+            if w == 0:
+                kk = kk * rs[:, :, None]
+            else:
+                vv = vv * rs[:, :, None]
     t0 = int(np.sum(inp.q_lens[:b]))
     qq = torch_decode(inp.q[t0:t0 + ql], inp.q_dtype)
     return qq.tolist(), kk.tolist(), vv.tolist()

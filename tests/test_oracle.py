@@ -151,7 +151,7 @@ def test_probabilities_sum_to_one():
         assert np.all(p >= 0)
 
 
-@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("kv", ["f16", "bf16", "fp8_e4m3", "int8"])
 def test_block_table_permutation_is_bitwise_invariant(kv):
     inp = _one(seq_lens=(61, 17, 4), q_lens=(2, 1, 4), kv_dtype=kv, pool_pages=80)
     o1, l1 = oracle.attention(inp)
@@ -222,6 +222,9 @@ BRUTE = [
     # come from a division by a page size that is no power of two
     dict(seq_lens=(100, 49), q_lens=(3, 1), page_size=48, window=30),
     dict(seq_lens=(1100,), q_lens=(2,), page_size=1056, kv_dtype="fp8_e4m3", q_dtype="bf16"),
+    # int8 codes with a scale per cached row
+    dict(seq_lens=(60, 9), q_lens=(4, 1), kv_dtype="int8", q_dtype="bf16", window=21, k_outlier_frac=0.1),
+    dict(seq_lens=(100,), q_lens=(2,), kv_dtype="int8", q_dtype="f16", page_size=48),
 ]
 
 
@@ -279,3 +282,93 @@ def test_window_nan_poison_finite_and_unchanged():
     o2, l2 = oracle.attention(dirty)
     assert np.all(np.isfinite(o2)) and np.all(np.isfinite(l2))
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+# ------------------------------------------------------------------ int8 with per-row scales
+
+def test_int8_decode_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch_decode(codes, "int8")
+    assert np.array_equal(oracle.decode_bits(codes, "int8"), ref)
+    assert oracle.decode_bits(np.array([0x80, 0x7F, 0xFF], np.uint8), "int8").tolist() == [-128.0, 127.0, -1.0]
+
+
+@pytest.mark.parametrize("window", [0, 7])
+def test_int8_row_scale_position_probe(window):
+    """Q = 0 makes every visible score equal; V codes of 1 with row scale
+    j + 1 (token j's own scale, set through its page and slot in the
+    generator's live order) put the mean of j + 1 over the visible keys in
+    every output column.  A scale taken from another page, slot or head
+    breaks it."""
+    s, ql, P = 100, 3, 16
+    inp = _one(seq_lens=(s, 40), q_lens=(ql, 2), num_q_heads=4, num_kv_heads=2, kv_dtype="int8", q_dtype="bf16",
+               page_size=P, window=window, pool_pages=30)
+    inp.q[:] = 0
+    inp.v_live[:] = 1
+    n0 = (s + P - 1) // P
+    for b, (sl, o0) in enumerate(((s, 0), (40, n0))):
+        for j in range(sl):
+            for g in range(2):
+                inp.row_scale[1, o0 + j // P, g, j % P] = np.float32(j + 1 + 1000 * g + 500 * b)
+    out, lse = oracle.attention(inp)
+    t = 0
+    for b, (sl, q) in enumerate(((s, ql), (40, 2))):
+        for i in range(q):
+            p = sl - q + i
+            lo = max(0, p - window + 1) if window > 0 else 0
+            for h in range(4):
+                g = h // 2
+                want = (lo + p) / 2 + 1 + 1000 * g + 500 * b
+                np.testing.assert_allclose(out[t + i, h], want, rtol=0, atol=1e-10)
+                assert lse[t + i, h] == pytest.approx(math.log(p - lo + 1), abs=1e-12)
+        t += q
+
+
+def test_int8_identical_rows_scale_the_score():
+    """Every key the same int8 row c but with its own scale s_j: the scores
+    are scale * s_j * (q . c), so the oracle's lse is the closed form
+    log sum_j exp(scale * s_j * (q . c))."""
+    n = 37
+    inp = _one(seq_lens=(n,), q_lens=(1,), num_q_heads=2, num_kv_heads=1, kv_dtype="int8", q_dtype="bf16",
+               head_dim=8)
+    c = inp.k_live[0, 0, 0].copy()
+    inp.k_live[:, 0, :, :] = c
+    rng = np.random.default_rng(5)
+    P = inp.page_size
+    sj = rng.uniform(0.01, 0.3, n).astype(np.float32)
+    for j in range(n):
+        inp.row_scale[0, j // P, 0, j % P] = sj[j]
+    _, lse = oracle.attention(inp)
+    cv = oracle.decode_bits(c, "int8")
+    for h in range(2):
+        qv = torch_decode(inp.q[0, h], "bf16")
+        dot = math.fsum(qv * cv)
+        sc = [float(np.float32(inp.scale)) * float(x) * dot for x in sj]
+        m = max(sc)
+        want = m + math.log(math.fsum(math.exp(x - m) for x in sc))
+        assert abs(lse[0, h] - want) < 1e-12
+
+
+def test_int8_window_nan_poison_finite_and_unchanged():
+    clean = _one(seq_lens=(130,), q_lens=(8,), window=20, pool_pages=64, kv_dtype="int8", q_dtype="bf16")
+    dirty = _one(seq_lens=(130,), q_lens=(8,), window=20, pool_pages=64, kv_dtype="int8", q_dtype="bf16",
+                 poison_out_of_window=True)
+    n_dead = dirty.extra["poisoned_pages"][0][1]
+    assert np.all(np.isnan(dirty.row_scale[:, :n_dead]))
+    o1, l1 = oracle.attention(clean)
+    o2, l2 = oracle.attention(dirty)
+    assert np.all(np.isfinite(o2)) and np.all(np.isfinite(l2))
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_int8_dequantisation_recovers_data():
+    """code * row scale reproduces the float data within half a code step
+    (scale / 2) on every live row."""
+    inp = _one(seq_lens=(40,), q_lens=(1,), kv_dtype="int8", q_dtype="bf16", keep_float=True)
+    for which, key in (("k", "k_float"), ("v", "v_float")):
+        ref = inp.extra[key]
+        for g in range(inp.num_kv_heads):
+            got = oracle.depage(inp, which, 0, g, 0, 40)
+            want = ref[:, g].reshape(-1, inp.head_dim)[:40].astype(np.float64)
+            rs = inp.row_scale[0 if which == "k" else 1][:, g].reshape(-1)[:40].astype(np.float64)
+            assert np.all(np.abs(got - want) <= rs[:, None] * 0.5 * (1 + 1e-6))

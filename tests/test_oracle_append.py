@@ -99,3 +99,76 @@ def test_append_brute_force(cache_dtype):
             if not touched[pg, sl]:
                 assert np.array_equal(k_out[pg, :, sl], k_pool[pg, :, sl])
                 assert np.array_equal(v_out[pg, :, sl], v_pool[pg, :, sl])
+
+
+# ------------------------------------------------------------------ int8 rows with their own scale
+
+def _torch_int8_row(x):
+    """The same definition through torch's ops: fp32 amax / 127, fp32
+    quotient, torch.round (half to even), clamp; NaN quotients to 0."""
+    t = torch.from_numpy(np.asarray(x, dtype=np.float32))
+    s = t.abs().max() / torch.tensor(127.0, dtype=torch.float32)
+    q = torch.round(t / s).clamp(-127, 127)
+    q = torch.where(torch.isnan(q), torch.zeros_like(q), q)
+    return q.to(torch.int8).view(torch.uint8).numpy(), np.float32(s.item())
+
+
+def test_int8_rows_match_torch_ops():
+    rng = np.random.default_rng(11)
+    for scale in (1e-3, 0.3, 1.0, 50.0, 3e4):
+        for _ in range(200):
+            x = (rng.standard_normal(128) * scale).astype(np.float32)
+            c, s = oracle.int8_encode_row(x)
+            tc, ts = _torch_int8_row(x)
+            assert s == ts
+            assert np.array_equal(c, tc)
+
+
+def test_int8_row_closed_forms():
+    # exact multiples of a power-of-two scale: the codes are the integers
+    k = np.arange(-127, 128, dtype=np.float32)
+    c, s = oracle.int8_encode_row(k * np.float32(0.125))
+    assert s == np.float32(0.125 * 127 / 127)
+    assert np.array_equal(c.view(np.int8), k.astype(np.int8))
+    # halfway between integers (exact in fp32): to the even integer
+    x = np.array([127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5], dtype=np.float32)
+    c, s = oracle.int8_encode_row(x)
+    assert s == np.float32(1.0)
+    assert c.view(np.int8).tolist() == [127, 0, 2, 2, 0, -2, -2, 126]
+    # the largest magnitude maps to +-127, a zero row to zeros with scale 0
+    c, s = oracle.int8_encode_row(np.array([-3.0, 1.0, 2.0], np.float32))
+    assert c.view(np.int8)[0] == -127
+    c, s = oracle.int8_encode_row(np.zeros(16, np.float32))
+    assert s == 0 and not c.any()
+    # a NaN in the row: NaN scale, codes 0
+    c, s = oracle.int8_encode_row(np.array([1.0, np.nan, 2.0], np.float32))
+    assert np.isnan(s) and not c.any()
+
+
+def test_int8_append_places_rows_and_scales():
+    """append_kv with an int8 cache writes each new row's codes and its scale
+    to the row's own page and slot (brute force over a small pool)."""
+    rng = np.random.default_rng(12)
+    hkv, D, P, pages = 2, 16, 16, 9
+    seq_lens, q_lens = np.array([20, 5, 33]), np.array([4, 0, 3])
+    T = int(q_lens.sum())
+    new = rng.standard_normal((2, T, hkv, D)).astype(np.float32)
+    bits = torch.from_numpy(new).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    pool = rng.integers(0, 256, (2, pages, hkv, P, D)).astype(np.uint8)
+    rs = rng.uniform(0, 1, (2, pages, hkv, P)).astype(np.float32)
+    bt = np.array([[3, 5, 0], [1, 0, 0], [7, 2, 8]], dtype=np.int32)
+    k2, v2, rs2 = append_kv(bits[0], bits[1], "bf16", pool[0], pool[1], "int8", bt, seq_lens, q_lens,
+                            page_size=P, row_scale=rs)
+    want_k, want_v, want_rs = pool[0].copy(), pool[1].copy(), rs.copy()
+    t = 0
+    for b in range(3):
+        for i in range(int(q_lens[b])):
+            p = int(seq_lens[b] - q_lens[b] + i)
+            pg, sl = int(bt[b, p // P]), p % P
+            for g in range(hkv):
+                for w, dst in ((0, want_k), (1, want_v)):
+                    x = oracle.decode_bits(bits[w, t + i, g], "bf16").astype(np.float32)
+                    dst[pg, g, sl], want_rs[w, pg, g, sl] = _torch_int8_row(x)
+        t += int(q_lens[b])
+    assert np.array_equal(k2, want_k) and np.array_equal(v2, want_v)
+    assert np.array_equal(rs2, want_rs)

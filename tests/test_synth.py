@@ -60,6 +60,22 @@ def test_fp8_codes_in_range():
     assert np.abs(fin).max() == 448.0     # amax maps to the largest code
 
 
+def test_int8_codes_and_row_scales():
+    x = generate(_small(seq_lens=(37, 5), q_lens=(2, 1), kv_dtype="int8", q_dtype="bf16", window=10,
+                        poison_out_of_window=True, keep_float=True))[0]
+    assert x.kv_scale is None and x.row_scale.shape == (2,) + x.k_live.shape[:3]
+    codes = x.k_live.view(np.int8)
+    live = np.isfinite(x.row_scale[0])
+    # live rows: codes in [-127, 127] and the row's largest |x| at +-127
+    assert np.abs(codes[live].astype(int)).max() <= 127
+    assert np.all(np.abs(codes[live].astype(int)).max(axis=-1) == 127)
+    # dead rows (tail slots, the poisoned page): code -128 and a NaN scale
+    assert np.all(codes[~live] == -128)
+    n_dead = x.extra["poisoned_pages"][0][1]
+    assert np.all(np.isnan(x.row_scale[:, :n_dead]))
+    assert np.isnan(x.row_scale[0, 2, :, 37 % 4:]).all()   # sequence 0 ends inside its last page
+
+
 def test_outlier_positions():
     x = generate(_small(seq_lens=(200,), q_lens=(1,), k_outlier_frac=0.01, keep_float=True))[0]
     pos = x.extra["outliers"][0]
@@ -72,6 +88,7 @@ def test_outlier_positions():
 #   verify_window: tokens 59,393..61,447 (2,055)        =   8,417,280 B
 #   prefill: 67,584 x 4 x 128 x 2 x 2                   = 138,412,032 B
 #   mixed_fp8: 367,950 x 8 x 128 x 1 x 2                = 753,561,600 B
+#   mixed_int8: 367,950 x 8 x (128 x 1 + 4) x 2         = 777,110,400 B (codes + row scales)
 @pytest.mark.parametrize("name,kv_bytes", [
     ("tiny_decode", 257 * 1 * 64 * 2 * 2),
     ("decode", 16_781_312),
@@ -79,6 +96,7 @@ def test_outlier_positions():
     ("verify_window", 8_417_280),
     ("prefill", 138_412_032),
     ("mixed_fp8", 753_561_600),
+    ("mixed_int8", 777_110_400),
 ])
 def test_named_kv_bytes(name, kv_bytes):
     spec = NAMED_SPECS[name]
