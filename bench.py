@@ -41,11 +41,13 @@ WORKLOADS = {
     "verify_window": "speculative verify, 2048-token window, out-of-window pages NaN (61,448 tokens, fp16 KV)",
     "prefill": "chunked prefill: 2,048-token chunk on 65,536 cached, 24/4 heads, D 128, bf16 KV",
     "mixed_fp8": "mixed batch: 4 seqs, 200,001/131,076/32,776/4,097 tokens, q_len 1/4/8/1, 32/8 heads, fp8 e4m3 KV",
+    "mixed_int8": "mixed batch as mixed_fp8 on an int8 KV cache with a fp32 scale per cached row",
     "append_fp8": "cache append: 64 seqs x 256 new rows, 8 KV heads, D 128, bf16 rows quantised into fp8 e4m3 pages",
 }
 # inputs as stored; every product is accumulated, and every softmax step computed, in fp32
 DTYPE_NAME = {"f16": "f16 in / f32 accumulate", "bf16": "bf16 in / f32 accumulate",
-              "fp8_e4m3": "fp8_e4m3 kv, bf16 q / f32 accumulate"}
+              "fp8_e4m3": "fp8_e4m3 kv, bf16 q / f32 accumulate",
+              "int8": "int8 kv (fp32 row scales), bf16 q / f32 accumulate"}
 
 
 def log(msg: str) -> None:
@@ -129,8 +131,9 @@ class Prepared:
         import paged_attention_long_amd as pal
 
         d = self.devs[i % self.copies]
+        ksc = self.pools["row_scale"] if "row_scale" in self.pools else d["kv_scale"]
         pal.paged_attn_forward(h, d["q"], self.pools["k"], self.pools["v"], d["block_table"], d["seq_lens"],
-                               d["q_lens"], self.base.window, self.base.scale, d["kv_scale"], self.out, self.lse,
+                               d["q_lens"], self.base.window, self.base.scale, ksc, self.out, self.lse,
                                stream=torch.cuda.current_stream())
 
     def free(self):
@@ -718,7 +721,8 @@ def profile_commands(workload: str, calib_mib: int = 512) -> list:
 
 # Per-configuration entries of the default run: steps sized so each timed
 # region lasts a few milliseconds.
-PER_CONFIG = {"tiny_decode": 300, "decode": 200, "verify": 60, "verify_window": 200, "prefill": 20}
+PER_CONFIG = {"tiny_decode": 300, "decode": 200, "verify": 60, "verify_window": 200, "prefill": 20,
+              "mixed_int8": 20}
 CPU_BUDGET_HEADLINE_S = 10.0
 CPU_BUDGET_PER_CONFIG_S = 3.0
 
@@ -818,7 +822,7 @@ def main():
         res = {"auto": res[paths[0]]}
     auto = res["auto"]
     t = auto["timing"]
-    kinds = {"f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3"}
+    kinds = {"f16": "f16", "bf16": "bf16", "fp8_e4m3": "fp8_e4m3", "int8": "int8"}
     line = {
         "metric": METRIC, "value": auto["value"], "unit": auto["unit"], "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": t["graph_wall_us"] / 1e3, "higher_is_better": True,

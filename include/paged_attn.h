@@ -64,6 +64,7 @@ extern "C" {
 #define PA_DTYPE_F16       1   /* IEEE binary16 */
 #define PA_DTYPE_BF16      2   /* bfloat16 */
 #define PA_DTYPE_FP8_E4M3  3   /* OCP E4M3FN: bias 7, max 448, no inf, S.1111.111 = NaN */
+#define PA_DTYPE_INT8      4   /* two's-complement int8 codes, one fp32 scale per cached row */
 
 /* execution paths (pa_tuning_t.path) */
 #define PA_PATH_AUTO   0   /* VALU split-KV kernel for rows-per-KV-head <= 8, MFMA tile kernel above */
@@ -84,7 +85,10 @@ typedef struct pa_config {
                                 x page_stride / (16 x token_stride) below 2^31, and
                                 block_table_stride x P below 2^28 (else PA_ERR_UNSUPPORTED). */
     int32_t q_dtype;         /* PA_DTYPE_F16 or PA_DTYPE_BF16 */
-    int32_t kv_dtype;        /* PA_DTYPE_F16, PA_DTYPE_BF16 (== q_dtype) or PA_DTYPE_FP8_E4M3 */
+    int32_t kv_dtype;        /* PA_DTYPE_F16, PA_DTYPE_BF16 (== q_dtype), PA_DTYPE_FP8_E4M3 or
+                                PA_DTYPE_INT8 (the pages' own cache: int8 codes with a fp32 scale per
+                                row, "Dual MI50, part 2", section "Prefill: teach the fork's fast kernel
+                                to read the int8 cache") */
     int32_t max_num_seqs;    /* largest num_seqs passed to forward, 1..1024 */
     int32_t max_q_len;       /* largest q_len of any sequence, >= 1 */
     int32_t min_q_len;       /* smallest q_len of any sequence with q_len > 0 (1..max_q_len); a
@@ -150,9 +154,19 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out);
  *               cfg.max_q_len); sum must equal num_tokens.
  *  window       host int: <= 0 no window; W >= 1 the W most recent keys.
  *  scale        host float > 0: multiplies q.k (after dequantisation).
- *  kv_scale     device float [2][Hkv] (K scales, then V scales) for an fp8
- *               cache: k~ = code * kv_scale[0][g], v~ = code * kv_scale[1][g];
+ *  kv_scale     fp8 cache: device float [2][Hkv] (K scales, then V scales):
+ *               k~ = code * kv_scale[0][g], v~ = code * kv_scale[1][g];
  *               every scale > 0.
+ *               int8 cache: device float [2][R] with R = num_pages *
+ *               page_stride / head_dim, one scale per cached row (one token
+ *               of one KV head), K rows then V rows: the row of page p, KV
+ *               head g, slot s has its scale at index (p * page_stride +
+ *               g * head_stride + s * token_stride) / head_dim, i.e. the
+ *               scales are laid out like the cache with rows of one element
+ *               ([2][pages][Hkv][P] for HND, [2][pages][P][Hkv] for NHD);
+ *               k~ = code * scale of its row.  Every stride must be a
+ *               multiple of head_dim.  Scales of slots no row reaches are
+ *               never read; dead rows' scales may hold anything (NaN).
  *               Must be NULL for fp16/bf16 caches.
  *  out          device float [T][Hq][D].
  *  lse          device float [T][Hq] (natural log), or NULL.
@@ -220,14 +234,21 @@ int paged_attn_debug_gather(pa_handle_t* h,
  * unchanged; an fp8 E4M3FN cache receives, per element, the code nearest to
  * x / s (s = kv_scale[0][g] for K, kv_scale[1][g] for V; the quotient
  * rounded once in fp32), ties to the even code, magnitudes of 448 and more
- * (and infinities) stored as 448, NaN as NaN, the sign kept.
+ * (and infinities) stored as 448, NaN as NaN, the sign kept.  An int8 cache
+ * receives, per row (one token of one KV head), the scale s = amax / 127
+ * (amax the largest |x| of the row's D values, NaN if one is NaN; fp32
+ * division), written to the row's place in the row-scale pool kv_scale
+ * (laid out as in paged_attn_forward), and per element the integer nearest
+ * to x / s (one fp32 division, ties to even) limited to [-127, 127], a NaN
+ * quotient (a zero or non-finite row) stored as 0.
  *
  *  k_new, v_new  device, q_dtype, contiguous [num_tokens][Hkv][D], rows of
  *                sequence 0 first; 16-byte aligned.  Read only.
  *  k_cache, v_cache, layout, block_table, num_seqs, block_table_stride,
  *  seq_lens, q_lens, kv_scale, stream: as in paged_attn_forward (the caches
- *                are written; kv_scale is required for an fp8 cache and must
- *                be NULL otherwise).
+ *                are written; kv_scale is required for an fp8 cache, which
+ *                only reads it, and for an int8 cache, whose row scales of
+ *                the written rows it receives; NULL otherwise).
  *
  * Only the addressed slots are written.  A sequence with q_len <= 0,
  * q_len > seq_len, or rows past num_tokens writes nothing; a row whose
@@ -239,7 +260,7 @@ int paged_attn_debug_gather(pa_handle_t* h,
 int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int64_t num_tokens,
                       void* k_cache, void* v_cache, const pa_cache_layout_t* layout,
                       const int32_t* block_table, int32_t num_seqs, int32_t block_table_stride,
-                      const int32_t* seq_lens, const int32_t* q_lens, const float* kv_scale, void* stream);
+                      const int32_t* seq_lens, const int32_t* q_lens, float* kv_scale, void* stream);
 
 /*
  * paged_attn_forward_noalloc: paged_attn_forward for callers that cannot

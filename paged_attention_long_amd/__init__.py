@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     PA_DTYPE_BF16,
     PA_DTYPE_F16,
     PA_DTYPE_FP8_E4M3,
+    PA_DTYPE_INT8,
     PA_PATH_AUTO,
     PA_PATH_MFMA,
     PA_PATH_VALU,

@@ -25,13 +25,14 @@ PA_ERR_HIP = 4
 PA_DTYPE_F16 = 1
 PA_DTYPE_BF16 = 2
 PA_DTYPE_FP8_E4M3 = 3
+PA_DTYPE_INT8 = 4
 
 PA_PATH_AUTO = 0
 PA_PATH_VALU = 1
 PA_PATH_MFMA = 2
 
-DTYPE_CODES = {"f16": PA_DTYPE_F16, "bf16": PA_DTYPE_BF16, "fp8_e4m3": PA_DTYPE_FP8_E4M3}
-ELEM_BYTES = {PA_DTYPE_F16: 2, PA_DTYPE_BF16: 2, PA_DTYPE_FP8_E4M3: 1}
+DTYPE_CODES = {"f16": PA_DTYPE_F16, "bf16": PA_DTYPE_BF16, "fp8_e4m3": PA_DTYPE_FP8_E4M3, "int8": PA_DTYPE_INT8}
+ELEM_BYTES = {PA_DTYPE_F16: 2, PA_DTYPE_BF16: 2, PA_DTYPE_FP8_E4M3: 1, PA_DTYPE_INT8: 1}
 
 
 class PagedAttnError(RuntimeError):
@@ -221,6 +222,19 @@ def _check_cache(h: Handle, k_cache):
                          f"{c.page_size}, {c.head_dim}]")
 
 
+def _check_row_scales(h, k_cache, kv_scale):
+    """An int8 cache's kv_scale is its row-scale pool: fp32, contiguous, one
+    scale per cached row of K and of V (laid out like the cache with rows of
+    one element)."""
+    c = h.cfg
+    if c.kv_dtype != PA_DTYPE_INT8 or kv_scale is None:
+        return
+    need = 2 * k_cache.shape[0] * k_cache.stride(0) // c.head_dim
+    if kv_scale.element_size() != 4 or not kv_scale.is_contiguous() or kv_scale.numel() != need:
+        raise ValueError(f"an int8 cache needs kv_scale as {need} contiguous fp32 row scales "
+                         "(K rows then V rows, laid out like the cache)")
+
+
 def _check_forward_args(h, q, k_cache, v_cache, block_table, out, lse):
     c = h.cfg
     if q.dim() != 3 or tuple(q.shape[1:]) != (c.num_q_heads, c.head_dim) or not q.is_contiguous():
@@ -241,6 +255,7 @@ def paged_attn_forward(h: Handle, q, k_cache, v_cache, block_table, seq_lens, q_
                        kv_scale, out, lse=None, stream=None) -> None:
     """Enqueue paged attention; see include/paged_attn.h for the contract."""
     _check_forward_args(h, q, k_cache, v_cache, block_table, out, lse)
+    _check_row_scales(h, k_cache, kv_scale)
     layout = cache_layout(k_cache)
     rc = load_library().paged_attn_forward(
         h.ptr, _ptr(q), q.shape[0], _ptr(k_cache), _ptr(v_cache), ctypes.byref(layout), _ptr(block_table),
@@ -262,6 +277,7 @@ def paged_attn_forward_noalloc(cfg: pa_config_t, q, k_cache, v_cache, block_tabl
     """Enqueue the forward that allocates nothing (fixed device array); see
     include/paged_attn.h.  Errors come from paged_attn_last_error(None)."""
     _check_forward_args(_CfgView(cfg), q, k_cache, v_cache, block_table, out, lse)
+    _check_row_scales(_CfgView(cfg), k_cache, kv_scale)
     layout = cache_layout(k_cache)
     rc = load_library().paged_attn_forward_noalloc(
         ctypes.byref(cfg), _ptr(q), q.shape[0], _ptr(k_cache), _ptr(v_cache), ctypes.byref(layout),
@@ -296,6 +312,7 @@ def paged_attn_append(h: Handle, k_new, v_new, k_cache, v_cache, block_table, se
         raise ValueError("v_cache must match k_cache in shape and strides")
     if block_table.dim() != 2 or block_table.stride(1) != 1 or block_table.element_size() != 4:
         raise ValueError("block_table must be int32 [num_seqs, width] with unit column stride")
+    _check_row_scales(h, k_cache, kv_scale)
     layout = cache_layout(k_cache)
     rc = load_library().paged_attn_append(
         h.ptr, _ptr(k_new), _ptr(v_new), k_new.shape[0], _ptr(k_cache), _ptr(v_cache), ctypes.byref(layout),

@@ -6,9 +6,13 @@
 // cache receives the input bits; an fp8 E4M3FN cache receives the code
 // nearest to x / s (s the KV head's K or V scale, the quotient rounded once
 // in fp32), ties to the even code, magnitudes from 448 up saturated to 448,
-// NaN kept as NaN, sign kept.  The pages quantise their own (int8) cache on
-// write in the same place of the step ("Dual MI50, part 2", section
-// "Prefill: teach the fork's fast kernel to read the int8 cache").
+// NaN kept as NaN, sign kept.  An int8 cache receives, per row (one token
+// of one KV head), the scale s = amax / 127 over the row's D values (fp32)
+// and per element the integer nearest to x / s (one fp32 division, ties to
+// even) within [-127, 127], a NaN quotient stored as 0; the scale goes to
+// the row's place in the row-scale pool.  The pages quantise their own int8
+// cache on write in the same place of the step ("Dual MI50, part 2",
+// section "Prefill: teach the fork's fast kernel to read the int8 cache").
 //
 // Bandwidth-bound and tiny per row: one thread per 8 elements (16 B in,
 // 16 B or 8 B out), workgroups along the sequence's rows.  Every store is
@@ -54,13 +58,33 @@ PA_DEVINLINE uint32_t e4m3_code(float q) {
     return sign | min(code, 0x7eu);
 }
 
+// Maximum over the aligned group of N lanes (N = 8 or 16: one row's
+// threads) that propagates NaN, through DPP moves inside 16-lane rows.
+template <int N>
+PA_DEVINLINE float group_max_nan(float x) {
+    auto mx = [](float a, float b) { return __builtin_elementwise_maximum(a, b); };
+    x = mx(x, dpp<kDppQuadXor1>(x));
+    x = mx(x, dpp<kDppQuadXor2>(x));
+    x = mx(x, dpp<kDppHalfMirror>(x));
+    if constexpr (N == 16) x = mx(x, dpp<kDppRowMirror>(x));
+    return x;
+}
+
+// int8 code of the fp32 quotient q: nearest integer, ties to even, within
+// [-127, 127]; NaN to 0.
+PA_DEVINLINE uint32_t i8_code(float q) {
+    if (q != q) return 0u;
+    const float r = __builtin_rintf(fminf(fmaxf(q, -127.0f), 127.0f));
+    return (uint32_t)((int)r & 0xff);
+}
+
 template <int IT>
 PA_DEVINLINE float to_f32(uint32_t bits16) {
     if constexpr (IT == PA_DTYPE_BF16) return __uint_as_float(bits16 << 16);
     else return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
 }
 
-template <int KVT, int IT>
+template <int KVT, int IT, int CPR = 16>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     const int b = blockIdx.x;
     __shared__ int red[kAppendThreads / kWave];
@@ -76,7 +100,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     for (int w = 0; w < kAppendThreads / kWave; ++w) q_off += red[w];
     const int ql = a.q_lens[b], sl = a.seq_lens[b];
     if (ql <= 0 || ql > sl || q_off + ql > a.num_tokens) return;
-    const int cpr = a.head_dim / 8;                                // 8-element chunks per head row
+    // 8-element chunks per head row; an int8 row's CPR threads are one aligned
+    // lane group (the loop's start and stride are multiples of CPR)
+    const int cpr = KVT == PA_DTYPE_INT8 ? CPR : a.head_dim / 8;
     const int64_t per_side = (int64_t)ql * a.num_kv_heads * cpr;
     const int64_t stride = (int64_t)gridDim.y * kAppendThreads;
     for (int64_t c = (int64_t)blockIdx.y * kAppendThreads + threadIdx.x; c < 2 * per_side; c += stride) {
@@ -88,6 +114,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         const int i = (int)(rg / a.num_kv_heads);
         const int p = sl - ql + i;
         const int lp = p / a.page_size;
+        // (an int8 row's threads share p and pid: they skip together)
         if (lp >= a.bt_stride) continue;
         const int pid = a.block_table[(int64_t)b * a.bt_stride + lp];
         if (pid < 0 || pid >= a.num_pages) continue;
@@ -96,7 +123,29 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         const uint4 in = *reinterpret_cast<const uint4*>(src);
         const int64_t off = (int64_t)pid * a.page_stride + (int64_t)g * a.head_stride +
                             (int64_t)(p - lp * a.page_size) * a.token_stride + ch * 8;
-        if constexpr (KVT != PA_DTYPE_FP8_E4M3) {
+        if constexpr (KVT == PA_DTYPE_INT8) {
+            const uint32_t w[4] = {in.x, in.y, in.z, in.w};
+            float x[8];
+            float amax = 0.f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                x[k] = to_f32<IT>((w[k / 2] >> (16 * (k & 1))) & 0xffffu);
+                amax = __builtin_elementwise_maximum(amax, fabsf(x[k]));
+            }
+            amax = group_max_nan<CPR>(amax);
+            const float s = __fdiv_rn(amax, 127.0f);
+            uint32_t lo = 0, hi = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t code = i8_code(__fdiv_rn(x[k], s));
+                if (k < 4) lo |= code << (8 * k);
+                else hi |= code << (8 * (k - 4));
+            }
+            *reinterpret_cast<uint2*>(static_cast<uint8_t*>(which ? a.v_cache : a.k_cache) + off) = make_uint2(lo, hi);
+            if (ch == 0)
+                a.row_scale[which * a.rs_v + (int64_t)pid * a.rs_page + (int64_t)g * a.rs_head +
+                            (int64_t)(p - lp * a.page_size) * a.rs_tok] = s;
+        } else if constexpr (KVT != PA_DTYPE_FP8_E4M3) {
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(which ? a.v_cache : a.k_cache) + off) = in;
         } else {
             const float s = a.kv_scale[which * a.num_kv_heads + g];
@@ -120,7 +169,16 @@ hipError_t launch_append(const AppendArgs& a, int kv_dtype, int in_dtype, int ma
     const int64_t chunks = 2LL * max_rows * a.num_kv_heads * (a.head_dim / 8);
     const int gy = (int)std::min<int64_t>(256, std::max<int64_t>(1, (chunks + kAppendThreads - 1) / kAppendThreads));
     const dim3 grid(a.num_seqs, gy);
-    if (kv_dtype == PA_DTYPE_FP8_E4M3) {
+    if (kv_dtype == PA_DTYPE_INT8) {
+        const bool bf = in_dtype == PA_DTYPE_BF16;
+        if (a.head_dim == 128) {
+            if (bf) hipLaunchKernelGGL((append_kernel<PA_DTYPE_INT8, PA_DTYPE_BF16, 16>), grid, dim3(kAppendThreads), 0, stream, a);
+            else hipLaunchKernelGGL((append_kernel<PA_DTYPE_INT8, PA_DTYPE_F16, 16>), grid, dim3(kAppendThreads), 0, stream, a);
+        } else {
+            if (bf) hipLaunchKernelGGL((append_kernel<PA_DTYPE_INT8, PA_DTYPE_BF16, 8>), grid, dim3(kAppendThreads), 0, stream, a);
+            else hipLaunchKernelGGL((append_kernel<PA_DTYPE_INT8, PA_DTYPE_F16, 8>), grid, dim3(kAppendThreads), 0, stream, a);
+        }
+    } else if (kv_dtype == PA_DTYPE_FP8_E4M3) {
         if (in_dtype == PA_DTYPE_BF16)
             hipLaunchKernelGGL((append_kernel<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16>), grid, dim3(kAppendThreads), 0, stream, a);
         else

@@ -51,6 +51,39 @@ PA_DEVINLINE f32x2_t fp8x2_to_f32(uint32_t u, bool hi) {
     return hi ? __builtin_amdgcn_cvt_pk_f32_fp8(u, true) : __builtin_amdgcn_cvt_pk_f32_fp8(u, false);
 }
 
+// Four int8 codes (one dword) -> four f16 values, exactly, as two packed
+// pairs (codes 0, 1 in lo; 2, 3 in hi).  Each byte b (signed v) becomes
+// u = v + 128 (flip its top bit); the f16 with bits 0x64uu is 1024 + u
+// (the unit in the last place of [1024, 2048) is 1), and subtracting 1152
+// in packed f16 leaves v.
+PA_DEVINLINE void i8x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    const uint32_t u = w ^ 0x80808080u;
+    // v_perm_b32: selector byte k picks byte k of {src1 (0..3), src0 (4..7)}
+    const uint32_t a = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+    const uint32_t b = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+    const f16x2_t off = {(_Float16)1152.0f, (_Float16)1152.0f};
+    lo = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, a) - off);
+    hi = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, b) - off);
+}
+
+// Four int8 codes -> four floats, exactly: the float with bits 0x4B0000uu is
+// 2^23 + u (u = v + 128), and subtracting 2^23 + 128 leaves v.
+PA_DEVINLINE void i8x4_to_f32x4(uint32_t w, float (&f)[4]) {
+    const uint32_t u = w ^ 0x80808080u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        f[k] = __uint_as_float(0x4B000000u | ((u >> (8 * k)) & 0xffu)) - 8388736.0f;
+}
+
+// Four int8 codes -> four bf16 values, exactly (|v| <= 128 has at most 8
+// significant bits, so the upper half of its float is the bf16 value).
+PA_DEVINLINE void i8x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    float f[4];
+    i8x4_to_f32x4(w, f);
+    lo = __builtin_amdgcn_perm(__float_as_uint(f[1]), __float_as_uint(f[0]), 0x07060302u);
+    hi = __builtin_amdgcn_perm(__float_as_uint(f[3]), __float_as_uint(f[2]), 0x07060302u);
+}
+
 // Exact narrowing of two floats that are representable in bf16 / f16.
 PA_DEVINLINE uint32_t f32x2_to_bf16x2(f32x2_t f) {
     bf16x2_t b = {(__bf16)f.x, (__bf16)f.y};

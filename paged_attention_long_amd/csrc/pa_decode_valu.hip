@@ -47,10 +47,12 @@ template <>
 struct KvChunk<PA_DTYPE_BF16> { using T = u32x4_t; static constexpr int bytes = 2; };
 template <>
 struct KvChunk<PA_DTYPE_FP8_E4M3> { using T = u32x2_t; static constexpr int bytes = 1; };
+template <>
+struct KvChunk<PA_DTYPE_INT8> { using T = u32x2_t; static constexpr int bytes = 1; };
 
 template <int KVT>
 PA_DEVINLINE typename KvChunk<KVT>::T load_chunk(const uint8_t* p) {
-    if constexpr (KVT == PA_DTYPE_FP8_E4M3) return load_b64(p);
+    if constexpr (KvChunk<KVT>::bytes == 1) return load_b64(p);
     else return load_b128(p);
 }
 
@@ -71,6 +73,12 @@ PA_DEVINLINE void k_pairs(const typename KvChunk<KVT>::T& c, uint32_t kp[4]) {
                 kp[2 * i + 1] = f32x2_to_f16x2(hi);
             }
         }
+    } else if constexpr (KVT == PA_DTYPE_INT8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if constexpr (QT == PA_DTYPE_BF16) i8x4_to_bf16x4(c[i], kp[2 * i], kp[2 * i + 1]);
+            else i8x4_to_f16x4(c[i], kp[2 * i], kp[2 * i + 1]);
+        }
     } else {
         kp[0] = c[0]; kp[1] = c[1]; kp[2] = c[2]; kp[3] = c[3];
     }
@@ -85,6 +93,13 @@ PA_DEVINLINE void v_floats(const typename KvChunk<KVT>::T& c, float v[8]) {
             f32x2_t lo = fp8x2_to_f32(c[i], false);
             f32x2_t hi = fp8x2_to_f32(c[i], true);
             v[4 * i] = lo.x; v[4 * i + 1] = lo.y; v[4 * i + 2] = hi.x; v[4 * i + 3] = hi.y;
+        }
+    } else if constexpr (KVT == PA_DTYPE_INT8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            float f[4];
+            i8x4_to_f32x4(c[i], f);
+            v[4 * i] = f[0]; v[4 * i + 1] = f[1]; v[4 * i + 2] = f[2]; v[4 * i + 3] = f[3];
         }
     } else if constexpr (KVT == PA_DTYPE_BF16) {
 #pragma unroll
@@ -160,6 +175,13 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         for (int rr = 0; rr < RPP; ++rr)
             lane_off[rr] = (uint32_t)(kv_offset(0, g, rr * TPR + tl, a.page_stride, a.head_stride, a.token_stride) * EB +
                                       ch * 8 * EB);
+        // int8: this lane's token row scales, at rs_page * page + lane_soff[rr]
+        constexpr bool ROWSC = (KVT == PA_DTYPE_INT8);
+        int64_t lane_soff[ROWSC ? RPP : 1];
+        if constexpr (ROWSC) {
+#pragma unroll
+            for (int rr = 0; rr < RPP; ++rr) lane_soff[rr] = (int64_t)g * a.rs_head + (int64_t)(rr * TPR + tl) * a.rs_tok;
+        }
 
         // passes over row groups: up to kWaves row groups at a time
         for (int rg0 = 0; rg0 < n_rg; rg0 += kWaves) {
@@ -202,7 +224,10 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
                     // Two page buffers in ping-pong: the next page's loads are in flight
                     // while the current one is scored (no register copies of pending loads).
                     Chunk ka[RPP], va[RPP], kb[RPP], vb[RPP];
-                    auto issue = [&](Chunk (&kd)[RPP], Chunk (&vd)[RPP], int pg) {
+                    // int8 row scales of the tokens the chunks hold (K, V)
+                    float ska[ROWSC ? RPP : 1], sva[ROWSC ? RPP : 1], skb[ROWSC ? RPP : 1], svb[ROWSC ? RPP : 1];
+                    auto issue = [&](Chunk (&kd)[RPP], Chunk (&vd)[RPP], float (&sk)[ROWSC ? RPP : 1],
+                                     float (&sv)[ROWSC ? RPP : 1], int pg) {
                         // wave-uniform page base (scalar registers) + per-lane 32-bit offsets
                         const int pid = __builtin_amdgcn_readfirstlane(sm.pid[pg - c0]);
                         const int64_t pbase = (int64_t)pid * page_bytes;
@@ -213,12 +238,25 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
                             kd[rr] = load_chunk<KVT>(kp + lane_off[rr]);
                             vd[rr] = load_chunk<KVT>(vp + lane_off[rr]);
                         }
+                        if constexpr (ROWSC) {
+                            const float* rk = a.row_scale + (int64_t)pid * a.rs_page;
+#pragma unroll
+                            for (int rr = 0; rr < RPP; ++rr) {
+                                sk[rr] = __builtin_nontemporal_load(rk + lane_soff[rr]);
+                                sv[rr] = __builtin_nontemporal_load(rk + a.rs_v + lane_soff[rr]);
+                            }
+                        }
                     };
-                    auto consume = [&](const Chunk (&kd)[RPP], const Chunk (&vd)[RPP], int pg) {
+                    auto consume = [&](const Chunk (&kd)[RPP], const Chunk (&vd)[RPP], const float (&sk)[ROWSC ? RPP : 1],
+                                       const float (&sv)[ROWSC ? RPP : 1], int pg) {
 #pragma unroll
                         for (int rr = 0; rr < RPP; ++rr) {
                             const int j = pg * kPage + rr * TPR + tl;
                             const bool live = (j >= si.lo) && (j < si.seq_len);
+                            // int8: the key's own scale folds into its score; the value's
+                            // multiplies its weight (0 for a dead key, whose scale may be NaN)
+                            const float s2j = ROWSC ? s2 * sk[ROWSC ? rr : 0] : s2;
+                            const float svj = ROWSC ? (live ? sv[ROWSC ? rr : 0] : 0.f) : 1.f;
                             uint32_t kp[4];
                             k_pairs<KVT, QT>(kd[rr], kp);
                             float s[RW];
@@ -234,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
                             for (int r = 0; r < RW; ++r) {
                                 const bool vis = (j <= pos[r]) && (j >= lo_r[r]) && live;
-                                s[r] = vis ? s[r] * s2 : kNegInf;
+                                s[r] = vis ? s[r] * s2j : kNegInf;
                                 need |= s[r] > m[r] + kTau;
                             }
                             if (__builtin_expect(wave_any(need), 0)) {
@@ -256,8 +294,9 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
                             for (int r = 0; r < RW; ++r) {
                                 const float p = (s[r] == kNegInf) ? 0.f : fast_exp2(s[r] - m[r]);
                                 l[r] += p;
+                                const float pv = ROWSC ? p * svj : p;
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(p, v[e], acc[r][e]);
+                                for (int e = 0; e < 8; ++e) acc[r][e] = fmaf(pv, v[e], acc[r][e]);
                             }
                         }
                     };
@@ -265,15 +304,15 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
                     // wave already holds) so the wait counts are the same on every path.
                     int pg = c0 + sub;
                     if (pg < c1) {
-                        issue(ka, va, pg);
+                        issue(ka, va, ska, sva, pg);
                         while (true) {
                             const int p1 = pg + wprg;
-                            issue(kb, vb, p1 < c1 ? p1 : pg);
-                            consume(ka, va, pg);
+                            issue(kb, vb, skb, svb, p1 < c1 ? p1 : pg);
+                            consume(ka, va, ska, sva, pg);
                             if (p1 >= c1) break;
                             const int p2 = p1 + wprg;
-                            issue(ka, va, p2 < c1 ? p2 : p1);
-                            consume(kb, vb, p1);
+                            issue(ka, va, ska, sva, p2 < c1 ? p2 : p1);
+                            consume(kb, vb, skb, svb, p1);
                             if (p2 >= c1) break;
                             pg = p2;
                         }
@@ -510,6 +549,10 @@ template <int D>
 static hipError_t launch_d(const DecodeArgs& a, int kvt, int qt, int rw, int grid, hipStream_t st) {
     if (kvt == PA_DTYPE_F16) return launch_rw<D, PA_DTYPE_F16, PA_DTYPE_F16>(a, rw, grid, st);
     if (kvt == PA_DTYPE_BF16) return launch_rw<D, PA_DTYPE_BF16, PA_DTYPE_BF16>(a, rw, grid, st);
+    if (kvt == PA_DTYPE_INT8) {
+        if (qt == PA_DTYPE_BF16) return launch_rw<D, PA_DTYPE_INT8, PA_DTYPE_BF16>(a, rw, grid, st);
+        return launch_rw<D, PA_DTYPE_INT8, PA_DTYPE_F16>(a, rw, grid, st);
+    }
     if (qt == PA_DTYPE_BF16) return launch_rw<D, PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16>(a, rw, grid, st);
     return launch_rw<D, PA_DTYPE_FP8_E4M3, PA_DTYPE_F16>(a, rw, grid, st);
 }

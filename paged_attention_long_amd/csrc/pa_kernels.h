@@ -34,7 +34,13 @@ struct DecodeArgs {
     const int32_t* block_table;
     const int32_t* seq_lens;
     const int32_t* q_lens;
-    const float* kv_scale;     // [2][Hkv] or null
+    const float* kv_scale;     // fp8: [2][Hkv]; int8: the row scales (see row_scale); else null
+    // int8 caches: one fp32 scale per cached row, laid out like the cache
+    // with rows of one element.  The scale of (virtual page p, KV head g,
+    // slot s) is row_scale[p * rs_page + g * rs_head + s * rs_tok], plus
+    // rs_v for V.
+    const float* row_scale;
+    int64_t rs_v, rs_page, rs_head, rs_tok;
     float* out;
     float* lse;                // may be null
     float* ws_o;               // split partials [max_items][r_max][D]
@@ -137,6 +143,8 @@ struct AppendArgs {
     const int32_t* seq_lens;
     const int32_t* q_lens;
     const float* kv_scale;     // [2][Hkv] (fp8 caches)
+    float* row_scale;          // int8 caches: the row-scale pool (written), laid out like the cache with
+    int64_t rs_v, rs_page, rs_head, rs_tok;   // rows of one element; rs_v: offset of the V scales
     int64_t num_pages, page_stride, head_stride, token_stride;   // elements
     int64_t num_tokens;
     int num_seqs, bt_stride, num_kv_heads, head_dim, page_size;

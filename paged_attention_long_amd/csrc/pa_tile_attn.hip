@@ -135,6 +135,17 @@ PA_DEVINLINE void async_load16(const void* src, lds_void_t* lds) {
 #endif
 }
 
+// Asynchronous 4-byte load per lane into LDS: lane l's dword lands at
+// lds + 4*l (global_load_lds_dword).
+PA_DEVINLINE void async_load4(const void* src, lds_void_t* lds) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_global_load_lds(src, lds, 4, 0, 0);
+#else
+    (void)src;
+    (void)lds;
+#endif
+}
+
 // Byte offset of 16-byte chunk c of row r inside a tile.  Rows are 256 B (one
 // full pass over the banks), so the chunk index is XOR-ed with a row key that
 // puts the row's low two bits into the chunk's high two bits: the K operand
@@ -338,11 +349,13 @@ struct Cfg {
     static constexpr int NB = BN / 32;                     // 32-key blocks of S^T
     static constexpr int TS = BN / 16;                     // 16-key k-steps of P.V
     static constexpr bool FP8 = (KVT == PA_DTYPE_FP8_E4M3);
-    static constexpr int EB = FP8 ? 1 : 2;
-    static constexpr int PVT = FP8 ? PA_DTYPE_F16 : KVT;   // P.V operand type
+    static constexpr bool INT8 = (KVT == PA_DTYPE_INT8);   // int8 codes with a fp32 scale per row
+    static constexpr bool BYTE = FP8 || INT8;              // one-byte cache elements
+    static constexpr int EB = BYTE ? 1 : 2;
+    static constexpr int PVT = BYTE ? PA_DTYPE_F16 : KVT;  // P.V operand type
     // memory-bound 16-bit caches: P.V always on the split P (fp8 caches never
     // split P: their own error is far larger than P's f16 rounding)
-    static constexpr bool PSPLIT = (WR == 1) && !FP8;
+    static constexpr bool PSPLIT = (WR == 1) && !BYTE;
     static constexpr int TILE = BN * kRowBytes;            // bytes of one K (or V) tile in LDS
     static constexpr int GROUP_LDS = 2 * TILE;             // a wave group's K and V tile in LDS
     static constexpr int DMA_PER_WAVE = BN * kRowBytes / 1024 / WR;   // 1 KB async loads per wave per tile
@@ -352,18 +365,23 @@ struct Cfg {
     // staging slots per wave (K then V, 8 KB a slot); both operands are read
     // raw (V by 8-bit transposing reads) and widened in registers at their
     // matrix ops.  RAW_DMA 1 KB loads per wave per tile (K and V).
-    static constexpr bool FSTAGE = FP8 && (WR == 1);
+    static constexpr bool FSTAGE = BYTE && (WR == 1);
     static constexpr int RAW_TILE = BN * D;                // bytes of one raw fp8 K (or V) tile
-    static constexpr int RAW_DMA = 2 * RAW_TILE / 1024;
+    // int8: one more 4-byte load per lane and tile brings the tile's K and V
+    // row scales into LDS
+    static constexpr int RAW_DMA = 2 * RAW_TILE / 1024 + (INT8 ? 1 : 0);
     static constexpr int STAGE_LDS = FSTAGE ? WK * 2 * 2 * RAW_TILE : 16;
     // 256-row items on 16-bit caches run a software pipeline: K tiles in a
     // ring of NKB buffers, V tiles in a ring of NVB, loads issued LEAD tiles
     // ahead; the item's page ids are staged in LDS (PID_CAP of them).  The
     // loop is unrolled over the ring, so buffer offsets are immediates.
-    static constexpr bool PIPE = (WR == 8) && !FP8;
+    static constexpr bool PIPE = (WR == 8) && !BYTE;
     static constexpr int NKB = 4, NVB = 4, LEAD = 3;
     static constexpr int PID_CAP = PIPE ? 4096 : (WR == 1 ? 1024 : 1);
     static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : (FSTAGE ? 16 : WK * GROUP_LDS);
+    // int8 row scales of a tile: BN K scales then BN V scales, per staging
+    // slot (FSTAGE) or per wave group's LDS tile
+    static constexpr int SC_FLOATS = INT8 ? (FSTAGE ? WK * 2 : WK) * 2 * BN : 4;
 };
 
 template <int KVT>
@@ -374,6 +392,8 @@ template <>
 struct Raw<PA_DTYPE_BF16> { using T = u32x4_t; };
 template <>
 struct Raw<PA_DTYPE_FP8_E4M3> { using T = u32x2_t; };
+template <>
+struct Raw<PA_DTYPE_INT8> { using T = u32x2_t; };
 
 // Eight fp8 e4m3 values to eight 16-bit values, exactly (both targets hold
 // every e4m3 value): the gfx950 scaled conversion with scale 1 turns two fp8
@@ -394,6 +414,25 @@ PA_DEVINLINE u32x4_t widen_fp8x8(const u32x2_t& c) {
     return r;
 }
 
+// Eight one-byte cache codes to eight 16-bit values of type T, exactly.
+template <int T, int KVT>
+PA_DEVINLINE u32x4_t widen8(const u32x2_t& c) {
+    if constexpr (KVT == PA_DTYPE_FP8_E4M3) {
+        return widen_fp8x8<T>(c);
+    } else {
+        u32x4_t r;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            uint32_t lo, hi;
+            if constexpr (T == PA_DTYPE_BF16) i8x4_to_bf16x4(c[i], lo, hi);
+            else i8x4_to_f16x4(c[i], lo, hi);
+            r[2 * i] = lo;
+            r[2 * i + 1] = hi;
+        }
+        return r;
+    }
+}
+
 struct ItemGeom {
     int b, g, qt, split, splits;
     SeqInfo si;
@@ -411,6 +450,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[C::TILES_LDS];
     __shared__ __attribute__((aligned(16))) int ipid[C::PID_CAP];
     __shared__ __attribute__((aligned(1024))) uint8_t stage[C::STAGE_LDS];
+    __shared__ __attribute__((aligned(16))) float tscale[C::SC_FLOATS];
     __shared__ float red_m[4][32];
     __shared__ float red_e[4][32];
     __shared__ long long redw[8], redq[8];
@@ -775,8 +815,17 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
 #pragma unroll
             for (int p = 0; p < PPT; ++p) pid[p] = tile_pid(t, p);
         };
-        // fp8 caches: registers, widened, then written in the same layout.
+        // int8 row scales: the scale of key slot `slot` of virtual page pid
+        // (K; V is rs_v further)
+        auto row_scale_ptr = [&](int pid, int slot) {
+            return a.row_scale + (int64_t)pid * a.rs_page + (int64_t)ig.g * a.rs_head + (int64_t)slot * a.rs_tok;
+        };
+        // one-byte caches at 128-row items: registers, widened, then written
+        // in the same layout; int8 row scales go to the group's scale array
+        // (threads 0 .. BN-1 a key's K scale, BN .. 2BN-1 its V scale).
         typename Raw<KVT>::T fk[C::FCH], fv[C::FCH];
+        float fsc = 0.f;
+        float* tsc_group = tscale + (C::FSTAGE ? 0 : gi * 2 * BN);
         auto fp8_load = [&](int t) {
             int pid[PPT];
 #pragma unroll
@@ -785,20 +834,38 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             for (int c = 0; c < C::FCH; ++c) {
                 const int ch = gtid + c * C::NT;
                 const int key = ch / (D / 8), e = ch % (D / 8);
-                if constexpr (C::FP8) {
+                if constexpr (C::BYTE) {
                     fk[c] = load_b64(row_src(kbase, pid, key) + e * 8);
                     fv[c] = load_b64(row_src(vbase, pid, key) + e * 8);
                 }
             }
+            if constexpr (C::INT8) {
+                if (gtid < 2 * BN) {
+                    const int key = gtid % BN;
+                    fsc = __builtin_nontemporal_load(row_scale_ptr(pid[key / kPage], key % kPage) +
+                                                     (gtid >= BN ? a.rs_v : 0));
+                }
+            }
         };
-        auto fp8_store = [&](int buf) {
+        auto fp8_store = [&](int buf, int t) {
 #pragma unroll
             for (int c = 0; c < C::FCH; ++c) {
                 const int ch = gtid + c * C::NT;
                 const int key = ch / (D / 8), e = ch % (D / 8);
-                if constexpr (C::FP8) {
-                    *reinterpret_cast<u32x4_t*>(kbuf(buf) + swz(key, e)) = widen_fp8x8<QT>(fk[c]);
-                    *reinterpret_cast<u32x4_t*>(vbuf(buf) + swz(key, e)) = widen_fp8x8<C::PVT>(fv[c]);
+                if constexpr (C::BYTE) {
+                    *reinterpret_cast<u32x4_t*>(kbuf(buf) + swz(key, e)) = widen8<QT, KVT>(fk[c]);
+                    *reinterpret_cast<u32x4_t*>(vbuf(buf) + swz(key, e)) = widen8<C::PVT, KVT>(fv[c]);
+                }
+            }
+            if constexpr (C::INT8) {
+                // a dead key's V scale (maybe NaN) is stored as 0, by the
+                // thread that stores it
+                if (gtid < 2 * BN) {
+                    const int key = gtid % BN;
+                    const int j = key_pos(t, 0) + key;
+                    const bool live = (j >= ig.si.lo) && (j < ig.si.seq_len) &&
+                                      (ig.pg_first + t * PPT + key / kPage < ig.pg_end);
+                    tsc_group[gtid] = (gtid >= BN && !live) ? 0.f : fsc;
                 }
             }
         };
@@ -826,6 +893,12 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                     const int64_t pb = (int64_t)pid[(8 * i) / kPage] * page_bytes;
                     async_load16(kbase + pb + raw_off[i], (lds_void_t*)(st + i * 1024));
                     async_load16(vbase + pb + raw_off[i], (lds_void_t*)(st + C::RAW_TILE + i * 1024));
+                }
+                if constexpr (C::INT8) {
+                    // lanes 0..31: K scales of keys 0..31; lanes 32..63: their V scales
+                    const int key = lane & 31;
+                    const float* src = row_scale_ptr(pid[key / kPage], key % kPage) + (lane >= 32 ? a.rs_v : 0);
+                    async_load4(src, (lds_void_t*)(tscale + (gi * 2 + decltype(slot_c)::value) * 2 * BN));
                 }
             }
         };
@@ -896,12 +969,40 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 split_thr = kSplitBelow * ((m_run == kNegInf) ? 1.f : fast_exp2(m_true - m_run));
             }
         };
+        // int8: the 16 row scales of this lane's keys in a tile (key
+        // nb*32 + 8*(i/4) + 4*h32 + i%4 for score i of block nb) from the
+        // tile's scale array in LDS.
+        auto lane_scales = [&](const float* base, float (&out)[C::NB][16]) {
+            asm volatile("" ::: "memory");   // after the waits for the array's loads and stores
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v = *reinterpret_cast<const float4*>(base + nb * 32 + 8 * q + 4 * h32);
+                    out[nb][4 * q] = v.x; out[nb][4 * q + 1] = v.y; out[nb][4 * q + 2] = v.z; out[nb][4 * q + 3] = v.w;
+                }
+        };
+        // int8: each key's own K scale multiplies its score (before masking,
+        // which replaces a dead key's NaN by select).
+        auto apply_kscale = [&](f32x16_t (&S)[C::NB], const float* ksc) {
+            float k[C::NB][16];
+            lane_scales(ksc, k);
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) S[nb][i] *= k[nb][i];
+        };
         // P = 2^(s*s2 - m_run) rounded to the P.V operand type; while a row has
         // few effective keys (weight sum small against its largest weight) the
-        // rounding error of P goes into pl as a second operand.
-        auto exp_pack = [&](f32x16_t (&S)[C::NB], u32x4_t (&pb)[C::TS], u32x4_t (&pl)[C::TS]) {
+        // rounding error of P goes into pl as a second operand.  int8: the
+        // weight that meets V is p times the key's V scale (vsc; 0 for dead
+        // keys), the normaliser sums p.
+        auto exp_pack = [&](f32x16_t (&S)[C::NB], u32x4_t (&pb)[C::TS], u32x4_t (&pl)[C::TS],
+                            const float* vsc = nullptr) {
             // a row that has seen no visible key yet keeps m_run = -inf; its p are 0
             const float nm = neg_m;
+            float vs[C::INT8 ? C::NB : 1][16];
+            if constexpr (C::INT8) lane_scales(vsc, vs);
 #pragma unroll
             for (int ts = 0; ts < C::TS; ++ts) {
                 const int nb = ts / 2, i0 = 8 * (ts % 2);
@@ -912,12 +1013,15 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                     S[nb][i0 + 2 * j] = p0;
                     S[nb][i0 + 2 * j + 1] = p1;
                     l_exact += p0 + p1;
-                    pb[ts][j] = pack2<C::PVT>(p0, p1);
+                    if constexpr (C::INT8)
+                        pb[ts][j] = pack2<C::PVT>(p0 * vs[nb][i0 + 2 * j], p1 * vs[nb][i0 + 2 * j + 1]);
+                    else
+                        pb[ts][j] = pack2<C::PVT>(p0, p1);
                 }
             }
-            // fp8 caches: P's f16 rounding (relative 2^-11) stays far inside
-            // the error the cache format already carries, so no split
-            const bool split = C::PSPLIT || (!C::FP8 && wave_any(l_exact < split_thr));
+            // one-byte caches: P's f16 rounding (relative 2^-11) stays far
+            // inside the error the cache format already carries, so no split
+            const bool split = C::PSPLIT || (!C::BYTE && wave_any(l_exact < split_thr));
             if (split) {
 #pragma unroll
                 for (int ts = 0; ts < C::TS; ++ts) {
@@ -985,10 +1089,11 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             }
             __builtin_amdgcn_sched_group_barrier(0x100, C::NB * C::KS, 0);   // LDS reads
             __builtin_amdgcn_sched_group_barrier(0x008, C::NB * C::KS, 0);   // MFMAs
+            if constexpr (C::INT8) apply_kscale(sacc, tsc_group);
             mask_scores(t, sacc);
             raise_max(sacc);
             u32x4_t pb[C::TS], pl[C::TS];
-            const bool split = exp_pack(sacc, pb, pl);
+            const bool split = exp_pack(sacc, pb, pl, C::INT8 ? tsc_group + BN : nullptr);
             pv((uint32_t)(uintptr_t)(lds_void_t*)vb, pb, pl, split);
         };
 
@@ -1141,7 +1246,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the clamped prefetches past the end
                 __syncthreads();
             }
-        } else if constexpr (!C::FP8) {
+        } else if constexpr (!C::BYTE) {
             // Register-staged tiles (32-row items, 16-bit caches): the next tile's K and V rows are in flight
             // in registers while this one is computed from the wave's LDS
             // buffer; then they are written there and the tile after is
@@ -1235,6 +1340,9 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                                     const bool live = (j >= ig.si.lo) && (j < ig.si.seq_len) &&
                                                       (ig.pg_first + t * PPT + key / kPage < ig.pg_end);
                                     if (!live) *reinterpret_cast<u32x4_t*>(vrows + key * 128 + c * 16) = u32x4_t{0u, 0u, 0u, 0u};
+                                    // int8: a dead key's V scale (maybe NaN) becomes 0
+                                    if constexpr (C::INT8)
+                                        if (!live && c == 0) tscale[(gi * 2 + J) * 2 * BN + BN + key] = 0.f;
                                 }
                                 __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
                             }
@@ -1245,17 +1353,19 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
 #pragma unroll
                         for (int i = 0; i < 16; ++i) S[0][i] = 0.f;
 #pragma unroll
-                        for (int s8 = 0; s8 < C::KS; ++s8) S[0] = mma32<QT>(widen_fp8x8<QT>(kr[s8]), qreg[s8], S[0]);
+                        for (int s8 = 0; s8 < C::KS; ++s8) S[0] = mma32<QT>(widen8<QT, KVT>(kr[s8]), qreg[s8], S[0]);
+                        const float* tsc_slot = tscale + (gi * 2 + J) * 2 * BN;
+                        if constexpr (C::INT8) apply_kscale(S, tsc_slot);
                         mask_scores(t, S);
                         raise_max(S);
-                        exp_pack(S, pb, pl);
+                        exp_pack(S, pb, pl, C::INT8 ? tsc_slot + BN : nullptr);
                         u32x2_t vr[8];
                         lds_read_raw_vt<J>(va, vr);
 #pragma unroll
                         for (int ts = 0; ts < C::TS; ++ts)
 #pragma unroll
                             for (int db = 0; db < C::DB; ++db)
-                                o_acc[db] = mma32<C::PVT>(widen_fp8x8<C::PVT>(vr[ts * 4 + db]), pb[ts], o_acc[db]);
+                                o_acc[db] = mma32<C::PVT>(widen8<C::PVT, KVT>(vr[ts * 4 + db]), pb[ts], o_acc[db]);
                     }
                     raw_dma(j_c, min(tile_of(k + 2), ig.t_end - 1));   // the slot's reads are complete
                     __builtin_amdgcn_wave_barrier();
@@ -1272,7 +1382,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 const int t = my_first + iter * C::WK;
                 const bool have = t < ig.t_end;
                 if constexpr (WR > 1) __syncthreads();
-                fp8_store(0);
+                fp8_store(0, t);
                 if (have) zero_dead_v(t, 0);
                 group_sync();
                 if (iter + 1 < n_iter) fp8_load(min(t + C::WK, ig.t_end - 1));
@@ -1423,6 +1533,14 @@ struct KernelTag {
 template <typename F>
 static bool with_kernel(int kv_dtype, int q_dtype, int wr, F&& f) {
     const bool fp8 = kv_dtype == PA_DTYPE_FP8_E4M3;
+    if (kv_dtype == PA_DTYPE_INT8 && (wr == 1 || wr == 4)) {
+        if (q_dtype == PA_DTYPE_BF16) {
+            if (wr == 1) return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_BF16, 1>{}), true;
+            return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_BF16, 4>{}), true;
+        }
+        if (wr == 1) return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_F16, 1>{}), true;
+        return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_F16, 4>{}), true;
+    }
     if (wr == 1) {
         if (kv_dtype == PA_DTYPE_F16) return f(KernelTag<PA_DTYPE_F16, PA_DTYPE_F16, 1>{}), true;
         if (kv_dtype == PA_DTYPE_BF16) return f(KernelTag<PA_DTYPE_BF16, PA_DTYPE_BF16, 1>{}), true;

@@ -21,7 +21,8 @@ namespace {
 
 thread_local char g_err[512];
 
-int elem_bytes(int dt) { return dt == PA_DTYPE_FP8_E4M3 ? 1 : 2; }
+int elem_bytes(int dt) { return (dt == PA_DTYPE_FP8_E4M3 || dt == PA_DTYPE_INT8) ? 1 : 2; }
+bool scaled_cache(int dt) { return dt == PA_DTYPE_FP8_E4M3 || dt == PA_DTYPE_INT8; }
 
 int pow2ceil(int x) {
     int p = 1;
@@ -79,9 +80,10 @@ int validate_config(const pa_config_t* c, char* why, size_t why_len) {
         return bad(PA_ERR_UNSUPPORTED, "page_size must be a multiple of 16 in 16..65536");
     if (c->q_dtype != PA_DTYPE_F16 && c->q_dtype != PA_DTYPE_BF16)
         return bad(PA_ERR_UNSUPPORTED, "q_dtype must be F16 or BF16");
-    if (c->kv_dtype != PA_DTYPE_F16 && c->kv_dtype != PA_DTYPE_BF16 && c->kv_dtype != PA_DTYPE_FP8_E4M3)
-        return bad(PA_ERR_UNSUPPORTED, "kv_dtype must be F16, BF16 or FP8_E4M3");
-    if (c->kv_dtype != PA_DTYPE_FP8_E4M3 && c->kv_dtype != c->q_dtype)
+    if (c->kv_dtype != PA_DTYPE_F16 && c->kv_dtype != PA_DTYPE_BF16 && c->kv_dtype != PA_DTYPE_FP8_E4M3 &&
+        c->kv_dtype != PA_DTYPE_INT8)
+        return bad(PA_ERR_UNSUPPORTED, "kv_dtype must be F16, BF16, FP8_E4M3 or INT8");
+    if (!scaled_cache(c->kv_dtype) && c->kv_dtype != c->q_dtype)
         return bad(PA_ERR_UNSUPPORTED, "a 16-bit cache must have the query's dtype");
     if (c->max_num_seqs < 1 || c->max_num_seqs > 1024) return bad(PA_ERR_INVALID_ARGUMENT, "max_num_seqs must be 1..1024");
     if (c->max_q_len < 1) return bad(PA_ERR_INVALID_ARGUMENT, "max_q_len must be >= 1");
@@ -115,7 +117,7 @@ void size_handle(pa_handle* h, const pa_config_t* cfg, int cu_count) {
     h->max_items_valu = grid_cap + cfg->max_num_seqs * cfg->num_kv_heads;
     // rows per tile-kernel item: 32 (verification widths), else 256 rows over
     // eight waves for 16-bit caches and 128 over four for fp8
-    h->mfma_wr = rows_max > 64 ? (cfg->kv_dtype == PA_DTYPE_FP8_E4M3 ? 4 : 8) : 1;
+    h->mfma_wr = rows_max > 64 ? (scaled_cache(cfg->kv_dtype) ? 4 : 8) : 1;
     // The tile kernel launches exactly one round of resident workgroups; its
     // in-kernel plan sizes the splits for that many items.
     h->mfma_grid = D == 128 ? h->cu_count * mfma_blocks_per_cu(cfg->kv_dtype, cfg->q_dtype, h->mfma_wr,
@@ -195,6 +197,9 @@ static int validate_cache(pa_handle* h, const pa_cache_layout_t* L, const void* 
     if ((L->page_stride * eb) % 16 || (L->head_stride * eb) % 16 || (L->token_stride * eb) % 16)
         return fail(h, PA_ERR_INVALID_ARGUMENT, "every stride must be a multiple of 16 bytes");
     if (L->num_pages > ((int64_t)1 << 31)) return fail(h, PA_ERR_INVALID_ARGUMENT, "num_pages must fit in int32");
+    if (c.kv_dtype == PA_DTYPE_INT8 &&
+        (L->page_stride % c.head_dim || L->head_stride % c.head_dim || L->token_stride % c.head_dim))
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "an int8 cache needs every stride to be a multiple of head_dim");
     const int cpp = c.page_size / 16;
     if (cpp > 1) {
         // pages of more than 16 tokens are addressed as 16-token virtual pages
@@ -222,8 +227,11 @@ int check_forward(pa_handle* h, const ForwardCall& f) {
     if ((int64_t)f.bt_stride * (c.page_size / 16) >= ((int64_t)1 << 24))
         return fail(h, PA_ERR_UNSUPPORTED, "block_table_stride x page_size must be below 2^28 tokens");
     if (!std::isfinite(f.scale) || !(f.scale > 0.f)) return fail(h, PA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
-    if ((c.kv_dtype == PA_DTYPE_FP8_E4M3) != (f.kv_scale != nullptr))
-        return fail(h, PA_ERR_INVALID_ARGUMENT, "kv_scale is required for an fp8 cache and must be NULL otherwise");
+    if (scaled_cache(c.kv_dtype) != (f.kv_scale != nullptr))
+        return fail(h, PA_ERR_INVALID_ARGUMENT,
+                    "kv_scale is required for an fp8 or int8 cache and must be NULL otherwise");
+    if (f.kv_scale && (reinterpret_cast<uintptr_t>(f.kv_scale) & 3u))
+        return fail(h, PA_ERR_INVALID_ARGUMENT, "kv_scale must be 4-byte aligned");
     return validate_cache(h, f.layout, f.k_cache, f.v_cache);
 }
 
@@ -286,6 +294,14 @@ int enqueue_forward(pa_handle* h, const ForwardCall& f, const LaunchPlan& lp) {
     a.num_seqs = f.num_seqs;
     a.bt_stride = f.bt_stride;
     a.bt_chunks = f.bt_stride * a.cpp;
+    if (c.kv_dtype == PA_DTYPE_INT8) {
+        // row scales: laid out like the cache with rows of one element
+        a.row_scale = f.kv_scale;
+        a.rs_v = f.layout->num_pages * f.layout->page_stride / c.head_dim;
+        a.rs_page = a.page_stride / c.head_dim;
+        a.rs_head = f.layout->head_stride / c.head_dim;
+        a.rs_tok = f.layout->token_stride / c.head_dim;
+    }
     a.num_q_heads = c.num_q_heads;
     a.num_kv_heads = c.num_kv_heads;
     a.group = G;
@@ -538,7 +554,7 @@ int paged_attn_debug_gather(pa_handle_t* h, const void* k_cache, const pa_cache_
 int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int64_t num_tokens, void* k_cache,
                       void* v_cache, const pa_cache_layout_t* layout, const int32_t* block_table, int32_t num_seqs,
                       int32_t block_table_stride, const int32_t* seq_lens, const int32_t* q_lens,
-                      const float* kv_scale, void* stream) {
+                      float* kv_scale, void* stream) {
     if (!h) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "handle is NULL");
     const pa_config_t& c = h->cfg;
     int rc = validate_cache(h, layout, k_cache, v_cache);
@@ -552,8 +568,9 @@ int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int6
     if (num_seqs < 1 || num_seqs > c.max_num_seqs)
         return fail(h, PA_ERR_INVALID_ARGUMENT, "num_seqs %d outside 1..%d", num_seqs, c.max_num_seqs);
     if (block_table_stride < 1) return fail(h, PA_ERR_INVALID_ARGUMENT, "block_table_stride must be >= 1");
-    if ((c.kv_dtype == PA_DTYPE_FP8_E4M3) != (kv_scale != nullptr))
-        return fail(h, PA_ERR_INVALID_ARGUMENT, "kv_scale is required for an fp8 cache and must be NULL otherwise");
+    if (scaled_cache(c.kv_dtype) != (kv_scale != nullptr))
+        return fail(h, PA_ERR_INVALID_ARGUMENT,
+                    "kv_scale is required for an fp8 or int8 cache and must be NULL otherwise");
     DeviceGuard guard(c.device);
     if (!guard.ok) return fail(h, PA_ERR_HIP, "hipSetDevice(%d) failed", c.device);
     pa::AppendArgs a{};
@@ -575,6 +592,14 @@ int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int6
     a.num_kv_heads = c.num_kv_heads;
     a.head_dim = c.head_dim;
     a.page_size = c.page_size;
+    if (c.kv_dtype == PA_DTYPE_INT8) {
+        a.kv_scale = nullptr;
+        a.row_scale = kv_scale;
+        a.rs_v = layout->num_pages * layout->page_stride / c.head_dim;
+        a.rs_page = layout->page_stride / c.head_dim;
+        a.rs_head = layout->head_stride / c.head_dim;
+        a.rs_tok = layout->token_stride / c.head_dim;
+    }
     hipError_t e = pa::launch_append(a, c.kv_dtype, c.q_dtype, c.max_q_len, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(h, PA_ERR_HIP, "append launch failed: %s", hipGetErrorString(e));
     return PA_OK;

@@ -16,8 +16,9 @@ from synth.torch_upload import upload_batch, upload_pool
 # Tolerances (max abs error against the fp64 oracle): fp16/bf16 caches with
 # fp32 accumulation 2e-3 on out and 1e-3 on lse; fp8 caches 2e-2 on out and
 # 1e-3 on lse (the oracle reads the same stored codes and scales, which
-# enter the scores exactly in fp32, so the lse carries no format error).
-TOL = {"f16": (2e-3, 1e-3), "bf16": (2e-3, 1e-3), "fp8_e4m3": (2e-2, 1e-3)}
+# enter the scores exactly in fp32, so the lse carries no format error);
+# int8 caches (per-row scales) the same as fp8.
+TOL = {"f16": (2e-3, 1e-3), "bf16": (2e-3, 1e-3), "fp8_e4m3": (2e-2, 1e-3), "int8": (2e-2, 1e-3)}
 
 
 def progress(msg: str) -> None:
@@ -66,10 +67,15 @@ class GpuCase:
                     for b in batches]
         self.lse = [torch.empty((b.num_tokens, b.num_q_heads), dtype=torch.float32, device="cuda") for b in batches]
 
+    def kv_scale(self, i: int = 0):
+        """The kv_scale argument: per-head scales (fp8) or the pool's row
+        scales (int8)."""
+        return self.pools["row_scale"] if "row_scale" in self.pools else self.dev[i]["kv_scale"]
+
     def forward(self, i: int = 0, stream=None):
         b, d = self.batches[i], self.dev[i]
         pal.paged_attn_forward(self.h, d["q"], self.pools["k"], self.pools["v"], d["block_table"], d["seq_lens"],
-                               d["q_lens"], b.window, b.scale, d["kv_scale"], self.out[i], self.lse[i],
+                               d["q_lens"], b.window, b.scale, self.kv_scale(i), self.out[i], self.lse[i],
                                stream=stream)
 
     def run(self, i: int = 0):

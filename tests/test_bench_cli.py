@@ -100,4 +100,4 @@ def test_kernel_trace_parser_takes_dispatches_between_markers(tmp_path):
 def test_default_run_is_the_mixed_batch():
     src = open(os.path.join(ROOT, "bench.py")).read()
     assert 'ap.add_argument("--workload", default="mixed_fp8"' in src
-    assert set(bench.PER_CONFIG) == {"tiny_decode", "decode", "verify", "verify_window", "prefill"}
+    assert {"tiny_decode", "decode", "verify", "verify_window", "prefill"} <= set(bench.PER_CONFIG)
