@@ -66,6 +66,15 @@ extern "C" {
 #define PA_DTYPE_FP8_E4M3  3   /* OCP E4M3FN: bias 7, max 448, no inf, S.1111.111 = NaN */
 #define PA_DTYPE_INT8      4   /* two's-complement int8 codes, one fp32 scale per cached row */
 
+/* pa_config_t.flags */
+#define PA_DEBUG_CHECKS    1   /* device-checked mode, see paged_attn_debug_status */
+
+/* bits of the device error word of the checked mode */
+#define PA_CHECK_LENGTHS   1   /* q_len < 0, q_len > seq_len, q_len > max_q_len or seq_len < 0 */
+#define PA_CHECK_TABLE     2   /* a sequence needs more pages than its block-table row holds */
+#define PA_CHECK_PAGE      4   /* a block-table entry that is read lies outside [0, num_pages) */
+#define PA_CHECK_TOKENS    8   /* the q_lens add up to more than num_tokens */
+
 /* execution paths (pa_tuning_t.path) */
 #define PA_PATH_AUTO   0   /* VALU split-KV kernel for rows-per-KV-head <= 8, MFMA tile kernel above */
 #define PA_PATH_VALU   1   /* every sequence through the VALU split-KV kernel (handles whose
@@ -95,7 +104,7 @@ typedef struct pa_config {
                                 hint: kernels for narrower rows are not launched */
     int64_t max_num_tokens;  /* largest T = sum of q_lens, >= 1 */
     int32_t device;          /* HIP device ordinal the handle runs on */
-    int32_t flags;           /* reserved, must be 0 */
+    int32_t flags;           /* 0 or PA_DEBUG_CHECKS; other bits must be 0 */
 } pa_config_t;
 
 /* Physical layout of the K and V page pools (identical for both).  Strides
@@ -173,7 +182,16 @@ int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out);
  *  stream       hipStream_t or NULL.
  *
  * Device-array contents (block table, lengths) are trusted: they are not
- * read on the host.  Violating the documented ranges is undefined.
+ * read on the host.  Violating the documented ranges is undefined, unless
+ * the handle was created with PA_DEBUG_CHECKS: then the kernels check every
+ * sequence's lengths against the block-table width, max_q_len and
+ * num_tokens, and every block-table entry they use against num_pages,
+ * before the accesses these values steer.  A bad sequence is skipped, a bad
+ * page id replaced by page 0, every kernel completes normally, and the kind
+ * of fault is recorded for paged_attn_debug_status (the freed-block reads
+ * of "Dual MI50, part 2", section "Bug 2: the drafter read freed memory",
+ * are this class of error).  The outputs of an affected forward are
+ * unspecified.
  * Returns PA_ERR_INVALID_ARGUMENT for a rejected host argument (null or
  * misaligned pointer, size out of range, scale not finite and positive, kv_scale given
  * or missing), PA_ERR_HIP if the launch fails.
@@ -194,8 +212,23 @@ void paged_attn_destroy(pa_handle_t* h);
 
 /* paged_attn_last_error: message of the last failed call on `h` (or of the
  * last failed create / handle-less call on this thread when h is NULL);
- * "" if none.  Valid until the next call on the same handle / thread. */
+ * "" if none.  Valid until the next call on the same handle / thread.  On a
+ * handle created with PA_DEBUG_CHECKS it first collects the device error
+ * word as paged_attn_debug_status does (a synchronous device read: call it
+ * once the stream work has finished), so a fault the kernels recorded is
+ * the message. */
 const char* paged_attn_last_error(const pa_handle_t* h);
+
+/*
+ * paged_attn_debug_status: on a handle created with PA_DEBUG_CHECKS, reads
+ * the device error word that forward and append set (a synchronous device
+ * read: the caller synchronises its stream first), stores its PA_CHECK_*
+ * bits in *bits_out (may be NULL), clears it, and returns PA_OK if it was 0
+ * or PA_ERR_INVALID_ARGUMENT with a message naming the faults.  Returns
+ * PA_ERR_UNSUPPORTED on a handle without the flag, PA_ERR_HIP if the read
+ * fails.
+ */
+int paged_attn_debug_status(pa_handle_t* h, int32_t* bits_out);
 
 /* paged_attn_set_tuning: replace the handle's knobs (NULL restores the
  * defaults).  Results stay within the stated tolerances for every setting;
@@ -280,7 +313,8 @@ int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int6
  * calls that overlap on one GPU (concurrent streams, threads) race and give
  * wrong results; serialise them.  A configuration whose workspace exceeds
  * the array -- prefill-sized row counts, large batches -- is rejected with
- * PA_ERR_UNSUPPORTED and a message naming the size it needs; decode and
+ * PA_ERR_UNSUPPORTED and a message naming the size it needs, as is
+ * cfg->flags = PA_DEBUG_CHECKS (its error word belongs to a handle); decode and
  * verification widths of the usual head counts fit.  Errors are reported by
  * paged_attn_last_error(NULL) on the calling thread.
  */

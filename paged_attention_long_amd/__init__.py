@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     make_config,
     paged_attn_create,
     paged_attn_debug_gather,
+    paged_attn_debug_status,
     paged_attn_append,
     paged_attn_destroy,
     paged_attn_forward,

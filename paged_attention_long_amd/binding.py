@@ -27,6 +27,12 @@ PA_DTYPE_BF16 = 2
 PA_DTYPE_FP8_E4M3 = 3
 PA_DTYPE_INT8 = 4
 
+PA_DEBUG_CHECKS = 1
+PA_CHECK_LENGTHS = 1
+PA_CHECK_TABLE = 2
+PA_CHECK_PAGE = 4
+PA_CHECK_TOKENS = 8
+
 PA_PATH_AUTO = 0
 PA_PATH_VALU = 1
 PA_PATH_MFMA = 2
@@ -113,6 +119,8 @@ def load_library() -> ctypes.CDLL:
         ctypes.POINTER(pa_config_t), vp, i64, vp, vp, ctypes.POINTER(pa_cache_layout_t), vp, i32, i32, vp, vp, i32,
         f32, vp, vp, vp, vp]
     lib.paged_attn_forward_noalloc.restype = ctypes.c_int
+    lib.paged_attn_debug_status.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
+    lib.paged_attn_debug_status.restype = ctypes.c_int
     lib.paged_attn_version.argtypes = []
     lib.paged_attn_version.restype = ctypes.c_char_p
     _lib = lib
@@ -163,9 +171,9 @@ def _stream_ptr(stream) -> Optional[int]:
 
 def make_config(num_q_heads: int, num_kv_heads: int, head_dim: int, q_dtype: str, kv_dtype: str,
                 max_num_seqs: int, max_q_len: int, max_num_tokens: int, page_size: int = 16,
-                device: int = 0, min_q_len: int = 1) -> pa_config_t:
+                device: int = 0, min_q_len: int = 1, flags: int = 0) -> pa_config_t:
     return pa_config_t(num_q_heads, num_kv_heads, head_dim, page_size, DTYPE_CODES[q_dtype],
-                       DTYPE_CODES[kv_dtype], max_num_seqs, max_q_len, min_q_len, max_num_tokens, device, 0)
+                       DTYPE_CODES[kv_dtype], max_num_seqs, max_q_len, min_q_len, max_num_tokens, device, flags)
 
 
 def paged_attn_create(cfg: pa_config_t) -> Handle:
@@ -319,6 +327,16 @@ def paged_attn_append(h: Handle, k_new, v_new, k_cache, v_cache, block_table, se
         _ptr(block_table), seq_lens.shape[0], block_table.stride(0), _ptr(seq_lens), _ptr(q_lens), _ptr(kv_scale),
         _stream_ptr(stream))
     _check(rc, h.ptr)
+
+
+def paged_attn_debug_status(h: Handle):
+    """(PA_CHECK_* bits, message) of a PA_DEBUG_CHECKS handle's device error
+    word, which the call clears; the caller synchronises its stream first."""
+    bits = ctypes.c_int32(0)
+    rc = load_library().paged_attn_debug_status(h.ptr, ctypes.byref(bits))
+    if rc not in (PA_OK, PA_ERR_INVALID_ARGUMENT):
+        _check(rc, h.ptr)
+    return bits.value, load_library().paged_attn_last_error(h.ptr).decode() if rc != PA_OK else ""
 
 
 def paged_attn_version() -> str:

@@ -99,7 +99,11 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
 #pragma unroll
     for (int w = 0; w < kAppendThreads / kWave; ++w) q_off += red[w];
     const int ql = a.q_lens[b], sl = a.seq_lens[b];
-    if (ql <= 0 || ql > sl || q_off + ql > a.num_tokens) return;
+    if (ql <= 0 || ql > sl || q_off + ql > a.num_tokens) {
+        if (a.checks && threadIdx.x == 0 && blockIdx.y == 0 && ql != 0)
+            debug_flag(a.err_word, (ql < 0 || ql > sl) ? PA_CHECK_LENGTHS : PA_CHECK_TOKENS);
+        return;
+    }
     // 8-element chunks per head row; an int8 row's CPR threads are one aligned
     // lane group (the loop's start and stride are multiples of CPR)
     const int cpr = KVT == PA_DTYPE_INT8 ? CPR : a.head_dim / 8;
@@ -115,9 +119,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
         const int p = sl - ql + i;
         const int lp = p / a.page_size;
         // (an int8 row's threads share p and pid: they skip together)
-        if (lp >= a.bt_stride) continue;
+        if (lp >= a.bt_stride) {
+            if (a.checks) debug_flag(a.err_word, PA_CHECK_TABLE);
+            continue;
+        }
         const int pid = a.block_table[(int64_t)b * a.bt_stride + lp];
-        if (pid < 0 || pid >= a.num_pages) continue;
+        if (pid < 0 || pid >= a.num_pages) {
+            if (a.checks) debug_flag(a.err_word, PA_CHECK_PAGE);
+            continue;
+        }
         const uint16_t* src = static_cast<const uint16_t*>(which ? a.v_new : a.k_new) +
                               ((int64_t)(q_off + i) * a.num_kv_heads + g) * a.head_dim + ch * 8;
         const uint4 in = *reinterpret_cast<const uint4*>(src);

@@ -276,11 +276,43 @@ PA_DEVINLINE int64_t kv_offset(int64_t page, int g, int slot, int64_t page_strid
 // part 2", section "Prefill: teach the fork's fast kernel to read the int8
 // cache": the cache is read in place at any block size).  The quotient is a
 // multiply-high and a shift with a magic number from the host.
+// In the checked mode a page id outside [0, num_pages) is reported and
+// replaced by page 0, so no access leaves the pool.
+PA_DEVINLINE void debug_flag(int* err_word, int bit) {
+    __hip_atomic_fetch_or(err_word, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename BT>
 PA_DEVINLINE int chunk_page(BT bt, int c, const DecodeArgs& a) {
-    if (a.cpp == 1) return bt[c];
-    const int q = (int)(__umulhi((uint32_t)c, a.cpp_magic) >> a.cpp_shift);
-    return bt[q] * a.vr + (c - q * a.cpp);
+    int q = c, sub = 0;
+    if (a.cpp != 1) {
+        q = (int)(__umulhi((uint32_t)c, a.cpp_magic) >> a.cpp_shift);
+        sub = c - q * a.cpp;
+    }
+    int pid = bt[q];
+    if (a.checks && (unsigned)pid >= (unsigned long long)a.num_pages) {
+        debug_flag(a.err_word, PA_CHECK_PAGE);
+        pid = 0;
+    }
+    return a.cpp == 1 ? pid : pid * a.vr + sub;
+}
+
+// The q_len a kernel uses for a sequence of seq_len sl: in the checked mode
+// an invalid pair (q_len < 0 or > seq_len or > max_q_len, seq_len < 0, or
+// more pages than the block-table row holds) is reported and the sequence
+// skipped (q_len 0).  The result depends on (sl, ql) alone, so every kernel
+// and every prefix sum over q_lens sees the same value.
+PA_DEVINLINE int checked_q_len(const DecodeArgs& a, int sl, int ql) {
+    if (!a.checks) return ql;
+    if (ql < 0 || sl < 0 || ql > sl || ql > a.max_q_len) {
+        debug_flag(a.err_word, PA_CHECK_LENGTHS);
+        return 0;
+    }
+    if (ql > 0 && (sl - 1) / 16 >= a.bt_chunks) {
+        debug_flag(a.err_word, PA_CHECK_TABLE);
+        return 0;
+    }
+    return ql;
 }
 
 // ----------------------------------------------------------------- split plan
@@ -383,7 +415,7 @@ PA_DEVINLINE void build_plan(Plan& pl, int* dyn, const DecodeArgs& a, const int3
         int ql = 0, np = 0;
         if (b < num_seqs) {
             const int sl = seq_lens[b];
-            ql = q_lens[b];
+            ql = checked_q_len(a, sl, q_lens[b]);
             pl.seq_len[b] = sl;
             pl.q_len[b] = ql;
             const int rows = ql * group;
@@ -394,6 +426,13 @@ PA_DEVINLINE void build_plan(Plan& pl, int* dyn, const DecodeArgs& a, const int3
         int tot;
         const int ex = block_exclusive_scan(ql, pl.red, &tot);
         if (b < num_seqs) pl.q_off[b] = carry_q + ex;
+        if (a.checks && b < num_seqs && ql > 0 && (int64_t)carry_q + ex + ql > a.num_tokens) {
+            // rows past num_tokens: skipped (and so is every later sequence)
+            debug_flag(a.err_word, PA_CHECK_TOKENS);
+            pl.q_len[b] = 0;
+            pl.aux[b] = 0;
+            np = 0;
+        }
         carry_q += tot;
         const int npw = (int)wave_sum_i64(np), npm = wave_max_i32(np);
         if (lane == 0) { pl.red[wid] = npw; pl.red[16 + wid] = npm; }

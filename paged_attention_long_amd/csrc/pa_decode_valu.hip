@@ -474,16 +474,25 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         if (b >= a.num_seqs) return;
         const int pps = a.static_pps;
         const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
-        for (int k = tid; k < pps; k += kThreads)
-            sm.pid[k] = (split * pps + k < a.bt_chunks) ? chunk_page(bt, split * pps + k, a) : 0;
+        // (checked mode: only the sequence's own pages are staged, below)
+        if (!a.checks)
+            for (int k = tid; k < pps; k += kThreads)
+                sm.pid[k] = (split * pps + k < a.bt_chunks) ? chunk_page(bt, split * pps + k, a) : 0;
         if (wid == 0) {
             int qs = 0;
-            for (int b0 = 0; b0 < b; b0 += kWave) qs += (b0 + lane < b) ? a.q_lens[b0 + lane] : 0;
+            for (int b0 = 0; b0 < b; b0 += kWave)
+                qs += (b0 + lane < b) ? checked_q_len(a, a.seq_lens[b0 + lane], a.q_lens[b0 + lane]) : 0;
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) qs += __shfl_xor(qs, o, kWave);
             if (lane == 0) {
-                sm.stat[0] = a.seq_lens[b];
-                sm.stat[1] = a.q_lens[b];
+                const int sl = a.seq_lens[b];
+                int ql = checked_q_len(a, sl, a.q_lens[b]);
+                if (a.checks && ql > 0 && (int64_t)qs + ql > a.num_tokens) {
+                    debug_flag(a.err_word, PA_CHECK_TOKENS);
+                    ql = 0;
+                }
+                sm.stat[0] = sl;
+                sm.stat[1] = ql;
                 sm.stat[2] = qs;
             }
         }
@@ -503,7 +512,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
         si.splits = s_last - s_first + 1;
         const int p_begin = max(split * pps, si.first_page);
         const int p_end = min((split + 1) * pps, last_page + 1);
-        if (p_begin > split * pps) {   // window start inside this split: realign the staged ids
+        if (a.checks || p_begin > split * pps) {   // window start inside this split: realign the staged ids
             __syncthreads();
             for (int k = tid; k < p_end - p_begin; k += kThreads) sm.pid[k] = chunk_page(bt, p_begin + k, a);
             __syncthreads();

@@ -71,6 +71,14 @@ struct DecodeArgs {
     int num_q_heads, num_kv_heads, group;
     int window;
     float scale;
+    // Checked mode (PA_DEBUG_CHECKS): lengths and page ids are validated
+    // before the accesses they steer; a bad value is replaced by a safe one
+    // (the sequence skipped, page 0 read) and its kind or-ed into *err_word.
+    int checks;
+    int* err_word;
+    int64_t num_pages;         // physical pages of the pool
+    int max_q_len;
+    int64_t num_tokens;
     int cls_side;              // 0: VALU launch (short, few-row sequences), 1: tile launch (the rest)
     int cls_rows, cls_len;     // VALU class: rows per KV head <= cls_rows and visible keys <= cls_len
     int target_items, min_pps, forced_pps, max_items, r_max;   // forced_pps: pages (VALU) or tiles (MFMA) per split
@@ -148,6 +156,8 @@ struct AppendArgs {
     int64_t num_pages, page_stride, head_stride, token_stride;   // elements
     int64_t num_tokens;
     int num_seqs, bt_stride, num_kv_heads, head_dim, page_size;
+    int checks;                // PA_DEBUG_CHECKS: skipped rows are reported in *err_word
+    int* err_word;
 };
 
 // max_rows: the largest q_len of the call (sizes the grid along the rows).

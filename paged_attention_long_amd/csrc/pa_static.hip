@@ -79,6 +79,8 @@ extern "C" int paged_attn_forward_noalloc(const pa_config_t* cfg, const void* q,
     int rc = validate_config(cfg, why, sizeof why);
     if (rc != PA_OK) return fail(nullptr, rc, "%s", why);
     if (cfg->device >= kMaxDevices) return fail(nullptr, PA_ERR_UNSUPPORTED, "device %d >= %d", cfg->device, kMaxDevices);
+    if (cfg->flags & PA_DEBUG_CHECKS)
+        return fail(nullptr, PA_ERR_UNSUPPORTED, "PA_DEBUG_CHECKS needs a handle (its error word belongs to it)");
     int ndev = 0;
     if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= cfg->device)
         return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "device %d not present (%d devices)", cfg->device, ndev);

@@ -527,7 +527,12 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
         const bool one = a.num_seqs == 1;
         int one_nqt = 0, one_tub = 0;
         if (one) {
-            const int sl = a.seq_lens[0], ql = a.q_lens[0];
+            const int sl = a.seq_lens[0];
+            int ql = checked_q_len(a, sl, a.q_lens[0]);
+            if (a.checks && ql > a.num_tokens) {
+                debug_flag(a.err_word, PA_CHECK_TOKENS);
+                ql = 0;
+            }
             seq_stats(sl, ql, one_nqt, one_tub);
             if (tid == 0) {
                 pl.seq_len[0] = sl;
@@ -544,7 +549,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             int ql = 0, nqt = 0, tub = 0;
             if (b < a.num_seqs) {
                 const int sl = a.seq_lens[b];
-                ql = a.q_lens[b];
+                ql = checked_q_len(a, sl, a.q_lens[b]);
                 pl.seq_len[b] = sl;
                 pl.q_len[b] = ql;
                 seq_stats(sl, ql, nqt, tub);
@@ -554,6 +559,15 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             int tot;
             const int ex = block_exclusive_scan(ql, pl.red, &tot);
             if (b < a.num_seqs) pl.q_off[b] = carry_q + ex;
+            if (a.checks && b < a.num_seqs && ql > 0 && (int64_t)carry_q + ex + ql > a.num_tokens) {
+                // rows past num_tokens: skipped (and so is every later sequence)
+                debug_flag(a.err_word, PA_CHECK_TOKENS);
+                pl.q_len[b] = 0;
+                pl.aux[b] = 0;
+                pl.item_base[b] = 0;
+                nqt = 0;
+                tub = 0;
+            }
             carry_q += tot;
             const long long w = wave_sum_i64((long long)nqt * tub), nq = wave_sum_i64(nqt);
             const int mt = wave_max_i32(tub);

@@ -95,7 +95,7 @@ int validate_config(const pa_config_t* c, char* why, size_t why_len) {
         return bad(PA_ERR_INVALID_ARGUMENT, "max_num_tokens must be 1..2^24");
     if ((int64_t)c->max_q_len * (c->num_q_heads / c->num_kv_heads) > (1 << 20))
         return bad(PA_ERR_UNSUPPORTED, "max_q_len * group too large");
-    if (c->flags != 0) return bad(PA_ERR_INVALID_ARGUMENT, "flags must be 0");
+    if (c->flags & ~PA_DEBUG_CHECKS) return bad(PA_ERR_INVALID_ARGUMENT, "flags must be 0 or PA_DEBUG_CHECKS");
     if (c->device < 0) return bad(PA_ERR_INVALID_ARGUMENT, "device must be >= 0");
     return PA_OK;
 }
@@ -307,6 +307,11 @@ int enqueue_forward(pa_handle* h, const ForwardCall& f, const LaunchPlan& lp) {
     a.group = G;
     a.window = f.window;
     a.scale = f.scale;
+    a.checks = (c.flags & PA_DEBUG_CHECKS) != 0;
+    a.err_word = h->err_word;
+    a.num_pages = f.layout->num_pages;
+    a.max_q_len = c.max_q_len;
+    a.num_tokens = f.num_tokens;
     const int grid = h->tune.grid > 0 ? h->tune.grid : h->grid_default;
     a.target_items = grid;
     hipStream_t st = f.stream;
@@ -432,7 +437,39 @@ extern "C" {
 
 const char* paged_attn_version(void) { return "0.2.0"; }
 
-const char* paged_attn_last_error(const pa_handle_t* h) { return h ? h->err : pa::thread_error(); }
+namespace {
+
+// Reads and clears the checked mode's device error word; a message on h.
+int collect_device_checks(pa_handle* h, int32_t* bits_out) {
+    int w = 0;
+    DeviceGuard guard(h->cfg.device);
+    if (!guard.ok || hipMemcpy(&w, h->err_word, sizeof w, hipMemcpyDeviceToHost) != hipSuccess ||
+        (w != 0 && hipMemset(h->err_word, 0, sizeof w) != hipSuccess))
+        return fail(h, PA_ERR_HIP, "reading the device error word failed");
+    if (bits_out) *bits_out = w;
+    if (w == 0) return PA_OK;
+    return fail(h, PA_ERR_INVALID_ARGUMENT, "device checks (0x%x):%s%s%s%s", w,
+                (w & PA_CHECK_LENGTHS) ? " q_len/seq_len outside their ranges;" : "",
+                (w & PA_CHECK_TABLE) ? " seq_len past the block-table width;" : "",
+                (w & PA_CHECK_PAGE) ? " block-table page id outside [0, num_pages);" : "",
+                (w & PA_CHECK_TOKENS) ? " q_lens add up past num_tokens;" : "");
+}
+
+}  // namespace
+
+const char* paged_attn_last_error(const pa_handle_t* h) {
+    if (!h) return pa::thread_error();
+    pa_handle* hm = const_cast<pa_handle*>(h);
+    if (hm->cfg.flags & PA_DEBUG_CHECKS) (void)collect_device_checks(hm, nullptr);
+    return h->err;
+}
+
+int paged_attn_debug_status(pa_handle_t* h, int32_t* bits_out) {
+    if (!h) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "handle is NULL");
+    if (bits_out) *bits_out = 0;
+    if (!(h->cfg.flags & PA_DEBUG_CHECKS)) return fail(h, PA_ERR_UNSUPPORTED, "the handle has no PA_DEBUG_CHECKS");
+    return collect_device_checks(h, bits_out);
+}
 
 int paged_attn_create(const pa_config_t* cfg, pa_handle_t** out) {
     if (!out) return fail(nullptr, PA_ERR_INVALID_ARGUMENT, "out is NULL");
@@ -592,6 +629,8 @@ int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int6
     a.num_kv_heads = c.num_kv_heads;
     a.head_dim = c.head_dim;
     a.page_size = c.page_size;
+    a.checks = (c.flags & PA_DEBUG_CHECKS) != 0;
+    a.err_word = h->err_word;
     if (c.kv_dtype == PA_DTYPE_INT8) {
         a.kv_scale = nullptr;
         a.row_scale = kv_scale;

@@ -80,11 +80,13 @@ def test_page_chunk_division_by_multiply_high():
         assert np.array_equal(q, c // np.uint64(d)), d
 
 
-def test_flags_rejected():
+def test_unknown_flags_rejected():
     cfg = _cfg()
-    cfg.flags = 1
-    with pytest.raises(pal.PagedAttnError):
+    cfg.flags = 2
+    with pytest.raises(pal.PagedAttnError) as e:
         pal.paged_attn_create(cfg)
+    assert e.value.code == B.PA_ERR_INVALID_ARGUMENT
+    assert "flags" in pal.paged_attn_last_error(None)
 
 
 def test_null_handle_calls_fail_cleanly():
