@@ -366,10 +366,15 @@ struct Cfg {
     // raw (V by 8-bit transposing reads) and widened in registers at their
     // matrix ops.  RAW_DMA 1 KB loads per wave per tile (K and V).
     static constexpr bool FSTAGE = BYTE && (WR == 1);
+    // V through registers (32-row one-byte items): V rows are loaded one
+    // step ahead into registers and written into the staging slot when their
+    // step begins, K alone takes the asynchronous path (which tops out lower
+    // than register loads, so the two paths together move more)
+    static constexpr bool VREG = FSTAGE && FP8;   // (int8's scale registers leave no room)
     static constexpr int RAW_TILE = BN * D;                // bytes of one raw fp8 K (or V) tile
     // int8: one more 4-byte load per lane and tile brings the tile's K and V
     // row scales into LDS
-    static constexpr int RAW_DMA = 2 * RAW_TILE / 1024 + (INT8 ? 1 : 0);
+    static constexpr int RAW_DMA = (VREG ? 1 : 2) * RAW_TILE / 1024 + (INT8 ? 1 : 0);
     static constexpr int STAGE_LDS = FSTAGE ? WK * 2 * 2 * RAW_TILE : 16;
     // 256-row items on 16-bit caches run a software pipeline: K tiles in a
     // ring of NKB buffers, V tiles in a ring of NVB, loads issued LEAD tiles
@@ -897,6 +902,29 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                                         (((lane & 7) ^ ((lane >> 3) & 7)) << 4));
             }
         }
+        // VREG: one tile's V rows in registers, in the staging layout (load i,
+        // lane l: the 16 bytes the asynchronous path would put at i*1024 + 16*l)
+        u32x4_t vreg[C::VREG ? 4 : 1];
+        auto v_load = [&](int t) {
+            if constexpr (C::VREG) {
+                int pid[PPT];
+                tile_pids(t, pid);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    vreg[i] = load_b128(vbase + (int64_t)pid[(8 * i) / kPage] * page_bytes + raw_off[i]);
+            }
+        };
+        auto v_store = [&](auto slot_c) {
+            if constexpr (C::VREG) {
+                const uint32_t v32 = (uint32_t)(uintptr_t)(lds_void_t*)(stage + gi * 4 * C::RAW_TILE +
+                                                                       decltype(slot_c)::value * 2 * C::RAW_TILE +
+                                                                       C::RAW_TILE) + 16 * lane;
+                lds_store_b128<0>(v32, vreg[0]);
+                lds_store_b128<1024>(v32, vreg[1]);
+                lds_store_b128<2048>(v32, vreg[2]);
+                lds_store_b128<3072>(v32, vreg[3]);
+            }
+        };
         auto raw_dma = [&](auto slot_c, int t) {
             if constexpr (C::FSTAGE) {
                 uint8_t* st = stage + gi * 4 * C::RAW_TILE + decltype(slot_c)::value * 2 * C::RAW_TILE;
@@ -906,7 +934,8 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 for (int i = 0; i < 4; ++i) {
                     const int64_t pb = (int64_t)pid[(8 * i) / kPage] * page_bytes;
                     async_load16(kbase + pb + raw_off[i], (lds_void_t*)(st + i * 1024));
-                    async_load16(vbase + pb + raw_off[i], (lds_void_t*)(st + C::RAW_TILE + i * 1024));
+                    if constexpr (!C::VREG)
+                        async_load16(vbase + pb + raw_off[i], (lds_void_t*)(st + C::RAW_TILE + i * 1024));
                 }
                 if constexpr (C::INT8) {
                     // lanes 0..31: K scales of keys 0..31; lanes 32..63: their V scales
@@ -1333,13 +1362,22 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                     }
                 }
                 auto tile_of = [&](int k) { return my_first + k * C::WK; };
+                // issue order: K(0), V(0), K(1); a step k finds K(k), V(k) and
+                // K(k+1) in flight and waits for the first two
                 raw_dma(I0{}, min(tile_of(0), ig.t_end - 1));
+                v_load(min(tile_of(0), ig.t_end - 1));
                 raw_dma(I1{}, min(tile_of(1), ig.t_end - 1));
                 u32x4_t pb[C::TS], pl[C::TS];
                 auto fstep = [&](auto j_c, int k) {
                     constexpr int J = decltype(j_c)::value;
                     const int t = tile_of(k);
                     __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::RAW_DMA));   // slot J's tile is the older in flight
+                    if constexpr (C::VREG) {
+                        // this tile's V rows into the slot (the stores take their
+                        // data at issue), then the next tile's V rows go out
+                        v_store(j_c);
+                        v_load(min(tile_of(k + 1), ig.t_end - 1));
+                    }
                     if (t < ig.t_end) {
                         // dead keys' V rows (range edges only) are zeroed in the slot
                         {
