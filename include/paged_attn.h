@@ -84,8 +84,9 @@ extern "C" {
 typedef struct pa_config {
     int32_t num_q_heads;     /* Hq >= 1 */
     int32_t num_kv_heads;    /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 16 */
-    int32_t head_dim;        /* D: 64 or 128; 64 runs on the VALU kernel only and needs
-                                max_q_len * Hq / Hkv <= 64 (else PA_ERR_UNSUPPORTED at create) */
+    int32_t head_dim;        /* D: 64, 128 or 256; 64 and 256 run on the VALU kernel only and need
+                                max_q_len * Hq / Hkv <= 64 (decode and verification widths; else
+                                PA_ERR_UNSUPPORTED at create) */
     int32_t page_size;       /* P: tokens per page, a multiple of 16 in 16..65536 (the cache is read in
                                 place at any such block size: "Dual MI50, part 2", section "Prefill:
                                 teach the fork's fast kernel to read the int8 cache"; the pages use

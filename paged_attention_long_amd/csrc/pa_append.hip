@@ -66,7 +66,12 @@ PA_DEVINLINE float group_max_nan(float x) {
     x = mx(x, dpp<kDppQuadXor1>(x));
     x = mx(x, dpp<kDppQuadXor2>(x));
     x = mx(x, dpp<kDppHalfMirror>(x));
-    if constexpr (N == 16) x = mx(x, dpp<kDppRowMirror>(x));
+    if constexpr (N >= 16) x = mx(x, dpp<kDppRowMirror>(x));
+    if constexpr (N == 32) {
+        const uint32_t u = __float_as_uint(x);
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        x = mx(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
     return x;
 }
 
@@ -181,7 +186,10 @@ hipError_t launch_append(const AppendArgs& a, int kv_dtype, int in_dtype, int ma
     const dim3 grid(a.num_seqs, gy);
     if (kv_dtype == PA_DTYPE_INT8) {
         const bool bf = in_dtype == PA_DTYPE_BF16;
-        if (a.head_dim == 128) {
+        if (a.head_dim == 256) {
+            if (bf) hipLaunchKernelGGL((append_kernel<PA_DTYPE_INT8, PA_DTYPE_BF16, 32>), grid, dim3(kAppendThreads), 0, stream, a);
+            else hipLaunchKernelGGL((append_kernel<PA_DTYPE_INT8, PA_DTYPE_F16, 32>), grid, dim3(kAppendThreads), 0, stream, a);
+        } else if (a.head_dim == 128) {
             if (bf) hipLaunchKernelGGL((append_kernel<PA_DTYPE_INT8, PA_DTYPE_BF16, 16>), grid, dim3(kAppendThreads), 0, stream, a);
             else hipLaunchKernelGGL((append_kernel<PA_DTYPE_INT8, PA_DTYPE_F16, 16>), grid, dim3(kAppendThreads), 0, stream, a);
         } else {

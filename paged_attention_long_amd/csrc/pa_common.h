@@ -123,14 +123,21 @@ PA_DEVINLINE float dpp(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
-// All-reduce over aligned groups of N lanes (N = 8 or 16) inside a row.
+// All-reduce over aligned groups of N lanes (N = 8 or 16 inside a row, 32: two rows).
 template <int N>
 PA_DEVINLINE float group_sum(float x) {
-    static_assert(N == 8 || N == 16, "group size");
+    static_assert(N == 8 || N == 16 || N == 32, "group size");
     x += dpp<kDppQuadXor1>(x);
     x += dpp<kDppQuadXor2>(x);
     x += dpp<kDppHalfMirror>(x);
-    if constexpr (N == 16) x += dpp<kDppRowMirror>(x);
+    if constexpr (N >= 16) x += dpp<kDppRowMirror>(x);
+    if constexpr (N == 32) {
+        // rows 2k and 2k+1 exchange through the gfx950 row swap (the sum of
+        // the pair is the same on both lanes)
+        const uint32_t u = __float_as_uint(x);
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
     return x;
 }
 

@@ -110,20 +110,22 @@ PA_DEVINLINE void v_floats(const typename KvChunk<KVT>::T& c, float v[8]) {
     }
 }
 
+template <int D>
 struct WaveShared {
-    float acc[kWaves][8][128];   // [wave][row][d] (D <= 128, RW <= 8)
+    float acc[kWaves][8][D];     // [wave][row][d] (RW <= 8)
     float m[kWaves][8];
     float l[kWaves][8];
 };
 
 constexpr int kPidChunk = kPidChunkPages;   // page ids staged in LDS at a time
 
+template <int D>
 struct Smem {
     Plan plan;
     int stat[4];
     int pid[kPidChunk];
     union {
-        WaveShared ws;
+        WaveShared<D> ws;
     } u;
 };
 
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
     constexpr int EB = KvChunk<KVT>::bytes;
     using Chunk = typename KvChunk<KVT>::T;
 
-    __shared__ Smem sm;
+    __shared__ Smem<D> sm;
     extern __shared__ int dyn_lds[];
     Plan& pl = sm.plan;
     if (a.static_pps <= 0)
@@ -324,15 +326,15 @@ __global__ __launch_bounds__(kThreads) void decode_valu_kernel(DecodeArgs a) {
             // merge the TPR token lanes of this wave (lanes ch, ch+LPT, ...)
             auto lanes_max = [](float x) {
                 if constexpr (LPT <= 8) x = xor_max<8>(x);
-                x = xor_max<16>(x);
+                if constexpr (LPT <= 16) x = xor_max<16>(x);
                 return xor_max<32>(x);
             };
             auto lanes_sum = [](float x) {
                 if constexpr (LPT <= 8) x = xor_sum<8>(x);
-                x = xor_sum<16>(x);
+                if constexpr (LPT <= 16) x = xor_sum<16>(x);
                 return xor_sum<32>(x);
             };
-            static_assert(LPT == 8 || LPT == 16, "token lanes differ in lane bits 3..5 or 4..5");
+            static_assert(LPT == 8 || LPT == 16 || LPT == 32, "token lanes differ in lane bits 3..5, 4..5 or 5");
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
                 const float M = lanes_max(m[r]);
@@ -569,6 +571,7 @@ static hipError_t launch_d(const DecodeArgs& a, int kvt, int qt, int rw, int gri
 hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int rw, int grid,
                               hipStream_t stream) {
     if (head_dim == 64) return launch_d<64>(a, kv_dtype, q_dtype, rw, grid, stream);
+    if (head_dim == 256) return launch_d<256>(a, kv_dtype, q_dtype, rw, grid, stream);
     return launch_d<128>(a, kv_dtype, q_dtype, rw, grid, stream);
 }
 

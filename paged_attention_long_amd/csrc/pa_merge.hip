@@ -220,6 +220,7 @@ int merge_rows_per_unit(int head_dim) { return merge_rpu(head_dim); }
 hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, int batch, hipStream_t stream) {
     if (m.static_units > 0) {
         if (head_dim == 64) hipLaunchKernelGGL((merge_slots_kernel<64>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+        else if (head_dim == 256) hipLaunchKernelGGL((merge_slots_kernel<256>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
         else hipLaunchKernelGGL((merge_slots_kernel<128>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
         return hipGetLastError();
     }
@@ -230,6 +231,7 @@ hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, int batch, h
         else hipLaunchKernelGGL((merge_kernel<D, 32>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
     };
     if (head_dim == 64) go(std::integral_constant<int, 64>{});
+    else if (head_dim == 256) go(std::integral_constant<int, 256>{});
     else go(std::integral_constant<int, 128>{});
     return hipGetLastError();
 }

@@ -75,7 +75,8 @@ int validate_config(const pa_config_t* c, char* why, size_t why_len) {
     if (c->num_q_heads < 1 || c->num_kv_heads < 1) return bad(PA_ERR_INVALID_ARGUMENT, "head counts must be >= 1");
     if (c->num_q_heads % c->num_kv_heads) return bad(PA_ERR_INVALID_ARGUMENT, "num_q_heads % num_kv_heads != 0");
     if (c->num_q_heads / c->num_kv_heads > 16) return bad(PA_ERR_UNSUPPORTED, "more than 16 query heads per KV head");
-    if (c->head_dim != 64 && c->head_dim != 128) return bad(PA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256)
+        return bad(PA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256");
     if (c->page_size < 16 || c->page_size > 65536 || c->page_size % 16)
         return bad(PA_ERR_UNSUPPORTED, "page_size must be a multiple of 16 in 16..65536");
     if (c->q_dtype != PA_DTYPE_F16 && c->q_dtype != PA_DTYPE_BF16)
@@ -89,8 +90,8 @@ int validate_config(const pa_config_t* c, char* why, size_t why_len) {
     if (c->max_q_len < 1) return bad(PA_ERR_INVALID_ARGUMENT, "max_q_len must be >= 1");
     if (c->min_q_len < 1 || c->min_q_len > c->max_q_len)
         return bad(PA_ERR_INVALID_ARGUMENT, "min_q_len must be 1..max_q_len");
-    if (c->head_dim == 64 && (int64_t)c->max_q_len * (c->num_q_heads / c->num_kv_heads) > 64)
-        return bad(PA_ERR_UNSUPPORTED, "head_dim 64 supports at most 64 rows per KV head");
+    if (c->head_dim != 128 && (int64_t)c->max_q_len * (c->num_q_heads / c->num_kv_heads) > 64)
+        return bad(PA_ERR_UNSUPPORTED, "head_dim 64 and 256 support at most 64 rows per KV head (max_q_len * group)");
     if (c->max_num_tokens < 1 || c->max_num_tokens > (int64_t)1 << 24)
         return bad(PA_ERR_INVALID_ARGUMENT, "max_num_tokens must be 1..2^24");
     if ((int64_t)c->max_q_len * (c->num_q_heads / c->num_kv_heads) > (1 << 20))

@@ -70,6 +70,11 @@ CASES = {
                                     q_lens=(8, 200, 16), scales="arbitrary"),
     "fp8_from_f16_any_scale": dict(kv="fp8_e4m3", q="f16", hkv=4, D=128, seq_lens=(500, 3), q_lens=(64, 3),
                                    scales="arbitrary"),
+    # head_dim 256
+    "bf16_d256": dict(kv="bf16", q="bf16", hkv=2, D=256, seq_lens=(33, 4097, 8), q_lens=(8, 1, 8)),
+    "fp8_from_bf16_d256": dict(kv="fp8_e4m3", q="bf16", hkv=2, D=256, seq_lens=(70, 16), q_lens=(8, 16)),
+    "fp8_from_f16_d256_any_scale": dict(kv="fp8_e4m3", q="f16", hkv=4, D=256, seq_lens=(300, 9), q_lens=(16, 9),
+                                        scales="arbitrary"),
 }
 
 

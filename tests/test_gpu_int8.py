@@ -123,7 +123,8 @@ def test_int8_nan_scale_poison_bit_identical():
     assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
 
 
-@pytest.mark.parametrize("in_dtype,page_size,D", [("bf16", 16, 128), ("f16", 48, 128), ("bf16", 16, 64)])
+@pytest.mark.parametrize("in_dtype,page_size,D", [("bf16", 16, 128), ("f16", 48, 128), ("bf16", 16, 64),
+                                                   ("bf16", 48, 256), ("f16", 16, 256)])
 def test_int8_append_bit_exact_then_forward(in_dtype, page_size, D):
     """The append quantises each new row (scale amax/127, nearest integer,
     ties to even) bit for bit as the oracle does, codes and scales, over the
@@ -133,7 +134,7 @@ def test_int8_append_bit_exact_then_forward(in_dtype, page_size, D):
 
     from synth.torch_upload import upload_batch, upload_pool
 
-    hq, hkv = (32, 8) if D == 128 else (8, 2)
+    hq, hkv = {128: (32, 8), 64: (8, 2), 256: (16, 2)}[D]
     inp = generate(_spec(page_size=page_size, head_dim=D, num_q_heads=hq, num_kv_heads=hkv, q_dtype=in_dtype,
                          seq_lens=(2500, 97, 33), q_lens=(8, 4, 1), seed=62))[0]
     T, P = inp.num_tokens, inp.page_size
