@@ -79,14 +79,16 @@ extern "C" {
 #define PA_PATH_AUTO   0   /* VALU split-KV kernel for rows-per-KV-head <= 8, MFMA tile kernel above */
 #define PA_PATH_VALU   1   /* every sequence through the VALU split-KV kernel (handles whose
                               max_q_len * Hq / Hkv is at most 64; else PA_ERR_UNSUPPORTED) */
-#define PA_PATH_MFMA   2   /* every sequence through the MFMA tile kernel (head_dim 128 only) */
+#define PA_PATH_MFMA   2   /* every sequence through the MFMA tile kernel (head_dim 128 or 256) */
 
 typedef struct pa_config {
     int32_t num_q_heads;     /* Hq >= 1 */
     int32_t num_kv_heads;    /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 16 */
-    int32_t head_dim;        /* D: 64, 128 or 256; 64 and 256 run on the VALU kernel only and need
-                                max_q_len * Hq / Hkv <= 64 (decode and verification widths; else
-                                PA_ERR_UNSUPPORTED at create) */
+    int32_t head_dim;        /* D: 64, 128 or 256.  64 runs on the VALU kernel only and needs
+                                max_q_len * Hq / Hkv <= 64 (else PA_ERR_UNSUPPORTED at create).
+                                256: the VALU kernel takes every sequence while no row count
+                                passes 64 per KV head; past that (chunked prefill) a tile kernel
+                                with 128-row items takes the sequences of more than 8 rows. */
     int32_t page_size;       /* P: tokens per page, a multiple of 16 in 16..65536 (the cache is read in
                                 place at any such block size: "Dual MI50, part 2", section "Prefill:
                                 teach the fork's fast kernel to read the int8 cache"; the pages use

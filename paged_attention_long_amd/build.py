@@ -17,8 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpaged_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["paged_attn.cpp", "pa_decode_valu.hip", "pa_tile_attn.hip", "pa_merge.hip", "pa_gather.hip", "pa_append.hip",
-           "pa_static.hip"]
+SOURCES = ["paged_attn.cpp", "pa_decode_valu.hip", "pa_tile_attn.hip", "pa_tile256.hip", "pa_merge.hip", "pa_gather.hip",
+           "pa_append.hip", "pa_static.hip"]
 
 OBJ_DIR = os.path.join(PKG, "_build")
 

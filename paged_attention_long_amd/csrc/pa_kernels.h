@@ -126,6 +126,10 @@ hipError_t launch_mfma_attn(const DecodeArgs& a, int head_dim, int kv_dtype, int
 int mfma_rows_per_item(int wr);
 // Workgroups of the tile kernel resident per CU (registers and LDS bound it).
 int mfma_blocks_per_cu(int kv_dtype, int q_dtype, int wr, int max_num_seqs);
+// head_dim 256 tile kernel (rows per item, resident workgroups per CU, launch)
+int tile256_rows_per_item();
+int tile256_blocks_per_cu(int kv_dtype, int q_dtype, int max_num_seqs);
+hipError_t launch_tile256(const DecodeArgs& a, int kv_dtype, int q_dtype, int grid, hipStream_t stream);
 
 struct GatherArgs {
     const uint8_t* k_cache;

@@ -90,8 +90,8 @@ int validate_config(const pa_config_t* c, char* why, size_t why_len) {
     if (c->max_q_len < 1) return bad(PA_ERR_INVALID_ARGUMENT, "max_q_len must be >= 1");
     if (c->min_q_len < 1 || c->min_q_len > c->max_q_len)
         return bad(PA_ERR_INVALID_ARGUMENT, "min_q_len must be 1..max_q_len");
-    if (c->head_dim != 128 && (int64_t)c->max_q_len * (c->num_q_heads / c->num_kv_heads) > 64)
-        return bad(PA_ERR_UNSUPPORTED, "head_dim 64 and 256 support at most 64 rows per KV head (max_q_len * group)");
+    if (c->head_dim == 64 && (int64_t)c->max_q_len * (c->num_q_heads / c->num_kv_heads) > 64)
+        return bad(PA_ERR_UNSUPPORTED, "head_dim 64 supports at most 64 rows per KV head (max_q_len * group)");
     if (c->max_num_tokens < 1 || c->max_num_tokens > (int64_t)1 << 24)
         return bad(PA_ERR_INVALID_ARGUMENT, "max_num_tokens must be 1..2^24");
     if ((int64_t)c->max_q_len * (c->num_q_heads / c->num_kv_heads) > (1 << 20))
@@ -119,15 +119,17 @@ void size_handle(pa_handle* h, const pa_config_t* cfg, int cu_count) {
     // rows per tile-kernel item: 32 (verification widths), else 256 rows over
     // eight waves for 16-bit caches and 128 over four for fp8
     h->mfma_wr = rows_max > 64 ? (scaled_cache(cfg->kv_dtype) ? 4 : 8) : 1;
+    if (D == 256) h->mfma_wr = 4;   // the head_dim 256 tile kernel: 128-row items
     // The tile kernel launches exactly one round of resident workgroups; its
     // in-kernel plan sizes the splits for that many items.
-    h->mfma_grid = D == 128 ? h->cu_count * mfma_blocks_per_cu(cfg->kv_dtype, cfg->q_dtype, h->mfma_wr,
-                                                                cfg->max_num_seqs)
-                            : h->cu_count;
+    h->mfma_grid = D == 128   ? h->cu_count * mfma_blocks_per_cu(cfg->kv_dtype, cfg->q_dtype, h->mfma_wr,
+                                                                  cfg->max_num_seqs)
+                   : D == 256 ? h->cu_count * tile256_blocks_per_cu(cfg->kv_dtype, cfg->q_dtype, cfg->max_num_seqs)
+                              : h->cu_count;
     const int bm = 32 * h->mfma_wr;
     const int64_t qblocks = ((int64_t)cfg->max_num_tokens * G + bm - 1) / bm + cfg->max_num_seqs;
     h->max_items_mfma = (int)std::min<int64_t>((int64_t)1 << 30, grid_cap + qblocks * cfg->num_kv_heads);
-    h->merge_rows = (int)std::max<int64_t>(h->r_max_valu, D == 128 ? bm : 0);
+    h->merge_rows = (int)std::max<int64_t>(h->r_max_valu, D != 64 ? bm : 0);
     // Fixed slots for the VALU kernel's static splits (at most 8 workgroups
     // per CU, so at most that many (sequence, KV head) groups).
     h->sdesc_upg = (h->r_max_valu + merge_rows_per_unit(D) - 1) / merge_rows_per_unit(D);
@@ -136,7 +138,7 @@ void size_handle(pa_handle* h, const pa_config_t* cfg, int cu_count) {
 
 WsLayout layout_workspace(const pa_handle* h, bool valu, bool mfma) {
     const int D = h->cfg.head_dim;
-    mfma = mfma && D == 128;
+    mfma = mfma && D != 64;
     const int bm = 32 * h->mfma_wr;
     WsLayout L{};
     // The two kernels' partials live side by side until the merge launch: VALU
@@ -248,12 +250,18 @@ LaunchPlan plan_launches(const pa_handle* h, const ForwardCall& f) {
     const int rows_min = c.min_q_len * G, rows_max = c.max_q_len * G;
     const int64_t cap_tokens = (int64_t)f.bt_stride * c.page_size;
     LaunchPlan lp{};
-    if (c.head_dim != 128 || h->tune.path == PA_PATH_VALU) {
+    if (c.head_dim == 64 || h->tune.path == PA_PATH_VALU) {
         lp.run_valu = true;
         lp.run_mfma = false;
     } else if (h->tune.path == PA_PATH_MFMA) {
         lp.run_valu = false;
         lp.run_mfma = true;
+    } else if (c.head_dim == 256) {
+        // The VALU kernel takes every sequence when no row count passes 64;
+        // otherwise the sequences of up to 8 rows per KV head (any length),
+        // and the tile kernel the rest.
+        lp.run_mfma = rows_max > 64;
+        lp.run_valu = !lp.run_mfma || rows_min <= kValuRowsMax;
     } else {
         lp.run_valu = rows_min <= kValuRowsMax;
         lp.run_mfma = rows_max > kValuRowsMax || cap_tokens > kValuMaxKeys;
@@ -320,10 +328,12 @@ int enqueue_forward(pa_handle* h, const ForwardCall& f, const LaunchPlan& lp) {
     const int window = f.window;
     const int32_t block_table_stride = f.bt_stride;
     const bool run_valu = lp.run_valu, run_mfma = lp.run_mfma;
-    if (c.head_dim != 128 || h->tune.path == PA_PATH_VALU) {
+    if (c.head_dim == 64 || h->tune.path == PA_PATH_VALU || (c.head_dim == 256 && !run_mfma)) {
         a.cls_rows = 1 << 30; a.cls_len = 1 << 30;
     } else if (h->tune.path == PA_PATH_MFMA || (run_mfma && h->mfma_wr == 1)) {
         a.cls_rows = 0; a.cls_len = 0;
+    } else if (c.head_dim == 256) {
+        a.cls_rows = kValuRowsMax; a.cls_len = 1 << 30;
     } else {
         a.cls_rows = kValuRowsMax; a.cls_len = kValuMaxKeys;
     }
@@ -393,7 +403,8 @@ int enqueue_forward(pa_handle* h, const ForwardCall& f, const LaunchPlan& lp) {
         a.item_off = h->mfma_item_off;
         const int tgrid = h->tune.grid > 0 ? h->tune.grid : h->mfma_grid;
         a.target_items = tgrid;
-        hipError_t e = pa::launch_mfma_attn(a, c.head_dim, c.kv_dtype, c.q_dtype, h->mfma_wr, tgrid, st);
+        hipError_t e = c.head_dim == 256 ? pa::launch_tile256(a, c.kv_dtype, c.q_dtype, tgrid, st)
+                                         : pa::launch_mfma_attn(a, c.head_dim, c.kv_dtype, c.q_dtype, h->mfma_wr, tgrid, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "tile launch failed: %s", hipGetErrorString(e));
     }
     if (static_merge && need_merge_valu) {
@@ -526,8 +537,8 @@ int paged_attn_set_tuning(pa_handle_t* h, const pa_tuning_t* t) {
         return PA_OK;
     }
     if (t->path < PA_PATH_AUTO || t->path > PA_PATH_MFMA) return fail(h, PA_ERR_INVALID_ARGUMENT, "bad path %d", t->path);
-    if (t->path == PA_PATH_MFMA && h->cfg.head_dim != 128)
-        return fail(h, PA_ERR_UNSUPPORTED, "the MFMA path needs head_dim 128");
+    if (t->path == PA_PATH_MFMA && h->cfg.head_dim == 64)
+        return fail(h, PA_ERR_UNSUPPORTED, "the MFMA path needs head_dim 128 or 256");
     if (t->path == PA_PATH_VALU && !h->valu_all_ok)
         return fail(h, PA_ERR_UNSUPPORTED, "the VALU path holds at most 64 rows per KV head");
     if (t->pages_per_split < 0 || t->kv_tiles_per_split < 0 || t->grid < 0 || t->grid > 8 * h->cu_count ||

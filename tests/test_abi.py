@@ -44,7 +44,6 @@ def _cfg(**kw):
     (dict(max_num_tokens=0), B.PA_ERR_INVALID_ARGUMENT),
     (dict(num_q_heads=64, num_kv_heads=2), B.PA_ERR_UNSUPPORTED),   # group 32
     (dict(head_dim=512), B.PA_ERR_UNSUPPORTED),
-    (dict(head_dim=256, max_q_len=17), B.PA_ERR_UNSUPPORTED),      # 68 rows per KV head at D = 256
     (dict(head_dim=64, max_q_len=17), B.PA_ERR_UNSUPPORTED),
 ])
 def test_create_rejects_bad_config_on_host(kw, code):

@@ -4,9 +4,10 @@ The dense models of the pages' prefill measurements use 256-wide heads
 ("Strix Halo dense cliff patch attribution", section "Which patch, and how I
 know").  At this width the library runs decode and verification widths (up
 to 64 query rows per KV head) on the VALU kernel: a token row is 32 lanes of
-8 elements, two tokens per wavefront load round.  Every KV format, page size
-and split mode the kernel has runs here; wider row counts are refused at
-create (tested on the CPU)."""
+8 elements, two tokens per wavefront load round.  Past 64 rows (chunked
+prefill) a tile kernel on the matrix cores with 128-row items takes the
+sequences of more than 8 rows.  Every KV format, page size and split mode of
+both kernels runs here."""
 import numpy as np
 import pytest
 
@@ -98,3 +99,92 @@ def test_d256_page_permutation_bit_identical():
         c2.close()
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
     assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+PREFILL = {
+    # 300 tokens x 8 heads = 2,400 rows per KV head: 19 row blocks, the last ragged
+    "bf16_prefill": dict(seq_lens=(3000,), q_lens=(300,), k_outlier_frac=0.01),
+    "f16_prefill_window": dict(seq_lens=(2500, 900), q_lens=(100, 40), q_dtype="f16", kv_dtype="f16", window=500,
+                               poison_out_of_window=True),
+    "fp8_prefill_g4": dict(num_q_heads=16, num_kv_heads=4, seq_lens=(2000, 700), q_lens=(100, 40),
+                           kv_dtype="fp8_e4m3", k_outlier_frac=0.01),
+    "int8_prefill": dict(seq_lens=(1800,), q_lens=(130,), kv_dtype="int8", k_outlier_frac=0.01),
+    "int8_f16q_prefill_window": dict(seq_lens=(2200,), q_lens=(64,), q_dtype="f16", kv_dtype="int8", window=300,
+                                     poison_out_of_window=True),
+    # prefill rows next to decode and verification rows: both kernels in one forward
+    "bf16_mixed_batch": dict(seq_lens=(4000, 1500, 333, 70), q_lens=(1, 200, 8, 70), k_outlier_frac=0.01),
+    "fp8_mixed_batch": dict(seq_lens=(20001, 3000, 100), q_lens=(1, 40, 9), kv_dtype="fp8_e4m3"),
+    # a window narrower than one 32-key tile
+    "bf16_window_16": dict(seq_lens=(1000,), q_lens=(90,), window=16, poison_out_of_window=True),
+}
+
+
+@pytest.mark.parametrize("name", list(PREFILL))
+def test_d256_prefill_parity(name):
+    inp = generate(_spec(name=name, **PREFILL[name]))[0]
+    ref_o, ref_l = oracle.attention(inp)
+    progress(f"d256 prefill {name}: seqs={inp.seq_lens.tolist()} q={inp.q_lens.tolist()} W={inp.window}")
+    c = GpuCase([inp])
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare(f"d256 prefill {name}", inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "f16", "fp8_e4m3", "int8"])
+def test_d256_tile_kernel_at_few_rows(kv):
+    """PA_PATH_MFMA sends decode and verification rows through the tile
+    kernel as well (one 128-row item with 1 to 64 live rows)."""
+    q = "f16" if kv == "f16" else "bf16"
+    inp = generate(_spec(seq_lens=(5000, 333, 17), q_lens=(1, 8, 3), q_dtype=q, kv_dtype=kv, window=1200,
+                         poison_out_of_window=True, k_outlier_frac=0.01))[0]
+    ref_o, ref_l = oracle.attention(inp)
+    progress(f"d256 tile kernel few rows {kv}")
+    c = GpuCase([inp], path=pal.PA_PATH_MFMA)
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare(f"d256 tile few rows {kv}", inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("tps", [1, 2, 3, 7])
+def test_d256_tile_split_invariance(tps):
+    inp = generate(_spec(seq_lens=(2100, 700), q_lens=(80, 20), kv_dtype="bf16", k_outlier_frac=0.01))[0]
+    ref_o, ref_l = oracle.attention(inp)
+    progress(f"d256 tile split tps={tps}")
+    c = GpuCase([inp], kv_tiles_per_split=tps)
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare(f"d256 tile tps={tps}", inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("page_size,layout", [(48, "nhd"), (1056, "hnd")])
+def test_d256_prefill_page_sizes(page_size, layout):
+    inp = generate(_spec(page_size=page_size, seq_lens=(3000, 500), q_lens=(120, 9), kv_dtype="fp8_e4m3",
+                         k_outlier_frac=0.01))[0]
+    ref_o, ref_l = oracle.attention(inp)
+    progress(f"d256 prefill P{page_size} {layout}")
+    c = GpuCase([inp], layout=layout)
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare(f"d256 prefill P{page_size} {layout}", inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+def test_d256_prefill_long_context():
+    """512 new tokens after 7,680 cached ones, 16 query heads over 2 KV heads
+    (4,096 rows per KV head, 32 row blocks): every row against the oracle."""
+    inp = generate(_spec(seq_lens=(8192,), q_lens=(512,), k_outlier_frac=0.01, seed=72))[0]
+    progress("d256 prefill long context (oracle)")
+    ref_o, ref_l = oracle.attention(inp)
+    c = GpuCase([inp])
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare("d256 prefill long", inp.kv_dtype, out, lse, ref_o, ref_l)
