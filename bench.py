@@ -40,6 +40,7 @@ WORKLOADS = {
     "verify": "speculative verify: 1 seq, q_len 8 causal, 32/8 heads, D 128, 61,448 tokens, fp16 KV, 1% K x4",
     "verify_window": "speculative verify, 2048-token window, out-of-window pages NaN (61,448 tokens, fp16 KV)",
     "prefill": "chunked prefill: 2,048-token chunk on 65,536 cached, 24/4 heads, D 128, bf16 KV",
+    "prefill_d256": "chunked prefill at head_dim 256: 2,048-token chunk on 65,536 cached, 16/2 heads, bf16 KV",
     "mixed_fp8": "mixed batch: 4 seqs, 200,001/131,076/32,776/4,097 tokens, q_len 1/4/8/1, 32/8 heads, fp8 e4m3 KV",
     "mixed_int8": "mixed batch as mixed_fp8 on an int8 KV cache with a fp32 scale per cached row",
     "append_fp8": "cache append: 64 seqs x 256 new rows, 8 KV heads, D 128, bf16 rows quantised into fp8 e4m3 pages",
@@ -81,6 +82,8 @@ def load_traffic(workload: str):
 PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 # Workloads measured on the VALU path as well as on the automatic (MFMA tile) one.
 ALT_PATH_WORKLOADS = ("verify", "mixed_fp8")
+# workloads measured in TFLOP/s against the bf16 MFMA peak (the rest: KV bytes against HBM)
+FLOP_WORKLOADS = ("prefill", "prefill_d256")
 # Timed regions per measurement: the median is reported, and the spread
 # (max - min) / median across them ("run it three times, watch the drift").
 REPEATS = 3
@@ -210,7 +213,7 @@ def time_path(prep: Prepared, path: str, steps: int, warmup: int, repeats: int =
 def rates(prep: Prepared, t: dict) -> dict:
     """Throughput and roofline of one timing (prefill in TFLOP/s against the
     bf16 MFMA peak, the others in KV GB/s against HBM)."""
-    if prep.workload == "prefill":
+    if prep.workload in FLOP_WORKLOADS:
         work, unit, peak, bound, scale = prep.flops, "TFLOP/s", BF16_MFMA_PEAK_TFS, "mfma", 1e-6
     else:
         work, unit, peak, bound, scale = prep.kv_bytes, "GB/s", HBM_PEAK_GBS, "hbm", 1e-3
@@ -288,7 +291,7 @@ def cpu_baseline(workload: str, base, budget_s: float = 10.0):
     el = time.perf_counter() - t0
     frac = done_heads / base.num_q_heads
     sample = f"all tokens of {done_heads} query head(s) of {base.num_q_heads}; scaled by heads"
-    if workload == "prefill":
+    if workload in FLOP_WORKLOADS:
         return {"value": base.flops() * frac / el / 1e12, "unit": "TFLOP/s", **common, "sample": sample,
                 "seconds": el}
     return {"value": kv_bytes * frac / el / 1e9, "unit": "GB/s", **common, "sample": sample, "seconds": el}
@@ -424,8 +427,8 @@ def kernel_roofline(prep_like: dict, tr: dict) -> dict:
 
 
 COPY_KERNEL_TAG = "neg_kernel"     # torch.neg: reads N bytes, writes N bytes
-OUR_KERNEL_TAGS = ("decode_valu_kernel", "tile_attn_kernel", "merge_kernel", "merge_slots_kernel", "append_kernel",
-                   "zero_words_kernel")
+OUR_KERNEL_TAGS = ("decode_valu_kernel", "tile_attn_kernel", "tile256_kernel", "merge_kernel", "merge_slots_kernel",
+                   "append_kernel", "zero_words_kernel")
 
 
 def calibrate_copy(mib: int) -> None:
@@ -503,7 +506,7 @@ def reduce_profiles(prof_dir: str, workload: str, calib_mib: int, commands: list
     from synth import named
 
     base = named(workload)[0]
-    alg = base.flops() if workload == "prefill" else base.kv_bytes()
+    alg = base.flops() if workload in FLOP_WORKLOADS else base.kv_bytes()
     hbm = 0.0
     for k, v in kern.items():
         v["per_forward"] = v["dispatches"] / max(1, fetch_run["forwards_run"])
@@ -546,9 +549,9 @@ def reduce_profiles(prof_dir: str, workload: str, calib_mib: int, commands: list
     for k, v in kern.items():
         lines.append(f"| {k} | {v['dispatches']} | {v['per_forward']:.2f} | {v['fetch_kib']:.0f} | "
                      f"{v['write_kib']:.0f} | {v['hbm_bytes']:.4g} |")
-    unit = "flop" if workload == "prefill" else "B of KV"
+    unit = "flop" if workload in FLOP_WORKLOADS else "B of KV"
     lines += ["", f"HBM bytes per forward: {hbm:.4g}; algorithmic {alg:.4g} {unit} per forward"
-              + ("" if workload == "prefill" else f" (ratio {hbm / alg:.3f})") + ".", ""]
+              + ("" if workload in FLOP_WORKLOADS else f" (ratio {hbm / alg:.3f})") + ".", ""]
     name = "_".join(sorted({k.split("<")[0] for k in kern})) or "kernels"
     out_md = os.path.join(ROOT, "profiles", f"{name}_{workload}.md")
     os.makedirs(os.path.dirname(out_md), exist_ok=True)
@@ -722,7 +725,7 @@ def profile_commands(workload: str, calib_mib: int = 512) -> list:
 # Per-configuration entries of the default run: steps sized so each timed
 # region lasts a few milliseconds.
 PER_CONFIG = {"tiny_decode": 300, "decode": 200, "verify": 60, "verify_window": 200, "prefill": 20,
-              "mixed_int8": 20}
+              "mixed_int8": 20, "prefill_d256": 20}
 CPU_BUDGET_HEADLINE_S = 10.0
 CPU_BUDGET_PER_CONFIG_S = 3.0
 
@@ -737,11 +740,11 @@ def _entry(workload: str, res: dict, base, trace: dict, cpu: dict = None) -> dic
          "eager_value": auto["eager_value"], "kv_bytes_per_step": base.kv_bytes(), "flops_per_step": base.flops()}
     tr = (trace or {}).get("workloads", {}).get(workload)
     if tr:
-        work = base.flops() if workload == "prefill" else base.kv_bytes()
+        work = base.flops() if workload in FLOP_WORKLOADS else base.kv_bytes()
         unit = e["unit"]
-        peak = BF16_MFMA_PEAK_TFS if workload == "prefill" else HBM_PEAK_GBS
+        peak = BF16_MFMA_PEAK_TFS if workload in FLOP_WORKLOADS else HBM_PEAK_GBS
         e["roofline"] = dict(e["roofline"], kernel=kernel_roofline(
-            {"work": work, "unit": unit, "peak": peak, "scale": 1e-6 if workload == "prefill" else 1e-3}, tr),
+            {"work": work, "unit": unit, "peak": peak, "scale": 1e-6 if workload in FLOP_WORKLOADS else 1e-3}, tr),
             kernels=tr["kernels"])
     for path, r in res.items():
         if path != "auto":

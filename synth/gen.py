@@ -334,7 +334,7 @@ def permute_pool(inp: PagedInputs, seed: int) -> PagedInputs:
     return new
 
 
-# The six named workloads (seed 1000 + k for the k-th).
+# The named workloads (seed 1000 + k for the k-th).
 NAMED_SPECS = {
     "tiny_decode": Spec(
         name="tiny_decode", num_q_heads=4, num_kv_heads=1, head_dim=64,
@@ -357,6 +357,11 @@ NAMED_SPECS = {
         name="mixed_fp8", num_q_heads=32, num_kv_heads=8, head_dim=128,
         seq_lens=(200001, 131076, 32776, 4097), q_lens=(1, 4, 8, 1),
         q_dtype="bf16", kv_dtype="fp8_e4m3", pool_pages=32768, seed=1005),
+    # chunked prefill at head_dim 256 (the width of the dense models in the
+    # pages' long-context prefill measurements); head counts are a reading
+    "prefill_d256": Spec(
+        name="prefill_d256", num_q_heads=16, num_kv_heads=2, head_dim=256,
+        seq_lens=(67584,), q_lens=(2048,), q_dtype="bf16", kv_dtype="bf16", pool_pages=8192, seed=1007),
     # the same long mixed batch on the pages' own cache format: int8 codes
     # with a fp32 scale per cached row
     "mixed_int8": Spec(

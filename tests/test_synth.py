@@ -97,6 +97,7 @@ def test_outlier_positions():
     ("prefill", 138_412_032),
     ("mixed_fp8", 753_561_600),
     ("mixed_int8", 777_110_400),
+    ("prefill_d256", 138_412_032),
 ])
 def test_named_kv_bytes(name, kv_bytes):
     spec = NAMED_SPECS[name]
@@ -129,3 +130,16 @@ def test_prefill_flops():
     assert m.pair_count() == pairs
     assert m.flops() == 4 * 128 * 24 * pairs       # 1,675.05 GF
     assert abs(m.flops() / 1e9 - 1675.05) < 0.01
+
+
+def test_prefill_d256_flops():
+    from synth.gen import PagedInputs
+    spec = NAMED_SPECS["prefill_d256"]
+    m = PagedInputs.__new__(PagedInputs)
+    m.seq_lens = np.array(spec.seq_lens)
+    m.q_lens = np.array(spec.q_lens)
+    m.window = 0
+    m.num_q_heads, m.head_dim = 16, 256
+    pairs = 2048 * 65536 + 2048 * 2049 // 2
+    assert m.pair_count() == pairs
+    assert m.flops() == 4 * 256 * 16 * pairs       # 2,233.4 GF
