@@ -503,10 +503,14 @@ def reduce_profiles(prof_dir: str, workload: str, calib_mib: int, commands: list
         fetch_run = json.loads(f.read().strip().splitlines()[-1])
     with open(os.path.join(prof_dir, "kt", "bench.json")) as f:
         n_fwd = json.loads(f.read().strip().splitlines()[-1])
-    from synth import named
+    if workload == "append_fp8":
+        sh = APPEND_SHAPE   # 16-bit rows read, fp8 codes written, K and V
+        alg = 2 * sh["num_seqs"] * sh["rows"] * sh["hkv"] * sh["head_dim"] * 3
+    else:
+        from synth import named
 
-    base = named(workload)[0]
-    alg = base.flops() if workload in FLOP_WORKLOADS else base.kv_bytes()
+        base = named(workload)[0]
+        alg = base.flops() if workload in FLOP_WORKLOADS else base.kv_bytes()
     hbm = 0.0
     for k, v in kern.items():
         v["per_forward"] = v["dispatches"] / max(1, fetch_run["forwards_run"])
@@ -552,6 +556,8 @@ def reduce_profiles(prof_dir: str, workload: str, calib_mib: int, commands: list
     unit = "flop" if workload in FLOP_WORKLOADS else "B of KV"
     lines += ["", f"HBM bytes per forward: {hbm:.4g}; algorithmic {alg:.4g} {unit} per forward"
               + ("" if workload in FLOP_WORKLOADS else f" (ratio {hbm / alg:.3f})") + ".", ""]
+    trace_avg = {_short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in stats}
+    lines += _mfma_summary(prof_dir, trace_avg)
     name = "_".join(sorted({k.split("<")[0] for k in kern})) or "kernels"
     out_md = os.path.join(ROOT, "profiles", f"{name}_{workload}.md")
     os.makedirs(os.path.dirname(out_md), exist_ok=True)
@@ -703,6 +709,40 @@ def cpu_baseline_append(base):
             "sample": f"{rows} rows of {n_seq} sequences, {reps} repetitions", "seconds": sec}
 
 
+# Counter passes of the MFMA-bound workloads (one rocprofv3 run each).
+MFMA_PASSES = (("mfma_util", "MfmaUtil"), ("mfma_raw", "SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE"),
+               ("mfma_mops", "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+
+
+def _mfma_summary(prof_dir: str, trace_avg_us: dict) -> list:
+    """Markdown lines for the MFMA counter passes (empty if they were not run)."""
+    import collections
+
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for sub, _ in MFMA_PASSES:
+        for r in _csv_rows(os.path.join(prof_dir, sub, "**", "*counter_collection.csv")):
+            k = _short(r["Kernel_Name"])
+            if any(t in k for t in OUR_KERNEL_TAGS):
+                vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if not vals:
+        return []
+    mean = lambda v: sum(v) / len(v) if v else float("nan")
+    lines = ["## Matrix cores (MfmaUtil; SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE; SQ_INSTS_VALU_MFMA_MOPS_BF16)", "",
+             "Per dispatch, averaged over the dispatches of the eager counter runs.  MfmaUtil is the profiler's "
+             "derived counter: MFMA-busy SIMD cycles / (GPU-active cycles x 1,024 SIMDs).  GRBM_GUI_ACTIVE / "
+             "kernel time is the clock (the raw counter as the profiler reports it, and per XCD if that value "
+             "sums the 8 XCDs).  Executed flop = MFMA ops x 512.", "",
+             "| kernel | MfmaUtil % | MFMA busy cycles | GPU-active cycles | kernel us (trace avg) | "
+             "cycles / us | executed TFLOP | executed TFLOP/s |", "|---|---|---|---|---|---|---|---|"]
+    for k, c in sorted(vals.items()):
+        us = trace_avg_us.get(k, float("nan"))
+        gui = mean(c.get("GRBM_GUI_ACTIVE", []))
+        fl = mean(c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])) * 512
+        lines.append(f"| {k} | {mean(c.get('MfmaUtil', [])):.1f} | {mean(c.get('SQ_VALU_MFMA_BUSY_CYCLES', [])):.4g} | "
+                     f"{gui:.4g} | {us:.1f} | {gui / us:.1f} | {fl / 1e12:.4f} | {fl / us / 1e6:.1f} |")
+    return lines + [""]
+
+
 def profile_commands(workload: str, calib_mib: int = 512) -> list:
     """The rocprofv3 runs behind profiles/<kernel>_<workload>.md, from the
     repository root $REPO (counters in passes of their own, as the profiler
@@ -718,6 +758,13 @@ def profile_commands(workload: str, calib_mib: int = 512) -> list:
         f"{run} --steps 5 --warmup 1 --repeats 1 --eager --calibrate-copy {calib_mib} --json-out {out}/fetch/bench.json",
         f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d {out}/write -o run -- "
         f"{run} --steps 5 --warmup 1 --repeats 1 --eager --calibrate-copy {calib_mib} --json-out {out}/write/bench.json",
+    ] + ([
+        # matrix-core utilisation of the prefill kernels: the profiler's MfmaUtil
+        # (MFMA-busy SIMD cycles over GPU-active cycles x SIMDs), the raw busy
+        # and GPU-active cycles, and the bf16 MFMA operations (512 flop each)
+        f"rocprofv3 --pmc {ctrs} --output-format csv -d {out}/{sub} -o run -- "
+        f"{run} --steps 5 --warmup 1 --repeats 1 --eager --json-out {out}/{sub}/bench.json"
+        for sub, ctrs in MFMA_PASSES] if workload in FLOP_WORKLOADS else []) + [
         f"python3 bench.py --workload {workload} --reduce-profiles gpurun_out/prof/{workload}   # on any host",
     ]
 

@@ -28,13 +28,21 @@ def test_more_than_one_gpu_is_refused():
 def test_profile_commands_keep_counters_and_traces_apart(workload):
     cmds = bench.profile_commands(workload)
     prof = [c for c in cmds if c.startswith("rocprofv3")]
-    assert len(prof) == 3
-    trace, fetch, write = prof
+    mfma = workload in bench.FLOP_WORKLOADS
+    assert len(prof) == (6 if mfma else 3)
+    trace, fetch, write = prof[:3]
     assert "--kernel-trace" in trace and "--stats" in trace and "--pmc" not in trace
-    for c, counter in ((fetch, "FETCH_SIZE"), (write, "WRITE_SIZE")):
-        assert f"--pmc {counter}" in c
+    passes = [(fetch, "FETCH_SIZE"), (write, "WRITE_SIZE")]
+    if mfma:
+        passes += [(c, ctrs) for c, (_, ctrs) in zip(prof[3:], bench.MFMA_PASSES)]
+    for c, counter in passes:
+        assert f"--pmc {counter} " in c
         for banned in ("--sys-trace", "--runtime-trace", "--kernel-trace", " -s ", " -r "):
             assert banned not in c
+    # at most 8 SQ and 2 GRBM counters in one pass
+    for _, ctrs in bench.MFMA_PASSES:
+        names = ctrs.split()
+        assert sum(n.startswith("SQ_") for n in names) <= 8 and sum(n.startswith("GRBM_") for n in names) <= 2
     # the program itself follows "--" (no launcher in between)
     for c in prof:
         assert " -- python3 " in c
