@@ -47,6 +47,10 @@ KINDS = {
     "tile_int8": (dict(seq_lens=(3000, 700), q_lens=(8, 4), kv_dtype="int8"), {}),
     "tile_prefill": (dict(num_q_heads=24, num_kv_heads=4, seq_lens=(2000,), q_lens=(300,)), {}),
     "tile_pages48": (dict(seq_lens=(3000, 700), q_lens=(8, 4), page_size=48), {}),
+    # head_dim 256: the VALU kernel, then the 128-row tile kernel
+    "d256_valu": (dict(num_q_heads=16, num_kv_heads=2, head_dim=256, seq_lens=(3000, 700), q_lens=(4, 1)), {}),
+    "d256_tile": (dict(num_q_heads=16, num_kv_heads=2, head_dim=256, seq_lens=(2000, 700), q_lens=(100, 20),
+                       kv_dtype="fp8_e4m3"), {}),
 }
 
 FAULTS = ["page_high", "page_negative", "q_len_over_seq_len", "seq_len_past_table", "tokens_over"]

@@ -21,7 +21,7 @@ def _noalloc_run(case: GpuCase, cfg, i: int = 0):
     out = torch.full_like(case.out[i], float("nan"))
     lse = torch.full_like(case.lse[i], float("nan"))
     pal.paged_attn_forward_noalloc(cfg, d["q"], case.pools["k"], case.pools["v"], d["block_table"], d["seq_lens"],
-                                   d["q_lens"], b.window, b.scale, d["kv_scale"], out, lse)
+                                   d["q_lens"], b.window, b.scale, case.kv_scale(i), out, lse)
     torch.cuda.synchronize()
     return out.cpu().numpy(), lse.cpu().numpy()
 
@@ -64,6 +64,17 @@ def test_noalloc_mixed_fp8_then_tiny():
     tiny = NAMED_SPECS["tiny_decode"].replace(seed=74)
     _check_pair("mixed fp8 4 seqs", mixed)
     _check_pair("tiny decode", tiny)
+
+
+def test_noalloc_head_dim_256_then_smaller():
+    # head_dim 256 on the VALU kernel (two new tokens, 16 rows per KV head,
+    # static splits), then a smaller decode of the same width
+    verify = NAMED_SPECS["decode"].replace(num_q_heads=16, num_kv_heads=2, head_dim=256, seq_lens=(9000,),
+                                           q_lens=(2,), pool_pages=1024, seed=75)
+    decode = NAMED_SPECS["decode"].replace(num_q_heads=16, num_kv_heads=2, head_dim=256, seq_lens=(2000, 31),
+                                           q_lens=(1, 1), pool_pages=512, kv_dtype="int8", seed=76)
+    _check_pair("d256 verify 9000x2 bf16", verify)
+    _check_pair("d256 decode int8", decode)
 
 
 def test_noalloc_rejects_oversized_config():
