@@ -150,8 +150,8 @@ __global__ __launch_bounds__(kThreads) void tile256_kernel(DecodeArgs a) {
     extern __shared__ int dyn_lds[];
     __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][2][kTile];   // [ring slot][K, V]
     __shared__ __attribute__((aligned(16))) float tsc[2][2 * kBN];         // int8: [slot][K scales | V scales]
-    __shared__ long long red_items[4][kNW];
-    __shared__ int red_big[4][kNW];
+    __shared__ long long red_items[8][kNW];
+    __shared__ int red_big[8][kNW];
     __shared__ long long redw[kNW], redq[kNW];
     __shared__ int redt[kNW];
 
@@ -165,8 +165,11 @@ __global__ __launch_bounds__(kThreads) void tile256_kernel(DecodeArgs a) {
     // A sequence is in this launch if in_launch() says so.  Its rows form
     // ceil(rows / 128) row blocks; each row block's visible keys are cut into
     // 32-key tiles, grouped into `splits` splits (the same number for every
-    // row block of the sequence).  Split sizes: the candidate (sized for 1..4
-    // rounds of the resident grid) whose rounds x largest item is smallest.
+    // row block of the sequence).  Split sizes: of the candidates sized for
+    // 1..4 rounds of the resident grid and four between the one-round lower
+    // bound (work / t) and a size that surely fits one round (work / (t - row
+    // blocks)), the one whose rounds x largest item is smallest, ties to the
+    // fewer items.
     plan_bind(pl, dyn_lds, a.num_seqs);
     auto widest_tiles = [&](int sl, int ql) {
         const int rows = ql * a.group;
@@ -239,13 +242,15 @@ __global__ __launch_bounds__(kThreads) void tile256_kernel(DecodeArgs a) {
             tps = max(a.forced_pps, tmin);
         } else {
             const long long t = a.target_items > 0 ? a.target_items : 1;
-            constexpr int NC = 4;
+            constexpr int NC = 8;
+            const long long c_lo = max((long long)tmin, div_ceil_i64(work, t));
+            const long long c_hi = min((long long)1 << 30, t > qtiles ? max(c_lo, div_ceil_i64(work, t - qtiles)) : c_lo);
             int cand[NC];
             long long items[NC];
             int big[NC];
 #pragma unroll
             for (int k = 0; k < NC; ++k) {
-                cand[k] = max(tmin, (int)div_ceil_i64(work, t * (k + 1)));
+                cand[k] = k < 4 ? max(tmin, (int)div_ceil_i64(work, t * (k + 1))) : (int)(c_lo + (c_hi - c_lo) * (k - 3) / 4);
                 items[k] = 0;
                 big[k] = 0;
             }
@@ -267,7 +272,7 @@ __global__ __launch_bounds__(kThreads) void tile256_kernel(DecodeArgs a) {
                 if (lane == 0) { red_items[k][wid] = it_w; red_big[k][wid] = big_w; }
             }
             __syncthreads();
-            long long best = -1;
+            long long best = -1, best_items = 0;
 #pragma unroll
             for (int k = 0; k < NC; ++k) {
                 long long it_k = 0;
@@ -277,7 +282,11 @@ __global__ __launch_bounds__(kThreads) void tile256_kernel(DecodeArgs a) {
                     big_k = max(big_k, red_big[k][ww]);
                 }
                 const long long cost = div_ceil_i64(it_k * a.num_kv_heads, t) * big_k;
-                if (best < 0 || cost < best) { best = cost; tps = cand[k]; }
+                if (best < 0 || cost < best || (cost == best && it_k < best_items)) {
+                    best = cost;
+                    best_items = it_k;
+                    tps = cand[k];
+                }
             }
         }
         int carry_i = 0;

@@ -600,12 +600,16 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             tps = max(a.forced_pps, tmin);
         } else {
             // The grid is one round of resident workgroups (t of them) and each
-            // takes items it, it + t, ...  Try splits sized for 1..4 rounds and
-            // keep the one whose rounds x largest item is smallest (split sizes
-            // are equalised within a sequence).  An item's tiles are shared by
-            // the WK waves of its workgroup, so an item takes ceil(tiles / WK)
-            // wave steps: candidates are rounded up to a multiple of WK (the
-            // same steps, fewer items and partials) and costed in wave steps.
+            // takes items it, it + t, ...  Try splits sized for 1..3 rounds and,
+            // for a batch, a size that surely fits one round (work / (t - row
+            // blocks): a sequence's items are fewer than tiles / size + 1 per
+            // row block; the size for one round by work alone can overshoot the
+            // grid by a few items and take two), and keep the one whose rounds x
+            // largest item is smallest (split sizes are equalised within a
+            // sequence).  An item's tiles are shared by the WK waves of its
+            // workgroup, so an item takes ceil(tiles / WK) wave steps:
+            // candidates are rounded up to a multiple of WK (the same steps,
+            // fewer items and partials) and costed in wave steps.
             const long long t = a.target_items > 0 ? a.target_items : 1;
             auto round_wk = [](int c) { return (c + C::WK - 1) / C::WK * C::WK; };
             auto wave_steps = [](int tiles) { return (tiles + C::WK - 1) / C::WK; };
@@ -616,6 +620,8 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
 #pragma unroll
             for (int k = 0; k < NC; ++k) {
                 cand[k] = one ? tmin : round_wk(max(tmin, (int)div_ceil_i64(work, t * (k + 1))));
+                if (k == NC - 1 && !one && t > qtiles)
+                    cand[k] = round_wk(max(tmin, (int)min(div_ceil_i64(work, t - qtiles), (long long)1 << 30)));
                 items[k] = 0;
                 big[k] = 0;
             }
