@@ -596,8 +596,17 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             tmin = max(tmin, (int)div_ceil_i64(work, cap));
         }
         int tps;
+        const long long t_grid = a.target_items > 0 ? a.target_items : 1;
         if (a.forced_pps > 0) {
             tps = max(a.forced_pps, tmin);
+        } else if (WR == 1 && qtiles * 8 <= t_grid) {
+            // Few row blocks (32-row items): the size that surely fits one
+            // round (below) is within t / (t - row blocks) <= 8/7 of the
+            // one-round lower bound work / t, so it is taken without costing
+            // the candidates (their evaluation takes every workgroup a few
+            // microseconds).
+            const long long c = min(div_ceil_i64(work, t_grid - qtiles), (long long)1 << 30);
+            tps = (max(tmin, (int)c) + C::WK - 1) / C::WK * C::WK;
         } else {
             // The grid is one round of resident workgroups (t of them) and each
             // takes items it, it + t, ...  Try splits sized for 1..3 rounds and,
