@@ -15,10 +15,12 @@
 // int8 cache").  Four waves own 32 rows each.
 //
 // Per tile of 32 keys (two 16-token chunks gathered through the block table):
-//   * every thread loads its share of the next tile's K and V rows into
-//     registers (16-byte loads; one-byte caches are widened exactly to 16
-//     bits) while the current tile is computed, then writes them into the
-//     other half of a two-tile LDS ring; rows are 512 B with their 16-byte
+//   * every thread loads its share of the K and V rows two tiles ahead into
+//     registers (16-byte loads, two register sets; one-byte caches are widened
+//     exactly to 16 bits) while the current tile is computed, and writes the
+//     next tile's rows into the other half of a two-tile LDS ring after it
+//     (two tiles of compute hide the load latency, which one does not: 4.16
+//     -> 3.97 ms on a 2,048-token chunk); rows are 512 B with their 16-byte
 //     chunks XOR-swizzled by the row, so the operand reads below (one chunk
 //     of many rows at once) spread over the banks;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16 (A = 32 K rows, B = Q^T held in
@@ -38,6 +40,8 @@
 #include "pa_common.h"
 #include "pa_merge.h"
 #include "pa_kernels.h"
+
+#include <type_traits>
 
 namespace pa {
 
@@ -413,9 +417,10 @@ __global__ __launch_bounds__(kThreads) void tile256_kernel(DecodeArgs a) {
             return (j >= lo) && (j < seq_len) && (pg_first + t * kPPT + key / kPage < pg_end);
         };
         using Raw = u32x4_t;
-        Raw kr[NL], vr[NL];
-        float fsc = 0.f;
-        auto tile_load = [&](int t) {
+        Raw kr[2][NL], vr[2][NL];
+        float fsc[2] = {0.f, 0.f};
+        auto tile_load = [&](int t, auto b_c) {
+            constexpr int B = decltype(b_c)::value;
             int pid[kPPT];
 #pragma unroll
             for (int p = 0; p < kPPT; ++p)
@@ -426,19 +431,20 @@ __global__ __launch_bounds__(kThreads) void tile256_kernel(DecodeArgs a) {
                 const int key = idx / CPR, c = idx % CPR;
                 const int64_t off = (int64_t)pid[key / kPage] * page_bytes + head_off + (int64_t)(key % kPage) * tok_bytes +
                                     c * 16;
-                kr[i] = load_b128(kbase + off);
-                vr[i] = load_b128(vbase + off);
+                kr[B][i] = load_b128(kbase + off);
+                vr[B][i] = load_b128(vbase + off);
             }
             if constexpr (INT8) {
                 if (tid < 2 * kBN) {
                     const int key = tid % kBN;
                     const int p = pid[key / kPage];
-                    fsc = __builtin_nontemporal_load(a.row_scale + (int64_t)p * a.rs_page + (int64_t)g * a.rs_head +
+                    fsc[B] = __builtin_nontemporal_load(a.row_scale + (int64_t)p * a.rs_page + (int64_t)g * a.rs_head +
                                                      (int64_t)(key % kPage) * a.rs_tok + (tid >= kBN ? a.rs_v : 0));
                 }
             }
         };
-        auto tile_store = [&](int slot, int t) {
+        auto tile_store = [&](int slot, int t, auto b_c) {
+            constexpr int B = decltype(b_c)::value;
             uint8_t* kt = tiles[slot][0];
             uint8_t* vt = tiles[slot][1];
 #pragma unroll
@@ -448,21 +454,21 @@ __global__ __launch_bounds__(kThreads) void tile256_kernel(DecodeArgs a) {
                 const bool live = key_live(t, key);
                 if constexpr (BYTE) {
                     // 16 codes -> two 16-byte chunks of 16-bit values
-                    const u32x2_t k0{kr[i][0], kr[i][1]}, k1{kr[i][2], kr[i][3]};
-                    const u32x2_t v0{vr[i][0], vr[i][1]}, v1{vr[i][2], vr[i][3]};
+                    const u32x2_t k0{kr[B][i][0], kr[B][i][1]}, k1{kr[B][i][2], kr[B][i][3]};
+                    const u32x2_t v0{vr[B][i][0], vr[B][i][1]}, v1{vr[B][i][2], vr[B][i][3]};
                     *reinterpret_cast<u32x4_t*>(kt + swz(key, 2 * c)) = widen8<QT, KVT>(k0);
                     *reinterpret_cast<u32x4_t*>(kt + swz(key, 2 * c + 1)) = widen8<QT, KVT>(k1);
                     const u32x4_t z{0u, 0u, 0u, 0u};
                     *reinterpret_cast<u32x4_t*>(vt + swz(key, 2 * c)) = live ? widen8<PVT, KVT>(v0) : z;
                     *reinterpret_cast<u32x4_t*>(vt + swz(key, 2 * c + 1)) = live ? widen8<PVT, KVT>(v1) : z;
                 } else {
-                    *reinterpret_cast<u32x4_t*>(kt + swz(key, c)) = kr[i];
-                    *reinterpret_cast<u32x4_t*>(vt + swz(key, c)) = live ? vr[i] : u32x4_t{0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4_t*>(kt + swz(key, c)) = kr[B][i];
+                    *reinterpret_cast<u32x4_t*>(vt + swz(key, c)) = live ? vr[B][i] : u32x4_t{0u, 0u, 0u, 0u};
                 }
             }
             if constexpr (INT8) {
                 // a dead key's V scale (maybe NaN) is stored as 0
-                if (tid < 2 * kBN) tsc[slot][tid] = (tid >= kBN && !key_live(t, tid - kBN)) ? 0.f : fsc;
+                if (tid < 2 * kBN) tsc[slot][tid] = (tid >= kBN && !key_live(t, tid - kBN)) ? 0.f : fsc[B];
             }
         };
 
@@ -570,15 +576,21 @@ __global__ __launch_bounds__(kThreads) void tile256_kernel(DecodeArgs a) {
         };
 
         if (t_begin < t_end) {
-            tile_load(t_begin);
-            tile_store(0, t_begin);
+            using B0 = std::integral_constant<int, 0>;
+            using B1 = std::integral_constant<int, 1>;
+            tile_load(t_begin, B0{});
+            if (t_begin + 1 < t_end) tile_load(t_begin + 1, B1{});
+            tile_store(0, t_begin, B0{});
             __syncthreads();
-            for (int t = t_begin; t < t_end; ++t) {
-                const int slot = (t - t_begin) & 1;
-                const bool more = t + 1 < t_end;
-                if (more) tile_load(t + 1);
-                compute_tile(t, slot);
-                if (more) tile_store(slot ^ 1, t + 1);
+            for (int t = t_begin; t < t_end; t += 2) {
+                if (t + 2 < t_end) tile_load(t + 2, B0{});
+                compute_tile(t, 0);
+                if (t + 1 < t_end) tile_store(1, t + 1, B1{});
+                __syncthreads();
+                if (t + 1 >= t_end) break;
+                if (t + 3 < t_end) tile_load(t + 3, B1{});
+                compute_tile(t + 1, 1);
+                if (t + 2 < t_end) tile_store(0, t + 2, B0{});
                 __syncthreads();
             }
         }
