@@ -558,6 +558,7 @@ def reduce_profiles(prof_dir: str, workload: str, calib_mib: int, commands: list
               + ("" if workload in FLOP_WORKLOADS else f" (ratio {hbm / alg:.3f})") + ".", ""]
     trace_avg = {_short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in stats}
     lines += _mfma_summary(prof_dir, trace_avg)
+    lines += _valu_summary(prof_dir, trace_avg)
     name = "_".join(sorted({k.split("<")[0] for k in kern})) or "kernels"
     out_md = os.path.join(ROOT, "profiles", f"{name}_{workload}.md")
     os.makedirs(os.path.dirname(out_md), exist_ok=True)
@@ -714,6 +715,33 @@ MFMA_PASSES = (("mfma_util", "MfmaUtil"), ("mfma_raw", "SQ_VALU_MFMA_BUSY_CYCLES
                ("mfma_mops", "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
 
 
+VALU_PASS = "SQ_INSTS_VALU SQ_WAVES"
+
+
+def _valu_summary(prof_dir: str, trace_avg_us: dict) -> list:
+    """Markdown lines for the VALU instruction pass (empty if it was not run)."""
+    import collections
+
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in _csv_rows(os.path.join(prof_dir, "valu", "**", "*counter_collection.csv")):
+        k = _short(r["Kernel_Name"])
+        if any(t in k for t in OUR_KERNEL_TAGS):
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if not vals:
+        return []
+    mean = lambda v: sum(v) / len(v) if v else float("nan")
+    lines = ["## Vector ALU (SQ_INSTS_VALU, SQ_WAVES)", "",
+             "Per dispatch.  A CU issues at most one 64-lane VALU instruction per cycle (four SIMDs, four "
+             "cycles each), so the chip's VALU floor is instructions / (256 CUs x the clock); at 2.4 GHz:", "",
+             "| kernel | VALU instructions | waves | per wave | VALU floor us at 2.4 GHz | kernel us (trace avg) |",
+             "|---|---|---|---|---|---|"]
+    for k, c in sorted(vals.items()):
+        ins, waves = mean(c.get("SQ_INSTS_VALU", [])), mean(c.get("SQ_WAVES", []))
+        lines.append(f"| {k} | {ins:.4g} | {waves:.4g} | {ins / waves:.0f} | {ins / (256 * 2.4e3):.1f} | "
+                     f"{trace_avg_us.get(k, float('nan')):.1f} |")
+    return lines + [""]
+
+
 def _mfma_summary(prof_dir: str, trace_avg_us: dict) -> list:
     """Markdown lines for the MFMA counter passes (empty if they were not run)."""
     import collections
@@ -729,17 +757,19 @@ def _mfma_summary(prof_dir: str, trace_avg_us: dict) -> list:
     mean = lambda v: sum(v) / len(v) if v else float("nan")
     lines = ["## Matrix cores (MfmaUtil; SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE; SQ_INSTS_VALU_MFMA_MOPS_BF16)", "",
              "Per dispatch, averaged over the dispatches of the eager counter runs.  MfmaUtil is the profiler's "
-             "derived counter: MFMA-busy SIMD cycles / (GPU-active cycles x 1,024 SIMDs).  GRBM_GUI_ACTIVE / "
-             "kernel time is the clock (the raw counter as the profiler reports it, and per XCD if that value "
-             "sums the 8 XCDs).  Executed flop = MFMA ops x 512.", "",
+             "derived counter: MFMA-busy SIMD cycles / (GPU-active cycles x 1,024 SIMDs).  The raw "
+             "GRBM_GUI_ACTIVE as the profiler reports it sums the 8 XCDs, so the clock is GRBM_GUI_ACTIVE / "
+             "kernel time / 8.  Executed flop = MFMA ops x 512.", "",
              "| kernel | MfmaUtil % | MFMA busy cycles | GPU-active cycles | kernel us (trace avg) | "
-             "cycles / us | executed TFLOP | executed TFLOP/s |", "|---|---|---|---|---|---|---|---|"]
+             "cycles / us | clock GHz (/ 8 XCDs) | executed TFLOP | executed TFLOP/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
     for k, c in sorted(vals.items()):
         us = trace_avg_us.get(k, float("nan"))
         gui = mean(c.get("GRBM_GUI_ACTIVE", []))
         fl = mean(c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])) * 512
         lines.append(f"| {k} | {mean(c.get('MfmaUtil', [])):.1f} | {mean(c.get('SQ_VALU_MFMA_BUSY_CYCLES', [])):.4g} | "
-                     f"{gui:.4g} | {us:.1f} | {gui / us:.1f} | {fl / 1e12:.4f} | {fl / us / 1e6:.1f} |")
+                     f"{gui:.4g} | {us:.1f} | {gui / us:.1f} | {gui / us / 8e3:.2f} | {fl / 1e12:.4f} | "
+                     f"{fl / us / 1e6:.1f} |")
     return lines + [""]
 
 
@@ -764,7 +794,11 @@ def profile_commands(workload: str, calib_mib: int = 512) -> list:
         # and GPU-active cycles, and the bf16 MFMA operations (512 flop each)
         f"rocprofv3 --pmc {ctrs} --output-format csv -d {out}/{sub} -o run -- "
         f"{run} --steps 5 --warmup 1 --repeats 1 --eager --json-out {out}/{sub}/bench.json"
-        for sub, ctrs in MFMA_PASSES] if workload in FLOP_WORKLOADS else []) + [
+        for sub, ctrs in MFMA_PASSES] if workload in FLOP_WORKLOADS else []) + ([
+        # the append's vector-ALU instruction count (its limiter)
+        f"rocprofv3 --pmc {VALU_PASS} --output-format csv -d {out}/valu -o run -- "
+        f"{run} --steps 5 --warmup 1 --repeats 1 --eager --json-out {out}/valu/bench.json"
+    ] if workload == "append_fp8" else []) + [
         f"python3 bench.py --workload {workload} --reduce-profiles gpurun_out/prof/{workload}   # on any host",
     ]
 

@@ -29,12 +29,15 @@ def test_profile_commands_keep_counters_and_traces_apart(workload):
     cmds = bench.profile_commands(workload)
     prof = [c for c in cmds if c.startswith("rocprofv3")]
     mfma = workload in bench.FLOP_WORKLOADS
-    assert len(prof) == (6 if mfma else 3)
+    valu = workload == "append_fp8"
+    assert len(prof) == 3 + (3 if mfma else 0) + (1 if valu else 0)
     trace, fetch, write = prof[:3]
     assert "--kernel-trace" in trace and "--stats" in trace and "--pmc" not in trace
     passes = [(fetch, "FETCH_SIZE"), (write, "WRITE_SIZE")]
     if mfma:
         passes += [(c, ctrs) for c, (_, ctrs) in zip(prof[3:], bench.MFMA_PASSES)]
+    if valu:
+        passes += [(prof[3], bench.VALU_PASS)]
     for c, counter in passes:
         assert f"--pmc {counter} " in c
         for banned in ("--sys-trace", "--runtime-trace", "--kernel-trace", " -s ", " -r "):
