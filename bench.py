@@ -87,7 +87,8 @@ FLOP_WORKLOADS = ("prefill", "prefill_d256")
 # Timed regions per measurement: the median is reported, and the spread
 # (max - min) / median across them ("run it three times, watch the drift").
 REPEATS = 3
-WARM_REPLAYS = 3   # untimed replays of the captured graph before the timed ones (clocks settle)
+WARM_REPLAYS = 3   # untimed replays of the captured graph before the timed ones (clocks settle) ...
+WARM_SECONDS = 0.2  # ... for at least this long (a cold GPU ramps its clock over tens of milliseconds)
 
 
 class Prepared:
@@ -182,9 +183,12 @@ def time_path(prep: Prepared, path: str, steps: int, warmup: int, repeats: int =
             with torch.cuda.graph(g):
                 for i in range(steps):
                     prep.step(h, i)
-            for _ in range(WARM_REPLAYS):
+            warm = 0
+            t_warm = time.perf_counter()
+            while warm < WARM_REPLAYS or time.perf_counter() - t_warm < WARM_SECONDS:
                 g.replay()
-            torch.cuda.synchronize()
+                torch.cuda.synchronize()
+                warm += 1
             runs = [_timed(g.replay) for _ in range(repeats)]
             del g
         else:
@@ -206,7 +210,7 @@ def time_path(prep: Prepared, path: str, steps: int, warmup: int, repeats: int =
         "eager_event_us": eager_ev / steps * 1e6,
         "eager_wall_us": eager_wall / steps * 1e6,
         "timing": "graph replay of the timed steps" if graph else "eager launches",
-        "forwards_run": warmup + steps + steps * (WARM_REPLAYS + repeats) if graph else warmup + steps * repeats,
+        "forwards_run": warmup + steps + steps * (warm + repeats) if graph else warmup + steps * repeats,
     }
 
 
@@ -648,8 +652,12 @@ def measure_append(steps: int, warmup: int, use_graph: bool = True, repeats: int
             with torch.cuda.graph(g):
                 for i in range(steps):
                     step(i)
-            g.replay()
-            torch.cuda.synchronize()
+            warm = 0
+            t_warm = time.perf_counter()
+            while warm < WARM_REPLAYS or time.perf_counter() - t_warm < WARM_SECONDS:
+                g.replay()
+                torch.cuda.synchronize()
+                warm += 1
             runs = [_timed(g.replay) for _ in range(repeats)]
             timing = "graph replay of the timed steps"
         else:
@@ -675,7 +683,7 @@ def measure_append(steps: int, warmup: int, use_graph: bool = True, repeats: int
                    "spread": (evs[-1] - evs[0]) / us, "eager_event_us": eager_ev / steps * 1e6,
                    "eager_wall_us": eager_wall / steps * 1e6},
         "eager_value": nbytes / (eager_wall / steps * 1e6) / 1e3,
-        "forwards_run": warmup + steps + (steps * (1 + repeats) if use_graph else steps * (repeats - 1)),
+        "forwards_run": warmup + steps + (steps * (warm + repeats) if use_graph else steps * (repeats - 1)),
     }
     return res, (seq_lens, q_lens, bt, pages, x, scale)
 
