@@ -32,7 +32,7 @@ struct pa_handle {
     int* arrive = nullptr;            // per-group arrival counters for static splits merged in-kernel (zeroed; the last arrival clears its own)
     int sdesc_upg = 1;                // merge units per (sequence, KV head) group in sdesc
     int64_t sdesc_groups = 0;         // groups sdesc holds
-    int* mcount = nullptr;            // [0] groups published, [1] merge workgroups done
+    int* mcount = nullptr;            // merge counters ([0] groups published; kMergeCounterInts ints)
     int* err_word = nullptr;          // device error word of the checked mode (PA_DEBUG_CHECKS)
     void* ws = nullptr;
     size_t ws_bytes = 0;

@@ -9,6 +9,11 @@ namespace pa {
 constexpr int kMaxSplits = 64;        // splits per (sequence, KV head) the merge reads in one pass
 constexpr int kPidChunkPages = 1024;  // page ids a workgroup stages in LDS at a time
 constexpr int kMergeThreads = 256;    // threads of a merge workgroup
+constexpr int kMergeArrive = 32;      // first-level arrival counters of a merge launch
+constexpr int kMergeArriveStride = 32;   // ints between counters (one 128-byte cache line each)
+// The merge counters: [0] groups published, [1] second-level arrivals, then
+// kMergeArrive first-level arrival counters kMergeArriveStride ints apart.
+constexpr int kMergeCounterInts = kMergeArriveStride * (1 + kMergeArrive);
 // Rows of one merge unit: a merge thread owns a float4 column of one row.
 constexpr int merge_rpu(int head_dim) { return kMergeThreads / (head_dim / 4); }
 
@@ -46,7 +51,7 @@ struct DecodeArgs {
     float* ws_o;               // split partials [max_items][r_max][D]
     float* ws_lse;             // [max_items][r_max] (log2 domain)
     MergeDesc* mdesc;          // merge groups published by this forward
-    int* mcount;               // [0]: groups published, [1]: merge workgroups done
+    int* mcount;               // merge counters: [0] groups published, then the merge's arrival counters
     // Fixed merge slots (static splits, VALU kernel only): when set, the group
     // of (sequence b, KV head g) writes its descriptor to slots
     // (b * Hkv + g) * sdesc_upg + u for each merge unit u its rows cover,

@@ -36,12 +36,28 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs m) {
     __syncthreads();
     if (tid == 0) {
         // Every workgroup has read the count (it is in LDS) before it arrives
-        // here; the last to arrive clears the count and the arrival counter
-        // for the next forward.
-        const int done = __hip_atomic_fetch_add(m.mcount + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (done == (int)gridDim.x - 1) {
-            __hip_atomic_store(m.mcount + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(m.mcount, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // here; the last to arrive clears the count for the next forward.
+        // Past 64 workgroups, arrivals go through kMergeArrive first-level
+        // counters on separate cache lines (workgroup w on counter
+        // w % kMergeArrive), whose last arrivals count themselves in on the
+        // second-level counter: atomics on one address are serialised, so a
+        // thousand workgroups on a single counter would queue for
+        // microseconds (prefill's merge: 15 us less).  Smaller grids count
+        // on the second-level counter directly (one hop less).  Every counter
+        // is cleared by the last arrival on it.
+        const int nc = gridDim.x > 64 ? kMergeArrive : 1;
+        const int j = (int)(blockIdx.x % nc);
+        const int expect = (int)gridDim.x / nc + (j < (int)gridDim.x % nc ? 1 : 0);
+        int* c1 = m.mcount + kMergeArriveStride * (1 + j);
+        const int done = nc == 1 ? expect - 1 : __hip_atomic_fetch_add(c1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == expect - 1) {
+            if (nc > 1) __hip_atomic_store(c1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int top = nc == 1 ? (int)gridDim.x : nc;
+            const int done2 = __hip_atomic_fetch_add(m.mcount + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (done2 == top - 1) {
+                __hip_atomic_store(m.mcount + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(m.mcount, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
         }
     }
     const int n_groups = n_sh;

@@ -152,7 +152,7 @@ WsLayout layout_workspace(const pa_handle* h, bool valu, bool mfma) {
     L.desc_cap = (int)std::max<size_t>(
         1, ((valu ? (size_t)h->max_items_valu : 0) + (mfma ? (size_t)h->max_items_mfma : 0)) / 2);
     const size_t d_bytes = (size_t)L.desc_cap * sizeof(MergeDesc);
-    const size_t c_bytes = 2 * sizeof(int);
+    const size_t c_bytes = kMergeCounterInts * sizeof(int);
     const size_t s_bytes = valu ? (size_t)h->sdesc_groups * h->sdesc_upg * sizeof(MergeDesc) : 0;
     const size_t a_bytes = valu ? (size_t)h->sdesc_groups * sizeof(int) : 0;
     const size_t e_bytes = sizeof(int);
