@@ -194,6 +194,13 @@ GRAPH_CASES = {
     "decode_in_kernel_merge": dict(seq_lens=(1003,), q_lens=(1,)),
     # verification width: tile kernel, published groups, merge launch
     "verify_merge_launch": dict(seq_lens=(3000,), q_lens=(8,), q_dtype="f16", kv_dtype="f16"),
+    # a mixed fp8 batch: the one-round split plan, a merge grid past 64
+    # workgroups (two-level arrival counters)
+    "mixed_two_level_arrival": dict(seq_lens=(40001, 9004, 3000, 257), q_lens=(1, 4, 8, 1), kv_dtype="fp8_e4m3"),
+    # prefill rows: ~1,000 merge workgroups on the two-level counters
+    "prefill_merge_launch": dict(num_q_heads=24, num_kv_heads=4, seq_lens=(3000,), q_lens=(300,)),
+    # head_dim 256 prefill on its tile kernel
+    "d256_prefill": dict(num_q_heads=16, num_kv_heads=2, head_dim=256, seq_lens=(2500, 700), q_lens=(200, 9)),
 }
 
 
