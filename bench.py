@@ -316,8 +316,10 @@ def _marker():
 
 def trace_child(workloads, steps: int, warmup: int, replays: int) -> None:
     """Runs inside rocprofv3 --kernel-trace: per workload, warm-up forwards,
-    then a marker kernel, `replays` replays of a graph of `steps` forwards,
-    and a marker again, so the replayed dispatches can be told apart."""
+    untimed replays of a graph of `steps` forwards for at least WARM_SECONDS
+    (as in the timed runs, so the clock has settled), then a marker kernel,
+    `replays` replays of the graph, and a marker again, so the replayed
+    dispatches can be told apart."""
     import torch
 
     import paged_attention_long_amd as pal
@@ -333,6 +335,10 @@ def trace_child(workloads, steps: int, warmup: int, replays: int) -> None:
                 for i in range(steps):
                     prep.step(h, i)
             torch.cuda.synchronize()
+            t_warm = time.perf_counter()
+            while time.perf_counter() - t_warm < WARM_SECONDS:
+                g.replay()
+                torch.cuda.synchronize()
             _marker()
             for _ in range(replays):
                 g.replay()
