@@ -773,7 +773,9 @@ def _mfma_summary(prof_dir: str, trace_avg_us: dict) -> list:
              "Per dispatch, averaged over the dispatches of the eager counter runs.  MfmaUtil is the profiler's "
              "derived counter: MFMA-busy SIMD cycles / (GPU-active cycles x 1,024 SIMDs).  The raw "
              "GRBM_GUI_ACTIVE as the profiler reports it sums the 8 XCDs, so the clock is GRBM_GUI_ACTIVE / "
-             "kernel time / 8.  Executed flop = MFMA ops x 512.", "",
+             "kernel time / 8 (given for the matrix kernels only: over a kernel of a few microseconds the "
+             "counter window, dispatch to completion, is longer than the traced kernel time).  Executed "
+             "flop = MFMA ops x 512.", "",
              "| kernel | MfmaUtil % | MFMA busy cycles | GPU-active cycles | kernel us (trace avg) | "
              "cycles / us | clock GHz (/ 8 XCDs) | executed TFLOP | executed TFLOP/s |",
              "|---|---|---|---|---|---|---|---|---|"]
@@ -781,9 +783,9 @@ def _mfma_summary(prof_dir: str, trace_avg_us: dict) -> list:
         us = trace_avg_us.get(k, float("nan"))
         gui = mean(c.get("GRBM_GUI_ACTIVE", []))
         fl = mean(c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", [])) * 512
+        clk = f"{gui / us:.1f} | {gui / us / 8e3:.2f}" if fl > 0 else "n/a | n/a"
         lines.append(f"| {k} | {mean(c.get('MfmaUtil', [])):.1f} | {mean(c.get('SQ_VALU_MFMA_BUSY_CYCLES', [])):.4g} | "
-                     f"{gui:.4g} | {us:.1f} | {gui / us:.1f} | {gui / us / 8e3:.2f} | {fl / 1e12:.4f} | "
-                     f"{fl / us / 1e6:.1f} |")
+                     f"{gui:.4g} | {us:.1f} | {clk} | {fl / 1e12:.4f} | {fl / us / 1e6:.1f} |")
     return lines + [""]
 
 
