@@ -569,6 +569,7 @@ def reduce_profiles(prof_dir: str, workload: str, calib_mib: int, commands: list
     trace_avg = {_short(r["Name"]): float(r["AverageNs"]) / 1e3 for r in stats}
     lines += _mfma_summary(prof_dir, trace_avg)
     lines += _valu_summary(prof_dir, trace_avg)
+    lines += _issue_summary(prof_dir)
     name = "_".join(sorted({k.split("<")[0] for k in kern})) or "kernels"
     out_md = os.path.join(ROOT, "profiles", f"{name}_{workload}.md")
     os.makedirs(os.path.dirname(out_md), exist_ok=True)
@@ -731,6 +732,52 @@ MFMA_PASSES = (("mfma_util", "MfmaUtil"), ("mfma_raw", "SQ_VALU_MFMA_BUSY_CYCLES
 
 VALU_PASS = "SQ_INSTS_VALU SQ_WAVES"
 
+# Issue and wait counters of the MFMA-bound workloads (wave-cycles, in units
+# of four cycles as the profiler counts them): where the waves' time goes.
+ISSUE_PASSES = (("issue", "SQ_WAVE_CYCLES SQ_ACTIVE_INST_ANY SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU "
+                          "SQ_INSTS_VALU SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_MISC"),
+                ("lds", "SQ_WAVE_CYCLES SQ_INSTS_LDS SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT "
+                        "SQ_LDS_ADDR_CONFLICT"))
+
+
+def _issue_summary(prof_dir: str) -> list:
+    """Markdown lines for the issue/wait and LDS passes (empty if they were not run)."""
+    import collections
+
+    vals = {sub: collections.defaultdict(lambda: collections.defaultdict(list)) for sub, _ in ISSUE_PASSES}
+    for sub, _ in ISSUE_PASSES:
+        for r in _csv_rows(os.path.join(prof_dir, sub, "**", "*counter_collection.csv")):
+            k = _short(r["Kernel_Name"])
+            if any(t in k for t in OUR_KERNEL_TAGS):
+                vals[sub][k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if not any(vals.values()):
+        return []
+    mean = lambda v: sum(v) / len(v) if v else float("nan")
+    lines = ["## Issue and waits (SQ_WAVE_CYCLES, SQ_ACTIVE_INST_*, SQ_WAIT_*; LDS)", "",
+             "Per dispatch, averaged over the dispatches of the eager counter runs.  Each share is of the "
+             "waves' resident time (SQ_WAVE_CYCLES of the same pass), with the profiler's meanings: issuing "
+             "(SQ_ACTIVE_INST_ANY), waiting on a counter or event (SQ_WAIT_ANY), an instruction waiting to "
+             "issue (SQ_WAIT_INST_ANY), VALU issue (SQ_ACTIVE_INST_VALU), LDS instructions waiting to issue "
+             "(SQ_WAIT_INST_LDS); the shares overlap.  VALU issue slots beyond one per VALU instruction "
+             "(SQ_ACTIVE_INST_VALU - SQ_INSTS_VALU) against SQ_INSTS_VALU_TRANS_F32 give the issue slots of "
+             "a transcendental.", "",
+             "| kernel | wave-cycles (x4) | issuing % | waiting % | instr. waiting % | VALU issue % | "
+             "VALU instr. | exp/log instr. | extra VALU slots | LDS instr. | LDS wait % | bank conflicts | "
+             "addr. conflicts |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(set(vals["issue"]) | set(vals["lds"])):
+        c, d = vals["issue"][k], vals["lds"][k]
+        wc, wl = mean(c.get("SQ_WAVE_CYCLES", [])), mean(d.get("SQ_WAVE_CYCLES", []))
+        pc = lambda n: 100.0 * mean(c.get(n, [])) / wc
+        extra = mean(c.get("SQ_ACTIVE_INST_VALU", [])) - mean(c.get("SQ_INSTS_VALU", []))
+        lines.append(f"| {k} | {wc:.4g} | {pc('SQ_ACTIVE_INST_ANY'):.1f} | {pc('SQ_WAIT_ANY'):.1f} | "
+                     f"{pc('SQ_WAIT_INST_ANY'):.1f} | {pc('SQ_ACTIVE_INST_VALU'):.1f} | "
+                     f"{mean(c.get('SQ_INSTS_VALU', [])):.4g} | {mean(c.get('SQ_INSTS_VALU_TRANS_F32', [])):.4g} | "
+                     f"{extra:.4g} | {mean(d.get('SQ_INSTS_LDS', [])):.4g} | "
+                     f"{100.0 * mean(d.get('SQ_WAIT_INST_LDS', [])) / wl:.1f} | "
+                     f"{mean(d.get('SQ_LDS_BANK_CONFLICT', [])):.4g} | {mean(d.get('SQ_LDS_ADDR_CONFLICT', [])):.4g} |")
+    return lines + [""]
+
 
 def _valu_summary(prof_dir: str, trace_avg_us: dict) -> list:
     """Markdown lines for the VALU instruction pass (empty if it was not run)."""
@@ -807,10 +854,11 @@ def profile_commands(workload: str, calib_mib: int = 512) -> list:
     ] + ([
         # matrix-core utilisation of the prefill kernels: the profiler's MfmaUtil
         # (MFMA-busy SIMD cycles over GPU-active cycles x SIMDs), the raw busy
-        # and GPU-active cycles, and the bf16 MFMA operations (512 flop each)
+        # and GPU-active cycles, and the bf16 MFMA operations (512 flop each);
+        # then the waves' issue and wait cycles and the LDS counters
         f"rocprofv3 --pmc {ctrs} --output-format csv -d {out}/{sub} -o run -- "
         f"{run} --steps 5 --warmup 1 --repeats 1 --eager --json-out {out}/{sub}/bench.json"
-        for sub, ctrs in MFMA_PASSES] if workload in FLOP_WORKLOADS else []) + ([
+        for sub, ctrs in MFMA_PASSES + ISSUE_PASSES] if workload in FLOP_WORKLOADS else []) + ([
         # the append's vector-ALU instruction count (its limiter)
         f"rocprofv3 --pmc {VALU_PASS} --output-format csv -d {out}/valu -o run -- "
         f"{run} --steps 5 --warmup 1 --repeats 1 --eager --json-out {out}/valu/bench.json"

@@ -30,12 +30,13 @@ def test_profile_commands_keep_counters_and_traces_apart(workload):
     prof = [c for c in cmds if c.startswith("rocprofv3")]
     mfma = workload in bench.FLOP_WORKLOADS
     valu = workload == "append_fp8"
-    assert len(prof) == 3 + (3 if mfma else 0) + (1 if valu else 0)
+    n_mfma = len(bench.MFMA_PASSES) + len(bench.ISSUE_PASSES)
+    assert len(prof) == 3 + (n_mfma if mfma else 0) + (1 if valu else 0)
     trace, fetch, write = prof[:3]
     assert "--kernel-trace" in trace and "--stats" in trace and "--pmc" not in trace
     passes = [(fetch, "FETCH_SIZE"), (write, "WRITE_SIZE")]
     if mfma:
-        passes += [(c, ctrs) for c, (_, ctrs) in zip(prof[3:], bench.MFMA_PASSES)]
+        passes += [(c, ctrs) for c, (_, ctrs) in zip(prof[3:], bench.MFMA_PASSES + bench.ISSUE_PASSES)]
     if valu:
         passes += [(prof[3], bench.VALU_PASS)]
     for c, counter in passes:
@@ -43,7 +44,7 @@ def test_profile_commands_keep_counters_and_traces_apart(workload):
         for banned in ("--sys-trace", "--runtime-trace", "--kernel-trace", " -s ", " -r "):
             assert banned not in c
     # at most 8 SQ and 2 GRBM counters in one pass
-    for _, ctrs in bench.MFMA_PASSES:
+    for _, ctrs in bench.MFMA_PASSES + bench.ISSUE_PASSES + (("valu", bench.VALU_PASS),):
         names = ctrs.split()
         assert sum(n.startswith("SQ_") for n in names) <= 8 and sum(n.startswith("GRBM_") for n in names) <= 2
     # the program itself follows "--" (no launcher in between)
