@@ -14,10 +14,19 @@
 // cache on write in the same place of the step ("Dual MI50, part 2",
 // section "Prefill: teach the fork's fast kernel to read the int8 cache").
 //
-// Bandwidth-bound and tiny per row: one thread per 8 elements (16 B in,
-// 16 B or 8 B out), workgroups along the sequence's rows.  Every store is
-// checked against the cache and the block table; rows whose position or page
-// falls outside them are skipped.
+// One thread per 8 elements (16 B in, 16 B or 8 B out).  A workgroup takes
+// four consecutive rows (tokens) of a sequence; its items run over the 8-element
+// chunks of a head row fastest, then over the four rows, then over the head
+// rows (K of every KV head, then V), so a wave stores one head row of four
+// consecutive slots, adjacent in the page.  A row's page comes from the block
+// table through a multiply-high by the host's magic number for page_size / 16;
+// the quotient x / s by a multiply with 1/s where that provably gives the
+// same code (else by the division itself), and the fp8 code by the hardware's
+// round-to-nearest-even conversion (with one row per workgroup, a division and
+// an integer rounding per element: 50.5 us for 64 sequences x 256 rows x 8
+// heads x 128; this way 32.4 us).  Every store is checked against the
+// cache and the block table; rows whose position or page falls outside them
+// are skipped.
 #include "pa_common.h"
 #include "pa_kernels.h"
 
@@ -27,36 +36,38 @@ namespace {
 
 constexpr int kAppendThreads = 256;
 
-// E4M3FN code of an fp32 value by integer rounding of its bits: the
-// mantissa is cut to 3 bits (exponent >= -6) or the significand is shifted
-// to units of 2^-9 (subnormal codes), rounding to nearest, ties to even.
-// Codes are ordered like the values they stand for, so a round-up that
-// carries into the exponent lands on the next code.
-PA_DEVINLINE uint32_t e4m3_code(float q) {
-    const uint32_t u = __float_as_uint(q);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const uint32_t a = u & 0x7fffffffu;
-    if (a > 0x7f800000u) return sign | 0x7fu;          // NaN
-    if (a >= 0x43e00000u) return sign | 0x7eu;         // >= 448 (and infinity): saturate
-    if (a < 0x00800000u) return sign;                  // zero and fp32 subnormals (< 2^-126)
-    const int e = (int)(a >> 23) - 127;
-    uint32_t code;
-    if (e >= -6) {
-        const uint32_t m = a & 0x7fffffu;
-        const uint32_t base = ((uint32_t)(e + 7) << 3) | (m >> 20);
-        const uint32_t rem = m & 0xfffffu;
-        code = base + ((rem > 0x80000u || (rem == 0x80000u && (base & 1u))) ? 1u : 0u);
-    } else {
-        const int sh = 14 - e;                         // significand in units of 2^-9
-        if (sh >= 32) return sign;
-        const uint32_t sig = (a & 0x7fffffu) | 0x800000u;
-        const uint32_t base = sig >> sh;
-        const uint32_t rem = sig & ((1u << sh) - 1u);
-        const uint32_t half = 1u << (sh - 1);
-        code = base + ((rem > half || (rem == half && (base & 1u))) ? 1u : 0u);
-    }
-    return sign | min(code, 0x7eu);
+// E4M3FN codes of two fp32 values (byte 0: x, byte 1: y): the hardware
+// conversion rounds to nearest, ties to even, at any magnitude below 448;
+// the median clamps larger magnitudes and infinity to +-448 first (they
+// saturate), and NaN becomes sign | 0x7f by select.
+PA_DEVINLINE uint32_t e4m3_pair(float x, float y) {
+    uint32_t v = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(x, -448.0f, 448.0f),
+                                                          __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f), 0, false) &
+                 0xffffu;
+    if (x != x) v = (v & 0xff00u) | ((__float_as_uint(x) >> 24) & 0x80u) | 0x7fu;
+    if (y != y) v = (v & 0x00ffu) | ((((__float_as_uint(y) >> 24) & 0x80u) | 0x7fu) << 8);
+    return v;
 }
+
+// x * fl(1/s) lies within 2.5 units in the last place of fl(x / s) when s
+// and 1/s are normal, so their codes can differ only where a point half-way
+// between two codes is that close: for magnitudes from 2^-6 up (normal codes)
+// where the 20 bits below the kept mantissa are within 3 of 0x80000.  Such
+// values, and smaller magnitudes (subnormal codes, zero), take the quotient.
+PA_DEVINLINE bool e4m3_needs_quotient(float q) {
+    const uint32_t a = __float_as_uint(q) & 0x7fffffffu;
+    return a < 0x3c800000u || ((a & 0xfffffu) - 0x7fffdu) <= 6u;
+}
+
+// Likewise for the nearest integer: within 3 ulp of a half-integer.
+PA_DEVINLINE bool int_needs_quotient(float q) {
+    const float d = fabsf(fabsf(q - __builtin_rintf(q)) - 0.5f);
+    const int eb = (int)(__float_as_uint(q) & 0x7f800000u) - (23 << 23);
+    return d <= 3.0f * __uint_as_float((uint32_t)max(eb, 0));
+}
+
+// A normal, finite fp32 value (exponent field 1 .. 254).
+PA_DEVINLINE bool f32_normal(float v) { return (__float_as_uint(v) & 0x7f800000u) - 0x00800000u < 0x7f000000u; }
 
 // Maximum over the aligned group of N lanes (N = 8 or 16: one row's
 // threads) that propagates NaN, through DPP moves inside 16-lane rows.
@@ -109,35 +120,44 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
             debug_flag(a.err_word, (ql < 0 || ql > sl) ? PA_CHECK_LENGTHS : PA_CHECK_TOKENS);
         return;
     }
-    // 8-element chunks per head row; an int8 row's CPR threads are one aligned
-    // lane group (the loop's start and stride are multiples of CPR)
+    // 8-element chunks per head row (a power of two); an int8 row's CPR
+    // threads are one aligned lane group (chunk indices start at the thread
+    // index and step by the workgroup size) and share the row's page
     const int cpr = KVT == PA_DTYPE_INT8 ? CPR : a.head_dim / 8;
-    const int64_t per_side = (int64_t)ql * a.num_kv_heads * cpr;
-    const int64_t stride = (int64_t)gridDim.y * kAppendThreads;
-    for (int64_t c = (int64_t)blockIdx.y * kAppendThreads + threadIdx.x; c < 2 * per_side; c += stride) {
-        const int which = c >= per_side;                           // 0: K, 1: V
-        const int64_t r = c - which * per_side;
-        const int ch = (int)(r % cpr);
-        const int64_t rg = r / cpr;
-        const int g = (int)(rg % a.num_kv_heads);
-        const int i = (int)(rg / a.num_kv_heads);
+    const int lcpr = 31 - __builtin_clz(cpr);
+    const int per_row = 2 * a.num_kv_heads * cpr;
+    const int64_t row_elems = (int64_t)a.num_kv_heads * a.head_dim;
+    // row i's page id (-1: outside the block table, -2: a page id outside
+    // the pool; both skipped, and reported in the checked mode) and slot
+    auto row_page = [&](int i, int& pid, int& slot) {
         const int p = sl - ql + i;
-        const int lp = p / a.page_size;
-        // (an int8 row's threads share p and pid: they skip together)
-        if (lp >= a.bt_stride) {
-            if (a.checks) debug_flag(a.err_word, PA_CHECK_TABLE);
-            continue;
+        // p / page_size as (p / 16) / (page_size / 16) by the host's magic number
+        const int lp = a.cpp == 1 ? p >> 4
+                       : p < (1 << 28) ? (int)(__umulhi((uint32_t)(p >> 4), a.cpp_magic) >> a.cpp_shift)
+                                       : p / a.page_size;
+        slot = p - lp * a.page_size;
+        pid = -1;
+        if (lp < a.bt_stride) {
+            pid = a.block_table[(int64_t)b * a.bt_stride + lp];
+            if (pid < 0 || pid >= a.num_pages) pid = -2;
         }
-        const int pid = a.block_table[(int64_t)b * a.bt_stride + lp];
-        if (pid < 0 || pid >= a.num_pages) {
-            if (a.checks) debug_flag(a.err_word, PA_CHECK_PAGE);
-            continue;
-        }
-        const uint16_t* src = static_cast<const uint16_t*>(which ? a.v_new : a.k_new) +
-                              ((int64_t)(q_off + i) * a.num_kv_heads + g) * a.head_dim + ch * 8;
-        const uint4 in = *reinterpret_cast<const uint4*>(src);
+    };
+    auto chunk_src = [&](int i, int cw) {
+        const int ch = cw & (cpr - 1);
+        const int hw = cw >> lcpr;
+        const int which = hw >= a.num_kv_heads;
+        const int g = hw - which * a.num_kv_heads;
+        return static_cast<const uint16_t*>(which ? a.v_new : a.k_new) + (int64_t)(q_off + i) * row_elems +
+               (int64_t)g * a.head_dim + ch * 8;
+    };
+    // converts and stores chunk cw (16 input bytes in `in`) of a row at page pid, slot slot
+    auto put = [&](int cw, const uint4& in, int pid, int slot) {
+        const int ch = cw & (cpr - 1);
+        const int hw = cw >> lcpr;
+        const int which = hw >= a.num_kv_heads;                     // 0: K, 1: V
+        const int g = hw - which * a.num_kv_heads;
         const int64_t off = (int64_t)pid * a.page_stride + (int64_t)g * a.head_stride +
-                            (int64_t)(p - lp * a.page_size) * a.token_stride + ch * 8;
+                            (int64_t)slot * a.token_stride + ch * 8;
         if constexpr (KVT == PA_DTYPE_INT8) {
             const uint32_t w[4] = {in.x, in.y, in.z, in.w};
             float x[8];
@@ -149,41 +169,72 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
             }
             amax = group_max_nan<CPR>(amax);
             const float s = __fdiv_rn(amax, 127.0f);
+            const float rs = __fdiv_rn(1.0f, s);
+            const bool fast = f32_normal(s) && f32_normal(rs);
             uint32_t lo = 0, hi = 0;
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const uint32_t code = i8_code(__fdiv_rn(x[k], s));
+                float q = x[k] * rs;
+                if (!fast || int_needs_quotient(q)) q = __fdiv_rn(x[k], s);
+                const uint32_t code = i8_code(q);
                 if (k < 4) lo |= code << (8 * k);
                 else hi |= code << (8 * (k - 4));
             }
             *reinterpret_cast<uint2*>(static_cast<uint8_t*>(which ? a.v_cache : a.k_cache) + off) = make_uint2(lo, hi);
             if (ch == 0)
                 a.row_scale[which * a.rs_v + (int64_t)pid * a.rs_page + (int64_t)g * a.rs_head +
-                            (int64_t)(p - lp * a.page_size) * a.rs_tok] = s;
+                            (int64_t)slot * a.rs_tok] = s;
         } else if constexpr (KVT != PA_DTYPE_FP8_E4M3) {
             *reinterpret_cast<uint4*>(static_cast<uint16_t*>(which ? a.v_cache : a.k_cache) + off) = in;
         } else {
             const float s = a.kv_scale[which * a.num_kv_heads + g];
+            const float rs = __fdiv_rn(1.0f, s);
+            const bool fast = f32_normal(s) && f32_normal(rs);
             const uint32_t w[4] = {in.x, in.y, in.z, in.w};
-            uint32_t lo = 0, hi = 0;
+            float q[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                const uint32_t bits = (w[k / 2] >> (16 * (k & 1))) & 0xffffu;
-                const uint32_t code = e4m3_code(__fdiv_rn(to_f32<IT>(bits), s));
-                if (k < 4) lo |= code << (8 * k);
-                else hi |= code << (8 * (k - 4));
+                const float x = to_f32<IT>((w[k / 2] >> (16 * (k & 1))) & 0xffffu);
+                q[k] = x * rs;
+                if (!fast || e4m3_needs_quotient(q[k])) q[k] = __fdiv_rn(x, s);
             }
+            const uint32_t lo = e4m3_pair(q[0], q[1]) | (e4m3_pair(q[2], q[3]) << 16);
+            const uint32_t hi = e4m3_pair(q[4], q[5]) | (e4m3_pair(q[6], q[7]) << 16);
             *reinterpret_cast<uint2*>(static_cast<uint8_t*>(which ? a.v_cache : a.k_cache) + off) = make_uint2(lo, hi);
         }
+    };
+    auto report = [&](int pid) {
+        if (a.checks) debug_flag(a.err_word, pid == -1 ? PA_CHECK_TABLE : PA_CHECK_PAGE);
+    };
+    // A workgroup takes kRows consecutive rows.  Items run chunk fastest,
+    // then row, then head row, so the kRows rows of one head row that a wave
+    // stores (consecutive slots of a page) are adjacent in the cache.
+    constexpr int kRows = 4;
+    const int i0 = blockIdx.y * kRows;
+    if (i0 >= ql) return;
+    const int n_items = per_row * kRows;
+    for (int it = threadIdx.x; it < n_items; it += kAppendThreads) {
+        const int ch = it & (cpr - 1);
+        const int r = (it >> lcpr) & (kRows - 1);
+        const int hw = it >> (lcpr + 2);
+        const int i = i0 + r;
+        if (i >= ql) continue;
+        int pid, slot;
+        row_page(i, pid, slot);
+        const int cw = (hw << lcpr) | ch;
+        if (pid < 0) {
+            if (cw == 0) report(pid);
+            continue;
+        }
+        put(cw, *reinterpret_cast<const uint4*>(chunk_src(i, cw)), pid, slot);
     }
 }
 
 }  // namespace
 
 hipError_t launch_append(const AppendArgs& a, int kv_dtype, int in_dtype, int max_rows, hipStream_t stream) {
-    const int64_t chunks = 2LL * max_rows * a.num_kv_heads * (a.head_dim / 8);
-    const int gy = (int)std::min<int64_t>(256, std::max<int64_t>(1, (chunks + kAppendThreads - 1) / kAppendThreads));
-    const dim3 grid(a.num_seqs, gy);
+    // workgroups along a sequence's rows, four rows each
+    const dim3 grid(a.num_seqs, (std::max(max_rows, 1) + 3) / 4);
     if (kv_dtype == PA_DTYPE_INT8) {
         const bool bf = in_dtype == PA_DTYPE_BF16;
         if (a.head_dim == 256) {

@@ -165,6 +165,9 @@ struct AppendArgs {
     int64_t num_pages, page_stride, head_stride, token_stride;   // elements
     int64_t num_tokens;
     int num_seqs, bt_stride, num_kv_heads, head_dim, page_size;
+    int cpp;                   // page_size / 16
+    uint32_t cpp_magic;        // c / cpp == umulhi(c, cpp_magic) >> cpp_shift for c < 2^24 (cpp > 1)
+    int cpp_shift;
     int checks;                // PA_DEBUG_CHECKS: skipped rows are reported in *err_word
     int* err_word;
 };

@@ -641,6 +641,8 @@ int paged_attn_append(pa_handle_t* h, const void* k_new, const void* v_new, int6
     a.num_kv_heads = c.num_kv_heads;
     a.head_dim = c.head_dim;
     a.page_size = c.page_size;
+    a.cpp = c.page_size / 16;
+    chunk_magic(a.cpp, &a.cpp_magic, &a.cpp_shift);
     a.checks = (c.flags & PA_DEBUG_CHECKS) != 0;
     a.err_word = h->err_word;
     if (c.kv_dtype == PA_DTYPE_INT8) {

@@ -128,6 +128,45 @@ def test_append_bit_exact(name, layout):
     assert np.array_equal(got_v, ref_v), f"V differs at {np.argwhere(got_v != ref_v)[:5].tolist()}"
 
 
+@pytest.mark.parametrize("in_dtype,page_size", [("bf16", 16), ("f16", 48)])
+def test_append_fp8_every_16bit_input(in_dtype, page_size):
+    """Every 16-bit input value (all 65,536 bit patterns: zeros, subnormals,
+    infinities, NaN of both signs) quantised to fp8 under scales from 2^-9 to
+    17.3, bit for bit against the oracle: the fast quotient, its fallback to
+    the exact one and the saturating conversion together reproduce the code of
+    the once-rounded quotient for every value the input type can hold."""
+    import torch
+
+    hkv, D, T = 4, 128, 128
+    rng = np.random.default_rng(zlib.crc32(f"every16{in_dtype}{page_size}".encode()))
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    bits = np.stack([rng.permutation(allbits), rng.permutation(allbits)]).reshape(2, T, hkv, D)
+    scale = np.array([[1.0, 0.0371, 2.0 ** -9, 17.3], [0.0071, 0.5, 3.3, 2.0 ** -5]], np.float32)
+    seq_lens, q_lens = np.array([T + 37], np.int32), np.array([T], np.int32)
+    pages = (int(seq_lens[0]) + page_size - 1) // page_size + 3
+    width = pages
+    bt = np.ascontiguousarray(rng.permutation(pages).astype(np.int32)[:width].reshape(1, width))
+    pools = rng.integers(0, 256, (2, pages, hkv, page_size, D)).astype(np.uint8)
+    progress(f"append every 16-bit {in_dtype} P{page_size}")
+    cfg = pal.make_config(hkv * 4, hkv, D, in_dtype, "fp8_e4m3", 1, T, T, page_size=page_size)
+    h = pal.paged_attn_create(cfg)
+    try:
+        dev = torch.device("cuda")
+        kc, vc = (torch.from_numpy(pools[w]).to(dev) for w in range(2))
+        qt = getattr(torch, TORCH_16[in_dtype])
+        kn, vn = (torch.from_numpy(bits[w].view(np.int16)).to(dev).view(qt).contiguous() for w in range(2))
+        pal.paged_attn_append(h, kn, vn, kc, vc, torch.from_numpy(bt).to(dev), torch.from_numpy(seq_lens).to(dev),
+                              torch.from_numpy(q_lens).to(dev), torch.from_numpy(scale.reshape(-1)).to(dev))
+        torch.cuda.synchronize()
+        got_k, got_v = kc.cpu().numpy(), vc.cpu().numpy()
+    finally:
+        pal.paged_attn_destroy(h)
+    ref_k, ref_v = oracle.append_kv(bits[0], bits[1], in_dtype, pools[0], pools[1], "fp8_e4m3", bt, seq_lens,
+                                    q_lens, scale, page_size)
+    assert np.array_equal(got_k, ref_k), f"K differs at {np.argwhere(got_k != ref_k)[:5].tolist()}"
+    assert np.array_equal(got_v, ref_v), f"V differs at {np.argwhere(got_v != ref_v)[:5].tolist()}"
+
+
 def test_append_skips_rows_outside_the_cache():
     """Rows whose page id is outside the pool, or whose position is past the
     block table, are not written; q_len > seq_len writes nothing."""
