@@ -31,6 +31,16 @@ SMALL = {
     "bf16_g6": dict(num_q_heads=24, num_kv_heads=4, seq_lens=(1234,), q_lens=(3,)),
     "f16_mha": dict(num_q_heads=4, num_kv_heads=4, seq_lens=(517,), q_lens=(1,), q_dtype="f16", kv_dtype="f16"),
     "bf16_g8": dict(num_q_heads=32, num_kv_heads=4, seq_lens=(2500,), q_lens=(1,)),
+    # the largest group (16 query heads per KV head): 16 rows per token, so a
+    # decode row set already takes the tile kernel and 4 new tokens fill its 64 rows
+    "bf16_g16_decode": dict(num_q_heads=32, num_kv_heads=2, seq_lens=(3001, 40), q_lens=(1, 1)),
+    "f16_g16_verify4": dict(num_q_heads=16, num_kv_heads=1, seq_lens=(2222,), q_lens=(4,), q_dtype="f16",
+                            kv_dtype="f16", k_outlier_frac=0.01),
+    "fp8_g16_mixed": dict(num_q_heads=32, num_kv_heads=2, seq_lens=(1800, 600), q_lens=(3, 1),
+                          kv_dtype="fp8_e4m3"),
+    "f16_d64_g16_max_rows": dict(num_q_heads=16, num_kv_heads=1, head_dim=64, seq_lens=(500, 90), q_lens=(4, 2),
+                                 q_dtype="f16", kv_dtype="f16"),
+    "bf16_d256_g16": dict(num_q_heads=16, num_kv_heads=1, head_dim=256, seq_lens=(1300,), q_lens=(2,)),
     "qlen0_in_batch": dict(seq_lens=(300, 50, 129), q_lens=(2, 0, 1)),
     "all_new_rows": dict(seq_lens=(8, 5), q_lens=(8, 5), q_dtype="f16", kv_dtype="f16"),
     "single_token": dict(seq_lens=(1,), q_lens=(1,)),

@@ -28,6 +28,10 @@ PREFILL = {
     "f16_outliers_g4": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(3000,), q_lens=(48,), q_dtype="f16",
                             kv_dtype="f16", k_outlier_frac=0.01),
     "mixed_lengths": dict(seq_lens=(513, 70, 2049), q_lens=(33, 70, 5), num_q_heads=8, num_kv_heads=2),
+    # the largest group (16 query heads per KV head) in 256-row items
+    "bf16_g16_chunk": dict(num_q_heads=32, num_kv_heads=2, seq_lens=(1400,), q_lens=(100,)),
+    "fp8_g16_chunk": dict(num_q_heads=16, num_kv_heads=1, seq_lens=(900, 300), q_lens=(50, 20),
+                          kv_dtype="fp8_e4m3"),
     # head_dim 64 (VALU kernel only) at its limit of 64 rows per KV head
     "f16_d64_max_rows": dict(num_q_heads=8, num_kv_heads=2, head_dim=64, seq_lens=(700, 16), q_lens=(16, 16),
                              q_dtype="f16", kv_dtype="f16"),
