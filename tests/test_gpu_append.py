@@ -128,7 +128,7 @@ def test_append_bit_exact(name, layout):
     assert np.array_equal(got_v, ref_v), f"V differs at {np.argwhere(got_v != ref_v)[:5].tolist()}"
 
 
-@pytest.mark.parametrize("in_dtype,page_size", [("bf16", 16), ("f16", 48)])
+@pytest.mark.parametrize("in_dtype,page_size", [("bf16", 16), ("f16", 48), ("bf16", 65520)])
 def test_append_fp8_every_16bit_input(in_dtype, page_size):
     """Every 16-bit input value (all 65,536 bit patterns: zeros, subnormals,
     infinities, NaN of both signs) quantised to fp8 under scales from 2^-9 to

@@ -64,6 +64,25 @@ def test_page_size_parity(name, page_size):
         compare(f"P{page_size} {name}/path{path}", inp.kv_dtype, out, lse, ref_o, ref_l)
 
 
+@pytest.mark.parametrize("page_size", [65520, 65536])
+def test_largest_page_sizes(page_size):
+    """The largest pages the ABI takes (65,536 tokens, and 65,520: 4,095
+    16-token chunks, the largest divisor the kernels' multiply-high division
+    covers): a sequence across two pages and a short one, decode and
+    verification rows, on the default and the VALU-only paths."""
+    inp = generate(_spec(page_size=page_size, num_q_heads=8, num_kv_heads=2, seq_lens=(70000, 3000), q_lens=(1, 8),
+                         q_dtype="f16", kv_dtype="f16", seed=93))[0]
+    ref_o, ref_l = oracle.attention(inp)
+    for path in (pal.PA_PATH_AUTO, pal.PA_PATH_VALU):
+        progress(f"pages {page_size} largest, path {path}")
+        c = GpuCase([inp], path=path)
+        try:
+            out, lse = c.run()
+        finally:
+            c.close()
+        compare(f"P{page_size} largest/path{path}", inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
 @pytest.mark.parametrize("page_size", [48, 1056])
 def test_page_size_nhd_layout(page_size):
     """[pages][P][Hkv][D] storage seen through strides: the page stride is
