@@ -75,6 +75,10 @@ CASES = {
     "fp8_from_bf16_d256": dict(kv="fp8_e4m3", q="bf16", hkv=2, D=256, seq_lens=(70, 16), q_lens=(8, 16)),
     "fp8_from_f16_d256_any_scale": dict(kv="fp8_e4m3", q="f16", hkv=4, D=256, seq_lens=(300, 9), q_lens=(16, 9),
                                         scales="arbitrary"),
+    # 40 KV heads: a row's 1,280 chunks take several passes of a workgroup
+    "fp8_from_bf16_40_heads": dict(kv="fp8_e4m3", q="bf16", hkv=40, D=128, seq_lens=(300, 20), q_lens=(9, 3),
+                                   scales="arbitrary"),
+    "bf16_40_heads": dict(kv="bf16", q="bf16", hkv=40, D=128, seq_lens=(35, 70), q_lens=(5, 6)),
 }
 
 
@@ -128,6 +132,7 @@ def test_append_bit_exact(name, layout):
     assert np.array_equal(got_v, ref_v), f"V differs at {np.argwhere(got_v != ref_v)[:5].tolist()}"
 
 
+@pytest.mark.filterwarnings("ignore:invalid value encountered in cast:RuntimeWarning")
 @pytest.mark.parametrize("in_dtype,page_size", [("bf16", 16), ("f16", 48), ("bf16", 65520)])
 def test_append_fp8_every_16bit_input(in_dtype, page_size):
     """Every 16-bit input value (all 65,536 bit patterns: zeros, subnormals,

@@ -41,6 +41,9 @@ SMALL = {
     "f16_d64_g16_max_rows": dict(num_q_heads=16, num_kv_heads=1, head_dim=64, seq_lens=(500, 90), q_lens=(4, 2),
                                  q_dtype="f16", kv_dtype="f16"),
     "bf16_d256_g16": dict(num_q_heads=16, num_kv_heads=1, head_dim=256, seq_lens=(1300,), q_lens=(2,)),
+    # many KV heads, not a power of two, one query head each
+    "f16_mha40": dict(num_q_heads=40, num_kv_heads=40, seq_lens=(900, 64), q_lens=(1, 8), q_dtype="f16",
+                      kv_dtype="f16"),
     "qlen0_in_batch": dict(seq_lens=(300, 50, 129), q_lens=(2, 0, 1)),
     "all_new_rows": dict(seq_lens=(8, 5), q_lens=(8, 5), q_dtype="f16", kv_dtype="f16"),
     "single_token": dict(seq_lens=(1,), q_lens=(1,)),
