@@ -381,7 +381,7 @@ struct Cfg {
     // ahead; the item's page ids are staged in LDS (PID_CAP of them).  The
     // loop is unrolled over the ring, so buffer offsets are immediates.
     static constexpr bool PIPE = (WR == 8) && !BYTE;
-    static constexpr int NKB = 4, NVB = 4, LEAD = 3;
+    static constexpr int NKB = 6, NVB = 6, LEAD = 6;
     static constexpr int PID_CAP = PIPE ? 4096 : (WR == 1 ? 1024 : 1);
     static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : (FSTAGE ? 16 : WK * GROUP_LDS);
     // int8 row scales of a tile: BN K scales then BN V scales, per staging
@@ -1168,11 +1168,16 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             __syncthreads();
         }
         if constexpr (C::PIPE) {
-            // Iteration k: P.V of tile k-1, then (after tile k+1 has landed) the
-            // scores of tile k+1 on the matrix cores while the VALU turns tile
-            // k's scores into P.  Tile k's K sits in K buffer k % NKB from its
-            // load (issued at iteration k - LEAD) to its QK (iteration k - 1); its
-            // V in V buffer k % NVB until its P.V (iteration k + 1).
+            // Iteration k holds tile k's scores (cur) and tile k+1's K
+            // fragments (kf).  In order: the scores of tile k+1 go to the
+            // matrix cores; tile k's V fragments are read from LDS (the read
+            // waits while those MFMAs run); the VALU turns tile k's scores into
+            // P; P.V of tile k goes to the matrix cores; past the barrier that
+            // certifies tile k+2 for every wave (and frees tile k's buffers),
+            // tile k+4 is requested into them and tile k+2's K fragments are
+            // read (that read waits while P.V runs).  Tile k's K and V sit in
+            // buffer k % NKB from its load (issued at iteration k - LEAD) until
+            // its V fragments are read in iteration k.
             // Page ids of the item's tiles and of the LEAD tiles prefetched past
             // its end (those read the last visible page: in bounds, unused),
             // staged in LDS when they fit; otherwise scalar loads per tile.
@@ -1193,7 +1198,6 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 n_live = max(0, t_hi - t_lo);
             }
             const uint32_t ring32 = (uint32_t)(uintptr_t)(lds_void_t*)tiles;
-            auto v_lds = [&](int k) { return ring32 + (uint32_t)((C::NKB + k % C::NVB) * C::TILE); };
             auto dma_pipe = [&](int k) {
                 int pid[PPT];
                 if (staged) {
@@ -1219,22 +1223,30 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             // This lane's LDS read addresses at ring offset 0: K fragments (row
             // l32, chunks 2*s8 + h32) and the transposing V reads.  A buffer's
             // offset from them is an immediate of the read instructions.
-            static_assert(C::NB == 1 && C::NKB == C::NVB, "one 32-key block per tile, rings of equal length");
+            static_assert(C::NB == 1 && C::NKB == C::NVB && C::TS == 2, "one 32-key block per tile, rings of equal length");
             uint32_t ka[8], va[8];
 #pragma unroll
             for (int s8 = 0; s8 < 8; ++s8) ka[s8] = ring32 + (uint32_t)swz(l32, 2 * s8 + h32);
 #pragma unroll
-            for (int k = 0; k < 8; ++k) va[k] = ring32 + v_lane_off[k];
-            // S^T of a tile = K Q^T: the K fragments are read in one batch,
-            // then eight MFMAs accumulate over the head dimension.
-            auto qk_at = [&](auto off_c, f32x16_t (&S)[C::NB]) {
-                constexpr int OFF = decltype(off_c)::value;
-                u32x4_t kf[C::KS];
-                lds_read_b128_x8<OFF>(ka, kf);
+            for (int k = 0; k < 8; ++k) va[k] = ring32 + (uint32_t)(C::NKB * C::TILE) + v_lane_off[k];
+            // S^T of a tile = K Q^T: eight MFMAs accumulate over the head dimension.
+            auto qk_mma = [&](const u32x4_t (&kf)[C::KS], f32x16_t (&S)[C::NB]) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) S[0][i] = 0.f;
 #pragma unroll
                 for (int s8 = 0; s8 < C::KS; ++s8) S[0] = mma32<QT>(kf[s8], qreg[s8], S[0]);
+            };
+            // O^T += V^T P^T over one tile from V fragments already in registers
+            // (r0: key step 0, r1: key step 1)
+            auto pv_mma = [&](const u32x2_t (&r0)[8], const u32x2_t (&r1)[8], const u32x4_t (&p)[C::TS]) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db) {
+                        const u32x2_t(&r)[8] = h ? r1 : r0;
+                        o_acc[db] = mma32<C::PVT>(u32x4_t{r[2 * db][0], r[2 * db][1], r[2 * db + 1][0], r[2 * db + 1][1]},
+                                                  p[h], o_acc[db]);
+                    }
             };
             // dead V rows of tile k (range edges only) are zeroed in its buffer
             auto zero_dead_v_pipe = [&](int k) {
@@ -1250,57 +1262,81 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 }
                 return true;
             };
+            // The second wave of each SIMD (waves 4-7) issues its P.V after the
+            // barrier instead of before it, so between two barriers the two
+            // waves of a SIMD are a phase apart: one's matrix ops meet the
+            // other's LDS reads and softmax.
+            const bool late_pv = wid >= C::NW / 2;
             const int n_it = ig.t_end - ig.t_begin;
             if (n_it > 0) {
+                static_assert(C::LEAD == C::NKB, "tile k+LEAD reuses tile k's buffers");
 #pragma unroll
                 for (int k = 0; k < C::LEAD; ++k) dma_pipe(k);
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 1) * 2 * C::DMA_PER_WAVE));   // tile 0 landed
+                __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 2) * 2 * C::DMA_PER_WAVE));   // tiles 0 and 1 landed
                 __syncthreads();
-                if (zero_dead_v_pipe(0)) __syncthreads();
-                u32x4_t pb[C::TS], pl[C::TS];
-                bool split = false;
-                // Iteration k (J = k % NKB): P.V of tile k-1, then (after tile
-                // k+1 has landed) the scores of tile k+1 on the matrix cores
-                // while the VALU turns tile k's scores (cur) into P.  Tile k+1's
-                // scores land in nxt; the unrolled loop alternates the two.
+                {
+                    const bool z0 = zero_dead_v_pipe(0);
+                    const bool z1 = zero_dead_v_pipe(1);
+                    if (z0 || z1) __syncthreads();
+                }
+                u32x4_t kf[C::KS];
+                f32x16_t S0[C::NB], S1[C::NB];
+                lds_read_b128_x8<0>(ka, kf);
+                qk_mma(kf, S0);
+                lds_read_b128_x8<C::TILE>(ka, kf);
                 auto step = [&](auto j_c, int k, f32x16_t (&cur)[C::NB], f32x16_t (&nxt)[C::NB]) {
                     constexpr int J = decltype(j_c)::value;
-                    constexpr int KOFF = ((J + 1) % C::NKB) * C::TILE;                     // K of tile k+1
-                    constexpr int VOFF = (C::NKB + (J + C::NVB - 1) % C::NVB) * C::TILE;   // V of tile k-1
+                    constexpr int VOFF = J * C::TILE;                             // V of tile k
+                    constexpr int KOFF = ((J + 2) % C::NKB) * C::TILE;            // K of tile k+2
+                    qk_mma(kf, nxt);                                              // scores of tile k+1
+                    __builtin_amdgcn_sched_barrier(0);
+                    u32x2_t vr0[8], vr1[8];
+                    lds_read_tr16_x16<VOFF, VOFF + 16 * kRowBytes>(va, vr0, vr1);
                     mask_scores(ig.t_begin + k, cur);
-                    if (J != 0 || k > 0) {
-                        pv_frags(va, std::integral_constant<int, VOFF>{}, pb);
-                        if (split) pv_frags(va, std::integral_constant<int, VOFF>{}, pl);
-                    }
                     raise_max(cur);
-                    // tile k+1 landed for this wave (tile k+2 may still be in flight) ...
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 2) * 2 * C::DMA_PER_WAVE));
-                    // ... and for every wave; every wave is past P.V of tile k-1
-                    // (K of tile k-1 and V of tile k-1 are free for tile k+3)
+                    u32x4_t pb[C::TS], pl[C::TS];
+                    const bool split = exp_pack(cur, pb, pl);
+                    if (!late_pv) {
+                        pv_mma(vr0, vr1, pb);
+                        if (split) pv_mma(vr0, vr1, pl);
+                    }
+                    // tile k+2 landed for this wave (tile k+3 may still be in
+                    // flight) ...
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 3) * 2 * C::DMA_PER_WAVE));
+                    // ... and for every wave; every wave has read tile k's V
+                    // (and, an iteration earlier, its K): its buffers take tile k+LEAD
                     barrier_no_fence();
-                    if (zero_dead_v_pipe(k + 1)) __syncthreads();
+                    if (zero_dead_v_pipe(k + 2)) __syncthreads();
                     dma_pipe(k + C::LEAD);
-                    qk_at(std::integral_constant<int, KOFF>{}, nxt);
-                    split = exp_pack(cur, pb, pl);
+                    if (late_pv) {
+                        pv_mma(vr0, vr1, pb);
+                        if (split) pv_mma(vr0, vr1, pl);
+                    }
+                    lds_read_b128_x8<KOFF>(ka, kf);
+                    __builtin_amdgcn_sched_barrier(0);
                 };
+                // the loop is unrolled over the ring (offsets are immediates)
                 using I0 = std::integral_constant<int, 0>;
                 using I1 = std::integral_constant<int, 1>;
                 using I2 = std::integral_constant<int, 2>;
                 using I3 = std::integral_constant<int, 3>;
-                static_assert(C::NKB == 4, "the loop below is unrolled four times");
-                f32x16_t S0[C::NB], S1[C::NB];
-                qk_at(I0{}, S0);
+                using I4 = std::integral_constant<int, 4>;
+                using I5 = std::integral_constant<int, 5>;
+                static_assert(C::NKB == 6, "the loop below is unrolled six times");
                 int k = 0;
-                for (; k + 4 <= n_it; k += 4) {
+                for (; k + 6 <= n_it; k += 6) {
                     step(I0{}, k, S0, S1);
                     step(I1{}, k + 1, S1, S0);
                     step(I2{}, k + 2, S0, S1);
                     step(I3{}, k + 3, S1, S0);
+                    step(I4{}, k + 4, S0, S1);
+                    step(I5{}, k + 5, S1, S0);
                 }
                 if (k < n_it) step(I0{}, k, S0, S1);
                 if (k + 1 < n_it) step(I1{}, k + 1, S1, S0);
                 if (k + 2 < n_it) step(I2{}, k + 2, S0, S1);
-                pv(v_lds(n_it - 1), pb, pl, split);
+                if (k + 3 < n_it) step(I3{}, k + 3, S1, S0);
+                if (k + 4 < n_it) step(I4{}, k + 4, S0, S1);
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the clamped prefetches past the end
                 __syncthreads();
             }
