@@ -119,6 +119,9 @@ struct MergeArgs {
 // many groups (prefill).
 hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, int batch, hipStream_t stream);
 int merge_rows_per_unit(int head_dim);
+// The published groups merged one row per unit (m.max_rows units per group),
+// each row's splits spread over the workgroup's threads.
+hipError_t launch_merge_rows(const MergeArgs& m, int head_dim, int grid, hipStream_t stream);
 
 hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int rw, int grid,
                               hipStream_t stream);

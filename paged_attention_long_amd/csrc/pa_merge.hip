@@ -229,9 +229,113 @@ __global__ __launch_bounds__(kMergeThreads) void merge_slots_kernel(MergeArgs m)
     }
 }
 
+
+// One row per unit, its splits spread over the workgroup: SG groups of D/4
+// threads each take every SG-th split of the row (kMaxSplits / SG partial
+// rows in flight per thread), and the groups' sums are added in LDS in group
+// order.  For launches with few rows and many splits (decode, verification,
+// mixed batches) this spreads the partial reads over many more workgroups
+// than units of several rows would.
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void merge_row_kernel(MergeArgs m) {
+    constexpr int EPR = D / 4;                    // float4 columns per row
+    constexpr int SG = kMergeThreads / EPR;       // split groups
+    constexpr int B = kMaxSplits / SG;            // partial rows in flight per thread
+    static_assert(SG * EPR == kMergeThreads && B * SG == kMaxSplits, "threads cover the row and the splits");
+    __shared__ float w_sh[kMaxSplits];
+    __shared__ float lse_sh;
+    __shared__ float4 red[SG][EPR];
+    __shared__ int n_sh;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int col = (tid % EPR) * 4;
+    const int sg = tid / EPR;
+
+    const int upg = m.max_rows;                   // units (rows) per group
+    const MergeDesc d_first = m.mdesc[min((int)(blockIdx.x / upg), m.desc_cap - 1)];
+    if (tid == 0) n_sh = __hip_atomic_load(m.mcount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (tid == 0) {
+        // the arrival turn and the clearing of the count, as in merge_kernel
+        const int nc = gridDim.x > 64 ? kMergeArrive : 1;
+        const int j = (int)(blockIdx.x % nc);
+        const int expect = (int)gridDim.x / nc + (j < (int)gridDim.x % nc ? 1 : 0);
+        int* c1 = m.mcount + kMergeArriveStride * (1 + j);
+        const int done = nc == 1 ? expect - 1 : __hip_atomic_fetch_add(c1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done == expect - 1) {
+            if (nc > 1) __hip_atomic_store(c1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int top = nc == 1 ? (int)gridDim.x : nc;
+            const int done2 = __hip_atomic_fetch_add(m.mcount + 1, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (done2 == top - 1) {
+                __hip_atomic_store(m.mcount + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(m.mcount, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+    const int64_t n_units = (int64_t)n_sh * upg;
+    MergeTarget tgt{m.out, m.lse, m.num_q_heads, m.group, 1.0f};
+    for (int64_t u = blockIdx.x; u < n_units; u += gridDim.x) {
+        const int gidx = (int)(u / upg);
+        const int r = (int)(u - (int64_t)gidx * upg);
+        const MergeDesc d = (u == blockIdx.x) ? d_first : m.mdesc[gidx];
+        if (r >= d.rows) continue;                    // uniform
+        const int S = d.n_splits;
+        const int64_t sstride = (int64_t)d.rstride * D;
+        // Branch-free requests: a split past the group's last re-reads the
+        // last one (finite, written this forward) with weight 0.
+        const float* src = m.ws_o + ((int64_t)d.first_item * d.rstride + r) * D + col;
+        float4 o[B];
+#pragma unroll
+        for (int k = 0; k < B; ++k) o[k] = *reinterpret_cast<const float4*>(src + (int64_t)min(sg + k * SG, S - 1) * sstride);
+        if (tid < kWave) {
+            const float ls = lane < S ? m.ws_lse[((int64_t)d.first_item + lane) * d.rstride + r] : kNegInf;
+            const float M = wave_max(ls);
+            const float w = (ls == kNegInf) ? 0.f : fast_exp2(ls - M);
+            const float L = wave_sum(w);
+            w_sh[lane] = (L > 0.f) ? w / L : 0.f;
+            if (lane == 0) lse_sh = (L > 0.f) ? M + fast_log2(L) : kNegInf;
+        }
+        __syncthreads();
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int k = 0; k < B; ++k) {
+            const float w = w_sh[sg + k * SG];   // 0 past the group's splits
+            acc.x = fmaf(w, o[k].x, acc.x);
+            acc.y = fmaf(w, o[k].y, acc.y);
+            acc.z = fmaf(w, o[k].z, acc.z);
+            acc.w = fmaf(w, o[k].w, acc.w);
+        }
+        red[sg][tid % EPR] = acc;
+        __syncthreads();
+        if (sg == 0) {
+            float4 t = red[0][tid];
+#pragma unroll
+            for (int q = 1; q < SG; ++q) {
+                const float4 v = red[q][tid];
+                t.x += v.x; t.y += v.y; t.z += v.z; t.w += v.w;
+            }
+            const int64_t orow = out_row(tgt, d.q_off, d.g, d.row0 + r);
+            const float sc = d.out_scale;
+            *reinterpret_cast<float4*>(m.out + orow * D + col) = make_float4(t.x * sc, t.y * sc, t.z * sc, t.w * sc);
+            if (m.lse != nullptr && tid == 0) {
+                const float l2 = lse_sh;
+                m.lse[orow] = (l2 == kNegInf) ? kNegInf : l2 * kLn2;
+            }
+        }
+        __syncthreads();   // w_sh and red are rewritten by the next unit
+    }
+}
+
 }  // namespace
 
 int merge_rows_per_unit(int head_dim) { return merge_rpu(head_dim); }
+
+hipError_t launch_merge_rows(const MergeArgs& m, int head_dim, int grid, hipStream_t stream) {
+    if (head_dim == 64) hipLaunchKernelGGL((merge_row_kernel<64>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+    else if (head_dim == 256) hipLaunchKernelGGL((merge_row_kernel<256>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+    else hipLaunchKernelGGL((merge_row_kernel<128>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+    return hipGetLastError();
+}
 
 hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, int batch, hipStream_t stream) {
     if (m.static_units > 0) {

@@ -437,7 +437,12 @@ int enqueue_forward(pa_handle* h, const ForwardCall& f, const LaunchPlan& lp) {
         const int batch = many ? 8 : (mgrid > h->cu_count ? 16 : 32);
         pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, f.out, f.lse, c.num_q_heads, G, h->merge_rows,
                         h->desc_cap, nullptr, 0, 1, 0, 0};
-        hipError_t e = pa::launch_merge(m, c.head_dim, mgrid, batch, st);
+        // Few units (decode, verification, mixed batches): one row per unit,
+        // each row's splits spread over a workgroup, up to two workgroups per CU.
+        const int64_t row_units = groups * h->merge_rows;
+        hipError_t e = many ? pa::launch_merge(m, c.head_dim, mgrid, batch, st)
+                            : pa::launch_merge_rows(m, c.head_dim,
+                                                    (int)std::max<int64_t>(1, std::min<int64_t>(2 * (int64_t)h->cu_count, row_units)), st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
     }
     return PA_OK;
