@@ -35,6 +35,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int kMinPagesPerSplit = 4;
 constexpr int kValuRowsMax = 8;   // rows per KV head handled by the VALU kernel under PA_PATH_AUTO
 constexpr int kValuMaxKeys = 16384;   // and visible keys (longer contexts go to the tile kernel)
+// A single sequence past this many tokens of block table goes to the tile
+// kernel even at a few rows per KV head: its one-sequence plan is a few
+// scalar instructions, and from about 1.5k keys on its forward is the shorter
+// one (4,097-token decode at 32/8 heads: 15.3 against 16.8 us; 1,025 tokens:
+// 14.0 against 13.7).  Batches keep kValuMaxKeys: their device plan costs the
+// tile kernel more (two 2,049-token sequences: 18.0 against 16.8 us).
+constexpr int kValuMaxKeysOne = 1536;
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -264,7 +271,7 @@ LaunchPlan plan_launches(const pa_handle* h, const ForwardCall& f) {
         lp.run_valu = !lp.run_mfma || rows_min <= kValuRowsMax;
     } else {
         lp.run_valu = rows_min <= kValuRowsMax;
-        lp.run_mfma = rows_max > kValuRowsMax || cap_tokens > kValuMaxKeys;
+        lp.run_mfma = rows_max > kValuRowsMax || cap_tokens > (f.num_seqs == 1 ? kValuMaxKeysOne : kValuMaxKeys);
         // A tile launch with 32-row items takes the few-row sequences as well:
         // a VALU launch before it on the same stream would add its whole
         // latency, and per key the tile kernel costs less.  (With prefill-sized

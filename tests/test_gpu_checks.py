@@ -41,7 +41,7 @@ def _checked_case(inp, extra_q: int = 0, **tuning):
 KINDS = {
     # (spec overrides, tuning): every kernel path
     "valu_planned": (dict(seq_lens=(3000, 700, 40), q_lens=(1, 1, 1)), dict(split_mode=2)),
-    "valu_static": (dict(seq_lens=(3000,), q_lens=(1,)), dict(split_mode=1)),
+    "valu_static": (dict(seq_lens=(3000,), q_lens=(1,)), dict(split_mode=1, path=pal.PA_PATH_VALU)),
     "tile_verify": (dict(seq_lens=(3000, 700), q_lens=(8, 4)), dict(path=pal.PA_PATH_MFMA)),
     "tile_fp8": (dict(seq_lens=(3000, 700), q_lens=(8, 4), kv_dtype="fp8_e4m3"), {}),
     "tile_int8": (dict(seq_lens=(3000, 700), q_lens=(8, 4), kv_dtype="int8"), {}),

@@ -176,7 +176,7 @@ def test_split_count_invariance(pps, mode):
 def test_rotating_batches_share_a_pool(mode):
     """Consecutive calls on different batches (split counters must reset)."""
     bs = generate(_spec(seq_lens=(2049,), q_lens=(1,)), batches=3)
-    c = GpuCase(bs, split_mode=mode)
+    c = GpuCase(bs, path=pal.PA_PATH_VALU, split_mode=mode)
     try:
         for i, b in enumerate(bs):
             ref_o, ref_l = oracle.attention(b)
@@ -201,8 +201,10 @@ def test_nhd_layout_through_strides():
 
 
 GRAPH_CASES = {
-    # static splits on 176 workgroups: fixed merge slots
+    # static splits on 176 workgroups (VALU path): fixed merge slots
     "decode_merge_slots": dict(seq_lens=(4097,), q_lens=(1,)),
+    # a single long decode sequence on the tile kernel, merged one row per unit
+    "decode_tile_row_merge": dict(seq_lens=(4097,), q_lens=(1,)),
     # static splits on a small grid: merged inside the attention kernel
     "decode_in_kernel_merge": dict(seq_lens=(1003,), q_lens=(1,)),
     # verification width: tile kernel, published groups, merge launch
@@ -217,6 +219,9 @@ GRAPH_CASES = {
 }
 
 
+GRAPH_TUNING = {"decode_merge_slots": dict(path=pal.PA_PATH_VALU)}
+
+
 @pytest.mark.parametrize("name", list(GRAPH_CASES))
 def test_graph_replay_matches_eager(name):
     """A captured forward replayed several times (eager work in between)
@@ -226,7 +231,7 @@ def test_graph_replay_matches_eager(name):
 
     inp = generate(_spec(**GRAPH_CASES[name]))[0]
     progress(f"graph replay {name}")
-    c = GpuCase([inp])
+    c = GpuCase([inp], **GRAPH_TUNING.get(name, {}))
     try:
         eager_o, eager_l = c.run()
         s = torch.cuda.Stream()
@@ -322,7 +327,7 @@ def test_fixed_merge_slots_do_not_leak_between_forwards():
     merge, or the second forward's direct output would be overwritten."""
     long = generate(_spec(seq_lens=(4097,), q_lens=(1,)))[0]
     short = generate(_spec(seq_lens=(40,), q_lens=(1,), seed=9))[0]
-    a = GpuCase([long], split_mode=1)
+    a = GpuCase([long], path=pal.PA_PATH_VALU, split_mode=1)
     b = GpuCase([short], handle=a.h)
     try:
         for i, (inp, case) in enumerate(((long, a), (short, b), (long, a), (short, b))):
