@@ -187,3 +187,35 @@ def test_mfma_deterministic():
         c.close()
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
     assert np.array_equal(l1.view(np.uint32), l2.view(np.uint32))
+
+
+ROW_MERGE = {
+    # head_dim 128 on the tile kernel: 128 tiles, two per split -> 64 splits
+    "d128_tile_64_splits": (dict(num_q_heads=32, num_kv_heads=8, seq_lens=(4096,), q_lens=(8,), q_dtype="f16",
+                                 kv_dtype="f16", k_outlier_frac=0.01), dict(kv_tiles_per_split=1)),
+    # head_dim 64 and 256 on the VALU kernel with the device plan and small splits
+    "d64_valu_planned": (dict(num_q_heads=8, num_kv_heads=2, head_dim=64, seq_lens=(2000, 900), q_lens=(4, 16),
+                              q_dtype="f16", kv_dtype="f16"), dict(split_mode=2, pages_per_split=2)),
+    "d256_valu_planned": (dict(num_q_heads=16, num_kv_heads=2, head_dim=256, seq_lens=(1500, 60), q_lens=(2, 1),
+                               kv_dtype="fp8_e4m3"), dict(split_mode=2, pages_per_split=2)),
+    # many groups: every unit of a wide grid loops over several rows
+    "d128_many_groups": (dict(num_q_heads=40, num_kv_heads=40, seq_lens=(3000, 2000, 900), q_lens=(8, 4, 2),
+                              q_dtype="f16", kv_dtype="f16"), dict(path=pal.PA_PATH_MFMA, kv_tiles_per_split=2)),
+}
+
+
+@pytest.mark.parametrize("name", list(ROW_MERGE))
+def test_row_merge_parity(name):
+    """The one-row-per-unit merge launch (each row's splits spread over the
+    workgroup's thread groups) at the 64-split limit, at head_dim 64 / 128 /
+    256, and over a grid whose workgroups take several rows."""
+    spec, tuning = ROW_MERGE[name]
+    inp = generate(_spec(name=name, **spec))[0]
+    progress(f"row merge {name}")
+    ref_o, ref_l = oracle.attention(inp)
+    c = GpuCase([inp], **tuning)
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare(name, inp.kv_dtype, out, lse, ref_o, ref_l)
