@@ -437,7 +437,8 @@ def kernel_roofline(prep_like: dict, tr: dict) -> dict:
 
 
 COPY_KERNEL_TAG = "neg_kernel"     # torch.neg: reads N bytes, writes N bytes
-OUR_KERNEL_TAGS = ("decode_valu_kernel", "tile_attn_kernel", "tile256_kernel", "merge_kernel", "merge_slots_kernel",
+OUR_KERNEL_TAGS = ("decode_valu_kernel", "tile_attn_kernel", "tile256_kernel", "merge_kernel", "merge_row_kernel",
+                   "merge_slots_kernel",
                    "append_kernel", "zero_words_kernel")
 
 
