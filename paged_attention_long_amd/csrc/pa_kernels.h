@@ -112,12 +112,11 @@ struct MergeArgs {
     MergeDesc* sdesc;
     int static_units, sdesc_upg, static_splits, static_rstride;
 };
-// batch: partial rows in flight per thread (8, 16 or 32).  32 covers the
-// split counts of decode and verification in one round trip at one resident
-// workgroup per CU; 16 and 8 keep the registers low enough for several
-// resident workgroups, for grids wider than the CUs and for launches with
-// many groups (prefill).
-hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, int batch, hipStream_t stream);
+// Fixed slots (m.static_units > 0): one workgroup per slot.  Otherwise the
+// published groups in units of merge_rows_per_unit rows, eight partial rows in
+// flight per thread (registers low enough for several resident workgroups:
+// launches with many groups, i.e. prefill).
+hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, hipStream_t stream);
 int merge_rows_per_unit(int head_dim);
 // The published groups merged one row per unit (m.max_rows units per group),
 // each row's splits spread over the workgroup's threads.

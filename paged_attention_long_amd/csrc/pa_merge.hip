@@ -337,22 +337,16 @@ hipError_t launch_merge_rows(const MergeArgs& m, int head_dim, int grid, hipStre
     return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, int batch, hipStream_t stream) {
+hipError_t launch_merge(const MergeArgs& m, int head_dim, int grid, hipStream_t stream) {
     if (m.static_units > 0) {
         if (head_dim == 64) hipLaunchKernelGGL((merge_slots_kernel<64>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
         else if (head_dim == 256) hipLaunchKernelGGL((merge_slots_kernel<256>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
         else hipLaunchKernelGGL((merge_slots_kernel<128>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
         return hipGetLastError();
     }
-    auto go = [&](auto d_c) {
-        constexpr int D = decltype(d_c)::value;
-        if (batch <= 8) hipLaunchKernelGGL((merge_kernel<D, 8>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
-        else if (batch <= 16) hipLaunchKernelGGL((merge_kernel<D, 16>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
-        else hipLaunchKernelGGL((merge_kernel<D, 32>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
-    };
-    if (head_dim == 64) go(std::integral_constant<int, 64>{});
-    else if (head_dim == 256) go(std::integral_constant<int, 256>{});
-    else go(std::integral_constant<int, 128>{});
+    if (head_dim == 64) hipLaunchKernelGGL((merge_kernel<64, 8>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+    else if (head_dim == 256) hipLaunchKernelGGL((merge_kernel<256, 8>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
+    else hipLaunchKernelGGL((merge_kernel<128, 8>), dim3(grid), dim3(kMergeThreads), 0, stream, m);
     return hipGetLastError();
 }
 

@@ -420,7 +420,7 @@ int enqueue_forward(pa_handle* h, const ForwardCall& f, const LaunchPlan& lp) {
         pa::MergeArgs m{h->ws_o,   h->ws_lse,   h->mdesc,     h->mcount,    f.out,       f.lse,
                         c.num_q_heads, G,       h->merge_rows, h->desc_cap, h->sdesc, (int)su,
                         h->sdesc_upg,  static_splits, h->r_max_valu};
-        hipError_t e = pa::launch_merge(m, c.head_dim, (int)su, 32, st);
+        hipError_t e = pa::launch_merge(m, c.head_dim, (int)su, st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
     } else if (need_merge_valu || run_mfma) {
         // Merges whatever split groups the launches above published.  Grid:
@@ -433,21 +433,18 @@ int enqueue_forward(pa_handle* h, const ForwardCall& f, const LaunchPlan& lp) {
             const int bm = pa::mfma_rows_per_item(h->mfma_wr);
             groups += (int64_t)c.num_kv_heads * ((f.num_tokens * G + bm - 1) / bm + num_seqs);
         }
-        // Many units (prefill): the low-register variant, four workgroups per
-        // CU (every workgroup also takes one turn on the shared arrival
-        // counter, so a wider grid costs more than it gains); otherwise at
-        // most two per CU, with fewer rows in flight per thread once the grid
-        // is wider than the CUs.
+        // Many units (prefill): units of a few rows, four workgroups per CU
+        // (every workgroup also takes one turn on the shared arrival counter,
+        // so a wider grid costs more than it gains).  Few units (decode,
+        // verification, mixed batches): one row per unit, each row's splits
+        // spread over a workgroup, up to two workgroups per CU.
         const int64_t units = groups * upg;
         const bool many = units > 4 * (int64_t)h->cu_count;
-        const int mgrid = (int)std::max<int64_t>(1, std::min<int64_t>((many ? 4 : 2) * (int64_t)h->cu_count, units));
-        const int batch = many ? 8 : (mgrid > h->cu_count ? 16 : 32);
         pa::MergeArgs m{h->ws_o, h->ws_lse, h->mdesc, h->mcount, f.out, f.lse, c.num_q_heads, G, h->merge_rows,
                         h->desc_cap, nullptr, 0, 1, 0, 0};
-        // Few units (decode, verification, mixed batches): one row per unit,
-        // each row's splits spread over a workgroup, up to two workgroups per CU.
         const int64_t row_units = groups * h->merge_rows;
-        hipError_t e = many ? pa::launch_merge(m, c.head_dim, mgrid, batch, st)
+        hipError_t e = many ? pa::launch_merge(m, c.head_dim,
+                                               (int)std::min<int64_t>(4 * (int64_t)h->cu_count, units), st)
                             : pa::launch_merge_rows(m, c.head_dim,
                                                     (int)std::max<int64_t>(1, std::min<int64_t>(2 * (int64_t)h->cu_count, row_units)), st);
         if (e != hipSuccess) return fail(h, PA_ERR_HIP, "merge launch failed: %s", hipGetErrorString(e));
