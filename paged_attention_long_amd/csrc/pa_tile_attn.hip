@@ -12,10 +12,13 @@
 //
 // Three shapes share the code:
 //   * WR = 8 (prefill, 16-bit caches): eight waves own 32 rows each
-//     (BM = 256), two per SIMD, and share 32-key tiles in a four-slot LDS
-//     ring filled three tiles ahead by asynchronous global->LDS loads; a
-//     software pipeline runs P.V of tile k-1, then the scores of tile k+1 on
-//     the matrix cores while the VALU turns tile k's scores into P;
+//     (BM = 256), two per SIMD, and share 32-key tiles in a six-slot LDS
+//     ring filled six tiles ahead by asynchronous global->LDS loads; a
+//     software pipeline puts the scores of tile k+1 on the matrix cores,
+//     reads tile k's V fragments while they run, turns tile k's scores into
+//     P on the VALU and runs P.V of tile k, then reads tile k+2's K
+//     fragments while P.V runs; the second wave of each SIMD issues its P.V
+//     after the per-tile barrier, a phase behind the first;
 //   * WR = 4 (prefill, fp8 caches): four waves own 32 rows each (BM = 128)
 //     and share 64-key tiles, loaded to registers, widened exactly (K to the
 //     query type, V to fp16) and written to LDS;
