@@ -59,7 +59,12 @@ constexpr int kDB = kD / 32;            // 32-wide head-dim blocks of O^T
 constexpr int kRowBytes = kD * 2;       // one 16-bit K or V row in LDS
 constexpr int kTile = kBN * kRowBytes;  // one K (or V) tile
 constexpr float kTau = 8.0f;            // lazy max: rescale when a score passes the reference by 2^8
-constexpr float kSplitBelow = 32.0f;    // weight sum (in units of the largest weight) below which P's rounding is added back
+// P.V also runs on P's rounding error while a row's weight sum is below
+// kSplitBelow times its largest weight.  Past that point the largest single
+// weight is at most 1/kSplitBelow of the sum, so rounding it to 16 bits
+// (relative 2^-9 for bf16) moves the output by at most 2^-9/8 |v| ~ 2.4e-4 |v|,
+// and the other weights' rounding errors are independent of it.
+constexpr float kSplitBelow = 8.0f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));

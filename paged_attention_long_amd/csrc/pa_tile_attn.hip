@@ -62,7 +62,12 @@ namespace pa {
 namespace {
 
 constexpr int kPage = 16;
-constexpr float kSplitBelow = 32.0f;   // weight sum (in units of the largest weight) below which P.V also runs on P's rounding error
+// P.V also runs on P's rounding error while a row's weight sum is below
+// kSplitBelow times its largest weight.  Past that point the largest single
+// weight is at most 1/kSplitBelow of the sum, so rounding it to 16 bits
+// (relative 2^-9 for bf16) moves the output by at most 2^-9/8 |v| ~ 2.4e-4 |v|,
+// and the other weights' rounding errors are independent of it.
+constexpr float kSplitBelow = 8.0f;
 constexpr float kTau = 8.0f;           // lazy max: rescale when a score passes the reference by 2^8
 constexpr int kRowBytes = 256;         // one K or V row in LDS: 128 16-bit elements
 
