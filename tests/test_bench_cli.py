@@ -88,7 +88,7 @@ def test_kernel_trace_parser_takes_dispatches_between_markers(tmp_path):
     kernels; per kernel the median duration and dispatches per forward."""
     rows = [("warm tile_attn_kernel<128, 3, 2, 1>(pa::DecodeArgs)", 0, 500)]
     t = 1000
-    names = ["tile_attn_kernel<128, 3, 2, 1>(pa::DecodeArgs)", "merge_kernel<128, 32>(pa::MergeArgs)"]
+    names = ["tile_attn_kernel<128, 3, 2, 1>(pa::DecodeArgs)", "merge_row_kernel<128>(pa::MergeArgs)"]
     for w, durs in (("mixed_fp8", (100, 10)), ("decode", (12, 5))):
         rows.append(("void at::native::bitwise_not_kernel(x)", t, t + 1)); t += 10
         for k in range(4):
@@ -106,7 +106,22 @@ def test_kernel_trace_parser_takes_dispatches_between_markers(tmp_path):
     assert m["kernels"]["tile_attn_kernel<128, 3, 2, 1>"]["per_forward"] == 1.0
     assert abs(m["kernels"]["tile_attn_kernel<128, 3, 2, 1>"]["median_us"] - 100.0015) < 1e-6
     assert abs(m["kernel_us_per_forward"] - (100.0015 + 10.0015)) < 1e-6
-    assert res["decode"]["kernels"]["merge_kernel<128, 32>"]["median_us"] < 6
+    assert res["decode"]["kernels"]["merge_row_kernel<128>"]["median_us"] < 6
+
+
+def test_every_launched_kernel_is_recognised():
+    """Each kernel the library launches has a tag the trace and counter
+    reductions know (an unrecognised one would drop out of the tables)."""
+    import re
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "paged_attention_long_amd", "csrc")):
+        if f.endswith(".hip"):
+            src = open(os.path.join(ROOT, "paged_attention_long_amd", "csrc", f)).read()
+            names |= set(re.findall(r"__global__[^;{]*?\bvoid\s+(\w+_kernel)\s*\(", src))
+    names.discard("debug_gather_kernel")   # test-only, never traced
+    assert len(names) >= 8, sorted(names)
+    for n in names:
+        assert any(tag == n for tag in bench.OUR_KERNEL_TAGS), n
 
 
 def test_default_run_is_the_mixed_batch():
