@@ -1186,10 +1186,11 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             // read (that read waits while P.V runs).  Tile k's K and V sit in
             // buffer k % NKB from its load (issued at iteration k - LEAD) until
             // its V fragments are read in iteration k.
-            // Page ids of the item's tiles and of the LEAD tiles prefetched past
-            // its end (those read the last visible page: in bounds, unused),
-            // staged in LDS when they fit; otherwise scalar loads per tile.
-            const int n_pid = (ig.t_end - ig.t_begin + C::LEAD) * PPT;
+            // Page ids of the item's tiles and of the LEAD + 1 tiles prefetched
+            // or fetched past its end (those read the last visible page: in
+            // bounds, unused), staged in LDS when they fit; otherwise scalar
+            // loads per tile.
+            const int n_pid = (ig.t_end - ig.t_begin + C::LEAD + 1) * PPT;
             const bool staged = n_pid <= C::PID_CAP;
             const int pid0 = ig.pg_first + ig.t_begin * PPT;
             if (staged)
@@ -1206,18 +1207,17 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 n_live = max(0, t_hi - t_lo);
             }
             const uint32_t ring32 = (uint32_t)(uintptr_t)(lds_void_t*)tiles;
-            auto dma_pipe = [&](int k) {
-                int pid[PPT];
-                if (staged) {
-                    static_assert(PPT == 2, "tiles of two pages");
-                    const int2 w = *reinterpret_cast<const int2*>(ipid + k * PPT);
-                    pid[0] = __builtin_amdgcn_readfirstlane(w.x);
-                    pid[1] = __builtin_amdgcn_readfirstlane(w.y);
-                } else {
-                    const int t = min(ig.t_begin + k, ig.t_end - 1);
-#pragma unroll
-                    for (int p = 0; p < PPT; ++p) pid[p] = tile_pid(t, p);
-                }
+            // page ids of tile k (its two pages), fetched a step before the
+            // loads that use them so the fetch's round trip is off the path
+            // between the barrier and the loads
+            auto pid_fetch = [&](int k) -> int2 {
+                static_assert(PPT == 2, "tiles of two pages");
+                if (staged) return *reinterpret_cast<const int2*>(ipid + k * PPT);
+                const int t = min(ig.t_begin + k, ig.t_end - 1);
+                return make_int2(tile_pid(t, 0), tile_pid(t, 1));
+            };
+            auto dma_pipe = [&](int k, int2 w) {
+                const int pid[PPT] = {__builtin_amdgcn_readfirstlane(w.x), __builtin_amdgcn_readfirstlane(w.y)};
                 uint8_t* kb = tiles + (k % C::NKB) * C::TILE;
                 uint8_t* vb = tiles + (C::NKB + k % C::NVB) * C::TILE;
 #pragma unroll
@@ -1279,7 +1279,8 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             if (n_it > 0) {
                 static_assert(C::LEAD == C::NKB, "tile k+LEAD reuses tile k's buffers");
 #pragma unroll
-                for (int k = 0; k < C::LEAD; ++k) dma_pipe(k);
+                for (int k = 0; k < C::LEAD; ++k) dma_pipe(k, pid_fetch(k));
+                int2 pid_nx = pid_fetch(C::LEAD);
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 2) * 2 * C::DMA_PER_WAVE));   // tiles 0 and 1 landed
                 __syncthreads();
                 {
@@ -1315,7 +1316,8 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                     // (and, an iteration earlier, its K): its buffers take tile k+LEAD
                     barrier_no_fence();
                     if (zero_dead_v_pipe(k + 2)) __syncthreads();
-                    dma_pipe(k + C::LEAD);
+                    dma_pipe(k + C::LEAD, pid_nx);
+                    pid_nx = pid_fetch(k + C::LEAD + 1);
                     if (late_pv) {
                         pv_mma(vr0, vr1, pb);
                         if (split) pv_mma(vr0, vr1, pl);
