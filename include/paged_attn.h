@@ -76,7 +76,10 @@ extern "C" {
 #define PA_CHECK_TOKENS    8   /* the q_lens add up to more than num_tokens */
 
 /* execution paths (pa_tuning_t.path) */
-#define PA_PATH_AUTO   0   /* VALU split-KV kernel for rows-per-KV-head <= 8, MFMA tile kernel above */
+#define PA_PATH_AUTO   0   /* head_dim 128: VALU split-KV kernel for <= 8 rows per KV head over a short
+                              block table (batches: <= 16,384 tokens; a single sequence: <= 1,536),
+                              MFMA tile kernel otherwise; head_dim 64: VALU; head_dim 256: VALU up
+                              to 64 rows per KV head, then the tile kernel past 8 */
 #define PA_PATH_VALU   1   /* every sequence through the VALU split-KV kernel (handles whose
                               max_q_len * Hq / Hkv is at most 64; else PA_ERR_UNSUPPORTED) */
 #define PA_PATH_MFMA   2   /* every sequence through the MFMA tile kernel (head_dim 128 or 256) */

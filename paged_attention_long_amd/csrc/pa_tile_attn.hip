@@ -1182,10 +1182,11 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             // waits while those MFMAs run); the VALU turns tile k's scores into
             // P; P.V of tile k goes to the matrix cores; past the barrier that
             // certifies tile k+2 for every wave (and frees tile k's buffers),
-            // tile k+4 is requested into them and tile k+2's K fragments are
-            // read (that read waits while P.V runs).  Tile k's K and V sit in
-            // buffer k % NKB from its load (issued at iteration k - LEAD) until
-            // its V fragments are read in iteration k.
+            // tile k+LEAD is requested into them and tile k+2's K fragments
+            // are read (that read waits while P.V runs).  Tile k's K and V sit
+            // in buffer k % NKB from its load (issued at iteration k - LEAD)
+            // until its V fragments are read in iteration k.  The second wave
+            // of each SIMD (waves NW/2 ..) issues its P.V after the barrier.
             // Page ids of the item's tiles and of the LEAD + 1 tiles prefetched
             // or fetched past its end (those read the last visible page: in
             // bounds, unused), staged in LDS when they fit; otherwise scalar
