@@ -219,3 +219,18 @@ def test_row_merge_parity(name):
     finally:
         c.close()
     compare(name, inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+def test_prefill_pipeline_unstaged_page_ids():
+    """A prefill item longer than the page-id staging area (more than 2,041
+    tiles of 32 keys in one split): the pipelined loop takes each tile's page
+    ids from the block table directly, a step ahead of its loads."""
+    inp = generate(_spec(num_q_heads=24, num_kv_heads=4, seq_lens=(70000,), q_lens=(64,), seed=23))[0]
+    progress("prefill, one split of ~2,190 tiles (page ids not staged)")
+    ref_o, ref_l = oracle.attention(inp)
+    c = GpuCase([inp], kv_tiles_per_split=100000)
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare("unstaged page ids", inp.kv_dtype, out, lse, ref_o, ref_l)
