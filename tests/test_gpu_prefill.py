@@ -234,3 +234,20 @@ def test_prefill_pipeline_unstaged_page_ids():
     finally:
         c.close()
     compare("unstaged page ids", inp.kv_dtype, out, lse, ref_o, ref_l)
+
+
+@pytest.mark.parametrize("kv", ["f16", "fp8_e4m3", "int8"])
+def test_verify_item_unstaged_page_ids(kv):
+    """A 32-row item longer than its page-id staging area (more than 511
+    tiles in one split): the register-staged (16-bit) and raw-staged
+    (one-byte) loops read each tile's page ids from the block table."""
+    inp = generate(_spec(num_q_heads=32, num_kv_heads=8, seq_lens=(20000,), q_lens=(8,), q_dtype="f16",
+                         kv_dtype=kv, k_outlier_frac=0.01, seed=29))[0]
+    progress(f"verify width, one split of 625 tiles (page ids not staged), {kv}")
+    ref_o, ref_l = oracle.attention(inp)
+    c = GpuCase([inp], kv_tiles_per_split=100000, path=pal.PA_PATH_MFMA)
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    compare(f"unstaged verify {kv}", inp.kv_dtype, out, lse, ref_o, ref_l)
