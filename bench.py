@@ -43,6 +43,7 @@ WORKLOADS = {
     "prefill_d256": "chunked prefill at head_dim 256: 2,048-token chunk on 65,536 cached, 16/2 heads, bf16 KV",
     "mixed_fp8": "mixed batch: 4 seqs, 200,001/131,076/32,776/4,097 tokens, q_len 1/4/8/1, 32/8 heads, fp8 e4m3 KV",
     "mixed_int8": "mixed batch as mixed_fp8 on an int8 KV cache with a fp32 scale per cached row",
+    "prefill_int8": "chunked prefill on an int8 KV cache (fp32 row scales): 2,048-token chunk on 65,536 cached, 24/4 heads, D 128",
     "append_fp8": "cache append: 64 seqs x 256 new rows, 8 KV heads, D 128, bf16 rows quantised into fp8 e4m3 pages",
 }
 # inputs as stored; every product is accumulated, and every softmax step computed, in fp32
@@ -83,7 +84,7 @@ PATHS = {"auto": 0, "valu": 1, "mfma": 2}
 # Workloads measured on the VALU path as well as on the automatic (MFMA tile) one.
 ALT_PATH_WORKLOADS = ("verify", "mixed_fp8")
 # workloads measured in TFLOP/s against the bf16 MFMA peak (the rest: KV bytes against HBM)
-FLOP_WORKLOADS = ("prefill", "prefill_d256")
+FLOP_WORKLOADS = ("prefill", "prefill_d256", "prefill_int8")
 # Timed regions per measurement: the median is reported, and the spread
 # (max - min) / median across them ("run it three times, watch the drift").
 REPEATS = 3
@@ -871,7 +872,7 @@ def profile_commands(workload: str, calib_mib: int = 512) -> list:
 # Per-configuration entries of the default run: steps sized so each timed
 # region lasts a few milliseconds.
 PER_CONFIG = {"tiny_decode": 300, "decode": 200, "verify": 60, "verify_window": 200, "prefill": 20,
-              "mixed_int8": 20, "prefill_d256": 20}
+              "mixed_int8": 20, "prefill_d256": 20, "prefill_int8": 10}
 CPU_BUDGET_HEADLINE_S = 10.0
 CPU_BUDGET_PER_CONFIG_S = 3.0
 

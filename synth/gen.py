@@ -368,6 +368,11 @@ NAMED_SPECS = {
         name="mixed_int8", num_q_heads=32, num_kv_heads=8, head_dim=128,
         seq_lens=(200001, 131076, 32776, 4097), q_lens=(1, 4, 8, 1),
         q_dtype="bf16", kv_dtype="int8", pool_pages=32768, seed=1006),
+    # the chunked prefill on the pages' int8 cache (codes and per-row scales
+    # read in place)
+    "prefill_int8": Spec(
+        name="prefill_int8", num_q_heads=24, num_kv_heads=4, head_dim=128,
+        seq_lens=(67584,), q_lens=(2048,), q_dtype="bf16", kv_dtype="int8", pool_pages=8192, seed=1008),
 }
 
 

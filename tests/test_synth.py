@@ -98,6 +98,7 @@ def test_outlier_positions():
     ("mixed_fp8", 753_561_600),
     ("mixed_int8", 777_110_400),
     ("prefill_d256", 138_412_032),
+    ("prefill_int8", 2 * 67_584 * 4 * (128 + 4)),
 ])
 def test_named_kv_bytes(name, kv_bytes):
     spec = NAMED_SPECS[name]
