@@ -388,7 +388,11 @@ struct Cfg {
     // ring of NKB buffers, V tiles in a ring of NVB, loads issued LEAD tiles
     // ahead; the item's page ids are staged in LDS (PID_CAP of them).  The
     // loop is unrolled over the ring, so buffer offsets are immediates.
-    static constexpr bool PIPE = (WR == 8) && !BYTE;
+    // fp8 caches join it with register-staged tiles: each wave brings its
+    // eighth of a tile through registers, widens it exactly to 16 bits and
+    // stores it into the ring slot (int8 keeps the 128-row items, whose row
+    // scales live beside the tile).
+    static constexpr bool PIPE = (WR == 8) && !INT8;
     static constexpr int NKB = 6, NVB = 6, LEAD = 6;
     static constexpr int PID_CAP = PIPE ? 4096 : (WR == 1 ? 1024 : 1);
     static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : (FSTAGE ? 16 : WK * GROUP_LDS);
@@ -1217,6 +1221,31 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 const int t = min(ig.t_begin + k, ig.t_end - 1);
                 return make_int2(tile_pid(t, 0), tile_pid(t, 1));
             };
+            // one-byte caches: wave wig brings tile rows 4 wig .. 4 wig + 3
+            // (8 bytes of K and of V per lane, 8-element chunk lane % 16 of
+            // row 4 wig + lane / 16) through register set R, then stores them
+            // widened to 16 bits at their swizzled place in the tile's slot
+            [[maybe_unused]] u32x2_t rk[2], rv[2];
+            [[maybe_unused]] uint32_t boff = 0, lds_off = 0;
+            if constexpr (C::BYTE) {
+                const int key = 4 * wig + (lane >> 4), c8 = lane & 15;
+                boff = (uint32_t)(head_off + (int64_t)(key % kPage) * tok_bytes + c8 * 8);
+                lds_off = (uint32_t)swz(key, c8);
+            }
+            auto reg_load = [&](auto r_c, int2 w) {
+                constexpr int R = decltype(r_c)::value;
+                static_assert(PPT == 2 && C::NW == 8, "rows 0-15 come from the first page, 16-31 the second");
+                const int64_t pb = (int64_t)__builtin_amdgcn_readfirstlane(wig < 4 ? w.x : w.y) * page_bytes;
+                rk[R] = load_b64(kbase + pb + boff);
+                rv[R] = load_b64(vbase + pb + boff);
+            };
+            auto reg_store = [&](auto r_c, int k) {
+                constexpr int R = decltype(r_c)::value;
+                uint8_t* kb = tiles + (k % C::NKB) * C::TILE;
+                uint8_t* vb = tiles + (C::NKB + k % C::NVB) * C::TILE;
+                *reinterpret_cast<u32x4_t*>(kb + lds_off) = widen8<QT, KVT>(rk[R]);
+                *reinterpret_cast<u32x4_t*>(vb + lds_off) = widen8<C::PVT, KVT>(rv[R]);
+            };
             auto dma_pipe = [&](int k, int2 w) {
                 const int pid[PPT] = {__builtin_amdgcn_readfirstlane(w.x), __builtin_amdgcn_readfirstlane(w.y)};
                 uint8_t* kb = tiles + (k % C::NKB) * C::TILE;
@@ -1279,11 +1308,27 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             const int n_it = ig.t_end - ig.t_begin;
             if (n_it > 0) {
                 static_assert(C::LEAD == C::NKB, "tile k+LEAD reuses tile k's buffers");
+                using R0 = std::integral_constant<int, 0>;
+                using R1 = std::integral_constant<int, 1>;
+                int2 pid_nx;
+                if constexpr (C::BYTE) {
+                    // tiles 0 and 1 stored, 2 and 3 in registers (tile t in set t % 2)
+                    reg_load(R0{}, pid_fetch(0));
+                    reg_load(R1{}, pid_fetch(1));
+                    reg_store(R0{}, 0);
+                    reg_store(R1{}, 1);
+                    reg_load(R0{}, pid_fetch(2));
+                    reg_load(R1{}, pid_fetch(3));
+                    pid_nx = pid_fetch(4);
+                    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wave's stores are done
+                    barrier_no_fence();
+                } else {
 #pragma unroll
-                for (int k = 0; k < C::LEAD; ++k) dma_pipe(k, pid_fetch(k));
-                int2 pid_nx = pid_fetch(C::LEAD);
-                __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 2) * 2 * C::DMA_PER_WAVE));   // tiles 0 and 1 landed
-                __syncthreads();
+                    for (int k = 0; k < C::LEAD; ++k) dma_pipe(k, pid_fetch(k));
+                    pid_nx = pid_fetch(C::LEAD);
+                    __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 2) * 2 * C::DMA_PER_WAVE));   // tiles 0 and 1 landed
+                    __syncthreads();
+                }
                 {
                     const bool z0 = zero_dead_v_pipe(0);
                     const bool z1 = zero_dead_v_pipe(1);
@@ -1310,15 +1355,27 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                         pv_mma(vr0, vr1, pb);
                         if (split) pv_mma(vr0, vr1, pl);
                     }
-                    // tile k+2 landed for this wave (tile k+3 may still be in
-                    // flight) ...
-                    __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 3) * 2 * C::DMA_PER_WAVE));
-                    // ... and for every wave; every wave has read tile k's V
-                    // (and, an iteration earlier, its K): its buffers take tile k+LEAD
-                    barrier_no_fence();
-                    if (zero_dead_v_pipe(k + 2)) __syncthreads();
-                    dma_pipe(k + C::LEAD, pid_nx);
-                    pid_nx = pid_fetch(k + C::LEAD + 1);
+                    if constexpr (C::BYTE) {
+                        // tile k+2 (in registers since iteration k-2) into the
+                        // slot tile k-4 held; tile k+4 requested into its set
+                        using RJ = std::integral_constant<int, J % 2>;
+                        reg_store(RJ{}, k + 2);
+                        reg_load(RJ{}, pid_nx);
+                        pid_nx = pid_fetch(k + 5);
+                        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);   // this wave's stores are done
+                        barrier_no_fence();                       // ... and every wave's
+                        if (zero_dead_v_pipe(k + 2)) __syncthreads();
+                    } else {
+                        // tile k+2 landed for this wave (tile k+3 may still be in
+                        // flight) ...
+                        __builtin_amdgcn_s_waitcnt(waitcnt_vm((C::LEAD - 3) * 2 * C::DMA_PER_WAVE));
+                        // ... and for every wave; every wave has read tile k's V
+                        // (and, an iteration earlier, its K): its buffers take tile k+LEAD
+                        barrier_no_fence();
+                        if (zero_dead_v_pipe(k + 2)) __syncthreads();
+                        dma_pipe(k + C::LEAD, pid_nx);
+                        pid_nx = pid_fetch(k + C::LEAD + 1);
+                    }
                     if (late_pv) {
                         pv_mma(vr0, vr1, pb);
                         if (split) pv_mma(vr0, vr1, pl);
@@ -1664,6 +1721,10 @@ static bool with_kernel(int kv_dtype, int q_dtype, int wr, F&& f) {
     if (wr == 4 && fp8) {
         if (q_dtype == PA_DTYPE_BF16) return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, 4>{}), true;
         return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, 4>{}), true;
+    }
+    if (wr == 8 && fp8) {
+        if (q_dtype == PA_DTYPE_BF16) return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, 8>{}), true;
+        return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, 8>{}), true;
     }
     if (wr == 8 && !fp8) {
         if (kv_dtype == PA_DTYPE_F16) return f(KernelTag<PA_DTYPE_F16, PA_DTYPE_F16, 8>{}), true;
