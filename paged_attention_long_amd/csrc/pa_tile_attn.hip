@@ -388,17 +388,17 @@ struct Cfg {
     // ring of NKB buffers, V tiles in a ring of NVB, loads issued LEAD tiles
     // ahead; the item's page ids are staged in LDS (PID_CAP of them).  The
     // loop is unrolled over the ring, so buffer offsets are immediates.
-    // fp8 caches join it with register-staged tiles: each wave brings its
-    // eighth of a tile through registers, widens it exactly to 16 bits and
-    // stores it into the ring slot (int8 keeps the 128-row items, whose row
-    // scales live beside the tile).
-    static constexpr bool PIPE = (WR == 8) && !INT8;
+    // One-byte caches join it with register-staged tiles: each wave brings
+    // its eighth of a tile through registers, widens it exactly to 16 bits
+    // and stores it into the ring slot (int8: with its rows' K and V scales
+    // into the slot's scale array).
+    static constexpr bool PIPE = (WR == 8);
     static constexpr int NKB = 6, NVB = 6, LEAD = 6;
     static constexpr int PID_CAP = PIPE ? 4096 : (WR == 1 ? 1024 : 1);
     static constexpr int TILES_LDS = PIPE ? (NKB + NVB) * TILE : (FSTAGE ? 16 : WK * GROUP_LDS);
     // int8 row scales of a tile: BN K scales then BN V scales, per staging
     // slot (FSTAGE) or per wave group's LDS tile
-    static constexpr int SC_FLOATS = INT8 ? (FSTAGE ? WK * 2 : WK) * 2 * BN : 4;
+    static constexpr int SC_FLOATS = INT8 ? (PIPE ? NKB : FSTAGE ? WK * 2 : WK) * 2 * BN : 4;
 };
 
 template <int KVT>
@@ -1225,8 +1225,12 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             // (8 bytes of K and of V per lane, 8-element chunk lane % 16 of
             // row 4 wig + lane / 16) through register set R, then stores them
             // widened to 16 bits at their swizzled place in the tile's slot
+            // (int8: lanes 0-7 also bring the K (lanes 0-3) and V (4-7) row
+            // scales of the wave's four rows; a dead key's V scale is stored as 0)
             [[maybe_unused]] u32x2_t rk[2], rv[2];
+            [[maybe_unused]] float rsc[2] = {0.f, 0.f};
             [[maybe_unused]] uint32_t boff = 0, lds_off = 0;
+            const int skey = 4 * wig + (lane & 3);   // int8: the key of this lane's scale
             if constexpr (C::BYTE) {
                 const int key = 4 * wig + (lane >> 4), c8 = lane & 15;
                 boff = (uint32_t)(head_off + (int64_t)(key % kPage) * tok_bytes + c8 * 8);
@@ -1235,9 +1239,14 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
             auto reg_load = [&](auto r_c, int2 w) {
                 constexpr int R = decltype(r_c)::value;
                 static_assert(PPT == 2 && C::NW == 8, "rows 0-15 come from the first page, 16-31 the second");
-                const int64_t pb = (int64_t)__builtin_amdgcn_readfirstlane(wig < 4 ? w.x : w.y) * page_bytes;
+                const int pid = __builtin_amdgcn_readfirstlane(wig < 4 ? w.x : w.y);
+                const int64_t pb = (int64_t)pid * page_bytes;
                 rk[R] = load_b64(kbase + pb + boff);
                 rv[R] = load_b64(vbase + pb + boff);
+                if constexpr (C::INT8) {
+                    if (lane < 8)
+                        rsc[R] = __builtin_nontemporal_load(row_scale_ptr(pid, skey % kPage) + (lane >= 4 ? a.rs_v : 0));
+                }
             };
             auto reg_store = [&](auto r_c, int k) {
                 constexpr int R = decltype(r_c)::value;
@@ -1245,6 +1254,15 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 uint8_t* vb = tiles + (C::NKB + k % C::NVB) * C::TILE;
                 *reinterpret_cast<u32x4_t*>(kb + lds_off) = widen8<QT, KVT>(rk[R]);
                 *reinterpret_cast<u32x4_t*>(vb + lds_off) = widen8<C::PVT, KVT>(rv[R]);
+                if constexpr (C::INT8) {
+                    if (lane < 8) {
+                        const int j = key_pos(ig.t_begin + k, skey);
+                        const bool live = (j >= ig.si.lo) && (j < ig.si.seq_len) &&
+                                          (ig.pg_first + (ig.t_begin + k) * PPT + skey / kPage < ig.pg_end);
+                        tscale[(k % C::NKB) * 2 * BN + (lane >= 4 ? BN : 0) + skey] =
+                            (lane >= 4 && !live) ? 0.f : rsc[R];
+                    }
+                }
             };
             auto dma_pipe = [&](int k, int2 w) {
                 const int pid[PPT] = {__builtin_amdgcn_readfirstlane(w.x), __builtin_amdgcn_readfirstlane(w.y)};
@@ -1347,10 +1365,12 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                     __builtin_amdgcn_sched_barrier(0);
                     u32x2_t vr0[8], vr1[8];
                     lds_read_tr16_x16<VOFF, VOFF + 16 * kRowBytes>(va, vr0, vr1);
+                    [[maybe_unused]] const float* tsc_k = tscale + (J % C::NKB) * 2 * BN;   // int8: tile k's scales
+                    if constexpr (C::INT8) apply_kscale(cur, tsc_k);
                     mask_scores(ig.t_begin + k, cur);
                     raise_max(cur);
                     u32x4_t pb[C::TS], pl[C::TS];
-                    const bool split = exp_pack(cur, pb, pl);
+                    const bool split = exp_pack(cur, pb, pl, C::INT8 ? tsc_k + BN : nullptr);
                     if (!late_pv) {
                         pv_mma(vr0, vr1, pb);
                         if (split) pv_mma(vr0, vr1, pl);
@@ -1704,12 +1724,14 @@ struct KernelTag {
 template <typename F>
 static bool with_kernel(int kv_dtype, int q_dtype, int wr, F&& f) {
     const bool fp8 = kv_dtype == PA_DTYPE_FP8_E4M3;
-    if (kv_dtype == PA_DTYPE_INT8 && (wr == 1 || wr == 4)) {
+    if (kv_dtype == PA_DTYPE_INT8 && (wr == 1 || wr == 4 || wr == 8)) {
         if (q_dtype == PA_DTYPE_BF16) {
             if (wr == 1) return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_BF16, 1>{}), true;
+            if (wr == 8) return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_BF16, 8>{}), true;
             return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_BF16, 4>{}), true;
         }
         if (wr == 1) return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_F16, 1>{}), true;
+        if (wr == 8) return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_F16, 8>{}), true;
         return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_F16, 4>{}), true;
     }
     if (wr == 1) {

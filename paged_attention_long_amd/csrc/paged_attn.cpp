@@ -124,8 +124,8 @@ void size_handle(pa_handle* h, const pa_config_t* cfg, int cu_count) {
     h->r_max_valu = (int)(h->valu_all_ok ? rows_max : kValuRowsMax);
     h->max_items_valu = grid_cap + cfg->max_num_seqs * cfg->num_kv_heads;
     // rows per tile-kernel item: 32 (verification widths), else 256 rows over
-    // eight waves (16-bit and fp8 caches) and 128 over four for int8
-    h->mfma_wr = rows_max > 64 ? (cfg->kv_dtype == PA_DTYPE_INT8 ? 4 : 8) : 1;
+    // eight waves
+    h->mfma_wr = rows_max > 64 ? 8 : 1;
     if (D == 256) h->mfma_wr = 4;   // the head_dim 256 tile kernel: 128-row items
     // The tile kernel launches exactly one round of resident workgroups; its
     // in-kernel plan sizes the splits for that many items.
