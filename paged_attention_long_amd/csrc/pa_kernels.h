@@ -125,9 +125,9 @@ hipError_t launch_merge_rows(const MergeArgs& m, int head_dim, int grid, hipStre
 hipError_t launch_decode_valu(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int rw, int grid,
                               hipStream_t stream);
 
-// wr: waves along query rows (8: 256-row blocks for prefill on 16-bit caches;
-// 4: 128-row blocks for prefill on fp8 caches; 1: 32-row blocks, four waves
-// splitting the keys, for verification widths and few-row sequences).
+// wr: waves along query rows (8: 256-row blocks for prefill, every cache
+// type; 1: 32-row blocks, four waves splitting the keys, for verification
+// widths and few-row sequences).
 hipError_t launch_mfma_attn(const DecodeArgs& a, int head_dim, int kv_dtype, int q_dtype, int wr, int grid,
                             hipStream_t stream);
 int mfma_rows_per_item(int wr);

@@ -10,18 +10,17 @@
 // "Prefill: teach the fork's fast kernel to read the int8 cache": 16 to 64
 // query rows per tile was 1.8x there).
 //
-// Three shapes share the code:
-//   * WR = 8 (prefill, 16-bit caches): eight waves own 32 rows each
-//     (BM = 256), two per SIMD, and share 32-key tiles in a six-slot LDS
-//     ring filled six tiles ahead by asynchronous global->LDS loads; a
+// Two shapes share the code:
+//   * WR = 8 (prefill): eight waves own 32 rows each (BM = 256), two per
+//     SIMD, and share 32-key tiles in a six-slot LDS ring, filled six tiles
+//     ahead by asynchronous global->LDS loads (16-bit caches) or by the waves
+//     themselves, each widening an eighth of a tile exactly to 16 bits
+//     through registers (one-byte caches; int8 row scales beside the slot); a
 //     software pipeline puts the scores of tile k+1 on the matrix cores,
 //     reads tile k's V fragments while they run, turns tile k's scores into
 //     P on the VALU and runs P.V of tile k, then reads tile k+2's K
 //     fragments while P.V runs; the second wave of each SIMD issues its P.V
 //     after the per-tile barrier, a phase behind the first;
-//   * WR = 4 (prefill, fp8 caches): four waves own 32 rows each (BM = 128)
-//     and share 64-key tiles, loaded to registers, widened exactly (K to the
-//     query type, V to fp16) and written to LDS;
 //   * WR = 1 (verification widths and few-row sequences, <= 64 rows per KV
 //     head): each wave owns the same 32 rows and streams its own 32-key
 //     tiles, so the tile loop has no workgroup barrier; the four waves'
@@ -348,7 +347,8 @@ struct Cfg {
     static constexpr int NTH = 64 * NW;                    // threads per workgroup
     static_assert(NTH == tile_threads<WR>(), "launch bounds");
     static constexpr int WK = NW / WR;                     // wave groups along keys
-    static constexpr int BN = (WR == 4) ? 64 : 32;         // keys per tile
+    static_assert(WR == 1 || WR == 8, "items of 32 rows (four key streams) or 256 rows (eight waves)");
+    static constexpr int BN = 32;                          // keys per tile
     static constexpr int PPT = BN / kPage;                 // pages per tile
     static constexpr int BM = 32 * WR;                     // query rows per item
     static constexpr int NT = 64 * WR;                     // threads per wave group
@@ -367,8 +367,6 @@ struct Cfg {
     static constexpr int TILE = BN * kRowBytes;            // bytes of one K (or V) tile in LDS
     static constexpr int GROUP_LDS = 2 * TILE;             // a wave group's K and V tile in LDS
     static constexpr int DMA_PER_WAVE = BN * kRowBytes / 1024 / WR;   // 1 KB async loads per wave per tile
-    // fp8 register staging: 8-element chunks per thread per tile
-    static constexpr int FCH = BN * (D / 8) / NT;
     // fp8 at WR = 1: raw tiles reach LDS by asynchronous loads into two
     // staging slots per wave (K then V, 8 KB a slot); both operands are read
     // raw (V by 8-bit transposing reads) and widened in registers at their
@@ -866,55 +864,9 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
         auto row_scale_ptr = [&](int pid, int slot) {
             return a.row_scale + (int64_t)pid * a.rs_page + (int64_t)ig.g * a.rs_head + (int64_t)slot * a.rs_tok;
         };
-        // one-byte caches at 128-row items: registers, widened, then written
-        // in the same layout; int8 row scales go to the group's scale array
-        // (threads 0 .. BN-1 a key's K scale, BN .. 2BN-1 its V scale).
-        typename Raw<KVT>::T fk[C::FCH], fv[C::FCH];
-        float fsc = 0.f;
+        // int8: the wave group's scale array (32-row items: the tile's K
+        // scales, then its V scales)
         float* tsc_group = tscale + (C::FSTAGE ? 0 : gi * 2 * BN);
-        auto fp8_load = [&](int t) {
-            int pid[PPT];
-#pragma unroll
-            for (int p = 0; p < PPT; ++p) pid[p] = tile_pid(t, p);
-#pragma unroll
-            for (int c = 0; c < C::FCH; ++c) {
-                const int ch = gtid + c * C::NT;
-                const int key = ch / (D / 8), e = ch % (D / 8);
-                if constexpr (C::BYTE) {
-                    fk[c] = load_b64(row_src(kbase, pid, key) + e * 8);
-                    fv[c] = load_b64(row_src(vbase, pid, key) + e * 8);
-                }
-            }
-            if constexpr (C::INT8) {
-                if (gtid < 2 * BN) {
-                    const int key = gtid % BN;
-                    fsc = __builtin_nontemporal_load(row_scale_ptr(pid[key / kPage], key % kPage) +
-                                                     (gtid >= BN ? a.rs_v : 0));
-                }
-            }
-        };
-        auto fp8_store = [&](int buf, int t) {
-#pragma unroll
-            for (int c = 0; c < C::FCH; ++c) {
-                const int ch = gtid + c * C::NT;
-                const int key = ch / (D / 8), e = ch % (D / 8);
-                if constexpr (C::BYTE) {
-                    *reinterpret_cast<u32x4_t*>(kbuf(buf) + swz(key, e)) = widen8<QT, KVT>(fk[c]);
-                    *reinterpret_cast<u32x4_t*>(vbuf(buf) + swz(key, e)) = widen8<C::PVT, KVT>(fv[c]);
-                }
-            }
-            if constexpr (C::INT8) {
-                // a dead key's V scale (maybe NaN) is stored as 0, by the
-                // thread that stores it
-                if (gtid < 2 * BN) {
-                    const int key = gtid % BN;
-                    const int j = key_pos(t, 0) + key;
-                    const bool live = (j >= ig.si.lo) && (j < ig.si.seq_len) &&
-                                      (ig.pg_first + t * PPT + key / kPage < ig.pg_end);
-                    tsc_group[gtid] = (gtid >= BN && !live) ? 0.f : fsc;
-                }
-            }
-        };
         // fp8 staging (FSTAGE): async load i of a raw K or V tile covers rows
         // 8i .. 8i+7 (128 B each), lane l row 8i + l/8.  Rows are stored with
         // 16-byte unit u at position u ^ (row & 7), so the operand reads (one
@@ -1568,18 +1520,7 @@ __global__ __launch_bounds__(tile_threads<WR>()) void tile_attn_kernel(DecodeArg
                 __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the clamped loads past the end
             }
         } else {
-            if (n_iter > 0) fp8_load(min(my_first, ig.t_end - 1));
-            for (int iter = 0; iter < n_iter; ++iter) {
-                const int t = my_first + iter * C::WK;
-                const bool have = t < ig.t_end;
-                if constexpr (WR > 1) __syncthreads();
-                fp8_store(0, t);
-                if (have) zero_dead_v(t, 0);
-                group_sync();
-                if (iter + 1 < n_iter) fp8_load(min(t + C::WK, ig.t_end - 1));
-                if (have) compute_tile(t, kbuf(0), vbuf(0));
-                if constexpr (WR == 1) __builtin_amdgcn_wave_barrier();
-            }
+            static_assert(C::PIPE || WR == 1, "items of 32 or 256 rows");
         }
 
         // ------------------------------------------------------------ finish the rows
@@ -1713,9 +1654,8 @@ static int blocks_per_cu_t(size_t dyn_lds) {
     return (e == hipSuccess && n > 0) ? n : 1;
 }
 
-// Instantiations by rows per item: 32-row items (WR = 1) for every cache type;
-// 128-row items (WR = 4) for fp8 caches; 256-row items (WR = 8) for 16-bit
-// caches.  f(tag) is called with the kernel's template arguments as types.
+// Instantiations by rows per item: 32-row items (WR = 1) and 256-row items
+// (WR = 8) for every cache type.  f(tag) is called with the kernel's template arguments as types.
 template <int KVT, int QT, int WR>
 struct KernelTag {
     static constexpr int kvt = KVT, qt = QT, wr = WR;
@@ -1724,25 +1664,19 @@ struct KernelTag {
 template <typename F>
 static bool with_kernel(int kv_dtype, int q_dtype, int wr, F&& f) {
     const bool fp8 = kv_dtype == PA_DTYPE_FP8_E4M3;
-    if (kv_dtype == PA_DTYPE_INT8 && (wr == 1 || wr == 4 || wr == 8)) {
+    if (kv_dtype == PA_DTYPE_INT8 && (wr == 1 || wr == 8)) {
         if (q_dtype == PA_DTYPE_BF16) {
             if (wr == 1) return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_BF16, 1>{}), true;
-            if (wr == 8) return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_BF16, 8>{}), true;
-            return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_BF16, 4>{}), true;
+            return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_BF16, 8>{}), true;
         }
         if (wr == 1) return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_F16, 1>{}), true;
-        if (wr == 8) return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_F16, 8>{}), true;
-        return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_F16, 4>{}), true;
+        return f(KernelTag<PA_DTYPE_INT8, PA_DTYPE_F16, 8>{}), true;
     }
     if (wr == 1) {
         if (kv_dtype == PA_DTYPE_F16) return f(KernelTag<PA_DTYPE_F16, PA_DTYPE_F16, 1>{}), true;
         if (kv_dtype == PA_DTYPE_BF16) return f(KernelTag<PA_DTYPE_BF16, PA_DTYPE_BF16, 1>{}), true;
         if (q_dtype == PA_DTYPE_BF16) return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, 1>{}), true;
         return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, 1>{}), true;
-    }
-    if (wr == 4 && fp8) {
-        if (q_dtype == PA_DTYPE_BF16) return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, 4>{}), true;
-        return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_F16, 4>{}), true;
     }
     if (wr == 8 && fp8) {
         if (q_dtype == PA_DTYPE_BF16) return f(KernelTag<PA_DTYPE_FP8_E4M3, PA_DTYPE_BF16, 8>{}), true;

@@ -31,7 +31,7 @@ CASES = {
     "verify8_window": dict(seq_lens=(7000,), q_lens=(8,), window=900, poison_out_of_window=True, k_outlier_frac=0.01),
     "verify16_mixed": dict(seq_lens=(4000, 1200, 16), q_lens=(16, 9, 16), k_outlier_frac=0.01),
     "f16q_verify": dict(seq_lens=(2500, 50), q_lens=(8, 4), q_dtype="f16", window=300, poison_out_of_window=True),
-    # prefill widths (128-row items, widened into LDS)
+    # prefill widths (256-row items, tiles widened into the pipelined ring)
     "prefill_g6": dict(num_q_heads=24, num_kv_heads=4, seq_lens=(3000,), q_lens=(300,), k_outlier_frac=0.01),
     "prefill_window_f16q": dict(num_q_heads=24, num_kv_heads=4, seq_lens=(2000, 700), q_lens=(100, 40),
                                 q_dtype="f16", window=500, poison_out_of_window=True),

@@ -42,7 +42,7 @@ CASES = {
                   [pal.PA_PATH_AUTO, pal.PA_PATH_VALU]),
     # 256-row prefill items (the pipelined ring)
     "bf16_prefill": (dict(num_q_heads=24, num_kv_heads=4, seq_lens=(3000,), q_lens=(300,)), [pal.PA_PATH_AUTO]),
-    # 128-row fp8 prefill items
+    # fp8 prefill on the 256-row pipelined ring (register-staged tiles)
     "fp8_prefill": (dict(num_q_heads=24, num_kv_heads=4, seq_lens=(2000, 700), q_lens=(100, 40),
                          kv_dtype="fp8_e4m3"), [pal.PA_PATH_AUTO]),
 }

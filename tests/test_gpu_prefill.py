@@ -74,8 +74,9 @@ def test_prefill_named_dense_rows():
 
 
 def test_prefill_int8_named_dense_rows():
-    """The same chunk on the int8 cache with per-row scales (the 128-row
-    one-byte tile kernel): every 16th token and the last, all 24 heads."""
+    """The same chunk on the int8 cache with per-row scales (the pipelined
+    256-row loop on register-staged, widened tiles): every 16th token and the
+    last, all 24 heads."""
     inp = named("prefill_int8")[0]
     progress("prefill int8 named dense rows")
     toks = sorted(set(list(range(0, 2048, 16)) + [1, 2047]))
