@@ -91,6 +91,24 @@ def test_prefill_int8_named_dense_rows():
     compare("prefill int8", inp.kv_dtype, out, lse, None, None, rows=ref)
 
 
+def test_prefill_fp8_named_dense_rows():
+    """The same chunk on an fp8 cache (per-head scales; tiles widened through
+    registers into the pipelined ring): every 16th token and the last, all 24
+    heads."""
+    inp = named("prefill", kv_dtype="fp8_e4m3", seed=1009)[0]
+    progress("prefill fp8 named dense rows")
+    toks = sorted(set(list(range(0, 2048, 16)) + [1, 2047]))
+    rows = [(t, h) for t in toks for h in range(inp.num_q_heads)]
+    ref = oracle.attention_rows(inp, rows)
+    c = GpuCase([inp])
+    try:
+        out, lse = c.run()
+    finally:
+        c.close()
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+    compare("prefill fp8", inp.kv_dtype, out, lse, None, None, rows=ref)
+
+
 VERIFY = {
     "f16_q8": dict(num_q_heads=32, num_kv_heads=8, seq_lens=(5000,), q_lens=(8,), q_dtype="f16", kv_dtype="f16",
                    k_outlier_frac=0.01),
